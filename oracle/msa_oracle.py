@@ -1,0 +1,238 @@
+"""CPU oracle for the MiniMax Sparse Attention (MSA) forward pass.
+
+TEST INFRASTRUCTURE ONLY.  This is the plain, slow, obviously correct
+definition of what the MSA forward computes, in float64 numpy.  Only the test
+suite, the smoke check and the benchmark's CPU-baseline leg may import it.  The
+HIP library never calls it and shares no code with it.
+
+What the method computes (sources: the MSA abstract page "MiniMax 稀疏注意力",
+sections 摘要 and 核心贡献; the snilld.dk page "MiniMax lancerer MSA",
+section "Hvad er MSA i praksis"; the Hungarian page "MiniMax új eljárása …",
+section "Hogyan működik az indexelő és a fő ág?"; the issue write-up
+"Substantial numerical differences with Minimax MSA attention vs Minimax's
+Reference", sections 原因分析 and 解决步骤):
+
+1. GQA substrate.  G = number of KV heads = number of index-query heads; the
+   r = Hq / G query heads h in [g*r, (g+1)*r) use KV head g and share group
+   g's block selection (the repeat_interleave fix in 解决步骤).
+2. Index branch.  Each group's index-query head is scored against the single
+   shared index-key head over the causally visible key tokens; token scores are
+   max-pooled over Bk-token blocks (block c = tokens [c*Bk, (c+1)*Bk), counted
+   from position 0); a Top-k is taken per query and per group, never pooled
+   across index heads (the amax(dim=1) defect described in 原因分析); the
+   query's own (local) block is always part of the selection.
+3. Main branch.  Exact scaled-dot-product softmax attention of each query head
+   over the causally visible tokens of the selected blocks, one softmax over
+   their union.
+
+Readings taken where the pages are silent (each is listed with its reason in
+the design notes of the repository):
+
+* the index score is the raw dot product q_idx . k_idx (no scale, no
+  activation): only two projections are added and softmax preserves order;
+* k counts the local block: local block + the best min(k-1, L) of the full
+  blocks 0..L-1, where L = floor(t / Bk) and t = q_offset + i;
+* only full blocks before the local block are ranked, so the causal mask never
+  cuts a ranked block (block c < L ends at (c+1)*Bk - 1 < t);
+* ties in block score go to the lower block index;
+* a selection row lists the chosen block ids ascending, then -1 padding;
+* the main-branch scale is 1/sqrt(d) unless one is given;
+* key j is visible to query row i iff j <= q_offset + i.
+
+Index scores are computed in float64; with integer-valued index inputs every
+partial sum is an integer far below 2**53, so they are exact.
+"""
+from __future__ import annotations
+
+import math
+from typing import Iterable, Optional, Sequence, Tuple
+
+import numpy as np
+
+__all__ = [
+    "block_maxima",
+    "select_from_maxima",
+    "index_select",
+    "sparse_attention",
+    "msa_forward",
+    "dense_causal_attention",
+    "token_set",
+]
+
+
+def _f64(x) -> np.ndarray:
+    return np.asarray(x, dtype=np.float64)
+
+
+# ---------------------------------------------------------------------------
+# Index branch
+# ---------------------------------------------------------------------------
+
+def block_maxima(qi: np.ndarray, k_idx_b: np.ndarray, L: int, block_size: int) -> np.ndarray:
+    """Max-pooled index scores of the full blocks 0..L-1 for one or more query
+    vectors of one sequence.
+
+    qi:       [n, D_idx] index-query vectors (one group's head, possibly many rows
+              sharing the same local block L)
+    k_idx_b:  [S_k, D_idx] the shared index-key head of that sequence
+    returns   [n, L] float64, M[:, c] = max_{j in block c} qi . k_idx_b[j]
+    """
+    qi = _f64(qi)
+    if L == 0:
+        return np.zeros((qi.shape[0], 0), dtype=np.float64)
+    keys = _f64(k_idx_b[: L * block_size])              # [L*Bk, D]
+    scores = qi @ keys.T                                 # [n, L*Bk] raw dot products
+    return scores.reshape(qi.shape[0], L, block_size).max(axis=2)
+
+
+def select_from_maxima(M: np.ndarray, L: int, topk: int) -> np.ndarray:
+    """Selection rows from block maxima.
+
+    M: [n, L] block maxima of the full blocks before the local block L.
+    Returns int32 [n, topk]: the best min(topk-1, L) blocks ordered by
+    (score descending, block index ascending), plus L, sorted ascending and
+    padded with -1.  No exponential is taken: softmax keeps the order of raw
+    scores (the exp-free Top-k of the abstract page, 摘要).
+    """
+    n = M.shape[0]
+    out = np.full((n, topk), -1, dtype=np.int32)
+    take = min(topk - 1, L)
+    if take > 0:
+        # a stable sort of -M keeps equal scores in ascending block order
+        order = np.argsort(-M, axis=1, kind="stable")[:, :take]
+    else:
+        order = np.zeros((n, 0), dtype=np.int64)
+    chosen = np.concatenate([order, np.full((n, 1), L, dtype=np.int64)], axis=1)
+    chosen.sort(axis=1)
+    out[:, : take + 1] = chosen
+    return out
+
+
+def _rows_by_block(q_offset: int, q_len: int, block_size: int, rows: Optional[Iterable[int]]):
+    """Group query rows by their local block so rows of one block share a key range."""
+    idx = np.arange(q_len) if rows is None else np.asarray(sorted(set(int(r) for r in rows)))
+    L = (q_offset + idx) // block_size
+    for Lv in np.unique(L):
+        yield int(Lv), idx[L == Lv]
+
+
+def index_select(q_idx, k_idx, topk: int, q_offset: int = 0, block_size: int = 128,
+                 rows: Optional[Sequence[Tuple[int, int]]] = None,
+                 chunk: int = 256) -> np.ndarray:
+    """Per-group block selection.
+
+    q_idx: [B, S_q, G, D_idx]; k_idx: [B, S_k, D_idx].
+    Returns int32 sel [B, G, S_q, topk].  When ``rows`` (pairs (b, i)) is given,
+    only those rows are computed and all other entries are left at -2.
+    """
+    q_idx = np.asarray(q_idx)
+    k_idx = np.asarray(k_idx)
+    B, S_q, G, _ = q_idx.shape
+    if k_idx.shape[1] < q_offset + S_q:
+        raise ValueError("kv_len must cover q_offset + q_len")
+    sel = np.full((B, G, S_q, topk), -2 if rows is not None else -1, dtype=np.int32)
+    per_b = {b: None for b in range(B)} if rows is None else {}
+    if rows is not None:
+        for b, i in rows:
+            per_b.setdefault(int(b), set()).add(int(i))
+    for b, rset in per_b.items():
+        for L, idx in _rows_by_block(q_offset, S_q, block_size, rset):
+            for s0 in range(0, len(idx), chunk):
+                part = idx[s0:s0 + chunk]
+                for g in range(G):
+                    M = block_maxima(q_idx[b, part, g, :], k_idx[b], L, block_size)
+                    sel[b, g, part, :] = select_from_maxima(M, L, topk)
+    return sel
+
+
+# ---------------------------------------------------------------------------
+# Main branch
+# ---------------------------------------------------------------------------
+
+def token_set(sel_row: np.ndarray, t: int, block_size: int) -> np.ndarray:
+    """Key tokens one query at absolute position t attends to: every token of the
+    selected blocks that is causally visible (j <= t), in ascending order."""
+    toks = []
+    for c in sorted(int(c) for c in sel_row if c >= 0):
+        lo = c * block_size
+        hi = min((c + 1) * block_size, t + 1)
+        if hi > lo:
+            toks.append(np.arange(lo, hi))
+    return np.concatenate(toks) if toks else np.zeros(0, dtype=np.int64)
+
+
+def _softmax_attend(qh: np.ndarray, kt: np.ndarray, vt: np.ndarray, scale: float):
+    """One softmax over the whole token set: qh [r, d], kt/vt [n, d]."""
+    s = scale * (qh @ kt.T)                   # [r, n]
+    m = s.max(axis=1, keepdims=True)
+    p = np.exp(s - m)
+    l = p.sum(axis=1, keepdims=True)
+    out = (p @ vt) / l
+    lse = (m + np.log(l))[:, 0]
+    return out, lse
+
+
+def sparse_attention(q, k, v, sel, q_offset: int = 0, block_size: int = 128,
+                     scale: Optional[float] = None,
+                     rows: Optional[Sequence[Tuple[int, int]]] = None):
+    """Exact softmax attention over the selected blocks.
+
+    q: [B, S_q, Hq, d]; k, v: [B, G, S_k, d]; sel: int [B, G, S_q, topk].
+    Returns (out [B, S_q, Hq, d], lse [B, Hq, S_q]) as float64; rows not listed in
+    ``rows`` (when given) are NaN.
+    """
+    q = np.asarray(q)
+    k = np.asarray(k)
+    v = np.asarray(v)
+    sel = np.asarray(sel)
+    B, S_q, Hq, d = q.shape
+    G = k.shape[1]
+    r = Hq // G
+    if scale is None or scale == 0.0:
+        scale = 1.0 / math.sqrt(d)
+    out = np.full((B, S_q, Hq, d), np.nan)
+    lse = np.full((B, Hq, S_q), np.nan)
+    todo = [(b, i) for b in range(B) for i in range(S_q)] if rows is None else rows
+    for b, i in todo:
+        t = q_offset + i
+        for g in range(G):
+            T = token_set(sel[b, g, i], t, block_size)
+            o, ls = _softmax_attend(_f64(q[b, i, g * r:(g + 1) * r]), _f64(k[b, g, T]),
+                                    _f64(v[b, g, T]), scale)
+            out[b, i, g * r:(g + 1) * r] = o
+            lse[b, g * r:(g + 1) * r, i] = ls
+    return out, lse
+
+
+def msa_forward(q, k, v, q_idx, k_idx, topk: int, q_offset: int = 0, block_size: int = 128,
+                scale: Optional[float] = None,
+                rows: Optional[Sequence[Tuple[int, int]]] = None):
+    """Index branch then main branch.  Returns (out, sel, lse)."""
+    sel = index_select(q_idx, k_idx, topk, q_offset, block_size, rows=rows)
+    out, lse = sparse_attention(q, k, v, sel, q_offset, block_size, scale, rows=rows)
+    return out, sel, lse
+
+
+def dense_causal_attention(q, k, v, q_offset: int = 0, scale: Optional[float] = None):
+    """Plain causal GQA softmax attention (every visible key), float64.
+
+    q: [B, S_q, Hq, d]; k, v: [B, G, S_k, d].  Returns (out, lse)."""
+    q = np.asarray(q)
+    k = np.asarray(k)
+    v = np.asarray(v)
+    B, S_q, Hq, d = q.shape
+    G = k.shape[1]
+    r = Hq // G
+    if scale is None or scale == 0.0:
+        scale = 1.0 / math.sqrt(d)
+    out = np.empty((B, S_q, Hq, d))
+    lse = np.empty((B, Hq, S_q))
+    for b in range(B):
+        for i in range(S_q):
+            t = q_offset + i
+            for g in range(G):
+                o, ls = _softmax_attend(_f64(q[b, i, g * r:(g + 1) * r]), _f64(k[b, g, :t + 1]),
+                                        _f64(v[b, g, :t + 1]), scale)
+                out[b, i, g * r:(g + 1) * r] = o
+                lse[b, g * r:(g + 1) * r, i] = ls
+    return out, lse

@@ -1,0 +1,190 @@
+"""Seeded synthetic inputs for the MSA forward pass.
+
+This module only draws random tensors of the right shapes, dtypes and value
+distributions.  It holds none of the attention arithmetic: both the CPU oracle
+(through the tests and the bench's CPU leg) and the HIP library (through the
+Python binding) receive what these functions return.
+
+Workloads (the MSA pages fix Bk = 128 and k = 16 with a GQA layout of 64 query
+heads over 4 KV heads; see "Hvad er MSA i praksis" on the snilld.dk MSA page and
+the 原因分析 section of the page "Substantial numerical differences with Minimax
+MSA attention vs Minimax's Reference"):
+
+* Q, K, V are standard normal; in bf16 workloads they are drawn in fp32 and
+  rounded to bf16 (round-to-nearest-even).
+* The index query/key tensors hold small integers drawn uniformly from an
+  inclusive range (-8..8 for the fp32 workload, -4..4 otherwise), stored exactly
+  in the workload dtype, so every index score is an exact integer in fp32.
+
+Two generators exist:
+
+* ``host_inputs``: numpy PCG64 seeded by
+  ``SeedSequence([0x4D5341, workload_id, tensor_id, b])`` (tensor ids 0 q, 1 k,
+  2 v, 3 q_idx, 4 k_idx; ``b`` the batch/sequence index), drawn per sequence in
+  the C order of the tensor's layout.  Used for every workload that fits
+  comfortably in host memory.
+* ``device_inputs``: torch's device generator (Philox) seeded from the same
+  tuple, for the workloads whose inputs are tens of GiB (128K decode cache, 1M
+  context) where host generation would dominate the run.  The oracle then reads
+  the very same values copied back to the host.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Dict, Optional
+
+import numpy as np
+import torch
+
+SEED_ROOT = 0x4D5341  # "MSA"
+
+TENSOR_IDS = {"q": 0, "k": 1, "v": 2, "q_idx": 3, "k_idx": 4}
+
+
+@dataclasses.dataclass(frozen=True)
+class Shape:
+    """Problem shape.  Layouts: q/out [B,S_q,Hq,d], k/v [B,Hkv,S_k,d],
+    q_idx [B,S_q,G,D_idx], k_idx [B,S_k,D_idx], sel int32 [B,G,S_q,k]."""
+
+    batch: int
+    q_len: int
+    kv_len: int
+    q_offset: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    index_dim: int
+    topk: int
+    block_size: int = 128
+    dtype: str = "bf16"  # "f32" or "bf16"
+    idx_lo: int = -4
+    idx_hi: int = 4
+
+    @property
+    def groups(self) -> int:
+        return self.num_kv_heads
+
+    @property
+    def torch_dtype(self) -> torch.dtype:
+        return torch.float32 if self.dtype == "f32" else torch.bfloat16
+
+    def replace(self, **kw) -> "Shape":
+        return dataclasses.replace(self, **kw)
+
+
+# The five workloads.  Names say what they are.
+WORKLOADS: Dict[int, Shape] = {
+    1: Shape(1, 1024, 1024, 0, 8, 2, 64, 32, 4, dtype="f32", idx_lo=-8, idx_hi=8),
+    2: Shape(1, 8192, 8192, 0, 64, 4, 128, 128, 16),
+    3: Shape(2, 32768, 32768, 0, 64, 4, 128, 128, 16),
+    4: Shape(64, 1, 131072, 131071, 64, 4, 128, 128, 16),
+    5: Shape(1, 4096, 1048576, 1044480, 64, 4, 128, 128, 16),
+}
+
+WORKLOAD_NAMES = {
+    1: "prefill_1k_fp32",
+    2: "prefill_8k_bf16",
+    3: "prefill_32k_b2_bf16",
+    4: "decode_128k_b64_bf16",
+    5: "chunked_prefill_1m_q4096_bf16",
+}
+
+
+def _seed(workload: int, tensor: str, b: int) -> np.random.SeedSequence:
+    return np.random.SeedSequence([SEED_ROOT, workload, TENSOR_IDS[tensor], b])
+
+
+def _per_seq_shape(s: Shape, tensor: str):
+    if tensor in ("q",):
+        return (s.q_len, s.num_q_heads, s.head_dim)
+    if tensor in ("k", "v"):
+        return (s.num_kv_heads, s.kv_len, s.head_dim)
+    if tensor == "q_idx":
+        return (s.q_len, s.groups, s.index_dim)
+    if tensor == "k_idx":
+        return (s.kv_len, s.index_dim)
+    raise KeyError(tensor)
+
+
+def _host_draw(s: Shape, workload: int, tensor: str, b: int) -> torch.Tensor:
+    rng = np.random.Generator(np.random.PCG64(_seed(workload, tensor, b)))
+    shp = _per_seq_shape(s, tensor)
+    if tensor in ("q", "k", "v"):
+        x = rng.standard_normal(size=shp, dtype=np.float32)
+    else:
+        x = rng.integers(s.idx_lo, s.idx_hi + 1, size=shp, dtype=np.int32).astype(np.float32)
+    return torch.from_numpy(x).to(s.torch_dtype)
+
+
+def host_inputs(s: Shape, workload: int = 0) -> Dict[str, torch.Tensor]:
+    """All five inputs as CPU tensors in the workload dtype (PCG64 recipe)."""
+    out = {}
+    for name in ("q", "k", "v", "q_idx", "k_idx"):
+        out[name] = torch.stack([_host_draw(s, workload, name, b) for b in range(s.batch)])
+    return out
+
+
+def _device_seed(workload: int, tensor: str, b: int) -> int:
+    ss = _seed(workload, tensor, b)
+    return int(ss.generate_state(1, dtype=np.uint64)[0] & ((1 << 63) - 1))
+
+
+def device_inputs(s: Shape, workload: int, device="cuda") -> Dict[str, torch.Tensor]:
+    """All five inputs generated on the device (Philox), per sequence."""
+    dt = s.torch_dtype
+    out = {}
+    for name in ("q", "k", "v", "q_idx", "k_idx"):
+        shp = _per_seq_shape(s, name)
+        t = torch.empty((s.batch,) + shp, dtype=dt, device=device)
+        for b in range(s.batch):
+            g = torch.Generator(device=device)
+            g.manual_seed(_device_seed(workload, name, b))
+            if name in ("q", "k", "v"):
+                # draw in fp32, round to the storage dtype; chunk to bound scratch
+                flat = t[b].view(-1)
+                n = flat.numel()
+                step = 1 << 28
+                for o in range(0, n, step):
+                    m = min(step, n - o)
+                    flat[o:o + m].copy_(torch.randn(m, generator=g, device=device,
+                                                    dtype=torch.float32).to(dt))
+            else:
+                t[b].copy_(torch.randint(s.idx_lo, s.idx_hi + 1, shp, generator=g,
+                                         device=device, dtype=torch.int32).to(dt))
+        out[name] = t
+    return out
+
+
+def host_bytes(s: Shape) -> int:
+    e = 4 if s.dtype == "f32" else 2
+    n = (2 * s.batch * s.q_len * s.num_q_heads * s.head_dim
+         + 2 * s.batch * s.num_kv_heads * s.kv_len * s.head_dim
+         + s.batch * s.q_len * s.groups * s.index_dim + s.batch * s.kv_len * s.index_dim)
+    return n * e
+
+
+def inputs_for(s: Shape, workload: int = 0, device: Optional[str] = None,
+               on_device_limit: int = 1 << 30) -> Dict[str, torch.Tensor]:
+    """Host recipe when the inputs are small, device recipe above ``on_device_limit``
+    bytes (only when a device is given)."""
+    if device is not None and host_bytes(s) > on_device_limit:
+        return device_inputs(s, workload, device)
+    x = host_inputs(s, workload)
+    if device is not None:
+        x = {n: t.to(device) for n, t in x.items()}
+    return x
+
+
+def as_f64(t) -> np.ndarray:
+    """Exact upcast of a stored fp32/bf16 tensor (or array) to a float64 array."""
+    if isinstance(t, torch.Tensor):
+        t = t.detach().to("cpu")
+        if t.dtype == torch.bfloat16:
+            t = t.float()
+        return t.numpy().astype(np.float64)
+    return np.asarray(t, dtype=np.float64)
+
+
+def n_blocks(kv_len: int, block_size: int = 128) -> int:
+    return int(math.ceil(kv_len / block_size))
