@@ -1,0 +1,239 @@
+"""MiniMax Sparse Attention (MSA) forward pass for AMD Instinct MI355X (gfx950).
+
+A thin ctypes binding over the C ABI of ``libmsa.so`` (declared in
+``include/msa.h``).  The Python layer only checks tensors, marshals pointers,
+allocates the workspace through torch and passes torch's current HIP stream;
+every step of the computation runs in the library's HIP kernels.  There is no
+fallback: without the built library the calls raise.
+
+Functions (same names as the C entry points):
+
+* ``index_select(q_idx, k_idx, topk, q_offset=0)`` -> sel int32 [B, G, S_q, k]
+* ``sparse_attn_fwd(q, k, v, sel, q_offset=0, scale=None, out_dtype=None,
+  return_lse=False)`` -> out [B, S_q, Hq, d] (and lse fp32 [B, Hq, S_q])
+* ``fwd(q, k, v, q_idx, k_idx, topk, q_offset=0, scale=None, out_dtype=None,
+  return_sel=False, return_lse=False)``
+
+Layouts: q [B,S_q,Hq,d], k/v [B,Hkv,S_k,d], q_idx [B,S_q,G,D_idx],
+k_idx [B,S_k,D_idx] with G = Hkv; all contiguous, on the GPU, fp32 or bf16.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+__all__ = ["index_select", "sparse_attn_fwd", "fwd", "workspace_size", "MsaShape", "lib", "LIB_PATH",
+           "MsaError", "OP_INDEX_SELECT", "OP_SPARSE_ATTN", "OP_FWD"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmsa.so")
+
+MSA_F32, MSA_BF16 = 0, 1
+OP_INDEX_SELECT, OP_SPARSE_ATTN, OP_FWD = 0, 1, 2
+BLOCK_SIZE = 128
+
+
+class MsaShape(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("q_len", ctypes.c_int32),
+        ("kv_len", ctypes.c_int32),
+        ("pad0", ctypes.c_int32),
+        ("q_offset", ctypes.c_int64),
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("index_dim", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("topk", ctypes.c_int32),
+        ("softmax_scale", ctypes.c_float),
+        ("dtype", ctypes.c_int32),
+        ("out_dtype", ctypes.c_int32),
+        ("pad1", ctypes.c_int32),
+    ]
+
+
+class MsaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{message} (status {status})")
+        self.status = status
+
+
+_LIB = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded C library.  Raises if it has not been built."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m block_sparse_attention_idx_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, sz = ctypes.c_void_p, ctypes.c_size_t
+        shp = ctypes.POINTER(MsaShape)
+        L.msa_workspace_size.argtypes = [shp, ctypes.c_int]
+        L.msa_workspace_size.restype = sz
+        L.msa_index_select.argtypes = [shp, vp, vp, vp, vp, sz, vp]
+        L.msa_index_select.restype = ctypes.c_int
+        L.msa_sparse_attn_fwd.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.msa_sparse_attn_fwd.restype = ctypes.c_int
+        L.msa_fwd.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.msa_fwd.restype = ctypes.c_int
+        L.msa_status_string.argtypes = [ctypes.c_int]
+        L.msa_status_string.restype = ctypes.c_char_p
+        L.msa_last_error.argtypes = []
+        L.msa_last_error.restype = ctypes.c_char_p
+        L.msa_version.argtypes = []
+        L.msa_version.restype = ctypes.c_char_p
+        _LIB = L
+    return _LIB
+
+
+def _dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.float32:
+        return MSA_F32
+    if dt == torch.bfloat16:
+        return MSA_BF16
+    raise TypeError(f"unsupported dtype {dt}: fp32 or bf16")
+
+
+def make_shape(B, S_q, S_k, q_offset, Hq, Hkv, d, D_idx, topk, dtype, out_dtype=None, scale=None,
+               block_size=BLOCK_SIZE) -> MsaShape:
+    s = MsaShape()
+    s.batch, s.q_len, s.kv_len, s.pad0 = B, S_q, S_k, 0
+    s.q_offset = q_offset
+    s.num_q_heads, s.num_kv_heads = Hq, Hkv
+    s.head_dim, s.index_dim = d, D_idx
+    s.block_size, s.topk = block_size, topk
+    s.softmax_scale = 0.0 if scale is None else float(scale)
+    s.dtype = _dtype_code(dtype)
+    s.out_dtype = _dtype_code(out_dtype if out_dtype is not None else dtype)
+    s.pad1 = 0
+    return s
+
+
+def _check(st: int):
+    if st != 0:
+        L = lib()
+        raise MsaError(st, f"{L.msa_status_string(st).decode()}: {L.msa_last_error().decode()}")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, ndim: int, device=None, dtype=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+
+
+def workspace_size(shape: MsaShape, op: int) -> int:
+    return int(lib().msa_workspace_size(ctypes.byref(shape), op))
+
+
+def _workspace(shape: MsaShape, op: int, device) -> Optional[torch.Tensor]:
+    n = workspace_size(shape, op)
+    if n == 0:
+        return None
+    ws = torch.empty(n + 256, dtype=torch.uint8, device=device)
+    off = (-ws.data_ptr()) % 256
+    return ws[off:off + n]
+
+
+def index_select(q_idx: torch.Tensor, k_idx: torch.Tensor, topk: int, q_offset: int = 0,
+                 sel: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Per-group block selection, int32 [B, G, S_q, topk] (ascending ids, -1 padded)."""
+    _need(q_idx, "q_idx", 4)
+    dev = q_idx.device
+    _need(k_idx, "k_idx", 3, dev, q_idx.dtype)
+    B, S_q, G, D = q_idx.shape
+    if k_idx.shape[0] != B or k_idx.shape[2] != D:
+        raise ValueError("k_idx must be [B, S_k, D_idx] matching q_idx")
+    S_k = k_idx.shape[1]
+    shape = make_shape(B, S_q, S_k, q_offset, G, G, 64, D, topk, q_idx.dtype)
+    if sel is None:
+        sel = torch.empty((B, G, S_q, topk), dtype=torch.int32, device=dev)
+    else:
+        _need(sel, "sel", 4, dev, torch.int32)
+    ws = workspace if workspace is not None else _workspace(shape, OP_INDEX_SELECT, dev)
+    L = lib()
+    st = L.msa_index_select(ctypes.byref(shape), _ptr(q_idx), _ptr(k_idx), _ptr(sel), _ptr(ws),
+                            0 if ws is None else ws.numel(), _stream(dev))
+    _check(st)
+    return sel
+
+
+def sparse_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sel: torch.Tensor, q_offset: int = 0,
+                    scale: Optional[float] = None, out_dtype: Optional[torch.dtype] = None,
+                    return_lse: bool = False, workspace: Optional[torch.Tensor] = None):
+    """Exact softmax attention over the selected blocks."""
+    _need(q, "q", 4)
+    dev = q.device
+    _need(k, "k", 4, dev, q.dtype)
+    _need(v, "v", 4, dev, q.dtype)
+    _need(sel, "sel", 4, dev, torch.int32)
+    B, S_q, Hq, d = q.shape
+    Hkv, S_k = k.shape[1], k.shape[2]
+    if tuple(k.shape) != (B, Hkv, S_k, d) or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("k and v must be [B, Hkv, S_k, d] matching q")
+    topk = sel.shape[3]
+    if tuple(sel.shape[:3]) != (B, Hkv, S_q):
+        raise ValueError("sel must be [B, G, S_q, topk]")
+    shape = make_shape(B, S_q, S_k, q_offset, Hq, Hkv, d, 32, topk, q.dtype, out_dtype, scale)
+    out = torch.empty((B, S_q, Hq, d), dtype=out_dtype or q.dtype, device=dev)
+    lse = torch.empty((B, Hq, S_q), dtype=torch.float32, device=dev) if return_lse else None
+    ws = workspace if workspace is not None else _workspace(shape, OP_SPARSE_ATTN, dev)
+    L = lib()
+    st = L.msa_sparse_attn_fwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(sel), _ptr(out), _ptr(lse),
+                               _ptr(ws), 0 if ws is None else ws.numel(), _stream(dev))
+    _check(st)
+    return (out, lse) if return_lse else out
+
+
+def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_idx: torch.Tensor, k_idx: torch.Tensor, topk: int,
+        q_offset: int = 0, scale: Optional[float] = None, out_dtype: Optional[torch.dtype] = None,
+        return_sel: bool = False, return_lse: bool = False, workspace: Optional[torch.Tensor] = None):
+    """Index branch and main branch.  Returns out, plus sel and/or lse when asked."""
+    _need(q, "q", 4)
+    dev = q.device
+    for name, t, nd in (("k", k, 4), ("v", v, 4), ("q_idx", q_idx, 4), ("k_idx", k_idx, 3)):
+        _need(t, name, nd, dev, q.dtype)
+    B, S_q, Hq, d = q.shape
+    Hkv, S_k = k.shape[1], k.shape[2]
+    D = q_idx.shape[3]
+    if tuple(k.shape) != (B, Hkv, S_k, d) or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("k and v must be [B, Hkv, S_k, d] matching q")
+    if tuple(q_idx.shape) != (B, S_q, Hkv, D) or tuple(k_idx.shape) != (B, S_k, D):
+        raise ValueError("q_idx must be [B, S_q, Hkv, D_idx] and k_idx [B, S_k, D_idx]")
+    shape = make_shape(B, S_q, S_k, q_offset, Hq, Hkv, d, D, topk, q.dtype, out_dtype, scale)
+    out = torch.empty((B, S_q, Hq, d), dtype=out_dtype or q.dtype, device=dev)
+    sel = torch.empty((B, Hkv, S_q, topk), dtype=torch.int32, device=dev) if return_sel else None
+    lse = torch.empty((B, Hq, S_q), dtype=torch.float32, device=dev) if return_lse else None
+    ws = workspace if workspace is not None else _workspace(shape, OP_FWD, dev)
+    L = lib()
+    st = L.msa_fwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(q_idx), _ptr(k_idx), _ptr(out), _ptr(sel),
+                   _ptr(lse), _ptr(ws), 0 if ws is None else ws.numel(), _stream(dev))
+    _check(st)
+    res = [out]
+    if return_sel:
+        res.append(sel)
+    if return_lse:
+        res.append(lse)
+    return res[0] if len(res) == 1 else tuple(res)

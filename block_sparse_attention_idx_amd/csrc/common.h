@@ -1,0 +1,67 @@
+// Shared device helpers for the MSA kernels (gfx950 / CDNA4).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace msa {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr float kNegInf = -__builtin_inff();
+
+// 32x32 MFMA tile traits.  Operand layout (checked on gfx950): lane l holds
+// A[l % 32][(l / 32) * KPL + e] and B[(l / 32) * KPL + e][l % 32] for
+// e < KPL; the 32x32 fp32 result has C[(j / 4) * 8 + (l / 32) * 4 + j % 4][l % 32]
+// in register j of lane l.
+template <typename T>
+struct Mma;
+
+template <>
+struct Mma<bf16> {
+  static constexpr int KPL = 8;    // k elements per lane per instruction
+  static constexpr int KSTEP = 16; // k per instruction
+  typedef bf16x8 frag;
+  __device__ static inline f32x16 mma(frag a, frag b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  __device__ static inline frag zero() { return frag{}; }
+};
+
+template <>
+struct Mma<float> {
+  static constexpr int KPL = 1;
+  static constexpr int KSTEP = 2;
+  typedef float frag;
+  __device__ static inline f32x16 mma(frag a, frag b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+  }
+  __device__ static inline frag zero() { return 0.0f; }
+};
+
+// row index (within the 32-row tile) held by register j of a lane in half h
+__device__ __forceinline__ constexpr int c_row(int j, int h) { return (j / 4) * 8 + h * 4 + (j % 4); }
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+
+template <typename T>
+__device__ __forceinline__ T from_f32(float x);
+template <>
+__device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <>
+__device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }  // round to nearest even
+
+__device__ __forceinline__ float wave_max_xor32(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
+
+struct alignas(16) Chunk16 {
+  uint32_t w[4];
+};
+
+}  // namespace msa

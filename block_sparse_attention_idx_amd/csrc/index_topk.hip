@@ -1,0 +1,302 @@
+// Index branch of MSA on gfx950: block max-pooled index scores and the
+// per-group exp-free Top-k with the forced local block.
+//
+// Method (snilld.dk page "MiniMax lancerer MSA", section "Hvad er MSA i
+// praksis"; abstract page "MiniMax 稀疏注意力", 摘要): every GQA group's
+// index-query head is scored against the single shared index-key head, the
+// token scores are max-pooled over 128-token blocks, and each (query, group)
+// keeps the Top-k blocks, always including the query's local block.  Softmax
+// preserves order, so raw scores are ranked (no exp).
+//
+// Design.  A workgroup owns 256 (query row, group) pairs of one sequence (the
+// rows of q_idx [B,S_q,G,D] are contiguous per (i, g)) and a contiguous range of
+// key blocks.  Per block, the shared k_idx tile (128 keys x D) is staged in LDS
+// (double-buffered) and multiplied against the rows' index queries held in
+// registers: S^T = K_idx * Q_idx^T with 32x32 MFMA tiles, so each lane owns
+// one query row and 64 of the block's 128 keys (the other 64 sit in lane ^ 32).
+// The block max is a register reduction plus one cross-half exchange; it goes
+// straight into a running top list in registers and is never stored.  The two
+// lane halves take alternate blocks, so each keeps its own list; lists of all
+// (split, half) pairs are merged per row by topk_merge_kernel, which also adds
+// the local block, sorts ascending and pads with -1.
+//
+// Exactness: with integer-valued inputs every score is an integer of
+// magnitude <= D * max|q| * max|k| < 2^24, so fp32 MFMA accumulation is exact in
+// any order, and ties are broken by block index exactly as the definition says.
+// Only full blocks before the local block are ranked (block c < L ends at or
+// before t), so no causal mask is needed inside the ranked blocks.
+#include "common.h"
+#include "kernels.h"
+
+namespace msa {
+
+template <int CAP>
+__device__ __forceinline__ void list_insert(float (&s)[CAP], int (&id)[CAP], float x, int c) {
+  // s is sorted descending; every index already present is smaller than c, so
+  // an equal score keeps the earlier (lower-index) entry first.
+  bool gt[CAP];
+#pragma unroll
+  for (int j = 0; j < CAP; ++j) gt[j] = x > s[j];
+#pragma unroll
+  for (int j = CAP - 1; j >= 1; --j) {
+    s[j] = gt[j - 1] ? s[j - 1] : (gt[j] ? x : s[j]);
+    id[j] = gt[j - 1] ? id[j - 1] : (gt[j] ? c : id[j]);
+  }
+  s[0] = gt[0] ? x : s[0];
+  id[0] = gt[0] ? c : id[0];
+}
+
+__device__ __forceinline__ bool ranks_before(float s1, int i1, float s2, int i2) {
+  return s1 > s2 || (s1 == s2 && i1 < i2);
+}
+
+template <typename T, int DI, int CAP, int RT>
+__global__ __launch_bounds__(256) void index_topk_kernel(IndexParams p) {
+  using M = Mma<T>;
+  using frag = typename M::frag;
+  constexpr int KPL = M::KPL, KSTEP = M::KSTEP, NKS = DI / KSTEP;
+  constexpr int PAD = 16 / (int)sizeof(T);
+  constexpr int LDW = DI + PAD;  // LDS pitch (elements): rows 16 B apart in bank space
+  constexpr int ROWS_WAVE = 32 * RT;
+  constexpr int ROWS_WG = 4 * ROWS_WAVE;
+  constexpr int CH_PER_ROW = DI * (int)sizeof(T) / 16;
+  constexpr int CH_PER_THREAD = kBlock * CH_PER_ROW / 256;
+  static_assert(CH_PER_THREAD >= 1 && (kBlock * CH_PER_ROW) % 256 == 0, "staging split");
+  __shared__ __align__(16) T Ks[2][kBlock * LDW];
+
+  // XCD-aware unit order: hardware hands consecutive workgroup ids to the 8
+  // XCDs in turn; give each XCD a contiguous run of units (one key range, many
+  // row tiles) so the k_idx range it streams stays in its own L2.
+  const int lin = blockIdx.x;
+  const int logical = (lin & 7) * p.grid_per_xcd + (lin >> 3);
+  if (logical >= p.nunits) return;
+  const int split = logical / p.ntile_total;
+  const int tg = logical - split * p.ntile_total;
+  const int b = tg / p.ntile;
+  const int tile = tg - b * p.ntile;
+  const int n_first = tile * ROWS_WG;
+  const int n_last = min(n_first + ROWS_WG, p.rows_per_b) - 1;
+  const int Lmax = (int)((p.q_offset + n_last / p.G) / kBlock);
+  const int c_begin = split * p.chunk;
+  const int c_end = min(c_begin + p.chunk, Lmax);
+  if (c_begin >= c_end) return;
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int h = lane >> 5, l32 = lane & 31;
+  const bool wave_active = n_first + wave * ROWS_WAVE < p.rows_per_b;
+
+  int rowL[RT];
+  bool rvalid[RT];
+  frag qf[RT][NKS];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int n = n_first + wave * ROWS_WAVE + rt * 32 + l32;
+    rvalid[rt] = n < p.rows_per_b;
+    rowL[rt] = rvalid[rt] ? (int)((p.q_offset + n / p.G) / kBlock) : 0;
+    const T* qrow = (const T*)p.q_idx + ((int64_t)b * p.rows_per_b + n) * DI;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+      qf[rt][ks] = rvalid[rt] ? *(const frag*)(qrow + ks * KSTEP + h * KPL) : M::zero();
+  }
+
+  float ls[RT][CAP];
+  int li[RT][CAP];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int j = 0; j < CAP; ++j) {
+      ls[rt][j] = kNegInf;
+      li[rt][j] = -1;
+    }
+
+  const char* kbase = (const char*)p.k_idx + (int64_t)b * p.S_k * DI * (int64_t)sizeof(T);
+  Chunk16 pre[CH_PER_THREAD];
+  auto gload = [&](int c) {
+    const Chunk16* src = (const Chunk16*)(kbase + (int64_t)c * kBlock * DI * (int64_t)sizeof(T));
+#pragma unroll
+    for (int u = 0; u < CH_PER_THREAD; ++u) pre[u] = src[threadIdx.x + u * 256];
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < CH_PER_THREAD; ++u) {
+      const int ch = threadIdx.x + u * 256;
+      const int row = ch / CH_PER_ROW, col = ch - row * CH_PER_ROW;
+      *(Chunk16*)((char*)&Ks[buf][row * LDW] + col * 16) = pre[u];
+    }
+  };
+  auto block_max = [&](int buf, float (&pm)[RT]) {
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) pm[rt] = kNegInf;
+    if (!wave_active) return;
+    f32x16 acc[4][RT];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) acc[kt][rt] = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        const frag a = *(const frag*)&Ks[buf][(kt * 32 + l32) * LDW + ks * KSTEP + h * KPL];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) acc[kt][rt] = M::mma(a, qf[rt][ks], acc[kt][rt]);
+      }
+    }
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      float m = acc[0][rt][0];
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) m = fmaxf(m, acc[kt][rt][j]);
+      pm[rt] = m;
+    }
+  };
+
+  gload(c_begin);
+  lstore(0);
+  __syncthreads();
+  int buf = 0;
+  for (int c = c_begin; c < c_end; c += 2) {
+    float pmA[RT], pmB[RT];
+    const bool hasB = c + 1 < c_end;
+    if (hasB) gload(c + 1);
+    block_max(buf, pmA);
+    if (hasB) lstore(buf ^ 1);
+    __syncthreads();
+    buf ^= 1;
+    if (hasB) {
+      const bool hasC = c + 2 < c_end;
+      if (hasC) gload(c + 2);
+      block_max(buf, pmB);
+      if (hasC) lstore(buf ^ 1);
+      __syncthreads();
+      buf ^= 1;
+    } else {
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) pmB[rt] = kNegInf;
+    }
+    // lanes of half 0 rank block c, lanes of half 1 rank block c + 1
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const float mine = h ? pmB[rt] : pmA[rt];
+      const float send = h ? pmA[rt] : pmB[rt];
+      float full = fmaxf(mine, __shfl_xor(send, 32));
+      const int cc = c + h;
+      if (!rvalid[rt] || cc >= rowL[rt]) full = kNegInf;
+      list_insert<CAP>(ls[rt], li[rt], full, cc);
+    }
+  }
+
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    if (!rvalid[rt]) continue;
+    const int n = n_first + wave * ROWS_WAVE + rt * 32 + l32;
+    const int64_t rowg = (int64_t)b * p.rows_per_b + n;
+    const int64_t base = ((rowg * p.nsplit + split) * 2 + h) * CAP;
+#pragma unroll
+    for (int j = 0; j < CAP; ++j) {
+      p.part_s[base + j] = ls[rt][j];
+      p.part_i[base + j] = li[rt][j];
+    }
+  }
+}
+
+// One wave per (b, i, g) row: k-way merge of the row's partial lists by
+// (score desc, block asc), then local block, ascending order, -1 padding.
+template <int CAP>
+__global__ __launch_bounds__(256) void topk_merge_kernel(IndexParams p) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t row = (int64_t)blockIdx.x * 4 + wave;
+  if (row >= (int64_t)p.B * p.rows_per_b) return;
+  const int b = (int)(row / p.rows_per_b);
+  const int n = (int)(row - (int64_t)b * p.rows_per_b);
+  const int i = n / p.G, g = n - (n / p.G) * p.G;
+  const int L = (int)((p.q_offset + i) / kBlock);
+  const int nspl = L > 0 ? (L + p.chunk - 1) / p.chunk : 0;
+  const int nlists = 2 * nspl;
+  const int take = min(p.topk - 1, L);
+
+  int pos[4] = {0, 0, 0, 0};
+  int mywin = 0x7fffffff;
+  for (int it = 0; it < take; ++it) {
+    float bs = kNegInf;
+    int bi = 0x7fffffff, bl = -1;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int lst = lane + 64 * q;
+      if (lst < nlists && pos[q] < CAP) {
+        const int64_t base = ((row * p.nsplit + (lst >> 1)) * 2 + (lst & 1)) * CAP + pos[q];
+        const float s = p.part_s[base];
+        const int id = p.part_i[base];
+        if (id >= 0 && ranks_before(s, id, bs, bi)) {
+          bs = s;
+          bi = id;
+          bl = q;
+        }
+      }
+    }
+    float ws = bs;
+    int wi = bi;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float os = __shfl_xor(ws, off);
+      const int oi = __shfl_xor(wi, off);
+      if (ranks_before(os, oi, ws, wi)) {
+        ws = os;
+        wi = oi;
+      }
+    }
+    // block ids are unique across a row's lists, so exactly one lane owns the winner
+    if (bl >= 0 && bi == wi) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (q == bl) ++pos[q];
+    }
+    if (lane == it) mywin = wi;
+  }
+  int rank = 0;
+  for (int m = 0; m < take; ++m) {
+    const int w = __shfl(mywin, m);
+    rank += (w < mywin) ? 1 : 0;
+  }
+  int32_t* out = p.sel + (((int64_t)b * p.G + g) * p.S_q + i) * p.topk;
+  if (lane < take) out[rank] = mywin;
+  else if (lane == take) out[take] = L;
+  else if (lane < p.topk) out[lane] = -1;
+}
+
+template <typename T, int DI, int CAP>
+static hipError_t launch_index_t(const IndexParams& p, hipStream_t s) {
+  hipLaunchKernelGGL((index_topk_kernel<T, DI, CAP, 2>), dim3(p.grid_per_xcd * 8), dim3(256), 0, s, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t rows = (int64_t)p.B * p.rows_per_b;
+  hipLaunchKernelGGL((topk_merge_kernel<CAP>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+template <typename T, int DI>
+static hipError_t launch_index_d(const IndexParams& p, hipStream_t s) {
+  if (p.topk <= 16) return launch_index_t<T, DI, 15>(p, s);
+  return launch_index_t<T, DI, 31>(p, s);
+}
+
+hipError_t launch_index_select(const IndexParams& p, bool bf16_inputs, int index_dim, hipStream_t s) {
+  if (bf16_inputs) {
+    switch (index_dim) {
+      case 32: return launch_index_d<bf16, 32>(p, s);
+      case 64: return launch_index_d<bf16, 64>(p, s);
+      case 128: return launch_index_d<bf16, 128>(p, s);
+    }
+  } else {
+    switch (index_dim) {
+      case 32: return launch_index_d<float, 32>(p, s);
+      case 64: return launch_index_d<float, 64>(p, s);
+      case 128: return launch_index_d<float, 128>(p, s);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace msa

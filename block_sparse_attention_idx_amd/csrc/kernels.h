@@ -1,0 +1,67 @@
+// Kernel parameter blocks and launchers shared by the host API and the .hip
+// translation units.  Host-only code includes this; device code lives in the
+// .hip files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace msa {
+
+constexpr int kBlock = 128;  // Bk: tokens per KV block, fixed on the GPU path
+
+// Index branch (index_topk.hip).
+struct IndexParams {
+  const void* q_idx;   // [B, S_q, G, D]
+  const void* k_idx;   // [B, S_k, D]
+  float* part_s;       // [B*S_q*G, nsplit, 2, CAP] partial top-list scores
+  int32_t* part_i;     // same shape: block ids (-1 = empty)
+  int32_t* sel;        // [B, G, S_q, topk]
+  int64_t q_offset;
+  int B, S_q, S_k, G, topk;
+  int rows_per_b;      // S_q * G
+  int ntile;           // row tiles per sequence
+  int ntile_total;     // B * ntile
+  int nsplit, chunk;   // key-block splits and blocks per split
+  int nunits;          // ntile_total * nsplit
+  int grid_per_xcd;    // ceil(nunits / 8)
+};
+
+constexpr int kIndexRowsPerWG = 256;
+
+hipError_t launch_index_select(const IndexParams& p, bool bf16_inputs, int index_dim, hipStream_t s);
+
+// Main branch (attn.hip).
+struct AttnParams {
+  const void* q;       // [B, S_q, Hq, d]
+  const void* k;       // [B, G, S_k, d]
+  const void* v;       // [B, G, S_k, d]
+  const int32_t* sel;  // [B, G, S_q, topk]
+  void* out;           // [B, S_q, Hq, d]
+  float* lse;          // [B, Hq, S_q] or null
+  // query gather (bucket = (b, g, c))
+  int32_t* counts;     // [nbuckets]
+  int32_t* offsets;    // [nbuckets + 1]
+  int32_t* cursor;     // [nbuckets]
+  int32_t* item_off;   // [nbuckets + 1]: first work item of each bucket
+  int32_t* entries;    // [B*G*S_q*topk]: (query row << 6) | slot, grouped by bucket
+  int32_t* n_items;    // device scalar
+  // partial softmax states per (b, i, g, slot, head)
+  void* part_o;        // o / l in the partial dtype, [.., d]
+  float* part_m;       // running max, log2 units of the scaled score
+  float* part_l;       // sum of 2^(s' - m)
+  int64_t q_offset;
+  int B, S_q, S_k, Hq, G, r, d, topk;
+  int nb;              // key blocks per sequence, ceil(S_k / 128)
+  int nbuckets;        // B * G * nb
+  int tpi;             // query tokens per work item
+  int direct;          // 1: one item per selection entry, no gather
+  int64_t n_direct;    // B * G * S_q * topk when direct
+  int grid;            // persistent grid size of the attention kernel
+  float scale_log2;    // softmax scale * log2(e)
+  int out_f32;         // output dtype: 1 fp32, 0 input dtype
+};
+
+hipError_t launch_sparse_attention(const AttnParams& p, bool bf16_inputs, hipStream_t s);
+
+}  // namespace msa

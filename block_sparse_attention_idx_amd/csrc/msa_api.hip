@@ -1,0 +1,320 @@
+// Host side of the MSA C ABI: argument checks, workspace layout, launch plans.
+// Every check runs before anything is enqueued, so an error leaves all outputs
+// untouched and needs no GPU.
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/msa.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+msa_status fail(msa_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+msa_status fail(msa_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+constexpr size_t kAlign = 256;
+constexpr int kTokensPerItem = 64;
+constexpr int kAttnGrid = 512;      // persistent attention grid: 2 workgroups per CU
+constexpr int kIndexTargetUnits = 2048;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+bool is_pow2_upto32(int r) { return r == 1 || r == 2 || r == 4 || r == 8 || r == 16 || r == 32; }
+
+int elem_bytes(int dtype) { return dtype == MSA_F32 ? 4 : 2; }
+
+// Shape checks shared by every op.  'op' selects the op-specific ones.
+msa_status check_shape(const msa_shape* s, int op) {
+  if (!s) return fail(MSA_ERR_INVALID, "shape is NULL");
+  if (s->pad0 != 0 || s->pad1 != 0) return fail(MSA_ERR_INVALID, "msa_shape padding fields must be 0");
+  if (s->batch < 1) return fail(MSA_ERR_INVALID, "batch must be >= 1 (got %d)", s->batch);
+  if (s->q_len < 0) return fail(MSA_ERR_INVALID, "q_len must be >= 0 (got %d)", s->q_len);
+  if (s->kv_len < 1) return fail(MSA_ERR_INVALID, "kv_len must be >= 1 (got %d)", s->kv_len);
+  if (s->q_offset < 0) return fail(MSA_ERR_INVALID, "q_offset must be >= 0");
+  if (s->q_offset + (int64_t)s->q_len > (int64_t)s->kv_len)
+    return fail(MSA_ERR_INVALID, "kv_len (%d) must be >= q_offset + q_len (%lld)", s->kv_len,
+                (long long)(s->q_offset + s->q_len));
+  if (s->num_q_heads < 1 || s->num_kv_heads < 1)
+    return fail(MSA_ERR_INVALID, "head counts must be >= 1");
+  if (s->num_q_heads % s->num_kv_heads != 0)
+    return fail(MSA_ERR_INVALID, "num_q_heads (%d) must be a multiple of num_kv_heads (%d)", s->num_q_heads,
+                s->num_kv_heads);
+  if (s->head_dim < 1 || s->index_dim < 1) return fail(MSA_ERR_INVALID, "head_dim and index_dim must be >= 1");
+  if (s->block_size < 1) return fail(MSA_ERR_INVALID, "block_size must be >= 1");
+  if (s->topk < 1) return fail(MSA_ERR_INVALID, "topk must be >= 1 (got %d)", s->topk);
+  if (s->dtype != MSA_F32 && s->dtype != MSA_BF16) return fail(MSA_ERR_INVALID, "unknown dtype %d", s->dtype);
+  if (s->out_dtype != MSA_F32 && s->out_dtype != MSA_BF16)
+    return fail(MSA_ERR_INVALID, "unknown out_dtype %d", s->out_dtype);
+  if (!std::isfinite(s->softmax_scale)) return fail(MSA_ERR_INVALID, "softmax_scale must be finite");
+
+  if (s->block_size != msa::kBlock)
+    return fail(MSA_ERR_UNSUPPORTED, "block_size %d: only 128 is built", s->block_size);
+  if (s->topk > 32) return fail(MSA_ERR_UNSUPPORTED, "topk %d: at most 32 is built", s->topk);
+  if (s->q_len >= (1 << 25)) return fail(MSA_ERR_UNSUPPORTED, "q_len must be < 2^25");
+  if ((int64_t)s->batch * s->num_kv_heads * ceil_div(s->kv_len, msa::kBlock) >= (1LL << 31))
+    return fail(MSA_ERR_UNSUPPORTED, "batch * kv heads * blocks exceeds 2^31");
+  if (op == MSA_OP_INDEX_SELECT || op == MSA_OP_FWD) {
+    if (s->index_dim != 32 && s->index_dim != 64 && s->index_dim != 128)
+      return fail(MSA_ERR_UNSUPPORTED, "index_dim %d: built for 32, 64, 128", s->index_dim);
+    if ((int64_t)s->q_len * s->num_kv_heads * s->batch >= (1LL << 31))
+      return fail(MSA_ERR_UNSUPPORTED, "batch * q_len * groups exceeds 2^31");
+  }
+  if (op == MSA_OP_SPARSE_ATTN || op == MSA_OP_FWD) {
+    if (s->head_dim != 64 && s->head_dim != 128)
+      return fail(MSA_ERR_UNSUPPORTED, "head_dim %d: built for 64 and 128", s->head_dim);
+    const int r = s->num_q_heads / s->num_kv_heads;
+    if (!is_pow2_upto32(r))
+      return fail(MSA_ERR_UNSUPPORTED, "query heads per group %d: built for 1, 2, 4, 8, 16, 32", r);
+    if (s->out_dtype != MSA_F32 && s->out_dtype != s->dtype)
+      return fail(MSA_ERR_UNSUPPORTED, "out_dtype must be MSA_F32 or the input dtype");
+    if ((int64_t)s->batch * s->num_kv_heads * s->q_len * s->topk >= (1LL << 31))
+      return fail(MSA_ERR_UNSUPPORTED, "batch * groups * q_len * topk exceeds 2^31");
+  }
+  return MSA_OK;
+}
+
+// ---- index plan -----------------------------------------------------------
+
+struct IndexPlan {
+  msa::IndexParams p;
+  int cap;
+  size_t bytes;  // workspace for the partial lists
+};
+
+IndexPlan plan_index(const msa_shape* s) {
+  IndexPlan ip{};
+  msa::IndexParams& p = ip.p;
+  p.B = s->batch;
+  p.S_q = s->q_len;
+  p.S_k = s->kv_len;
+  p.G = s->num_kv_heads;
+  p.topk = s->topk;
+  p.q_offset = s->q_offset;
+  p.rows_per_b = s->q_len * s->num_kv_heads;
+  p.ntile = (int)ceil_div(p.rows_per_b, msa::kIndexRowsPerWG);
+  p.ntile_total = p.B * p.ntile;
+  const int64_t Lmax = s->q_len > 0 ? (s->q_offset + s->q_len - 1) / msa::kBlock : 0;
+  int64_t chunk = 1, nsplit = 1;
+  if (Lmax > 0) {
+    const int64_t want = std::max<int64_t>(1, ceil_div(kIndexTargetUnits, std::max(1, p.ntile_total)));
+    chunk = std::max<int64_t>({16, ceil_div(Lmax, want), ceil_div(Lmax, 128)});
+    nsplit = ceil_div(Lmax, chunk);
+  }
+  p.chunk = (int)chunk;
+  p.nsplit = (int)nsplit;
+  p.nunits = p.ntile_total * p.nsplit;
+  p.grid_per_xcd = (int)ceil_div(p.nunits, 8);
+  ip.cap = s->topk <= 16 ? 15 : 31;
+  const size_t entries = (size_t)p.B * p.rows_per_b * p.nsplit * 2 * ip.cap;
+  ip.bytes = 2 * align_up(entries * 4);
+  return ip;
+}
+
+void bind_index(IndexPlan& ip, char* ws, const void* q_idx, const void* k_idx, int32_t* sel) {
+  const size_t half = ip.bytes / 2;
+  ip.p.part_s = (float*)ws;
+  ip.p.part_i = (int32_t*)(ws + half);
+  ip.p.q_idx = q_idx;
+  ip.p.k_idx = k_idx;
+  ip.p.sel = sel;
+}
+
+// ---- attention plan -------------------------------------------------------
+
+struct AttnPlan {
+  msa::AttnParams p;
+  size_t off_counts, off_offsets, off_cursor, off_item_off, off_nitems, off_entries, off_po, off_pm, off_pl;
+  size_t bytes;
+};
+
+AttnPlan plan_attn(const msa_shape* s) {
+  AttnPlan ap{};
+  msa::AttnParams& p = ap.p;
+  p.B = s->batch;
+  p.S_q = s->q_len;
+  p.S_k = s->kv_len;
+  p.Hq = s->num_q_heads;
+  p.G = s->num_kv_heads;
+  p.r = s->num_q_heads / s->num_kv_heads;
+  p.d = s->head_dim;
+  p.topk = s->topk;
+  p.q_offset = s->q_offset;
+  p.nb = (int)ceil_div(s->kv_len, msa::kBlock);
+  p.nbuckets = p.B * p.G * p.nb;
+  p.tpi = kTokensPerItem;
+  const int64_t Lmax = s->q_len > 0 ? (s->q_offset + s->q_len - 1) / msa::kBlock : 0;
+  // queries per (b, g, block) on average; below 2 the gather buys nothing
+  const double per_bucket = (double)s->q_len * std::min<int64_t>(s->topk, Lmax + 1) / (double)(Lmax + 1);
+  p.direct = per_bucket < 2.0 ? 1 : 0;
+  p.n_direct = (int64_t)p.B * p.G * p.S_q * p.topk;
+  p.grid = kAttnGrid;
+  const float scale = s->softmax_scale != 0.0f ? s->softmax_scale : 1.0f / std::sqrt((float)s->head_dim);
+  p.scale_log2 = scale * 1.4426950408889634f;
+  p.out_f32 = s->out_dtype == MSA_F32 ? 1 : 0;
+
+  const size_t nbk = (size_t)p.nbuckets + 1;
+  const size_t entries = (size_t)p.B * p.G * p.S_q * p.topk;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += align_up(bytes);
+    return o;
+  };
+  if (!p.direct) {
+    ap.off_counts = take(nbk * 4);
+    ap.off_offsets = take(nbk * 4);
+    ap.off_cursor = take(nbk * 4);
+    ap.off_item_off = take(nbk * 4);
+    ap.off_nitems = take(4);
+    ap.off_entries = take(entries * 4);
+  }
+  const size_t prow = entries * (size_t)p.r;  // (b, i, g, slot, head)
+  ap.off_po = take(prow * p.d * elem_bytes(s->dtype));
+  ap.off_pm = take(prow * 4);
+  ap.off_pl = take(prow * 4);
+  ap.bytes = off;
+  return ap;
+}
+
+void bind_attn(AttnPlan& ap, char* ws) {
+  msa::AttnParams& p = ap.p;
+  if (!p.direct) {
+    p.counts = (int32_t*)(ws + ap.off_counts);
+    p.offsets = (int32_t*)(ws + ap.off_offsets);
+    p.cursor = (int32_t*)(ws + ap.off_cursor);
+    p.item_off = (int32_t*)(ws + ap.off_item_off);
+    p.n_items = (int32_t*)(ws + ap.off_nitems);
+    p.entries = (int32_t*)(ws + ap.off_entries);
+  }
+  p.part_o = ws + ap.off_po;
+  p.part_m = (float*)(ws + ap.off_pm);
+  p.part_l = (float*)(ws + ap.off_pl);
+}
+
+size_t sel_bytes(const msa_shape* s) {
+  return align_up((size_t)s->batch * s->num_kv_heads * s->q_len * s->topk * 4);
+}
+
+msa_status check_ws(void* ws, size_t ws_bytes, size_t need) {
+  if (need == 0) return MSA_OK;
+  if (!ws) return fail(MSA_ERR_WORKSPACE, "workspace is NULL but %zu bytes are needed", need);
+  if (((uintptr_t)ws) % kAlign != 0) return fail(MSA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (ws_bytes < need) return fail(MSA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", ws_bytes, need);
+  return MSA_OK;
+}
+
+msa_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return MSA_OK;
+  return fail(MSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* msa_version(void) { return "0.1.0"; }
+
+const char* msa_status_string(msa_status st) {
+  switch (st) {
+    case MSA_OK: return "MSA_OK";
+    case MSA_ERR_INVALID: return "MSA_ERR_INVALID";
+    case MSA_ERR_UNSUPPORTED: return "MSA_ERR_UNSUPPORTED";
+    case MSA_ERR_WORKSPACE: return "MSA_ERR_WORKSPACE";
+    case MSA_ERR_HIP: return "MSA_ERR_HIP";
+  }
+  return "MSA_ERR_UNKNOWN";
+}
+
+const char* msa_last_error(void) { return g_last_error.c_str(); }
+
+size_t msa_workspace_size(const msa_shape* s, int op) {
+  const std::string saved = g_last_error;
+  size_t r = 0;
+  if (op >= MSA_OP_INDEX_SELECT && op <= MSA_OP_FWD && check_shape(s, op) == MSA_OK && s->q_len > 0) {
+    if (op == MSA_OP_INDEX_SELECT) r = plan_index(s).bytes;
+    else if (op == MSA_OP_SPARSE_ATTN) r = plan_attn(s).bytes;
+    else r = sel_bytes(s) + std::max(plan_index(s).bytes, plan_attn(s).bytes);
+  }
+  g_last_error = saved;
+  return r;
+}
+
+msa_status msa_index_select(const msa_shape* s, const void* q_idx, const void* k_idx, int32_t* sel, void* ws,
+                            size_t ws_bytes, void* stream) {
+  msa_status st = check_shape(s, MSA_OP_INDEX_SELECT);
+  if (st != MSA_OK) return st;
+  if (!q_idx || !k_idx || !sel) return fail(MSA_ERR_INVALID, "q_idx, k_idx and sel must be non-NULL");
+  if (s->q_len == 0) return MSA_OK;
+  IndexPlan ip = plan_index(s);
+  if ((st = check_ws(ws, ws_bytes, ip.bytes)) != MSA_OK) return st;
+  bind_index(ip, (char*)ws, q_idx, k_idx, sel);
+  return hip_status(msa::launch_index_select(ip.p, s->dtype == MSA_BF16, s->index_dim, (hipStream_t)stream),
+                    "index select launch");
+}
+
+msa_status msa_sparse_attn_fwd(const msa_shape* s, const void* q, const void* k, const void* v,
+                               const int32_t* sel, void* out, float* lse, void* ws, size_t ws_bytes,
+                               void* stream) {
+  msa_status st = check_shape(s, MSA_OP_SPARSE_ATTN);
+  if (st != MSA_OK) return st;
+  if (!q || !k || !v || !sel || !out) return fail(MSA_ERR_INVALID, "q, k, v, sel and out must be non-NULL");
+  if (s->q_len == 0) return MSA_OK;
+  AttnPlan ap = plan_attn(s);
+  if ((st = check_ws(ws, ws_bytes, ap.bytes)) != MSA_OK) return st;
+  bind_attn(ap, (char*)ws);
+  ap.p.q = q;
+  ap.p.k = k;
+  ap.p.v = v;
+  ap.p.sel = sel;
+  ap.p.out = out;
+  ap.p.lse = lse;
+  return hip_status(msa::launch_sparse_attention(ap.p, s->dtype == MSA_BF16, (hipStream_t)stream),
+                    "sparse attention launch");
+}
+
+msa_status msa_fwd(const msa_shape* s, const void* q, const void* k, const void* v, const void* q_idx,
+                   const void* k_idx, void* out, int32_t* sel_out, float* lse, void* ws, size_t ws_bytes,
+                   void* stream) {
+  msa_status st = check_shape(s, MSA_OP_FWD);
+  if (st != MSA_OK) return st;
+  if (!q || !k || !v || !q_idx || !k_idx || !out)
+    return fail(MSA_ERR_INVALID, "q, k, v, q_idx, k_idx and out must be non-NULL");
+  if (s->q_len == 0) return MSA_OK;
+  IndexPlan ip = plan_index(s);
+  AttnPlan ap = plan_attn(s);
+  const size_t need = sel_bytes(s) + std::max(ip.bytes, ap.bytes);
+  if ((st = check_ws(ws, ws_bytes, need)) != MSA_OK) return st;
+  char* w = (char*)ws;
+  int32_t* sel = sel_out ? sel_out : (int32_t*)w;
+  char* scratch = w + sel_bytes(s);  // index lists and attention state reuse one region
+  bind_index(ip, scratch, q_idx, k_idx, sel);
+  hipStream_t hs = (hipStream_t)stream;
+  st = hip_status(msa::launch_index_select(ip.p, s->dtype == MSA_BF16, s->index_dim, hs), "index select launch");
+  if (st != MSA_OK) return st;
+  bind_attn(ap, scratch);
+  ap.p.q = q;
+  ap.p.k = k;
+  ap.p.v = v;
+  ap.p.sel = sel;
+  ap.p.out = out;
+  ap.p.lse = lse;
+  return hip_status(msa::launch_sparse_attention(ap.p, s->dtype == MSA_BF16, hs), "sparse attention launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,140 @@
+/*
+ * msa.h - C ABI of the MiniMax Sparse Attention (MSA) forward pass on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * What is computed.  MSA is block-sparse grouped-query attention with two
+ * branches (abstract page "MiniMax 稀疏注意力", sections 摘要 and 核心贡献;
+ * snilld.dk page "MiniMax lancerer MSA", section "Hvad er MSA i praksis"):
+ *
+ *  - Index branch.  For every GQA group g (G = num_kv_heads groups, one
+ *    index-query head each) and every query row i at absolute position
+ *    t = q_offset + i, the raw dot products of q_idx[b,i,g,:] with the single
+ *    shared index-key head k_idx[b,j,:] are max-pooled over absolute blocks of
+ *    Bk tokens (block c = tokens [c*Bk, (c+1)*Bk)).  With L = floor(t / Bk)
+ *    the query's local block, the selection is L plus the best min(k-1, L) of
+ *    the full blocks 0..L-1, ranked by block score descending and, on equal
+ *    scores, block index ascending.  Ranking is done on raw scores: softmax is
+ *    monotone, so no exponential is needed (the exp-free Top-k of the
+ *    abstract).  Selections are per group and are never pooled across index
+ *    heads (issue write-up "Substantial numerical differences with Minimax MSA
+ *    attention vs Minimax's Reference", sections 原因分析 and 解决步骤).
+ *  - Main branch.  Query head h belongs to group g = floor(h / r), r = Hq/G.
+ *    It attends with exact scaled-dot-product softmax to the causally visible
+ *    tokens (j <= t) of its group's selected blocks: one softmax over their
+ *    union, keys and values of KV head g.
+ *
+ * Layouts (all dense, contiguous, row-major; e = 4 bytes for MSA_F32, 2 for
+ * MSA_BF16):
+ *    q, out   [B, S_q, Hq, d]
+ *    k, v     [B, Hkv, S_k, d]       one (head, block) is a contiguous span
+ *    q_idx    [B, S_q, G, D_idx]     G = Hkv index-query heads
+ *    k_idx    [B, S_k, D_idx]        the one shared index-key head
+ *    sel      int32 [B, G, S_q, k]   ascending block ids, then -1 padding
+ *    lse      fp32 [B, Hq, S_q]      natural-log log-sum-exp of the scaled
+ *                                    scores over the attended tokens
+ *
+ * Ownership and threading.  Every data pointer is a device pointer owned by
+ * the caller.  The library allocates no device memory and keeps no state
+ * between calls; scratch memory is the caller's workspace (256-byte aligned,
+ * at least msa_workspace_size() bytes).  Work is enqueued on the given HIP
+ * stream (hipStream_t passed as void*, NULL = the null stream) and the calls
+ * return without synchronising.  Different threads may call concurrently on
+ * different streams with different workspaces.
+ *
+ * Errors.  Arguments are checked on the host before anything is enqueued; on
+ * an error nothing is launched and outputs are untouched.  A failed launch
+ * returns MSA_ERR_HIP.  msa_last_error() gives a thread-local message for the
+ * last failing call of the calling thread.  Device faults surface at the
+ * caller's synchronisation.
+ *
+ * Supported on the GPU: block_size == 128; 1 <= topk <= 32; head_dim in
+ * {64, 128}; index_dim in {32, 64, 128}; r = Hq / Hkv in {1, 2, 4, 8, 16,
+ * 32}; dtype MSA_F32 or MSA_BF16 (the same for q, k, v, q_idx, k_idx);
+ * out_dtype MSA_F32 or the input dtype.  Other values give
+ * MSA_ERR_UNSUPPORTED.  Selections are exact when the index inputs make every
+ * index score exactly representable in fp32 (for example small integers).
+ */
+#ifndef MSA_H_
+#define MSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MSA_OK = 0,
+  MSA_ERR_INVALID = -1,      /* a null pointer, a negative or inconsistent size */
+  MSA_ERR_UNSUPPORTED = -2,  /* a valid shape this build has no kernel for      */
+  MSA_ERR_WORKSPACE = -3,    /* workspace missing, too small or misaligned      */
+  MSA_ERR_HIP = -4           /* a HIP launch or runtime call failed             */
+} msa_status;
+
+typedef enum { MSA_F32 = 0, MSA_BF16 = 1 } msa_dtype;
+
+typedef struct {
+  int32_t batch;        /* B: sequences                                         */
+  int32_t q_len;        /* S_q: query rows per sequence (0 = nothing to do)     */
+  int32_t kv_len;       /* S_k: cached tokens per sequence, >= q_offset + S_q   */
+  int32_t pad0;         /* must be 0                                            */
+  int64_t q_offset;     /* absolute position of query row 0 (every sequence)    */
+  int32_t num_q_heads;  /* Hq                                                   */
+  int32_t num_kv_heads; /* Hkv = G, also the number of index-query heads        */
+  int32_t head_dim;     /* d                                                    */
+  int32_t index_dim;    /* D_idx                                                */
+  int32_t block_size;   /* Bk                                                   */
+  int32_t topk;         /* k: blocks per (query, group), local block included   */
+  float softmax_scale;  /* main-branch scale; 0 means 1/sqrt(d)                 */
+  int32_t dtype;        /* msa_dtype of q, k, v, q_idx, k_idx                   */
+  int32_t out_dtype;    /* msa_dtype of out                                     */
+  int32_t pad1;         /* must be 0                                            */
+} msa_shape;
+
+enum { MSA_OP_INDEX_SELECT = 0, MSA_OP_SPARSE_ATTN = 1, MSA_OP_FWD = 2 };
+
+/* Bytes of workspace the given op needs for this shape (0 when the shape is
+ * invalid or unsupported; the call itself then reports why).  The same shape
+ * always gives the same size. */
+size_t msa_workspace_size(const msa_shape* shape, int op);
+
+/* Index branch: block max-pooled index scores and the per-group exp-free
+ * Top-k with the forced local block (snilld.dk page, "Hvad er MSA i praksis";
+ * the issue write-up, 解决步骤, for the per-index-head [B, H_idx, S_q, topk]
+ * result).  Reads q_idx and k_idx, writes sel [B, G, S_q, k].  The token score
+ * matrix is never stored: block maxima stream through a running Top-k. */
+msa_status msa_index_select(const msa_shape* shape, const void* q_idx, const void* k_idx,
+                            int32_t* sel, void* workspace, size_t workspace_bytes,
+                            void* stream);
+
+/* Main branch for a given selection: exact softmax attention of every query
+ * head over the visible tokens of its group's selected blocks (snilld.dk page,
+ * "Hvad er MSA i praksis"), computed KV-block-outer with the queries that chose
+ * each block gathered together (snilld.dk page, "Teknisk forklaring …"; the
+ * abstract page, 引言, on the swapped FlashAttention loop order).  sel rows must
+ * hold distinct block ids <= the row's local block, ascending, -1 padded, and
+ * must contain the local block.  lse may be NULL. */
+msa_status msa_sparse_attn_fwd(const msa_shape* shape, const void* q, const void* k,
+                               const void* v, const int32_t* sel, void* out, float* lse,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/* Both branches.  sel_out (may be NULL) receives the selection; lse may be NULL. */
+msa_status msa_fwd(const msa_shape* shape, const void* q, const void* k, const void* v,
+                   const void* q_idx, const void* k_idx, void* out, int32_t* sel_out,
+                   float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static string naming a status code. */
+const char* msa_status_string(msa_status status);
+
+/* Thread-local description of the last failing call on this thread ("" if none). */
+const char* msa_last_error(void);
+
+/* Library version, e.g. "0.1.0". */
+const char* msa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MSA_H_ */

@@ -1,0 +1,133 @@
+"""The C ABI without a GPU: the library loads, exports what include/msa.h
+declares, and rejects bad arguments before anything is launched."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import block_sparse_attention_idx_amd as msa
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "msa.h")
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every case below fails validation first
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(msa_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = msa.lib()
+    names = _declared()
+    assert {"msa_index_select", "msa_sparse_attn_fwd", "msa_fwd", "msa_workspace_size",
+            "msa_status_string", "msa_last_error", "msa_version"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", msa.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (msa_\w+)", out))
+    assert set(names) <= exported
+
+
+def test_struct_layout_matches_header():
+    assert ctypes.sizeof(msa.MsaShape) == 64
+    assert msa.MsaShape.q_offset.offset == 16
+    assert msa.MsaShape.softmax_scale.offset == 48
+
+
+def _shape(wid=2, **kw):
+    s = synth.WORKLOADS[wid]
+    import torch
+    sh = msa.make_shape(s.batch, s.q_len, s.kv_len, s.q_offset, s.num_q_heads, s.num_kv_heads, s.head_dim,
+                        s.index_dim, s.topk, torch.float32 if s.dtype == "f32" else torch.bfloat16)
+    for k, v in kw.items():
+        setattr(sh, k, v)
+    return sh
+
+
+def _fwd(sh, ws=None, ws_bytes=0, **ptrs):
+    L = msa.lib()
+    p = {n: FAKE for n in ("q", "k", "v", "q_idx", "k_idx", "out")}
+    p.update(ptrs)
+    return L.msa_fwd(ctypes.byref(sh) if sh is not None else None, p["q"], p["k"], p["v"], p["q_idx"],
+                     p["k_idx"], p["out"], None, None, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("batch", 0, -1), ("q_len", -1, -1), ("kv_len", 0, -1), ("q_offset", -5, -1), ("kv_len", 100, -1),
+    ("num_q_heads", 62, -1), ("num_kv_heads", 0, -1), ("topk", 0, -1), ("block_size", 0, -1),
+    ("dtype", 7, -1), ("out_dtype", 9, -1), ("pad0", 1, -1), ("pad1", 3, -1), ("head_dim", 0, -1),
+    ("block_size", 64, -2), ("topk", 33, -2), ("head_dim", 96, -2), ("index_dim", 48, -2),
+    ("num_q_heads", 12, -2),
+])
+def test_invalid_and_unsupported_shapes(field, value, status):
+    sh = _shape(**{field: value})
+    assert _fwd(sh) == status
+    assert msa.lib().msa_last_error().decode() != ""
+    assert msa.workspace_size(sh, msa.OP_FWD) == 0
+
+
+def test_null_pointers_rejected():
+    L = msa.lib()
+    sh = _shape()
+    assert _fwd(None) == -1
+    for name in ("q", "k", "v", "q_idx", "k_idx", "out"):
+        assert _fwd(sh, **{name: None}) == -1, name
+    assert L.msa_index_select(ctypes.byref(sh), FAKE, None, FAKE, None, 0, None) == -1
+    assert L.msa_sparse_attn_fwd(ctypes.byref(sh), FAKE, FAKE, FAKE, None, FAKE, None, None, 0, None) == -1
+
+
+def test_nonfinite_scale_rejected():
+    sh = _shape()
+    sh.softmax_scale = float("nan")
+    assert _fwd(sh) == -1
+
+
+def test_workspace_checks():
+    sh = _shape()
+    need = msa.workspace_size(sh, msa.OP_FWD)
+    assert need > 0
+    assert _fwd(sh) == -3  # NULL workspace
+    assert _fwd(sh, ctypes.c_void_p(0x10010), need) == -3  # not 256-byte aligned
+    assert _fwd(sh, ctypes.c_void_p(0x10000), need - 1) == -3  # too small
+    assert "workspace" in msa.lib().msa_last_error().decode()
+
+
+def test_empty_query_is_a_no_op():
+    sh = _shape(q_len=0)
+    assert _fwd(sh) == 0
+    assert msa.workspace_size(sh, msa.OP_FWD) == 0
+
+
+def test_status_strings_and_version():
+    L = msa.lib()
+    for st, name in ((0, "MSA_OK"), (-1, "MSA_ERR_INVALID"), (-2, "MSA_ERR_UNSUPPORTED"),
+                     (-3, "MSA_ERR_WORKSPACE"), (-4, "MSA_ERR_HIP")):
+        assert L.msa_status_string(st).decode() == name
+    assert re.match(r"\d+\.\d+\.\d+", L.msa_version().decode())
+
+
+def test_workspace_sizes_for_the_workloads():
+    # deterministic, and large enough for the partial states the main branch keeps
+    for wid, s in synth.WORKLOADS.items():
+        sh = _shape(wid)
+        a = msa.workspace_size(sh, msa.OP_FWD)
+        assert a == msa.workspace_size(sh, msa.OP_FWD) and a % 256 == 0
+        e = 4 if s.dtype == "f32" else 2
+        partials = s.batch * s.q_len * s.num_q_heads * s.topk * s.head_dim * e
+        assert a >= partials
+        assert msa.workspace_size(sh, msa.OP_INDEX_SELECT) > 0
+        assert msa.workspace_size(sh, msa.OP_SPARSE_ATTN) <= a
+    # a bad op code gives 0
+    assert msa.lib().msa_workspace_size(ctypes.byref(_shape()), 7) == 0
+
+
+def test_python_layer_rejects_cpu_tensors():
+    import torch
+    q = torch.zeros(1, 4, 2, 64)
+    with pytest.raises(ValueError):
+        msa.sparse_attn_fwd(q, q, q, torch.zeros(1, 2, 4, 1, dtype=torch.int32))
