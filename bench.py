@@ -1,0 +1,291 @@
+"""Benchmark of the MSA forward on one MI355X.
+
+Prints ONE JSON line.  A step is one msa_fwd call (index branch: scores,
+block max-pool, per-group Top-k; main branch: query gather, KV-outer sparse
+attention, combine) over one batch of the prefill workload (B=2, S=32768,
+Hq=64, Hkv=4, d=128, D_idx=128, Bk=128, k=16, bf16), inputs resident in HBM.
+``value`` is the algorithmic TFLOP/s of the whole step (main + index branch
+FLOPs, the masked half of the local block and the skipped blocks excluded).
+
+``roofline`` is for the dominant kernel (the KV-outer attention kernel): its
+algorithmic FLOPs per launch over its own average duration, timed with HIP
+events recorded around that kernel on the stream it runs on.  The decode
+workload (64 sequences x 128K cache) is reported beside it in GB/s of
+algorithmic HBM bytes.  ``cpu_baseline`` times the fp64 CPU oracle on a bounded
+sample of query rows of the same workload.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--decode-steps 50]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+METRIC = "MSA fwd TFLOP/s (prefill 32K/128K) + decode KV GB/s, % of MI355X roofline"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+KERNELS = {"index_score": 1, "topk_merge": 2, "gather": 3, "attention": 4, "combine": 5}
+
+
+class HipEvents:
+    """Raw hipEvent_t pairs (the library records them around one kernel)."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self):
+        e = ctypes.c_void_p()
+        if self.hip.hipEventCreate(ctypes.byref(e)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        return e
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        if self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(ms.value)
+
+    def destroy(self, e):
+        self.hip.hipEventDestroy(e)
+
+
+def algorithmic_work(s: synth.Shape):
+    """(main-branch FLOP, index-branch FLOP, decode HBM bytes) of one msa_fwd call.
+
+    main:  4*d*Hq*B * sum_i [(n_sel(t)-1)*Bk + (t mod Bk) + 1], n_sel = min(k, L+1)
+    index: 2*D_idx*G*B * sum_i L(t)*Bk           (only full blocks before L are scored)
+    bytes: B*[S_k*D_idx*e + G*n_sel*Bk*d*e*2 + 2*Hq*d*e + G*D_idx*e + 4*G*k]
+    """
+    t = s.q_offset + np.arange(s.q_len, dtype=np.int64)
+    L = t // s.block_size
+    n_sel = np.minimum(s.topk, L + 1)
+    toks = (n_sel - 1) * s.block_size + (t % s.block_size) + 1
+    flop_main = 4.0 * s.head_dim * s.num_q_heads * s.batch * float(toks.sum())
+    flop_index = 2.0 * s.index_dim * s.groups * s.batch * float((L * s.block_size).sum())
+    e = 2 if s.dtype == "bf16" else 4
+    nsel_last = int(n_sel[-1])
+    bytes_dec = s.batch * (s.kv_len * s.index_dim * e + s.groups * nsel_last * s.block_size * s.head_dim * e * 2
+                           + 2 * s.num_q_heads * s.head_dim * e + s.groups * s.index_dim * e + 4 * s.groups * s.topk)
+    return flop_main, flop_index, float(bytes_dec)
+
+
+class Runner:
+    """One workload on the GPU: inputs, outputs and workspace allocated once."""
+
+    def __init__(self, msa, s: synth.Shape, wid: int):
+        self.msa, self.s = msa, s
+        self.x = synth.inputs_for(s, wid, device="cuda")
+        dev = self.x["q"].device
+        self.out = torch.empty((s.batch, s.q_len, s.num_q_heads, s.head_dim), dtype=s.torch_dtype, device=dev)
+        self.sel = torch.empty((s.batch, s.groups, s.q_len, s.topk), dtype=torch.int32, device=dev)
+        self.shape = msa.make_shape(s.batch, s.q_len, s.kv_len, s.q_offset, s.num_q_heads, s.num_kv_heads,
+                                    s.head_dim, s.index_dim, s.topk, s.torch_dtype)
+        n = msa.workspace_size(self.shape, msa.OP_FWD)
+        self.ws_raw = torch.empty(n + 256, dtype=torch.uint8, device=dev)
+        off = (-self.ws_raw.data_ptr()) % 256
+        self.ws = self.ws_raw[off:off + n]
+        self.L = msa.lib()
+        self.stream = torch.cuda.current_stream(dev)
+        self.args = [ctypes.byref(self.shape)] + [ctypes.c_void_p(self.x[n_].data_ptr())
+                                                   for n_ in ("q", "k", "v", "q_idx", "k_idx")]
+        self.args += [ctypes.c_void_p(self.out.data_ptr()), ctypes.c_void_p(self.sel.data_ptr()), None,
+                      ctypes.c_void_p(self.ws.data_ptr()), ctypes.c_size_t(self.ws.numel()),
+                      ctypes.c_void_p(self.stream.cuda_stream)]
+
+    def step(self):
+        st = self.L.msa_fwd(*self.args)
+        if st != 0:
+            raise RuntimeError(self.L.msa_last_error().decode())
+
+    def time_steps(self, steps, warmup, timed_kernel=None):
+        """Returns (ms per step, list of per-step ms of timed_kernel or None)."""
+        for _ in range(warmup):
+            self.step()
+        torch.cuda.synchronize()
+        ev = HipEvents() if timed_kernel else None
+        kev = [(ev.create(), ev.create()) for _ in range(steps)] if timed_kernel else None
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record(self.stream)
+        for i in range(steps):
+            if kev:
+                self.L.msa_set_kernel_timer(KERNELS[timed_kernel], kev[i][0], kev[i][1])
+            self.step()
+        t1.record(self.stream)
+        torch.cuda.synchronize()
+        self.L.msa_set_kernel_timer(0, None, None)
+        total = t0.elapsed_time(t1)
+        per_kernel = None
+        if kev:
+            per_kernel = [ev.elapsed_ms(a, b) for a, b in kev]
+            for a, b in kev:
+                ev.destroy(a)
+                ev.destroy(b)
+        return total / steps, per_kernel
+
+    def kernel_breakdown(self, steps=3):
+        res = {}
+        for name in KERNELS:
+            if name == "gather" and self.s.q_len <= 4:
+                continue
+            _, ks = self.time_steps(steps, 0, name)
+            res[name] = float(np.median(ks))
+        return res
+
+
+def cpu_baseline(s: synth.Shape, x, out_gpu, sel_gpu, budget_s: float):
+    """Time the fp64 oracle on growing samples of query rows until ~budget_s."""
+    from oracle import msa_oracle as orc
+    import threadpoolctl
+
+    def host(t):
+        t = t.detach().cpu()
+        return (t.float() if t.dtype == torch.bfloat16 else t).numpy()
+
+    q, k, v = host(x["q"]), host(x["k"]), host(x["v"])
+    q_idx, k_idx = host(x["q_idx"]), host(x["k_idx"])
+    rng = np.random.default_rng(1234)
+    flop_per_row = []
+    rows_done = []
+    elapsed = 0.0
+    sel_ok, max_err = True, 0.0
+    out_np = host(out_gpu)
+    sel_np = sel_gpu.cpu().numpy()
+    batch = 16
+    while elapsed < budget_s and len(rows_done) < s.batch * s.q_len:
+        rows = [(int(rng.integers(0, s.batch)), int(rng.integers(0, s.q_len))) for _ in range(batch)]
+        t0 = time.perf_counter()
+        o, sel, _ = orc.msa_forward(q, k, v, q_idx, k_idx, s.topk, s.q_offset, s.block_size, rows=rows)
+        elapsed += time.perf_counter() - t0
+        for b, i in rows:
+            t = s.q_offset + i
+            L = t // s.block_size
+            n_sel = min(s.topk, L + 1)
+            flop_per_row.append(4.0 * s.head_dim * s.num_q_heads * ((n_sel - 1) * s.block_size + t % s.block_size + 1)
+                                + 2.0 * s.index_dim * s.groups * L * s.block_size)
+            sel_ok &= bool(np.array_equal(sel_np[b, :, i], sel[b, :, i]))
+            max_err = max(max_err, float(np.abs(out_np[b, i] - o[b, i]).max()))
+        rows_done += rows
+    info = threadpoolctl.threadpool_info()
+    threads = max([d.get("num_threads", 1) for d in info if d.get("user_api") == "blas"] or [1])
+    return {
+        "value": sum(flop_per_row) / elapsed / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{len(rows_done)} random query rows (all {s.groups} groups, both branches) of "
+                  f"the {synth.WORKLOAD_NAMES.get(3)} workload, {elapsed:.1f} s of fp64 numpy",
+        "host_cpus": os.cpu_count(),
+        "gpu_rows_match": {"selection_equal": sel_ok, "max_abs_err": max_err},
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-steps", type=int, default=50)
+    ap.add_argument("--workload", type=int, default=3)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this MSA build has no multi-GPU path (asked for --gpus {args.gpus})",
+              file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+
+    import block_sparse_attention_idx_amd as msa
+    msa.lib()
+    wid = args.workload
+    s = synth.WORKLOADS[wid]
+    flop_main, flop_index, _ = algorithmic_work(s)
+    print(f"[bench] {synth.WORKLOAD_NAMES[wid]}: generating inputs", file=sys.stderr, flush=True)
+    run = Runner(msa, s, wid)
+    print("[bench] timing msa_fwd", file=sys.stderr, flush=True)
+    ms, attn_ms = run.time_steps(args.steps, args.warmup, "attention")
+    kern = run.kernel_breakdown()
+    attn_avg = float(np.mean(attn_ms))
+    value = (flop_main + flop_index) / (ms * 1e-3) / 1e12
+    achieved = flop_main / (attn_avg * 1e-3) / 1e12
+    result = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": synth.WORKLOAD_NAMES[wid], "batch": s.batch, "q_len": s.q_len,
+                   "kv_len": s.kv_len, "q_offset": s.q_offset, "num_q_heads": s.num_q_heads,
+                   "num_kv_heads": s.num_kv_heads, "head_dim": s.head_dim, "index_dim": s.index_dim,
+                   "block_size": s.block_size, "topk": s.topk},
+        "roofline": {"bound": "mfma", "kernel": "attn_kvouter", "achieved": round(achieved, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "flop_per_launch": flop_main, "avg_launch_ms": round(attn_avg, 4)},
+        "work": {"flop_main": flop_main, "flop_index": flop_index,
+                 "index_tflops": round(flop_index / (kern["index_score"] * 1e-3) / 1e12, 2)},
+        "kernels_ms": {k: round(v, 4) for k, v in kern.items()},
+    }
+    print(f"[bench] {ms:.3f} ms/step, attention {attn_avg:.3f} ms", file=sys.stderr, flush=True)
+
+    if not args.no_cpu:
+        print("[bench] cpu baseline (oracle on sampled rows)", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(s, run.x, run.out, run.sel, args.cpu_budget)
+    else:
+        result["cpu_baseline"] = None
+    del run
+    torch.cuda.empty_cache()
+
+    if not args.no_decode:
+        sd = synth.WORKLOADS[4]
+        _, _, dec_bytes = algorithmic_work(sd)
+        print("[bench] decode_128k_b64: generating inputs", file=sys.stderr, flush=True)
+        drun = Runner(msa, sd, 4)
+        dms, idx_ms = drun.time_steps(args.decode_steps, args.warmup, "index_score")
+        dk = drun.kernel_breakdown()
+        gbs = dec_bytes / (dms * 1e-3) / 1e9
+        idx_avg = float(np.mean(idx_ms))
+        kidx_bytes = float(sd.batch * sd.kv_len * sd.index_dim * 2)
+        result["decode"] = {
+            "workload": synth.WORKLOAD_NAMES[4], "value": round(gbs, 1), "unit": "GB/s",
+            "ms_per_step": round(dms, 4), "steps": args.decode_steps, "bytes_per_step": dec_bytes,
+            "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+            "roofline": {"bound": "hbm", "kernel": "index_topk", "achieved": round(kidx_bytes / (idx_avg * 1e-3) / 1e9, 1),
+                         "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(kidx_bytes / (idx_avg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                         "bytes_per_launch": kidx_bytes, "avg_launch_ms": round(idx_avg, 4)},
+            "kernels_ms": {k: round(v, 4) for k, v in dk.items()},
+        }
+        del drun
+        torch.cuda.empty_cache()
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

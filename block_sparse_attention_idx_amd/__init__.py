@@ -88,6 +88,8 @@ def lib() -> ctypes.CDLL:
         L.msa_last_error.restype = ctypes.c_char_p
         L.msa_version.argtypes = []
         L.msa_version.restype = ctypes.c_char_p
+        L.msa_set_kernel_timer.argtypes = [ctypes.c_int, vp, vp]
+        L.msa_set_kernel_timer.restype = ctypes.c_int
         _LIB = L
     return _LIB
 

@@ -361,45 +361,51 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnParams p) {
 }
 
 template <typename T, int D, int R>
-static hipError_t launch_attn_t(const AttnParams& p, hipStream_t s) {
+static hipError_t launch_attn_t(const AttnParams& p, hipStream_t s, const KernelTimer* tm) {
   const int64_t entries = (int64_t)p.B * p.G * p.S_q * p.topk;
   if (!p.direct) {
+    timer_start(tm, kKernGather, s);
     hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)((p.nbuckets + 255) / 256)), dim3(256), 0, s,
                        p.counts, (int64_t)p.nbuckets);
     hipLaunchKernelGGL(gather_count_kernel, dim3((unsigned)((entries + 255) / 256)), dim3(256), 0, s, p);
     hipLaunchKernelGGL(gather_scan_kernel, dim3(1), dim3(1024), 0, s, p);
     hipLaunchKernelGGL(gather_scatter_kernel, dim3((unsigned)((entries + 255) / 256)), dim3(256), 0, s, p);
+    timer_stop(tm, kKernGather, s);
   }
+  timer_start(tm, kKernAttention, s);
   hipLaunchKernelGGL((attn_kvouter_kernel<T, D, R>), dim3(p.grid), dim3(256), 0, s, p);
+  timer_stop(tm, kKernAttention, s);
+  timer_start(tm, kKernCombine, s);
   constexpr int CE = 16 / (int)sizeof(T);
   const int64_t units = (int64_t)p.B * p.S_q * p.Hq * (D / CE);
   if (p.out_f32)
     hipLaunchKernelGGL((combine_kernel<T, float, D>), dim3((unsigned)((units + 255) / 256)), dim3(256), 0, s, p);
   else
     hipLaunchKernelGGL((combine_kernel<T, T, D>), dim3((unsigned)((units + 255) / 256)), dim3(256), 0, s, p);
+  timer_stop(tm, kKernCombine, s);
   return hipGetLastError();
 }
 
 template <typename T, int D>
-static hipError_t launch_attn_d(const AttnParams& p, hipStream_t s) {
+static hipError_t launch_attn_d(const AttnParams& p, hipStream_t s, const KernelTimer* tm) {
   switch (p.r) {
-    case 1: return launch_attn_t<T, D, 1>(p, s);
-    case 2: return launch_attn_t<T, D, 2>(p, s);
-    case 4: return launch_attn_t<T, D, 4>(p, s);
-    case 8: return launch_attn_t<T, D, 8>(p, s);
-    case 16: return launch_attn_t<T, D, 16>(p, s);
-    case 32: return launch_attn_t<T, D, 32>(p, s);
+    case 1: return launch_attn_t<T, D, 1>(p, s, tm);
+    case 2: return launch_attn_t<T, D, 2>(p, s, tm);
+    case 4: return launch_attn_t<T, D, 4>(p, s, tm);
+    case 8: return launch_attn_t<T, D, 8>(p, s, tm);
+    case 16: return launch_attn_t<T, D, 16>(p, s, tm);
+    case 32: return launch_attn_t<T, D, 32>(p, s, tm);
   }
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_sparse_attention(const AttnParams& p, bool bf16_inputs, hipStream_t s) {
+hipError_t launch_sparse_attention(const AttnParams& p, bool bf16_inputs, hipStream_t s, const KernelTimer* tm) {
   if (bf16_inputs) {
-    if (p.d == 64) return launch_attn_d<bf16, 64>(p, s);
-    if (p.d == 128) return launch_attn_d<bf16, 128>(p, s);
+    if (p.d == 64) return launch_attn_d<bf16, 64>(p, s, tm);
+    if (p.d == 128) return launch_attn_d<bf16, 128>(p, s, tm);
   } else {
-    if (p.d == 64) return launch_attn_d<float, 64>(p, s);
-    if (p.d == 128) return launch_attn_d<float, 128>(p, s);
+    if (p.d == 64) return launch_attn_d<float, 64>(p, s, tm);
+    if (p.d == 128) return launch_attn_d<float, 128>(p, s, tm);
   }
   return hipErrorInvalidValue;
 }

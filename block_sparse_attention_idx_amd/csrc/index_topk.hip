@@ -267,33 +267,38 @@ __global__ __launch_bounds__(256) void topk_merge_kernel(IndexParams p) {
 }
 
 template <typename T, int DI, int CAP>
-static hipError_t launch_index_t(const IndexParams& p, hipStream_t s) {
+static hipError_t launch_index_t(const IndexParams& p, hipStream_t s, const KernelTimer* tm) {
+  timer_start(tm, kKernIndexScore, s);
   hipLaunchKernelGGL((index_topk_kernel<T, DI, CAP, 2>), dim3(p.grid_per_xcd * 8), dim3(256), 0, s, p);
+  timer_stop(tm, kKernIndexScore, s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t rows = (int64_t)p.B * p.rows_per_b;
+  timer_start(tm, kKernTopkMerge, s);
   hipLaunchKernelGGL((topk_merge_kernel<CAP>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, p);
+  timer_stop(tm, kKernTopkMerge, s);
   return hipGetLastError();
 }
 
 template <typename T, int DI>
-static hipError_t launch_index_d(const IndexParams& p, hipStream_t s) {
-  if (p.topk <= 16) return launch_index_t<T, DI, 15>(p, s);
-  return launch_index_t<T, DI, 31>(p, s);
+static hipError_t launch_index_d(const IndexParams& p, hipStream_t s, const KernelTimer* tm) {
+  if (p.topk <= 16) return launch_index_t<T, DI, 15>(p, s, tm);
+  return launch_index_t<T, DI, 31>(p, s, tm);
 }
 
-hipError_t launch_index_select(const IndexParams& p, bool bf16_inputs, int index_dim, hipStream_t s) {
+hipError_t launch_index_select(const IndexParams& p, bool bf16_inputs, int index_dim, hipStream_t s,
+                               const KernelTimer* tm) {
   if (bf16_inputs) {
     switch (index_dim) {
-      case 32: return launch_index_d<bf16, 32>(p, s);
-      case 64: return launch_index_d<bf16, 64>(p, s);
-      case 128: return launch_index_d<bf16, 128>(p, s);
+      case 32: return launch_index_d<bf16, 32>(p, s, tm);
+      case 64: return launch_index_d<bf16, 64>(p, s, tm);
+      case 128: return launch_index_d<bf16, 128>(p, s, tm);
     }
   } else {
     switch (index_dim) {
-      case 32: return launch_index_d<float, 32>(p, s);
-      case 64: return launch_index_d<float, 64>(p, s);
-      case 128: return launch_index_d<float, 128>(p, s);
+      case 32: return launch_index_d<float, 32>(p, s, tm);
+      case 64: return launch_index_d<float, 64>(p, s, tm);
+      case 128: return launch_index_d<float, 128>(p, s, tm);
     }
   }
   return hipErrorInvalidValue;

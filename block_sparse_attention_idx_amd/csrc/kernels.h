@@ -10,6 +10,21 @@ namespace msa {
 
 constexpr int kBlock = 128;  // Bk: tokens per KV block, fixed on the GPU path
 
+// Optional events recorded around one kernel (see msa_set_kernel_timer).
+struct KernelTimer {
+  int which;  // msa_kernel id, 0 = off
+  hipEvent_t start, stop;
+};
+
+inline void timer_start(const KernelTimer* t, int which, hipStream_t s) {
+  if (t && t->which == which) (void)hipEventRecord(t->start, s);
+}
+inline void timer_stop(const KernelTimer* t, int which, hipStream_t s) {
+  if (t && t->which == which) (void)hipEventRecord(t->stop, s);
+}
+
+enum { kKernIndexScore = 1, kKernTopkMerge = 2, kKernGather = 3, kKernAttention = 4, kKernCombine = 5 };
+
 // Index branch (index_topk.hip).
 struct IndexParams {
   const void* q_idx;   // [B, S_q, G, D]
@@ -29,7 +44,8 @@ struct IndexParams {
 
 constexpr int kIndexRowsPerWG = 256;
 
-hipError_t launch_index_select(const IndexParams& p, bool bf16_inputs, int index_dim, hipStream_t s);
+hipError_t launch_index_select(const IndexParams& p, bool bf16_inputs, int index_dim, hipStream_t s,
+                               const KernelTimer* timer);
 
 // Main branch (attn.hip).
 struct AttnParams {
@@ -62,6 +78,6 @@ struct AttnParams {
   int out_f32;         // output dtype: 1 fp32, 0 input dtype
 };
 
-hipError_t launch_sparse_attention(const AttnParams& p, bool bf16_inputs, hipStream_t s);
+hipError_t launch_sparse_attention(const AttnParams& p, bool bf16_inputs, hipStream_t s, const KernelTimer* timer);
 
 }  // namespace msa

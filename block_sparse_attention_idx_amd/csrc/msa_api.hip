@@ -14,6 +14,9 @@
 namespace {
 
 thread_local std::string g_last_error;
+thread_local msa::KernelTimer g_timer = {0, nullptr, nullptr};
+
+const msa::KernelTimer* timer() { return g_timer.which ? &g_timer : nullptr; }
 
 msa_status fail(msa_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 msa_status fail(msa_status st, const char* fmt, ...) {
@@ -230,6 +233,17 @@ extern "C" {
 
 const char* msa_version(void) { return "0.1.0"; }
 
+msa_status msa_set_kernel_timer(int kernel, void* start_event, void* stop_event) {
+  if (kernel < MSA_KERNEL_NONE || kernel > MSA_KERNEL_COMBINE)
+    return fail(MSA_ERR_INVALID, "unknown kernel id %d", kernel);
+  if (kernel == MSA_KERNEL_NONE || !start_event || !stop_event) {
+    g_timer = {0, nullptr, nullptr};
+    return MSA_OK;
+  }
+  g_timer = {kernel, (hipEvent_t)start_event, (hipEvent_t)stop_event};
+  return MSA_OK;
+}
+
 const char* msa_status_string(msa_status st) {
   switch (st) {
     case MSA_OK: return "MSA_OK";
@@ -264,7 +278,7 @@ msa_status msa_index_select(const msa_shape* s, const void* q_idx, const void* k
   IndexPlan ip = plan_index(s);
   if ((st = check_ws(ws, ws_bytes, ip.bytes)) != MSA_OK) return st;
   bind_index(ip, (char*)ws, q_idx, k_idx, sel);
-  return hip_status(msa::launch_index_select(ip.p, s->dtype == MSA_BF16, s->index_dim, (hipStream_t)stream),
+  return hip_status(msa::launch_index_select(ip.p, s->dtype == MSA_BF16, s->index_dim, (hipStream_t)stream, timer()),
                     "index select launch");
 }
 
@@ -284,7 +298,7 @@ msa_status msa_sparse_attn_fwd(const msa_shape* s, const void* q, const void* k,
   ap.p.sel = sel;
   ap.p.out = out;
   ap.p.lse = lse;
-  return hip_status(msa::launch_sparse_attention(ap.p, s->dtype == MSA_BF16, (hipStream_t)stream),
+  return hip_status(msa::launch_sparse_attention(ap.p, s->dtype == MSA_BF16, (hipStream_t)stream, timer()),
                     "sparse attention launch");
 }
 
@@ -305,7 +319,7 @@ msa_status msa_fwd(const msa_shape* s, const void* q, const void* k, const void*
   char* scratch = w + sel_bytes(s);  // index lists and attention state reuse one region
   bind_index(ip, scratch, q_idx, k_idx, sel);
   hipStream_t hs = (hipStream_t)stream;
-  st = hip_status(msa::launch_index_select(ip.p, s->dtype == MSA_BF16, s->index_dim, hs), "index select launch");
+  st = hip_status(msa::launch_index_select(ip.p, s->dtype == MSA_BF16, s->index_dim, hs, timer()), "index select launch");
   if (st != MSA_OK) return st;
   bind_attn(ap, scratch);
   ap.p.q = q;
@@ -314,7 +328,7 @@ msa_status msa_fwd(const msa_shape* s, const void* q, const void* k, const void*
   ap.p.sel = sel;
   ap.p.out = out;
   ap.p.lse = lse;
-  return hip_status(msa::launch_sparse_attention(ap.p, s->dtype == MSA_BF16, hs), "sparse attention launch");
+  return hip_status(msa::launch_sparse_attention(ap.p, s->dtype == MSA_BF16, hs, timer()), "sparse attention launch");
 }
 
 }  // extern "C"

@@ -124,6 +124,23 @@ msa_status msa_fwd(const msa_shape* shape, const void* q, const void* k, const v
                    const void* q_idx, const void* k_idx, void* out, int32_t* sel_out,
                    float* lse, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Kernels of the forward path, for msa_set_kernel_timer. */
+typedef enum {
+  MSA_KERNEL_NONE = 0,
+  MSA_KERNEL_INDEX_SCORE = 1, /* index scores, block max-pool, partial top lists */
+  MSA_KERNEL_TOPK_MERGE = 2,  /* merge of the partial lists, local block, -1 pad   */
+  MSA_KERNEL_GATHER = 3,      /* query gather: histogram, scan, scatter (4 launches) */
+  MSA_KERNEL_ATTENTION = 4,   /* KV-outer sparse attention (partial states)         */
+  MSA_KERNEL_COMBINE = 5      /* merge of the partial states into out and lse       */
+} msa_kernel;
+
+/* Profiling hook.  For the calling thread, every later msa_* call records
+ * start_event (a hipEvent_t) on its stream right before launching `kernel` and
+ * stop_event right after it, so hipEventElapsedTime gives that kernel's own
+ * duration.  kernel = MSA_KERNEL_NONE (or NULL events) turns the hook off.
+ * The events stay owned by the caller. */
+msa_status msa_set_kernel_timer(int kernel, void* start_event, void* stop_event);
+
 /* Static string naming a status code. */
 const char* msa_status_string(msa_status status);
 
