@@ -206,6 +206,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--no-breakdown", action="store_true", help="skip the per-kernel timing passes")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this MSA build has no multi-GPU path (asked for --gpus {args.gpus})",
@@ -224,7 +225,7 @@ def main():
     run = Runner(msa, s, wid)
     print("[bench] timing msa_fwd", file=sys.stderr, flush=True)
     ms, attn_ms = run.time_steps(args.steps, args.warmup, "attention")
-    kern = run.kernel_breakdown()
+    kern = {} if args.no_breakdown else run.kernel_breakdown()
     attn_avg = float(np.mean(attn_ms))
     value = (flop_main + flop_index) / (ms * 1e-3) / 1e12
     achieved = flop_main / (attn_avg * 1e-3) / 1e12
@@ -249,7 +250,7 @@ def main():
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": None, "flop_per_launch": flop_main, "avg_launch_ms": round(attn_avg, 4)},
         "work": {"flop_main": flop_main, "flop_index": flop_index,
-                 "index_tflops": round(flop_index / (kern["index_score"] * 1e-3) / 1e12, 2)},
+                 "index_tflops": round(flop_index / (kern["index_score"] * 1e-3) / 1e12, 2) if kern else None},
         "kernels_ms": {k: round(v, 4) for k, v in kern.items()},
     }
     print(f"[bench] {ms:.3f} ms/step, attention {attn_avg:.3f} ms", file=sys.stderr, flush=True)
@@ -268,7 +269,7 @@ def main():
         print("[bench] decode_128k_b64: generating inputs", file=sys.stderr, flush=True)
         drun = Runner(msa, sd, 4)
         dms, idx_ms = drun.time_steps(args.decode_steps, args.warmup, "index_score")
-        dk = drun.kernel_breakdown()
+        dk = {} if args.no_breakdown else drun.kernel_breakdown()
         gbs = dec_bytes / (dms * 1e-3) / 1e9
         idx_avg = float(np.mean(idx_ms))
         kidx_bytes = float(sd.batch * sd.kv_len * sd.index_dim * 2)

@@ -35,14 +35,81 @@ __global__ void fill_zero_kernel(int32_t* __restrict__ p, int64_t n) {
   if (i < n) p[i] = 0;
 }
 
+// Query gather.  A workgroup takes kGatherRows query rows of one (b, g),
+// histograms their selection entries in LDS, and adds each non-zero bin to the
+// global bucket count with one atomic.  The scatter pass redoes the histogram,
+// reserves one contiguous range per bin with one atomic on the bucket cursor,
+// and places entries with LDS atomics.  The order of entries inside a bucket is
+// arbitrary; every entry's result is computed independently of its neighbours.
+constexpr int kGatherRows = 256;
+constexpr int kMaxHistBins = 16384;  // 64 KiB of LDS counters
+
+template <bool SCATTER>
+__global__ __launch_bounds__(256) void gather_hist_kernel(AttnParams p) {
+  extern __shared__ int32_t hist[];
+  const int bg = blockIdx.y;
+  const int i0 = blockIdx.x * kGatherRows;
+  const int rows = min(kGatherRows, p.S_q - i0);
+  for (int c = threadIdx.x; c < p.nb; c += 256) hist[c] = 0;
+  __syncthreads();
+  const int32_t* sbase = p.sel + ((int64_t)bg * p.S_q + i0) * p.topk;
+  const int n = rows * p.topk;
+  for (int e = threadIdx.x; e < n; e += 256) {
+    const int c = sbase[e];
+    if (c >= 0 && c < p.nb) atomicAdd(&hist[c], 1);  // ids outside the cache are ignored
+  }
+  __syncthreads();
+  int32_t* gcount = (SCATTER ? p.cursor : p.counts) + (int64_t)bg * p.nb;
+  for (int c = threadIdx.x; c < p.nb; c += 256) {
+    const int h = hist[c];
+    if (h) {
+      const int base = atomicAdd(&gcount[c], h);
+      if (SCATTER) hist[c] = base;
+    }
+  }
+  if (!SCATTER) return;
+  __syncthreads();
+  for (int e = threadIdx.x; e < n; e += 256) {
+    const int c = sbase[e];
+    if (c >= 0 && c < p.nb) {
+      const int pos = atomicAdd(&hist[c], 1);
+      const int i = i0 + e / p.topk, slot = e - (e / p.topk) * p.topk;
+      p.entries[pos] = (i << 6) | slot;
+    }
+  }
+}
+
+// Same result for caches too long for an LDS histogram: one global atomic per entry.
 __global__ __launch_bounds__(256) void gather_count_kernel(AttnParams p) {
   const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t total = (int64_t)p.B * p.G * p.S_q * p.topk;
   if (e >= total) return;
   const int c = p.sel[e];
-  if (c < 0 || c >= p.nb) return;  // ids outside the cache are ignored, never dereferenced
+  if (c < 0 || c >= p.nb) return;
   const int64_t bg = e / ((int64_t)p.S_q * p.topk);  // b * G + g
   atomicAdd(&p.counts[bg * p.nb + c], 1);
+}
+
+// item -> bucket table: one thread per bucket writes the ids of its items.
+__global__ __launch_bounds__(256) void item_table_kernel(AttnParams p) {
+  const int bk = blockIdx.x * 256 + threadIdx.x;
+  if (bk >= p.nbuckets) return;
+  const int a = p.item_off[bk], e = p.item_off[bk + 1];
+  for (int it = a; it < e; ++it) p.item_bucket[it] = bk;
+}
+
+__global__ __launch_bounds__(256) void gather_scatter_kernel(AttnParams p) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t total = (int64_t)p.B * p.G * p.S_q * p.topk;
+  if (e >= total) return;
+  const int c = p.sel[e];
+  if (c < 0 || c >= p.nb) return;
+  const int slot = (int)(e % p.topk);
+  const int64_t rest = e / p.topk;
+  const int i = (int)(rest % p.S_q);
+  const int64_t bg = rest / p.S_q;
+  const int pos = atomicAdd(&p.cursor[bg * p.nb + c], 1);
+  p.entries[pos] = (i << 6) | slot;
 }
 
 // Single workgroup: exclusive scans of the bucket sizes (entries and items).
@@ -88,20 +155,6 @@ __global__ __launch_bounds__(1024) void gather_scan_kernel(AttnParams p) {
   }
 }
 
-__global__ __launch_bounds__(256) void gather_scatter_kernel(AttnParams p) {
-  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t total = (int64_t)p.B * p.G * p.S_q * p.topk;
-  if (e >= total) return;
-  const int c = p.sel[e];
-  if (c < 0 || c >= p.nb) return;
-  const int slot = (int)(e % p.topk);
-  const int64_t rest = e / p.topk;
-  const int i = (int)(rest % p.S_q);
-  const int64_t bg = rest / p.S_q;
-  const int pos = atomicAdd(&p.cursor[bg * p.nb + c], 1);
-  p.entries[pos] = (i << 6) | slot;
-}
-
 // E x E transpose of 16-byte rows (E = 16 / sizeof(T)).
 template <typename T, int E>
 __device__ __forceinline__ void transpose_tile(const Chunk16 (&in)[E], Chunk16 (&out)[E]) {
@@ -114,13 +167,15 @@ __device__ __forceinline__ void transpose_tile(const Chunk16 (&in)[E], Chunk16 (
 }
 
 template <typename T, int D, int R>
-__global__ __launch_bounds__(256) void attn_kvouter_kernel(AttnParams p) {
+__global__ __launch_bounds__(256, 2) void attn_kvouter_kernel(AttnParams p) {
   using M = Mma<T>;
   using frag = typename M::frag;
   constexpr int KPL = M::KPL, KSTEP = M::KSTEP, NKS = D / KSTEP;
   constexpr int E = 16 / (int)sizeof(T);  // elements per 16-byte chunk
   constexpr int LDK = D + E;              // K row pitch (elements)
-  constexpr int LDV = kBlock + E;         // V^T row pitch (elements)
+  // V^T row pitch: 8 bytes beyond a multiple of 256 B, so the 32 rows one
+  // 8-byte read instruction touches fall in distinct LDS banks
+  constexpr int LDV = kBlock + 8 / (int)sizeof(T);
   constexpr int TPW = 32 / R;             // query tokens per wave per pass
   constexpr int TPP = 4 * TPW;            // query tokens per pass
   constexpr int NDT = D / 32;             // 32-wide output tiles along d
@@ -149,14 +204,7 @@ __global__ __launch_bounds__(256) void attn_kvouter_kernel(AttnParams p) {
       toks = nullptr;
       ntok = 1;
     } else {
-      // bucket = last one whose first item is <= item
-      int lo = 0, hi = p.nbuckets;  // item_off[lo] <= item < item_off[hi]
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (p.item_off[mid] <= item) lo = mid;
-        else hi = mid;
-      }
-      const int bk = lo;
+      const int bk = p.item_bucket[item];
       const int start = (int)(item - p.item_off[bk]) * p.tpi;
       ntok = min(p.tpi, p.counts[bk] - start);
       toks = p.entries + p.offsets[bk] + start;
@@ -170,54 +218,82 @@ __global__ __launch_bounds__(256) void attn_kvouter_kernel(AttnParams p) {
     {
       const int64_t kv0 = (((int64_t)b * p.G + g) * p.S_k + (int64_t)c * kBlock) * D;
       const int rows_ok = (int)min((int64_t)kBlock, (int64_t)p.S_k - (int64_t)c * kBlock);
-      // K: 128 rows of D, row-major
+      // Every load below is unconditional (rows past the cache end re-read its
+      // last row and are zeroed afterwards), so all of them are in flight at once.
       constexpr int KCH = kBlock * D / E;
-      const Chunk16* ksrc = (const Chunk16*)((const T*)p.k + kv0);
-      for (int ch = threadIdx.x; ch < KCH; ch += 256) {
+      static_assert(KCH % 256 == 0, "K staging covers the block exactly");
+      constexpr int KU = KCH / 256;
+      constexpr int VT = (D / E) * (kBlock / E);
+      constexpr int VU = (VT + 255) / 256;
+      const T* ksrc = (const T*)p.k + kv0;
+      const T* vsrc = (const T*)p.v + kv0;
+      Chunk16 kx[KU];
+      Chunk16 vin[VU][E];
+#pragma unroll
+      for (int u = 0; u < KU; ++u) {
+        const int ch = threadIdx.x + u * 256;
         const int row = ch / (D / E), col = ch - row * (D / E);
-        Chunk16 x = {};
-        if (row < rows_ok) x = ksrc[ch];
+        kx[u] = *(const Chunk16*)(ksrc + (int64_t)min(row, rows_ok - 1) * D + col * E);
+      }
+#pragma unroll
+      for (int u = 0; u < VU; ++u) {
+        const int tl = min((int)threadIdx.x + u * 256, VT - 1);
+        const int dg = tl % (D / E), kg = tl / (D / E);
+#pragma unroll
+        for (int r = 0; r < E; ++r)
+          vin[u][r] = *(const Chunk16*)(vsrc + (int64_t)min(kg * E + r, rows_ok - 1) * D + dg * E);
+      }
+      __builtin_amdgcn_sched_barrier(0);  // keep every staging load ahead of the first use
+#pragma unroll
+      for (int u = 0; u < KU; ++u) {
+        const int ch = threadIdx.x + u * 256;
+        const int row = ch / (D / E), col = ch - row * (D / E);
+        Chunk16 x = kx[u];
+        if (row >= rows_ok) x = Chunk16{};
         *(Chunk16*)&Ks[row * LDK + col * E] = x;
       }
-      // V^T: E x E tiles, transposed in registers
-      constexpr int VT = (D / E) * (kBlock / E);
-      const T* vsrc = (const T*)p.v + kv0;
-      for (int tl = threadIdx.x; tl < VT; tl += 256) {
+#pragma unroll
+      for (int u = 0; u < VU; ++u) {
+        const int tl = threadIdx.x + u * 256;
+        if (VT % 256 != 0 && tl >= VT) break;
         const int dg = tl % (D / E), kg = tl / (D / E);
-        Chunk16 in[E], outc[E];
 #pragma unroll
-        for (int r = 0; r < E; ++r) {
-          const int key = kg * E + r;
-          Chunk16 x = {};
-          if (key < rows_ok) x = *(const Chunk16*)(vsrc + (int64_t)key * D + dg * E);
-          in[r] = x;
+        for (int r = 0; r < E; ++r)
+          if (kg * E + r >= rows_ok) vin[u][r] = Chunk16{};
+        Chunk16 outc[E];
+        transpose_tile<T, E>(vin[u], outc);
+#pragma unroll
+        for (int r = 0; r < E; ++r) {  // rows are 8-byte aligned: two 8-byte stores
+          uint2* dst = (uint2*)&Vt[(dg * E + r) * LDV + kg * E];
+          dst[0] = make_uint2(outc[r].w[0], outc[r].w[1]);
+          dst[1] = make_uint2(outc[r].w[2], outc[r].w[3]);
         }
-        transpose_tile<T, E>(in, outc);
-#pragma unroll
-        for (int r = 0; r < E; ++r) *(Chunk16*)&Vt[(dg * E + r) * LDV + kg * E] = outc[r];
       }
     }
     __syncthreads();
 
+    const int64_t key0 = (int64_t)c * kBlock;
     for (int p0 = 0; p0 < ntok; p0 += TPP) {
       if (p0 + wave * TPW >= ntok) continue;  // this wave has no rows in this pass
       const int tslot = p0 + wave * TPW + l32 / R;
       const bool in_list = tslot < ntok;
       const int32_t entry = in_list ? (toks ? toks[tslot] : direct_tok) : 0;
       const int i = entry >> 6, slot = entry & 63;
-      // a block entirely after the query has no visible key: the row is skipped
-      const bool rv = in_list && (int64_t)c * kBlock <= p.q_offset + i;
-      const int64_t t = rv ? p.q_offset + i : (int64_t)1 << 62;
+      // keys of this block visible to the row: index within block <= lim
+      const int64_t rel = p.q_offset + i - key0;  // query position relative to the block
+      const bool rv = in_list && rel >= 0;        // a block after the query is skipped
+      const int lim = (!rv || rel >= kBlock) ? kBlock : (int)rel;
       const int hh = l32 % R;
       const int head = g * R + hh;
 
+      // rows that are skipped still read a valid Q row (entry 0) and are never stored
       frag qf[NKS];
       {
         const T* qrow = (const T*)p.q + (((int64_t)b * p.S_q + i) * p.Hq + head) * D;
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks)
-          qf[ks] = rv ? *(const frag*)(qrow + ks * KSTEP + h * KPL) : M::zero();
+        for (int ks = 0; ks < NKS; ++ks) qf[ks] = *(const frag*)(qrow + ks * KSTEP + h * KPL);
       }
+      __builtin_amdgcn_sched_barrier(0);  // all Q loads in flight before the first MFMA
       f32x16 sacc[4];
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) sacc[kt] = f32x16{};
@@ -229,25 +305,29 @@ __global__ __launch_bounds__(256) void attn_kvouter_kernel(AttnParams p) {
           sacc[kt] = M::mma(a, qf[ks], sacc[kt]);
         }
       }
-      // scale into log2 units, causal mask inside the block, block-local softmax
-      const int64_t key0 = (int64_t)c * kBlock;
+      // the causal mask only bites in a row's local block
+      if (__any(lim < kBlock - 1)) {
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int j = 0; j < 16; ++j)
+            if (kt * 32 + c_row(j, h) > lim) sacc[kt][j] = kNegInf;
+      }
+      // block-local softmax in log2 units: p = 2^(s * scale*log2(e) - m), scale > 0
       float mx = kNegInf;
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          float s = sacc[kt][j] * p.scale_log2;
-          if (key0 + kt * 32 + c_row(j, h) > t) s = kNegInf;
-          sacc[kt][j] = s;
-          mx = fmaxf(mx, s);
-        }
+        for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sacc[kt][j]);
       mx = wave_max_xor32(mx);
+      const float sl2 = p.scale_log2;
+      const float moff = -mx * sl2;
       float lsum = 0.f;
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-          const float e = exp2f(sacc[kt][j] - mx);
+          const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][j], sl2, moff));
           sacc[kt][j] = e;
           lsum += e;
         }
@@ -284,80 +364,102 @@ __global__ __launch_bounds__(256) void attn_kvouter_kernel(AttnParams p) {
         }
       }
 
+      // Partial state of this (token, slot): o / l in the lane-native order of the
+      // O^T tile (chunk q of lane (head, h) at ((q * 2 + h) * R + head) * 16 bytes),
+      // so one store instruction writes 2 * R * 16 contiguous bytes per token.
       if (rv) {
         const float inv = 1.0f / lsum;
-        const int64_t prow = (((((int64_t)b * p.S_q + i) * p.G + g) * p.topk + slot) * R + hh);
-        T* po = (T*)p.part_o + prow * D;
+        const int64_t ptok = (((int64_t)b * p.S_q + i) * p.G + g) * p.topk + slot;
+        T* po = (T*)p.part_o + ptok * (R * D);
+        constexpr int NQ = NDT * 16 / E;
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
+        for (int q = 0; q < NQ; ++q) {
+          Chunk16 w;
+          if constexpr (sizeof(T) == 2) {
+            bf16x8 v;
 #pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4) {
-            const int d0 = dt * 32 + q4 * 8 + h * 4;
-            if constexpr (sizeof(T) == 2) {
-              bf16x4 w;
+            for (int e = 0; e < 8; ++e) v[e] = from_f32<T>(oacc[(q * 8 + e) / 16][(q * 8 + e) % 16] * inv);
+            w = __builtin_bit_cast(Chunk16, v);
+          } else {
+            f32x4 v;
 #pragma unroll
-              for (int e = 0; e < 4; ++e) w[e] = from_f32<T>(oacc[dt][q4 * 4 + e] * inv);
-              *(bf16x4*)(po + d0) = w;
-            } else {
-              f32x4 w;
-#pragma unroll
-              for (int e = 0; e < 4; ++e) w[e] = oacc[dt][q4 * 4 + e] * inv;
-              *(f32x4*)(po + d0) = w;
-            }
+            for (int e = 0; e < 4; ++e) v[e] = oacc[(q * 4 + e) / 16][(q * 4 + e) % 16] * inv;
+            w = __builtin_bit_cast(Chunk16, v);
           }
-        if (h == 0) {
-          p.part_m[prow] = mx;
-          p.part_l[prow] = lsum;
+          *(Chunk16*)(po + ((q * 2 + h) * R + hh) * E) = w;
         }
+        if (h == 0) p.part_lse[ptok * R + hh] = mx * sl2 + __builtin_amdgcn_logf(lsum);
       }
     }
   }
 }
 
-// Merge the partial states of one (token, head) over its selected slots.
-template <typename T, typename TO, int D>
+// Merge the partial states of one (token, group) over its selected slots:
+// out = sum_s 2^(lse_s - M) o_s / sum_s 2^(lse_s - M), M = max_s lse_s.
+// A thread owns one 16-byte chunk of the lane-native partial layout (E values
+// of one head: runs of four consecutive d).  Every load is unconditional, from a
+// clamped address, so all of a thread's loads are in flight together; unused
+// slots are removed by selects.
+template <typename T, typename TO, int D, int R, int KMAX>
 __global__ __launch_bounds__(256) void combine_kernel(AttnParams p) {
-  constexpr int CE = 16 / (int)sizeof(T);
-  constexpr int NCH = D / CE;
+  constexpr int E = 16 / (int)sizeof(T);
+  constexpr int NCHT = D * R / E;  // chunks per (token, slot) partial
   const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t total = (int64_t)p.B * p.S_q * p.Hq * NCH;
+  const int64_t total = (int64_t)p.B * p.S_q * p.G * NCHT;
   if (u >= total) return;
-  const int dc = (int)(u % NCH);
-  const int64_t rowq = u / NCH;
-  const int hq = (int)(rowq % p.Hq);
-  const int64_t bi = rowq / p.Hq;  // b * S_q + i
+  const int ch = (int)(u % NCHT);
+  const int64_t rowg = u / NCHT;  // (b * S_q + i) * G + g
+  const int g = (int)(rowg % p.G);
+  const int64_t bi = rowg / p.G;
   const int i = (int)(bi % p.S_q);
   const int b = (int)(bi / p.S_q);
-  const int g = hq / p.r, hh = hq - g * p.r;
-  const int32_t* srow = p.sel + (((int64_t)b * p.G + g) * p.S_q + i) * p.topk;
-  const int64_t pbase = (bi * p.G + g) * p.topk;
+  const int hh = ch % R, h = (ch / R) & 1, q = ch / (2 * R);
   const int64_t t = p.q_offset + i;
-  auto used = [&](int s) {
-    const int c = srow[s];
-    return c >= 0 && c < p.nb && (int64_t)c * kBlock <= t;
-  };
+  const int32_t* srow = p.sel + (((int64_t)b * p.G + g) * p.S_q + i) * p.topk;
+  const int64_t pbase = rowg * p.topk;
+
+  int cs[KMAX];
+  float ls[KMAX];
+  Chunk16 x[KMAX];
+#pragma unroll
+  for (int s = 0; s < KMAX; ++s) {
+    const int sc = min(s, p.topk - 1);
+    cs[s] = srow[sc];
+    ls[s] = p.part_lse[(pbase + sc) * R + hh];
+    x[s] = *(const Chunk16*)((const T*)p.part_o + (pbase + sc) * (R * D) + ch * E);
+  }
   float mx = kNegInf;
-  for (int s = 0; s < p.topk; ++s)
-    if (used(s)) mx = fmaxf(mx, p.part_m[(pbase + s) * p.r + hh]);
+#pragma unroll
+  for (int s = 0; s < KMAX; ++s) {
+    const int c = cs[s];
+    const bool used = s < p.topk && c >= 0 && c < p.nb && (int64_t)c * kBlock <= t;
+    ls[s] = used ? ls[s] : kNegInf;
+    mx = fmaxf(mx, ls[s]);
+  }
   float W = 0.f;
-  float acc[CE];
+  float acc[E];
 #pragma unroll
-  for (int e = 0; e < CE; ++e) acc[e] = 0.f;
-  for (int s = 0; s < p.topk; ++s) {
-    if (!used(s)) continue;
-    const int64_t pr = (pbase + s) * p.r + hh;
-    const float w = p.part_l[pr] * exp2f(p.part_m[pr] - mx);
+  for (int e = 0; e < E; ++e) acc[e] = 0.f;
+#pragma unroll
+  for (int s = 0; s < KMAX; ++s) {
+    const bool used = ls[s] != kNegInf;
+    const float w = used ? exp2f(ls[s] - mx) : 0.f;
     W += w;
-    const Chunk16 x = *(const Chunk16*)((const T*)p.part_o + pr * D + dc * CE);
-    const T* xv = (const T*)&x;
+    const T* xv = (const T*)&x[s];
 #pragma unroll
-    for (int e = 0; e < CE; ++e) acc[e] += w * to_f32(xv[e]);
+    for (int e = 0; e < E; ++e) acc[e] += used ? w * to_f32(xv[e]) : 0.f;
   }
   const float inv = 1.0f / W;
-  TO* o = (TO*)p.out + rowq * D + dc * CE;
+  const int r0 = (q * E) % 16, dt = (q * E) / 16;
+  TO* orow = (TO*)p.out + (bi * p.Hq + g * R + hh) * D;
 #pragma unroll
-  for (int e = 0; e < CE; ++e) o[e] = from_f32<TO>(acc[e] * inv);
-  if (dc == 0 && p.lse) p.lse[((int64_t)b * p.Hq + hq) * p.S_q + i] = (mx + log2f(W)) * 0.69314718055994531f;
+  for (int m = 0; m < E / 4; ++m) {
+    const int d0 = dt * 32 + (r0 / 4 + m) * 8 + 4 * h;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) orow[d0 + e] = from_f32<TO>(acc[4 * m + e] * inv);
+  }
+  if (q == 0 && h == 0 && p.lse)
+    p.lse[((int64_t)b * p.Hq + g * R + hh) * p.S_q + i] = (mx + log2f(W)) * 0.69314718055994531f;
 }
 
 template <typename T, int D, int R>
@@ -367,21 +469,34 @@ static hipError_t launch_attn_t(const AttnParams& p, hipStream_t s, const Kernel
     timer_start(tm, kKernGather, s);
     hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)((p.nbuckets + 255) / 256)), dim3(256), 0, s,
                        p.counts, (int64_t)p.nbuckets);
-    hipLaunchKernelGGL(gather_count_kernel, dim3((unsigned)((entries + 255) / 256)), dim3(256), 0, s, p);
+    const bool lds_hist = p.nb <= kMaxHistBins;
+    const dim3 hgrid((unsigned)((p.S_q + kGatherRows - 1) / kGatherRows), (unsigned)(p.B * p.G));
+    if (lds_hist)
+      hipLaunchKernelGGL(gather_hist_kernel<false>, hgrid, dim3(256), p.nb * 4, s, p);
+    else
+      hipLaunchKernelGGL(gather_count_kernel, dim3((unsigned)((entries + 255) / 256)), dim3(256), 0, s, p);
     hipLaunchKernelGGL(gather_scan_kernel, dim3(1), dim3(1024), 0, s, p);
-    hipLaunchKernelGGL(gather_scatter_kernel, dim3((unsigned)((entries + 255) / 256)), dim3(256), 0, s, p);
+    hipLaunchKernelGGL(item_table_kernel, dim3((unsigned)((p.nbuckets + 255) / 256)), dim3(256), 0, s, p);
+    if (lds_hist)
+      hipLaunchKernelGGL(gather_hist_kernel<true>, hgrid, dim3(256), p.nb * 4, s, p);
+    else
+      hipLaunchKernelGGL(gather_scatter_kernel, dim3((unsigned)((entries + 255) / 256)), dim3(256), 0, s, p);
     timer_stop(tm, kKernGather, s);
   }
   timer_start(tm, kKernAttention, s);
   hipLaunchKernelGGL((attn_kvouter_kernel<T, D, R>), dim3(p.grid), dim3(256), 0, s, p);
   timer_stop(tm, kKernAttention, s);
   timer_start(tm, kKernCombine, s);
-  constexpr int CE = 16 / (int)sizeof(T);
-  const int64_t units = (int64_t)p.B * p.S_q * p.Hq * (D / CE);
-  if (p.out_f32)
-    hipLaunchKernelGGL((combine_kernel<T, float, D>), dim3((unsigned)((units + 255) / 256)), dim3(256), 0, s, p);
-  else
-    hipLaunchKernelGGL((combine_kernel<T, T, D>), dim3((unsigned)((units + 255) / 256)), dim3(256), 0, s, p);
+  constexpr int E = 16 / (int)sizeof(T);
+  const int64_t units = (int64_t)p.B * p.S_q * p.G * (D * R / E);
+  const dim3 cgrid((unsigned)((units + 255) / 256));
+  if (p.topk <= 16) {
+    if (p.out_f32) hipLaunchKernelGGL((combine_kernel<T, float, D, R, 16>), cgrid, dim3(256), 0, s, p);
+    else hipLaunchKernelGGL((combine_kernel<T, T, D, R, 16>), cgrid, dim3(256), 0, s, p);
+  } else {
+    if (p.out_f32) hipLaunchKernelGGL((combine_kernel<T, float, D, R, 32>), cgrid, dim3(256), 0, s, p);
+    else hipLaunchKernelGGL((combine_kernel<T, T, D, R, 32>), cgrid, dim3(256), 0, s, p);
+  }
   timer_stop(tm, kKernCombine, s);
   return hipGetLastError();
 }

@@ -61,11 +61,11 @@ struct AttnParams {
   int32_t* cursor;     // [nbuckets]
   int32_t* item_off;   // [nbuckets + 1]: first work item of each bucket
   int32_t* entries;    // [B*G*S_q*topk]: (query row << 6) | slot, grouped by bucket
+  int32_t* item_bucket;  // [max items]: bucket of each work item
   int32_t* n_items;    // device scalar
   // partial softmax states per (b, i, g, slot, head)
   void* part_o;        // o / l in the partial dtype, [.., d]
-  float* part_m;       // running max, log2 units of the scaled score
-  float* part_l;       // sum of 2^(s' - m)
+  float* part_lse;     // log2 of sum_j 2^(s'_j), s' = scale * log2(e) * q.k
   int64_t q_offset;
   int B, S_q, S_k, Hq, G, r, d, topk;
   int nb;              // key blocks per sequence, ceil(S_k / 128)

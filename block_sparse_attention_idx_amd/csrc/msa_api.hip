@@ -30,7 +30,7 @@ msa_status fail(msa_status st, const char* fmt, ...) {
 }
 
 constexpr size_t kAlign = 256;
-constexpr int kTokensPerItem = 64;
+constexpr int kTokensPerItem = 128;
 constexpr int kAttnGrid = 512;      // persistent attention grid: 2 workgroups per CU
 constexpr int kIndexTargetUnits = 2048;
 
@@ -64,7 +64,8 @@ msa_status check_shape(const msa_shape* s, int op) {
   if (s->dtype != MSA_F32 && s->dtype != MSA_BF16) return fail(MSA_ERR_INVALID, "unknown dtype %d", s->dtype);
   if (s->out_dtype != MSA_F32 && s->out_dtype != MSA_BF16)
     return fail(MSA_ERR_INVALID, "unknown out_dtype %d", s->out_dtype);
-  if (!std::isfinite(s->softmax_scale)) return fail(MSA_ERR_INVALID, "softmax_scale must be finite");
+  if (!std::isfinite(s->softmax_scale) || s->softmax_scale < 0.0f)
+    return fail(MSA_ERR_INVALID, "softmax_scale must be finite and >= 0 (0 selects 1/sqrt(head_dim))");
 
   if (s->block_size != msa::kBlock)
     return fail(MSA_ERR_UNSUPPORTED, "block_size %d: only 128 is built", s->block_size);
@@ -142,7 +143,7 @@ void bind_index(IndexPlan& ip, char* ws, const void* q_idx, const void* k_idx, i
 
 struct AttnPlan {
   msa::AttnParams p;
-  size_t off_counts, off_offsets, off_cursor, off_item_off, off_nitems, off_entries, off_po, off_pm, off_pl;
+  size_t off_counts, off_offsets, off_cursor, off_item_off, off_nitems, off_entries, off_items, off_po, off_pl;
   size_t bytes;
 };
 
@@ -186,10 +187,11 @@ AttnPlan plan_attn(const msa_shape* s) {
     ap.off_item_off = take(nbk * 4);
     ap.off_nitems = take(4);
     ap.off_entries = take(entries * 4);
+    // items: at most one partial item per bucket plus entries / tpi full ones
+    ap.off_items = take(((size_t)p.nbuckets + entries / p.tpi + 1) * 4);
   }
   const size_t prow = entries * (size_t)p.r;  // (b, i, g, slot, head)
   ap.off_po = take(prow * p.d * elem_bytes(s->dtype));
-  ap.off_pm = take(prow * 4);
   ap.off_pl = take(prow * 4);
   ap.bytes = off;
   return ap;
@@ -204,10 +206,10 @@ void bind_attn(AttnPlan& ap, char* ws) {
     p.item_off = (int32_t*)(ws + ap.off_item_off);
     p.n_items = (int32_t*)(ws + ap.off_nitems);
     p.entries = (int32_t*)(ws + ap.off_entries);
+    p.item_bucket = (int32_t*)(ws + ap.off_items);
   }
   p.part_o = ws + ap.off_po;
-  p.part_m = (float*)(ws + ap.off_pm);
-  p.part_l = (float*)(ws + ap.off_pl);
+  p.part_lse = (float*)(ws + ap.off_pl);
 }
 
 size_t sel_bytes(const msa_shape* s) {

@@ -81,9 +81,10 @@ def test_null_pointers_rejected():
     assert L.msa_sparse_attn_fwd(ctypes.byref(sh), FAKE, FAKE, FAKE, None, FAKE, None, None, 0, None) == -1
 
 
-def test_nonfinite_scale_rejected():
+@pytest.mark.parametrize("scale", [float("nan"), float("inf"), -0.5])
+def test_bad_scale_rejected(scale):
     sh = _shape()
-    sh.softmax_scale = float("nan")
+    sh.softmax_scale = scale
     assert _fwd(sh) == -1
 
 
