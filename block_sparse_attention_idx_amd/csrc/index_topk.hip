@@ -16,9 +16,10 @@
 // one query row and 64 of the block's 128 keys (the other 64 sit in lane ^ 32).
 // The block max is a register reduction plus one cross-half exchange; it goes
 // straight into a running top list in registers and is never stored.  The two
-// lane halves take alternate blocks, so each keeps its own list; lists of all
-// (split, half) pairs are merged per row by topk_merge_kernel, which also adds
-// the local block, sorts ascending and pads with -1.
+// lane halves take alternate blocks, so each keeps its own list; at the end the
+// two are merged through LDS into one list per (row, key split).  The lists of
+// a row's splits are merged by topk_merge_kernel, which also adds the local
+// block, sorts ascending and pads with -1.
 //
 // Exactness: with integer-valued inputs every score is an integer of
 // magnitude <= D * max|q| * max|k| < 2^24, so fp32 MFMA accumulation is exact in
@@ -51,7 +52,7 @@ __device__ __forceinline__ bool ranks_before(float s1, int i1, float s2, int i2)
 }
 
 template <typename T, int DI, int CAP, int RT>
-__global__ __launch_bounds__(256) void index_topk_kernel(IndexParams p) {
+__global__ __launch_bounds__(256, 2) void index_topk_kernel(IndexParams p) {
   using M = Mma<T>;
   using frag = typename M::frag;
   constexpr int KPL = M::KPL, KSTEP = M::KSTEP, NKS = DI / KSTEP;
@@ -62,7 +63,11 @@ __global__ __launch_bounds__(256) void index_topk_kernel(IndexParams p) {
   constexpr int CH_PER_ROW = DI * (int)sizeof(T) / 16;
   constexpr int CH_PER_THREAD = kBlock * CH_PER_ROW / 256;
   static_assert(CH_PER_THREAD >= 1 && (kBlock * CH_PER_ROW) % 256 == 0, "staging split");
-  __shared__ __align__(16) T Ks[2][kBlock * LDW];
+  constexpr int KS_BYTES = 2 * kBlock * LDW * (int)sizeof(T);
+  constexpr int LIST_BYTES = 4 * 2 * CAP * 32 * 8;  // one row tile of lists, all waves
+  constexpr int SMEM = KS_BYTES > LIST_BYTES ? KS_BYTES : LIST_BYTES;
+  __shared__ __align__(16) char smem[SMEM];
+  T* Ks = (T*)smem;  // [2][kBlock * LDW]
 
   // XCD-aware unit order: hardware hands consecutive workgroup ids to the 8
   // XCDs in turn; give each XCD a contiguous run of units (one key range, many
@@ -92,11 +97,11 @@ __global__ __launch_bounds__(256) void index_topk_kernel(IndexParams p) {
   for (int rt = 0; rt < RT; ++rt) {
     const int n = n_first + wave * ROWS_WAVE + rt * 32 + l32;
     rvalid[rt] = n < p.rows_per_b;
-    rowL[rt] = rvalid[rt] ? (int)((p.q_offset + n / p.G) / kBlock) : 0;
-    const T* qrow = (const T*)p.q_idx + ((int64_t)b * p.rows_per_b + n) * DI;
+    const int nc = rvalid[rt] ? n : p.rows_per_b - 1;  // invalid rows read a valid row
+    rowL[rt] = (int)((p.q_offset + nc / p.G) / kBlock);
+    const T* qrow = (const T*)p.q_idx + ((int64_t)b * p.rows_per_b + nc) * DI;
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks)
-      qf[rt][ks] = rvalid[rt] ? *(const frag*)(qrow + ks * KSTEP + h * KPL) : M::zero();
+    for (int ks = 0; ks < NKS; ++ks) qf[rt][ks] = *(const frag*)(qrow + ks * KSTEP + h * KPL);
   }
 
   float ls[RT][CAP];
@@ -110,102 +115,132 @@ __global__ __launch_bounds__(256) void index_topk_kernel(IndexParams p) {
     }
 
   const char* kbase = (const char*)p.k_idx + (int64_t)b * p.S_k * DI * (int64_t)sizeof(T);
-  Chunk16 pre[CH_PER_THREAD];
-  auto gload = [&](int c) {
-    const Chunk16* src = (const Chunk16*)(kbase + (int64_t)c * kBlock * DI * (int64_t)sizeof(T));
+  i32x4 pre[CH_PER_THREAD];  // a native vector type keeps the prefetch in registers
+  {
+    const i32x4* src = (const i32x4*)(kbase + (int64_t)c_begin * kBlock * DI * (int64_t)sizeof(T));
 #pragma unroll
     for (int u = 0; u < CH_PER_THREAD; ++u) pre[u] = src[threadIdx.x + u * 256];
-  };
-  auto lstore = [&](int buf) {
 #pragma unroll
     for (int u = 0; u < CH_PER_THREAD; ++u) {
       const int ch = threadIdx.x + u * 256;
       const int row = ch / CH_PER_ROW, col = ch - row * CH_PER_ROW;
-      *(Chunk16*)((char*)&Ks[buf][row * LDW] + col * 16) = pre[u];
+      *(i32x4*)((char*)&Ks[row * LDW] + col * 16) = pre[u];
     }
-  };
-  auto block_max = [&](int buf, float (&pm)[RT]) {
+  }
+  __syncthreads();
+
+  float pmA[RT], pmB[RT];
+  int buf = 0;
+  for (int c = c_begin; c < c_end; ++c) {
+    const bool has_next = c + 1 < c_end;
+    if (has_next) {
+      const i32x4* src = (const i32x4*)(kbase + (int64_t)(c + 1) * kBlock * DI * (int64_t)sizeof(T));
+#pragma unroll
+      for (int u = 0; u < CH_PER_THREAD; ++u) pre[u] = src[threadIdx.x + u * 256];
+    }
+    // block max of scores q_idx . k_idx over the block's 128 keys, one 32-key
+    // tile of accumulators at a time
+    float pm[RT];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) pm[rt] = kNegInf;
-    if (!wave_active) return;
-    f32x16 acc[4][RT];
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) acc[kt][rt] = f32x16{};
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
+    if (wave_active) {
+      const T* kt_base = Ks + buf * (kBlock * LDW);
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
-        const frag a = *(const frag*)&Ks[buf][(kt * 32 + l32) * LDW + ks * KSTEP + h * KPL];
+        f32x16 acc[RT];
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) acc[kt][rt] = M::mma(a, qf[rt][ks], acc[kt][rt]);
+        for (int rt = 0; rt < RT; ++rt) acc[rt] = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+          const frag a = *(const frag*)&kt_base[(kt * 32 + l32) * LDW + ks * KSTEP + h * KPL];
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt) acc[rt] = M::mma(a, qf[rt][ks], acc[rt]);
+        }
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) pm[rt] = fmaxf(pm[rt], acc[rt][j]);
       }
     }
+    if (has_next) {
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      float m = acc[0][rt][0];
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) m = fmaxf(m, acc[kt][rt][j]);
-      pm[rt] = m;
+      for (int u = 0; u < CH_PER_THREAD; ++u) {
+        const int ch = threadIdx.x + u * 256;
+        const int row = ch / CH_PER_ROW, col = ch - row * CH_PER_ROW;
+        *(i32x4*)((char*)&Ks[(buf ^ 1) * (kBlock * LDW) + row * LDW] + col * 16) = pre[u];
+      }
     }
-  };
-
-  gload(c_begin);
-  lstore(0);
-  __syncthreads();
-  int buf = 0;
-  for (int c = c_begin; c < c_end; c += 2) {
-    float pmA[RT], pmB[RT];
-    const bool hasB = c + 1 < c_end;
-    if (hasB) gload(c + 1);
-    block_max(buf, pmA);
-    if (hasB) lstore(buf ^ 1);
     __syncthreads();
     buf ^= 1;
-    if (hasB) {
-      const bool hasC = c + 2 < c_end;
-      if (hasC) gload(c + 2);
-      block_max(buf, pmB);
-      if (hasC) lstore(buf ^ 1);
-      __syncthreads();
-      buf ^= 1;
-    } else {
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) pmB[rt] = kNegInf;
-    }
-    // lanes of half 0 rank block c, lanes of half 1 rank block c + 1
+    // blocks pair up: lanes of half 0 rank the even one, half 1 the odd one
+    const bool second = ((c - c_begin) & 1) != 0;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-      const float mine = h ? pmB[rt] : pmA[rt];
-      const float send = h ? pmA[rt] : pmB[rt];
-      float full = fmaxf(mine, __shfl_xor(send, 32));
-      const int cc = c + h;
-      if (!rvalid[rt] || cc >= rowL[rt]) full = kNegInf;
-      list_insert<CAP>(ls[rt], li[rt], full, cc);
+      if (!second) pmA[rt] = pm[rt];
+      else pmB[rt] = pm[rt];
+    }
+    if (second || c + 1 == c_end) {
+      const int c0 = second ? c - 1 : c;
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        const float b_val = second ? pmB[rt] : kNegInf;
+        const float mine = h ? b_val : pmA[rt];
+        const float send = h ? pmA[rt] : b_val;
+        float full = fmaxf(mine, __shfl_xor(send, 32));
+        const int cc = c0 + h;
+        if (!rvalid[rt] || cc >= rowL[rt]) full = kNegInf;
+        list_insert<CAP>(ls[rt], li[rt], full, cc);
+      }
     }
   }
 
+  // Merge the two half lists of each row through LDS (the K tiles are free
+  // now), then write one list per (row, split).
+  float* xs = (float*)smem;                       // [4 waves][2 halves][CAP][32 rows]
+  int* xi = (int*)(smem + LIST_BYTES / 2);
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
-    if (!rvalid[rt]) continue;
-    const int n = n_first + wave * ROWS_WAVE + rt * 32 + l32;
-    const int64_t rowg = (int64_t)b * p.rows_per_b + n;
-    const int64_t base = ((rowg * p.nsplit + split) * 2 + h) * CAP;
+    __syncthreads();
 #pragma unroll
     for (int j = 0; j < CAP; ++j) {
-      p.part_s[base + j] = ls[rt][j];
-      p.part_i[base + j] = li[rt][j];
+      const int o = ((wave * 2 + h) * CAP + j) * 32 + l32;
+      xs[o] = ls[rt][j];
+      xi[o] = li[rt][j];
+    }
+    __syncthreads();
+    if (h == 0 && rvalid[rt]) {
+      const int n = n_first + wave * ROWS_WAVE + rt * 32 + l32;
+      const int64_t rowg = (int64_t)b * p.rows_per_b + n;
+      float* ds = p.part_s + (rowg * p.nsplit + split) * CAP;
+      int32_t* di = p.part_i + (rowg * p.nsplit + split) * CAP;
+      const int oa = ((wave * 2 + 0) * CAP) * 32 + l32;
+      const int ob = ((wave * 2 + 1) * CAP) * 32 + l32;
+      int ia = 0, ib = 0;
+      for (int j = 0; j < CAP; ++j) {
+        const float sa = ia < CAP ? xs[oa + ia * 32] : kNegInf;
+        const int ida = ia < CAP ? xi[oa + ia * 32] : -1;
+        const float sb = ib < CAP ? xs[ob + ib * 32] : kNegInf;
+        const int idb = ib < CAP ? xi[ob + ib * 32] : -1;
+        // empty entries (id -1) rank last
+        const bool take_a = idb < 0 || (ida >= 0 && ranks_before(sa, ida, sb, idb));
+        ds[j] = take_a ? sa : sb;
+        di[j] = take_a ? ida : idb;
+        ia += take_a ? 1 : 0;
+        ib += take_a ? 0 : 1;
+      }
     }
   }
 }
 
-// One wave per (b, i, g) row: k-way merge of the row's partial lists by
-// (score desc, block asc), then local block, ascending order, -1 padding.
+// One wave per (b, i, g) row: the row's lists (one per key split, sorted by
+// score desc then block asc) are loaded into LDS, then k-1 rounds of a
+// wave-wide argmax over the list heads pick the Top-(k-1); the local block is
+// added, ids are sorted ascending and padded with -1.
 template <int CAP>
 __global__ __launch_bounds__(256) void topk_merge_kernel(IndexParams p) {
+  // dynamic LDS: [4 waves][nsplit * CAP] scores, then the same for block ids
+  extern __shared__ __align__(16) char msmem[];
+  const int per_wave = p.nsplit * CAP;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t row = (int64_t)blockIdx.x * 4 + wave;
   if (row >= (int64_t)p.B * p.rows_per_b) return;
@@ -213,28 +248,35 @@ __global__ __launch_bounds__(256) void topk_merge_kernel(IndexParams p) {
   const int n = (int)(row - (int64_t)b * p.rows_per_b);
   const int i = n / p.G, g = n - (n / p.G) * p.G;
   const int L = (int)((p.q_offset + i) / kBlock);
-  const int nspl = L > 0 ? (L + p.chunk - 1) / p.chunk : 0;
-  const int nlists = 2 * nspl;
+  const int nl = L > 0 ? (L + p.chunk - 1) / p.chunk : 0;
   const int take = min(p.topk - 1, L);
 
-  int pos[4] = {0, 0, 0, 0};
+  const float* gs = p.part_s + row * p.nsplit * CAP;
+  const int32_t* gi = p.part_i + row * p.nsplit * CAP;
+  float* ss = (float*)msmem + wave * per_wave;
+  int* si = (int*)msmem + 4 * per_wave + wave * per_wave;
+  for (int e = lane; e < nl * CAP; e += 64) {
+    ss[e] = gs[e];
+    si[e] = gi[e];
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+  int pos0 = 0, pos1 = 0;  // heads of lists lane and lane + 64
   int mywin = 0x7fffffff;
   for (int it = 0; it < take; ++it) {
     float bs = kNegInf;
     int bi = 0x7fffffff, bl = -1;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int lst = lane + 64 * q;
-      if (lst < nlists && pos[q] < CAP) {
-        const int64_t base = ((row * p.nsplit + (lst >> 1)) * 2 + (lst & 1)) * CAP + pos[q];
-        const float s = p.part_s[base];
-        const int id = p.part_i[base];
-        if (id >= 0 && ranks_before(s, id, bs, bi)) {
-          bs = s;
-          bi = id;
-          bl = q;
-        }
-      }
+    if (lane < nl && pos0 < CAP) {
+      const float s = ss[lane * CAP + pos0];
+      const int id = si[lane * CAP + pos0];
+      if (id >= 0) { bs = s; bi = id; bl = 0; }
+    }
+    if (lane + 64 < nl && pos1 < CAP) {
+      const float s = ss[(lane + 64) * CAP + pos1];
+      const int id = si[(lane + 64) * CAP + pos1];
+      if (id >= 0 && ranks_before(s, id, bs, bi)) { bs = s; bi = id; bl = 1; }
     }
     float ws = bs;
     int wi = bi;
@@ -249,9 +291,8 @@ __global__ __launch_bounds__(256) void topk_merge_kernel(IndexParams p) {
     }
     // block ids are unique across a row's lists, so exactly one lane owns the winner
     if (bl >= 0 && bi == wi) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        if (q == bl) ++pos[q];
+      if (bl == 0) ++pos0;
+      else ++pos1;
     }
     if (lane == it) mywin = wi;
   }
@@ -269,13 +310,16 @@ __global__ __launch_bounds__(256) void topk_merge_kernel(IndexParams p) {
 template <typename T, int DI, int CAP>
 static hipError_t launch_index_t(const IndexParams& p, hipStream_t s, const KernelTimer* tm) {
   timer_start(tm, kKernIndexScore, s);
-  hipLaunchKernelGGL((index_topk_kernel<T, DI, CAP, 2>), dim3(p.grid_per_xcd * 8), dim3(256), 0, s, p);
+  constexpr int RT = CAP <= 15 ? 2 : 1;
+  static_assert(4 * 32 * RT == index_rows_per_wg(CAP + 1), "host and kernel agree on the row tile");
+  hipLaunchKernelGGL((index_topk_kernel<T, DI, CAP, RT>), dim3(p.grid_per_xcd * 8), dim3(256), 0, s, p);
   timer_stop(tm, kKernIndexScore, s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t rows = (int64_t)p.B * p.rows_per_b;
   timer_start(tm, kKernTopkMerge, s);
-  hipLaunchKernelGGL((topk_merge_kernel<CAP>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, p);
+  const size_t lds = (size_t)8 * p.nsplit * CAP * 4;
+  hipLaunchKernelGGL((topk_merge_kernel<CAP>), dim3((unsigned)((rows + 3) / 4)), dim3(256), lds, s, p);
   timer_stop(tm, kKernTopkMerge, s);
   return hipGetLastError();
 }

@@ -29,7 +29,7 @@ enum { kKernIndexScore = 1, kKernTopkMerge = 2, kKernGather = 3, kKernAttention 
 struct IndexParams {
   const void* q_idx;   // [B, S_q, G, D]
   const void* k_idx;   // [B, S_k, D]
-  float* part_s;       // [B*S_q*G, nsplit, 2, CAP] partial top-list scores
+  float* part_s;       // [B*S_q*G, nsplit, CAP] partial top-list scores
   int32_t* part_i;     // same shape: block ids (-1 = empty)
   int32_t* sel;        // [B, G, S_q, topk]
   int64_t q_offset;
@@ -42,7 +42,10 @@ struct IndexParams {
   int grid_per_xcd;    // ceil(nunits / 8)
 };
 
-constexpr int kIndexRowsPerWG = 256;
+// Index rows per workgroup: 4 waves x 32 rows x RT row tiles, RT = 2 for lists
+// of up to 15 entries (k <= 16), 1 for the longer lists of k <= 32.
+constexpr int index_row_tiles(int topk) { return topk <= 16 ? 2 : 1; }
+constexpr int index_rows_per_wg(int topk) { return 4 * 32 * index_row_tiles(topk); }
 
 hipError_t launch_index_select(const IndexParams& p, bool bf16_inputs, int index_dim, hipStream_t s,
                                const KernelTimer* timer);

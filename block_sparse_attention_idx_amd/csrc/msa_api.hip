@@ -111,7 +111,7 @@ IndexPlan plan_index(const msa_shape* s) {
   p.topk = s->topk;
   p.q_offset = s->q_offset;
   p.rows_per_b = s->q_len * s->num_kv_heads;
-  p.ntile = (int)ceil_div(p.rows_per_b, msa::kIndexRowsPerWG);
+  p.ntile = (int)ceil_div(p.rows_per_b, msa::index_rows_per_wg(s->topk));
   p.ntile_total = p.B * p.ntile;
   const int64_t Lmax = s->q_len > 0 ? (s->q_offset + s->q_len - 1) / msa::kBlock : 0;
   int64_t chunk = 1, nsplit = 1;
@@ -125,7 +125,7 @@ IndexPlan plan_index(const msa_shape* s) {
   p.nunits = p.ntile_total * p.nsplit;
   p.grid_per_xcd = (int)ceil_div(p.nunits, 8);
   ip.cap = s->topk <= 16 ? 15 : 31;
-  const size_t entries = (size_t)p.B * p.rows_per_b * p.nsplit * 2 * ip.cap;
+  const size_t entries = (size_t)p.B * p.rows_per_b * p.nsplit * ip.cap;
   ip.bytes = 2 * align_up(entries * 4);
   return ip;
 }

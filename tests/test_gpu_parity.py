@@ -56,6 +56,8 @@ SMALL_SHAPES = [
     (3, 1, 2000, 1999, 64, 4, 128, 128, 16, "bf16"),   # decode
     (2, 5, 3000, 2990, 32, 1, 128, 128, 8, "bf16"),    # few queries, one group
     (1, 640, 640, 0, 32, 1, 64, 32, 32, "f32"),        # k above the visible blocks
+    (1, 700, 6000, 5300, 16, 2, 128, 128, 24, "bf16"), # k > 16: the longer top lists
+    (2, 300, 9000, 8700, 32, 2, 128, 128, 32, "bf16"), # k = 32, several key splits
 ]
 
 
