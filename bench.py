@@ -65,6 +65,22 @@ class HipEvents:
         self.hip.hipEventDestroy(e)
 
 
+def recorded_traffic(profile: str, source: str, key: str = "traffic_bytes_per_launch"):
+    """HBM bytes per launch from a committed counter summary under profiles/, or None when
+    the kernel source has changed since those counters were taken (hash mismatch)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", profile)
+    src = os.path.join(ROOT, "block_sparse_attention_idx_amd", "csrc", source)
+    try:
+        fields = dict(line.split(": ", 1) for line in open(path).read().splitlines() if ": " in line)
+        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    except OSError:
+        return None
+    if fields.get("source_sha256_16", "").strip() != digest or key not in fields:
+        return None
+    return float(fields[key])
+
+
 def algorithmic_work(s: synth.Shape):
     """(main-branch FLOP, index-branch FLOP, decode HBM bytes) of one msa_fwd call.
 
@@ -207,6 +223,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-breakdown", action="store_true", help="skip the per-kernel timing passes")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run 4 plain device copies of 1 GiB (known bytes, for scaling HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this MSA build has no multi-GPU path (asked for --gpus {args.gpus})",
@@ -218,6 +236,14 @@ def main():
 
     import block_sparse_attention_idx_amd as msa
     msa.lib()
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        print("[bench] copy calibration: 4 copies of 1073741824 bytes", file=sys.stderr, flush=True)
     wid = args.workload
     s = synth.WORKLOADS[wid]
     flop_main, flop_index, _ = algorithmic_work(s)
@@ -248,7 +274,9 @@ def main():
                    "block_size": s.block_size, "topk": s.topk},
         "roofline": {"bound": "mfma", "kernel": "attn_kvouter", "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None, "flop_per_launch": flop_main, "avg_launch_ms": round(attn_avg, 4)},
+                     "traffic": recorded_traffic("attn_kvouter_prefill_32k_b2_hbm.md", "attn.hip")
+                     if wid == 3 else None,
+                     "traffic_unit": "bytes", "flop_per_launch": flop_main, "avg_launch_ms": round(attn_avg, 4)},
         "work": {"flop_main": flop_main, "flop_index": flop_index,
                  "index_tflops": round(flop_index / (kern["index_score"] * 1e-3) / 1e12, 2) if kern else None},
         "kernels_ms": {k: round(v, 4) for k, v in kern.items()},
@@ -280,7 +308,9 @@ def main():
             "roofline": {"bound": "hbm", "kernel": "index_topk", "achieved": round(kidx_bytes / (idx_avg * 1e-3) / 1e9, 1),
                          "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": round(kidx_bytes / (idx_avg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-                         "bytes_per_launch": kidx_bytes, "avg_launch_ms": round(idx_avg, 4)},
+                         "bytes_per_launch": kidx_bytes, "avg_launch_ms": round(idx_avg, 4),
+                         "traffic": recorded_traffic("index_topk_decode_128k_b64_hbm.md", "index_topk.hip",
+                                                     "traffic_read_bytes_per_launch")},
             "kernels_ms": {k: round(v, 4) for k, v in dk.items()},
         }
         del drun
