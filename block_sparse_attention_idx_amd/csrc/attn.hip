@@ -11,9 +11,10 @@
 // two loops swapped.
 //
 // Pipeline (all on the caller's stream, no host round trip):
-//   1. gather_count / gather_scan / gather_scatter: bucket every selection
-//      entry (b, g, i, slot) by its block (b, g, c): histogram, exclusive scan,
-//      scatter.  A bucket is cut into work items of up to tpi query tokens.
+//   1. gather_hist / gather_scan / item_table: bucket every selection entry
+//      (b, g, i, slot) by its block (b, g, c): LDS histograms with one global
+//      atomic per bin, exclusive scan, scatter.  A bucket is cut into work items
+//      of up to tpi query tokens.
 //   2. attn_kvouter: a persistent grid walks the work items.  An item stages
 //      K (128 x d) and V^T (d x 128) of its block in LDS once, then runs passes
 //      of 4 waves x 32 rows; a row is one (token, head) and the r heads of a
@@ -21,9 +22,9 @@
 //      S^T = K Q^T and O^T = V^T P^T are 32x32 MFMA tiles; every lane owns one
 //      row, so the block-local softmax needs one cross-half exchange.  The
 //      result is a partial state per (token, slot, head): o / l in the input
-//      dtype plus m and l in fp32.
+//      dtype plus the fp32 log2-sum-exp of the block's scaled scores.
 //   3. combine: per (token, head) the partial states of its slots are merged
-//      (max of m, rescaled sums) into the output and the log-sum-exp.
+//      (weights 2^(lse_s - max)) into the output and the log-sum-exp.
 // With S_q small (decode) the gather is skipped: one item per selection entry.
 #include "common.h"
 #include "kernels.h"
@@ -386,9 +387,10 @@ __global__ __launch_bounds__(256, 2) void attn_kvouter_kernel(AttnParams p) {
             for (int e = 0; e < 4; ++e) v[e] = oacc[(q * 4 + e) / 16][(q * 4 + e) % 16] * inv;
             w = __builtin_bit_cast(Chunk16, v);
           }
-          *(Chunk16*)(po + ((q * 2 + h) * R + hh) * E) = w;
+          // streamed out and read once by the combine: keep it out of the caches' way
+          __builtin_nontemporal_store(__builtin_bit_cast(i32x4, w), (i32x4*)(po + ((q * 2 + h) * R + hh) * E));
         }
-        if (h == 0) p.part_lse[ptok * R + hh] = mx * sl2 + __builtin_amdgcn_logf(lsum);
+        if (h == 0) __builtin_nontemporal_store(mx * sl2 + __builtin_amdgcn_logf(lsum), &p.part_lse[ptok * R + hh]);
       }
     }
   }
@@ -399,16 +401,22 @@ __global__ __launch_bounds__(256, 2) void attn_kvouter_kernel(AttnParams p) {
 // A thread owns one 16-byte chunk of the lane-native partial layout (E values
 // of one head: runs of four consecutive d).  Every load is unconditional, from a
 // clamped address, so all of a thread's loads are in flight together; unused
-// slots are removed by selects.
+// slots are removed by selects.  When a workgroup covers whole (token, group)
+// rows, the result goes through LDS so the output is written in full lines.
 template <typename T, typename TO, int D, int R, int KMAX>
 __global__ __launch_bounds__(256) void combine_kernel(AttnParams p) {
   constexpr int E = 16 / (int)sizeof(T);
   constexpr int NCHT = D * R / E;  // chunks per (token, slot) partial
+  constexpr bool STAGED = NCHT <= 256 && 256 % NCHT == 0;
+  constexpr int RPW = STAGED ? 256 / NCHT : 1;  // (token, group) rows per workgroup
+  __shared__ __align__(16) TO ostage[STAGED ? RPW * R * D : 1];
   const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t total = (int64_t)p.B * p.S_q * p.G * NCHT;
-  if (u >= total) return;
-  const int ch = (int)(u % NCHT);
-  const int64_t rowg = u / NCHT;  // (b * S_q + i) * G + g
+  const int64_t rows_total = (int64_t)p.B * p.S_q * p.G;
+  const int64_t total = rows_total * NCHT;
+  const bool live = u < total;
+  const int64_t uc = live ? u : total - 1;
+  const int ch = (int)(uc % NCHT);
+  const int64_t rowg = uc / NCHT;  // (b * S_q + i) * G + g
   const int g = (int)(rowg % p.G);
   const int64_t bi = rowg / p.G;
   const int i = (int)(bi % p.S_q);
@@ -426,7 +434,8 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnParams p) {
     const int sc = min(s, p.topk - 1);
     cs[s] = srow[sc];
     ls[s] = p.part_lse[(pbase + sc) * R + hh];
-    x[s] = *(const Chunk16*)((const T*)p.part_o + (pbase + sc) * (R * D) + ch * E);
+    x[s] = __builtin_bit_cast(
+        Chunk16, __builtin_nontemporal_load((const i32x4*)((const T*)p.part_o + (pbase + sc) * (R * D) + ch * E)));
   }
   float mx = kNegInf;
 #pragma unroll
@@ -451,14 +460,37 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnParams p) {
   }
   const float inv = 1.0f / W;
   const int r0 = (q * E) % 16, dt = (q * E) / 16;
-  TO* orow = (TO*)p.out + (bi * p.Hq + g * R + hh) * D;
+  if constexpr (STAGED) {
+    TO* srow_o = ostage + (int)(threadIdx.x / NCHT) * (R * D) + hh * D;
 #pragma unroll
-  for (int m = 0; m < E / 4; ++m) {
-    const int d0 = dt * 32 + (r0 / 4 + m) * 8 + 4 * h;
+    for (int m = 0; m < E / 4; ++m) {
+      const int d0 = dt * 32 + (r0 / 4 + m) * 8 + 4 * h;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) orow[d0 + e] = from_f32<TO>(acc[4 * m + e] * inv);
+      for (int e = 0; e < 4; ++e) srow_o[d0 + e] = from_f32<TO>(acc[4 * m + e] * inv);
+    }
+    __syncthreads();
+    // the workgroup's rows are consecutive (b, i, g) rows: one contiguous output range
+    const int64_t row0 = (int64_t)blockIdx.x * RPW;
+    const int64_t nrows = rows_total - row0 < RPW ? rows_total - row0 : RPW;
+    constexpr int CHUNKS = RPW * R * D * (int)sizeof(TO) / 16;
+    const int live_chunks = (int)(nrows * R * D * (int64_t)sizeof(TO) / 16);
+    const Chunk16* src = (const Chunk16*)ostage;
+    Chunk16* dst = (Chunk16*)((TO*)p.out + row0 * R * D);
+#pragma unroll
+    for (int k = 0; k < (CHUNKS + 255) / 256; ++k) {
+      const int c = (int)threadIdx.x + k * 256;
+      if (c < live_chunks) dst[c] = src[c];
+    }
+  } else if (live) {
+    TO* orow = (TO*)p.out + (bi * p.Hq + g * R + hh) * D;
+#pragma unroll
+    for (int m = 0; m < E / 4; ++m) {
+      const int d0 = dt * 32 + (r0 / 4 + m) * 8 + 4 * h;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) orow[d0 + e] = from_f32<TO>(acc[4 * m + e] * inv);
+    }
   }
-  if (q == 0 && h == 0 && p.lse)
+  if (live && q == 0 && h == 0 && p.lse)
     p.lse[((int64_t)b * p.Hq + g * R + hh) * p.S_q + i] = (mx + log2f(W)) * 0.69314718055994531f;
 }
 

@@ -19,7 +19,8 @@
 // lane halves take alternate blocks, so each keeps its own list; at the end the
 // two are merged through LDS into one list per (row, key split).  The lists of
 // a row's splits are merged by topk_merge_kernel, which also adds the local
-// block, sorts ascending and pads with -1.
+// block, sorts ascending and pads with -1; with a single split the index kernel
+// does that itself.
 //
 // Exactness: with integer-valued inputs every score is an integer of
 // magnitude <= D * max|q| * max|k| < 2^24, so fp32 MFMA accumulation is exact in
@@ -69,12 +70,14 @@ __global__ __launch_bounds__(256, 2) void index_topk_kernel(IndexParams p) {
   __shared__ __align__(16) char smem[SMEM];
   T* Ks = (T*)smem;  // [2][kBlock * LDW]
 
-  // XCD-aware unit order: hardware hands consecutive workgroup ids to the 8
-  // XCDs in turn; give each XCD a contiguous run of units (one key range, many
-  // row tiles) so the k_idx range it streams stays in its own L2.
+  // Unit order.  With key splits, hardware hands consecutive workgroup ids to
+  // the 8 XCDs in turn, so each XCD gets a contiguous run of units (one key
+  // range, many row tiles) and the k_idx range it streams stays in its L2.
+  // Without splits (one unit per row tile), the tiles with the most causal
+  // blocks go first, spread over all XCDs.
   const int lin = blockIdx.x;
-  const int logical = (lin & 7) * p.grid_per_xcd + (lin >> 3);
-  if (logical >= p.nunits) return;
+  const int logical = p.nsplit > 1 ? (lin & 7) * p.grid_per_xcd + (lin >> 3) : p.nunits - 1 - lin;
+  if (logical < 0 || logical >= p.nunits) return;
   const int split = logical / p.ntile_total;
   const int tg = logical - split * p.ntile_total;
   const int b = tg / p.ntile;
@@ -84,7 +87,8 @@ __global__ __launch_bounds__(256, 2) void index_topk_kernel(IndexParams p) {
   const int Lmax = (int)((p.q_offset + n_last / p.G) / kBlock);
   const int c_begin = split * p.chunk;
   const int c_end = min(c_begin + p.chunk, Lmax);
-  if (c_begin >= c_end) return;
+  const bool has_blocks = c_begin < c_end;
+  if (!has_blocks && p.nsplit > 1) return;  // a single split still writes rows with L = 0
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int h = lane >> 5, l32 = lane & 31;
@@ -116,7 +120,7 @@ __global__ __launch_bounds__(256, 2) void index_topk_kernel(IndexParams p) {
 
   const char* kbase = (const char*)p.k_idx + (int64_t)b * p.S_k * DI * (int64_t)sizeof(T);
   i32x4 pre[CH_PER_THREAD];  // a native vector type keeps the prefetch in registers
-  {
+  if (has_blocks) {
     const i32x4* src = (const i32x4*)(kbase + (int64_t)c_begin * kBlock * DI * (int64_t)sizeof(T));
 #pragma unroll
     for (int u = 0; u < CH_PER_THREAD; ++u) pre[u] = src[threadIdx.x + u * 256];
@@ -210,12 +214,12 @@ __global__ __launch_bounds__(256, 2) void index_topk_kernel(IndexParams p) {
     __syncthreads();
     if (h == 0 && rvalid[rt]) {
       const int n = n_first + wave * ROWS_WAVE + rt * 32 + l32;
-      const int64_t rowg = (int64_t)b * p.rows_per_b + n;
-      float* ds = p.part_s + (rowg * p.nsplit + split) * CAP;
-      int32_t* di = p.part_i + (rowg * p.nsplit + split) * CAP;
       const int oa = ((wave * 2 + 0) * CAP) * 32 + l32;
       const int ob = ((wave * 2 + 1) * CAP) * 32 + l32;
+      float ms[CAP];
+      int mi[CAP];
       int ia = 0, ib = 0;
+#pragma unroll
       for (int j = 0; j < CAP; ++j) {
         const float sa = ia < CAP ? xs[oa + ia * 32] : kNegInf;
         const int ida = ia < CAP ? xi[oa + ia * 32] : -1;
@@ -223,10 +227,38 @@ __global__ __launch_bounds__(256, 2) void index_topk_kernel(IndexParams p) {
         const int idb = ib < CAP ? xi[ob + ib * 32] : -1;
         // empty entries (id -1) rank last
         const bool take_a = idb < 0 || (ida >= 0 && ranks_before(sa, ida, sb, idb));
-        ds[j] = take_a ? sa : sb;
-        di[j] = take_a ? ida : idb;
+        ms[j] = take_a ? sa : sb;
+        mi[j] = take_a ? ida : idb;
         ia += take_a ? 1 : 0;
         ib += take_a ? 0 : 1;
+      }
+      if (p.nsplit > 1) {
+        const int64_t rowg = (int64_t)b * p.rows_per_b + n;
+        float* ds = p.part_s + (rowg * p.nsplit + split) * CAP;
+        int32_t* di = p.part_i + (rowg * p.nsplit + split) * CAP;
+#pragma unroll
+        for (int j = 0; j < CAP; ++j) {
+          ds[j] = ms[j];
+          di[j] = mi[j];
+        }
+      } else {
+        // the only split: the first min(k-1, L) entries are the selection; add
+        // the local block, order ids ascending, pad with -1
+        const int L = rowL[rt];
+        const int take = min(p.topk - 1, L);
+        const int i = n / p.G, g = n - (n / p.G) * p.G;
+        int32_t* out = p.sel + (((int64_t)b * p.G + g) * p.S_q + i) * p.topk;
+#pragma unroll
+        for (int j = 0; j < CAP; ++j) {
+          if (j < take) {
+            int r = 0;
+#pragma unroll
+            for (int m = 0; m < CAP; ++m) r += (m < take && mi[m] < mi[j]) ? 1 : 0;
+            out[r] = mi[j];
+          }
+        }
+        out[take] = L;
+        for (int j = take + 1; j < p.topk; ++j) out[j] = -1;
       }
     }
   }
@@ -316,6 +348,7 @@ static hipError_t launch_index_t(const IndexParams& p, hipStream_t s, const Kern
   timer_stop(tm, kKernIndexScore, s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (p.nsplit == 1) return hipGetLastError();  // the index kernel wrote the selection
   const int64_t rows = (int64_t)p.B * p.rows_per_b;
   timer_start(tm, kKernTopkMerge, s);
   const size_t lds = (size_t)8 * p.nsplit * CAP * 4;

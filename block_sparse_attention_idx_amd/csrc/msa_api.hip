@@ -33,6 +33,7 @@ constexpr size_t kAlign = 256;
 constexpr int kTokensPerItem = 128;
 constexpr int kAttnGrid = 512;      // persistent attention grid: 2 workgroups per CU
 constexpr int kIndexTargetUnits = 2048;
+constexpr int kIndexMinTiles = 512;  // row tiles that fill 256 CUs without key splits
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -114,8 +115,10 @@ IndexPlan plan_index(const msa_shape* s) {
   p.ntile = (int)ceil_div(p.rows_per_b, msa::index_rows_per_wg(s->topk));
   p.ntile_total = p.B * p.ntile;
   const int64_t Lmax = s->q_len > 0 ? (s->q_offset + s->q_len - 1) / msa::kBlock : 0;
-  int64_t chunk = 1, nsplit = 1;
-  if (Lmax > 0) {
+  // Enough row tiles to fill the GPU: one unit per tile, no merge.  Otherwise
+  // split the key blocks so that about kIndexTargetUnits units exist.
+  int64_t chunk = std::max<int64_t>(1, Lmax), nsplit = 1;
+  if (Lmax > 0 && p.ntile_total < kIndexMinTiles) {
     const int64_t want = std::max<int64_t>(1, ceil_div(kIndexTargetUnits, std::max(1, p.ntile_total)));
     chunk = std::max<int64_t>({16, ceil_div(Lmax, want), ceil_div(Lmax, 128)});
     nsplit = ceil_div(Lmax, chunk);
@@ -126,7 +129,7 @@ IndexPlan plan_index(const msa_shape* s) {
   p.grid_per_xcd = (int)ceil_div(p.nunits, 8);
   ip.cap = s->topk <= 16 ? 15 : 31;
   const size_t entries = (size_t)p.B * p.rows_per_b * p.nsplit * ip.cap;
-  ip.bytes = 2 * align_up(entries * 4);
+  ip.bytes = p.nsplit > 1 ? 2 * align_up(entries * 4) : 0;
   return ip;
 }
 
@@ -224,6 +227,11 @@ msa_status check_ws(void* ws, size_t ws_bytes, size_t need) {
   return MSA_OK;
 }
 
+// An error left by an earlier, unrelated HIP call on this thread would be read
+// back by hipGetLastError after our launches; drop it first so a status names
+// only this call's failures.
+void clear_stale_hip_error() { (void)hipGetLastError(); }
+
 msa_status hip_status(hipError_t e, const char* what) {
   if (e == hipSuccess) return MSA_OK;
   return fail(MSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
@@ -280,6 +288,7 @@ msa_status msa_index_select(const msa_shape* s, const void* q_idx, const void* k
   IndexPlan ip = plan_index(s);
   if ((st = check_ws(ws, ws_bytes, ip.bytes)) != MSA_OK) return st;
   bind_index(ip, (char*)ws, q_idx, k_idx, sel);
+  clear_stale_hip_error();
   return hip_status(msa::launch_index_select(ip.p, s->dtype == MSA_BF16, s->index_dim, (hipStream_t)stream, timer()),
                     "index select launch");
 }
@@ -300,6 +309,7 @@ msa_status msa_sparse_attn_fwd(const msa_shape* s, const void* q, const void* k,
   ap.p.sel = sel;
   ap.p.out = out;
   ap.p.lse = lse;
+  clear_stale_hip_error();
   return hip_status(msa::launch_sparse_attention(ap.p, s->dtype == MSA_BF16, (hipStream_t)stream, timer()),
                     "sparse attention launch");
 }
@@ -321,6 +331,7 @@ msa_status msa_fwd(const msa_shape* s, const void* q, const void* k, const void*
   char* scratch = w + sel_bytes(s);  // index lists and attention state reuse one region
   bind_index(ip, scratch, q_idx, k_idx, sel);
   hipStream_t hs = (hipStream_t)stream;
+  clear_stale_hip_error();
   st = hip_status(msa::launch_index_select(ip.p, s->dtype == MSA_BF16, s->index_dim, hs, timer()), "index select launch");
   if (st != MSA_OK) return st;
   bind_attn(ap, scratch);

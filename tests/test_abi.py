@@ -121,7 +121,7 @@ def test_workspace_sizes_for_the_workloads():
         e = 4 if s.dtype == "f32" else 2
         partials = s.batch * s.q_len * s.num_q_heads * s.topk * s.head_dim * e
         assert a >= partials
-        assert msa.workspace_size(sh, msa.OP_INDEX_SELECT) > 0
+        assert msa.workspace_size(sh, msa.OP_INDEX_SELECT) >= 0  # 0 when one key split needs no lists
         assert msa.workspace_size(sh, msa.OP_SPARSE_ATTN) <= a
     # a bad op code gives 0
     assert msa.lib().msa_workspace_size(ctypes.byref(_shape()), 7) == 0
