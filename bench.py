@@ -221,6 +221,7 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=50)
     ap.add_argument("--workload", type=int, default=3)
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the 8K and 1M-context prefill workloads")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-breakdown", action="store_true", help="skip the per-kernel timing passes")
@@ -291,6 +292,25 @@ def main():
         result["cpu_baseline"] = None
     del run
     torch.cuda.empty_cache()
+
+    if not args.no_extra:
+        # the other prefill workloads, reported beside the headline one
+        result["extra"] = {}
+        for ew in (2, 5):
+            se = synth.WORKLOADS[ew]
+            fm, fi, _ = algorithmic_work(se)
+            print(f"[bench] {synth.WORKLOAD_NAMES[ew]}: generating inputs", file=sys.stderr, flush=True)
+            er = Runner(msa, se, ew)
+            ems, eatt = er.time_steps(10, 2, "attention")
+            eidx = er.time_steps(5, 0, "index_score")[1]
+            eatt_ms, eidx_ms = float(np.mean(eatt)), float(np.median(eidx))
+            result["extra"][synth.WORKLOAD_NAMES[ew]] = {
+                "ms_per_step": round(ems, 4), "tflops": round((fm + fi) / (ems * 1e-3) / 1e12, 2),
+                "attention_ms": round(eatt_ms, 4), "attention_frac_of_mfma_peak": round(fm / (eatt_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                "index_ms": round(eidx_ms, 4), "index_frac_of_mfma_peak": round(fi / (eidx_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                "flop_main": fm, "flop_index": fi}
+            del er
+            torch.cuda.empty_cache()
 
     if not args.no_decode:
         sd = synth.WORKLOADS[4]

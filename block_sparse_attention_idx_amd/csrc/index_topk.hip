@@ -119,17 +119,30 @@ __global__ __launch_bounds__(256, 2) void index_topk_kernel(IndexParams p) {
     }
 
   const char* kbase = (const char*)p.k_idx + (int64_t)b * p.S_k * DI * (int64_t)sizeof(T);
-  i32x4 pre[CH_PER_THREAD];  // a native vector type keeps the prefetch in registers
+  // K tiles are prefetched two blocks ahead: `pre` holds block c + 1 (stored to
+  // LDS after block c is scored), `pre2` is in flight for block c + 2.  Native
+  // vector types keep both in registers.
+  i32x4 pre[CH_PER_THREAD], pre2[CH_PER_THREAD];
+  auto kblock = [&](int c) {
+    return (const i32x4*)(kbase + (int64_t)c * kBlock * DI * (int64_t)sizeof(T));
+  };
   if (has_blocks) {
-    const i32x4* src = (const i32x4*)(kbase + (int64_t)c_begin * kBlock * DI * (int64_t)sizeof(T));
+    const i32x4* src = kblock(c_begin);
 #pragma unroll
     for (int u = 0; u < CH_PER_THREAD; ++u) pre[u] = src[threadIdx.x + u * 256];
+    if (c_begin + 1 < c_end) {
+      const i32x4* src1 = kblock(c_begin + 1);
+#pragma unroll
+      for (int u = 0; u < CH_PER_THREAD; ++u) pre2[u] = src1[threadIdx.x + u * 256];
+    }
 #pragma unroll
     for (int u = 0; u < CH_PER_THREAD; ++u) {
       const int ch = threadIdx.x + u * 256;
       const int row = ch / CH_PER_ROW, col = ch - row * CH_PER_ROW;
       *(i32x4*)((char*)&Ks[row * LDW] + col * 16) = pre[u];
     }
+#pragma unroll
+    for (int u = 0; u < CH_PER_THREAD; ++u) pre[u] = pre2[u];
   }
   __syncthreads();
 
@@ -137,10 +150,10 @@ __global__ __launch_bounds__(256, 2) void index_topk_kernel(IndexParams p) {
   int buf = 0;
   for (int c = c_begin; c < c_end; ++c) {
     const bool has_next = c + 1 < c_end;
-    if (has_next) {
-      const i32x4* src = (const i32x4*)(kbase + (int64_t)(c + 1) * kBlock * DI * (int64_t)sizeof(T));
+    if (c + 2 < c_end) {
+      const i32x4* src = kblock(c + 2);
 #pragma unroll
-      for (int u = 0; u < CH_PER_THREAD; ++u) pre[u] = src[threadIdx.x + u * 256];
+      for (int u = 0; u < CH_PER_THREAD; ++u) pre2[u] = src[threadIdx.x + u * 256];
     }
     // block max of scores q_idx . k_idx over the block's 128 keys, one 32-key
     // tile of accumulators at a time
@@ -173,6 +186,8 @@ __global__ __launch_bounds__(256, 2) void index_topk_kernel(IndexParams p) {
         const int row = ch / CH_PER_ROW, col = ch - row * CH_PER_ROW;
         *(i32x4*)((char*)&Ks[(buf ^ 1) * (kBlock * LDW) + row * LDW] + col * 16) = pre[u];
       }
+#pragma unroll
+      for (int u = 0; u < CH_PER_THREAD; ++u) pre[u] = pre2[u];
     }
     __syncthreads();
     buf ^= 1;

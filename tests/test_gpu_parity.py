@@ -167,3 +167,60 @@ def test_workload_8k_bf16():
     rows = [(0, int(i)) for i in np.concatenate([rng.integers(0, s.q_len, 120), [0, 1, 127, 128, 8191]])]
     ref_out, _ = orc.sparse_attention(f["q"], f["k"], f["v"], ref_sel, rows=rows)
     assert _max_err(out, ref_out, rows) <= TOL["bf16"]
+
+
+@gpu
+@pytest.mark.parametrize("seed", range(12))
+def test_random_shapes_match_oracle(seed):
+    # seeded sweep over the supported shape space (several tiles, ragged tails)
+    msa = _msa()
+    rng = np.random.default_rng(1000 + seed)
+    dt = "f32" if seed % 4 == 0 else "bf16"
+    G = int(rng.choice([1, 2, 4]))
+    r = int(rng.choice([1, 2, 4, 8, 16, 32]))
+    d = int(rng.choice([64, 128]))
+    D = int(rng.choice([32, 64, 128]))
+    k = int(rng.integers(1, 33))
+    B = int(rng.integers(1, 3))
+    S_q = int(rng.integers(1, 600))
+    q_offset = int(rng.integers(0, 2500))
+    S_k = q_offset + S_q + int(rng.integers(0, 300))
+    lo, hi = (-8, 8) if dt == "f32" else (-4, 4)
+    s = synth.Shape(B, S_q, S_k, q_offset, G * r, G, d, D, k, dtype=dt, idx_lo=lo, idx_hi=hi)
+    print(f"case {s}", flush=True)
+    x, xh = _inputs(s, 2000 + seed)
+    out, sel, lse = msa.fwd(x["q"], x["k"], x["v"], x["q_idx"], x["k_idx"], k, q_offset=q_offset,
+                            return_sel=True, return_lse=True)
+    torch.cuda.synchronize()
+    f = {n: synth.as_f64(t) for n, t in xh.items()}
+    ref_out, ref_sel, ref_lse = orc.msa_forward(f["q"], f["k"], f["v"], f["q_idx"], f["k_idx"], k, q_offset)
+    _check_sel_rows(sel, ref_sel)
+    assert _max_err(out, ref_out) <= TOL[dt]
+    assert float(np.abs(lse.cpu().numpy() - ref_lse).max()) <= 1e-3
+
+
+@gpu
+def test_user_selection_with_invalid_ids_is_safe():
+    # ids beyond the cache or after the query's local block are ignored; -1
+    # padding anywhere in a row is skipped; the rest is exact attention
+    msa = _msa()
+    s = synth.Shape(1, 300, 1000, 600, 16, 2, 128, 64, 6, dtype="bf16")
+    x, xh = _inputs(s, 11)
+    f = {n: synth.as_f64(t) for n, t in xh.items()}
+    good = orc.index_select(f["q_idx"], f["k_idx"], s.topk, s.q_offset)
+    bad = good.copy()
+    nb = (s.kv_len + 127) // 128
+    rng = np.random.default_rng(4)
+    for g in range(s.groups):
+        for i in range(s.q_len):
+            row = [c for c in good[0, g, i] if c >= 0]
+            L = (s.q_offset + i) // 128
+            extra = [nb + 3, 10 ** 6, L + 1] if L + 1 < nb else [nb + 3, 10 ** 6]
+            row = row + extra[: s.topk - len(row)]
+            rng.shuffle(row)
+            bad[0, g, i, :len(row)] = row
+            bad[0, g, i, len(row):] = -1
+    out = msa.sparse_attn_fwd(x["q"], x["k"], x["v"], torch.from_numpy(bad).cuda(), q_offset=s.q_offset)
+    torch.cuda.synchronize()
+    ref, _ = orc.sparse_attention(f["q"], f["k"], f["v"], good, s.q_offset)
+    assert _max_err(out, ref) <= TOL["bf16"]
