@@ -396,6 +396,157 @@ __global__ __launch_bounds__(256, 2) void attn_kvouter_kernel(AttnParams p) {
   }
 }
 
+// Decode form of the main branch: one work item = one selection entry
+// (b, g, i, slot), i.e. the r rows of one token against one block.  All four
+// waves work on the item: wave w scores keys [32w, 32w + 32) (S^T = K Q^T with K
+// read straight from global memory as the A operand), the block-local softmax
+// is combined across waves through LDS, P^T goes to LDS, and wave w then forms
+// the d-slice [32w, 32w + 32) of O^T = V^T P^T from the LDS copies of V^T and
+// P^T.  The partial state is written in the same lane-native layout as the
+// KV-outer kernel, so the combine is shared.
+template <typename T, int D, int R>
+__global__ __launch_bounds__(256) void attn_decode_kernel(AttnParams p) {
+  using M = Mma<T>;
+  using frag = typename M::frag;
+  constexpr int KPL = M::KPL, KSTEP = M::KSTEP, NKS = D / KSTEP;
+  constexpr int E = 16 / (int)sizeof(T);
+  constexpr int LDV = kBlock + E;  // V^T pitch (elements), 16-byte aligned rows
+  constexpr int LDP = kBlock + E;  // P^T pitch
+  constexpr int NDT = D / 32;
+  constexpr int NPV = kBlock / KSTEP;
+  static_assert(R <= 32, "one 32-row tile holds the token's heads");
+  __shared__ __align__(16) T Vt[D * LDV];
+  __shared__ __align__(16) T Ps[32 * LDP];
+  __shared__ float red_m[4][32];
+  __shared__ float red_l[4][32];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int h = lane >> 5, l32 = lane & 31;
+  const float sl2 = p.scale_log2;
+
+  for (int64_t item = blockIdx.x; item < p.n_direct; item += gridDim.x) {
+    const int c = p.sel[item];
+    if (c < 0 || c >= p.nb) continue;  // uniform across the workgroup
+    const int slot = (int)(item % p.topk);
+    const int64_t rest = item / p.topk;
+    const int i = (int)(rest % p.S_q);
+    const int64_t bg = rest / p.S_q;
+    const int g = (int)(bg % p.G);
+    const int b = (int)(bg / p.G);
+    const int64_t key0 = (int64_t)c * kBlock;
+    const int64_t rel = p.q_offset + i - key0;
+    if (rel < 0) continue;  // a block after the query: nothing visible (uniform)
+    const int lim = rel >= kBlock ? kBlock : (int)rel;
+    const int rows_ok = (int)min((int64_t)kBlock, (int64_t)p.S_k - key0);
+    const int64_t kv0 = (((int64_t)b * p.G + g) * p.S_k + key0) * D;
+
+    // loads: this wave's 32 K rows (A operand), the token's Q rows (B operand), and
+    // this thread's share of V; all issued before any is used
+    const int krow = min(wave * 32 + l32, rows_ok - 1);
+    const T* kp = (const T*)p.k + kv0 + (int64_t)krow * D;
+    const int qh = l32 < R ? l32 : 0;  // rows past r repeat head 0 and are never stored
+    const T* qp = (const T*)p.q + (((int64_t)b * p.S_q + i) * p.Hq + g * R + qh) * D;
+    frag ka[NKS], qb[NKS];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      ka[ks] = *(const frag*)(kp + ks * KSTEP + h * KPL);
+      qb[ks] = *(const frag*)(qp + ks * KSTEP + h * KPL);
+    }
+    constexpr int VT = (D / E) * (kBlock / E);
+    constexpr int VU = (VT + 255) / 256;
+    Chunk16 vin[VU][E];
+    const T* vsrc = (const T*)p.v + kv0;
+#pragma unroll
+    for (int u = 0; u < VU; ++u) {
+      const int tl = min((int)threadIdx.x + u * 256, VT - 1);
+      const int dg = tl % (D / E), kg = tl / (D / E);
+#pragma unroll
+      for (int r = 0; r < E; ++r)
+        vin[u][r] = *(const Chunk16*)(vsrc + (int64_t)min(kg * E + r, rows_ok - 1) * D + dg * E);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    __syncthreads();  // the previous item is done with the LDS tiles
+#pragma unroll
+    for (int u = 0; u < VU; ++u) {
+      const int tl = threadIdx.x + u * 256;
+      if (VT % 256 != 0 && tl >= VT) break;
+      const int dg = tl % (D / E), kg = tl / (D / E);
+#pragma unroll
+      for (int r = 0; r < E; ++r)
+        if (kg * E + r >= rows_ok) vin[u][r] = Chunk16{};
+      Chunk16 outc[E];
+      transpose_tile<T, E>(vin[u], outc);
+#pragma unroll
+      for (int r = 0; r < E; ++r) *(Chunk16*)&Vt[(dg * E + r) * LDV + kg * E] = outc[r];
+    }
+
+    // S^T for keys [32w, 32w + 32): lane (row l32, half h) holds keys 32w + c_row(j, h)
+    f32x16 sacc = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) sacc = M::mma(ka[ks], qb[ks], sacc);
+    if (lim < kBlock - 1) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        if (wave * 32 + c_row(j, h) > lim) sacc[j] = kNegInf;
+    }
+    float mw = kNegInf;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) mw = fmaxf(mw, sacc[j]);
+    mw = wave_max_xor32(mw);
+    if (h == 0) red_m[wave][l32] = mw;
+    __syncthreads();
+    const float mx = fmaxf(fmaxf(red_m[0][l32], red_m[1][l32]), fmaxf(red_m[2][l32], red_m[3][l32]));
+    const float moff = -mx * sl2;
+    float lw = 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[j], sl2, moff));
+      sacc[j] = e;
+      lw += e;
+    }
+    lw += __shfl_xor(lw, 32);
+    if (h == 0) red_l[wave][l32] = lw;
+    // P^T row l32: keys 32w + c_row(j, h) come in runs of four
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      T* dst = &Ps[l32 * LDP + wave * 32 + q4 * 8 + h * 4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dst[e] = from_f32<T>(sacc[q4 * 4 + e]);
+    }
+    __syncthreads();
+
+    if (wave < NDT) {
+      // O^T slice d in [32w, 32w + 32) over all 128 keys, natural key order
+      f32x16 oacc = f32x16{};
+#pragma unroll
+      for (int ks2 = 0; ks2 < NPV; ++ks2) {
+        const frag va = *(const frag*)&Vt[(wave * 32 + l32) * LDV + ks2 * KSTEP + h * KPL];
+        const frag pb = *(const frag*)&Ps[l32 * LDP + ks2 * KSTEP + h * KPL];
+        oacc = M::mma(va, pb, oacc);
+      }
+      const float lsum = red_l[0][l32] + red_l[1][l32] + red_l[2][l32] + red_l[3][l32];
+      if (l32 < R) {
+        const float inv = 1.0f / lsum;
+        const int64_t ptok = (((int64_t)b * p.S_q + i) * p.G + g) * p.topk + slot;
+        T* po = (T*)p.part_o + ptok * (R * D);
+        // lane-native chunks q = (wave * 16 + j) / E of this lane's registers
+#pragma unroll
+        for (int qq = 0; qq < 16 / E; ++qq) {
+          const int q = wave * (16 / E) + qq;
+          Chunk16 w;
+          T* wv = (T*)&w;
+#pragma unroll
+          for (int e = 0; e < E; ++e) wv[e] = from_f32<T>(oacc[qq * E + e] * inv);
+          __builtin_nontemporal_store(__builtin_bit_cast(i32x4, w), (i32x4*)(po + ((q * 2 + h) * R + l32) * E));
+        }
+        if (wave == 0 && h == 0)
+          __builtin_nontemporal_store(mx * sl2 + __builtin_amdgcn_logf(lsum), &p.part_lse[ptok * R + l32]);
+      }
+    }
+  }
+}
+
 // Merge the partial states of one (token, group) over its selected slots:
 // out = sum_s 2^(lse_s - M) o_s / sum_s 2^(lse_s - M), M = max_s lse_s.
 // A thread owns one 16-byte chunk of the lane-native partial layout (E values
@@ -516,7 +667,10 @@ static hipError_t launch_attn_t(const AttnParams& p, hipStream_t s, const Kernel
     timer_stop(tm, kKernGather, s);
   }
   timer_start(tm, kKernAttention, s);
-  hipLaunchKernelGGL((attn_kvouter_kernel<T, D, R>), dim3(p.grid), dim3(256), 0, s, p);
+  if (p.direct)
+    hipLaunchKernelGGL((attn_decode_kernel<T, D, R>), dim3(p.grid_decode), dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL((attn_kvouter_kernel<T, D, R>), dim3(p.grid), dim3(256), 0, s, p);
   timer_stop(tm, kKernAttention, s);
   timer_start(tm, kKernCombine, s);
   constexpr int E = 16 / (int)sizeof(T);

@@ -77,6 +77,7 @@ struct AttnParams {
   int direct;          // 1: one item per selection entry, no gather
   int64_t n_direct;    // B * G * S_q * topk when direct
   int grid;            // persistent grid size of the attention kernel
+  int grid_decode;     // persistent grid size of the decode-form attention kernel
   float scale_log2;    // softmax scale * log2(e)
   int out_f32;         // output dtype: 1 fp32, 0 input dtype
 };

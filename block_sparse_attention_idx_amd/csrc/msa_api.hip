@@ -171,6 +171,7 @@ AttnPlan plan_attn(const msa_shape* s) {
   p.direct = per_bucket < 2.0 ? 1 : 0;
   p.n_direct = (int64_t)p.B * p.G * p.S_q * p.topk;
   p.grid = kAttnGrid;
+  p.grid_decode = 768;  // 3 workgroups per CU (44 KiB of LDS each)
   const float scale = s->softmax_scale != 0.0f ? s->softmax_scale : 1.0f / std::sqrt((float)s->head_dim);
   p.scale_log2 = scale * 1.4426950408889634f;
   p.out_f32 = s->out_dtype == MSA_F32 ? 1 : 0;
