@@ -156,15 +156,25 @@ __global__ __launch_bounds__(1024) void gather_scan_kernel(AttnParams p) {
   }
 }
 
-// E x E transpose of 16-byte rows (E = 16 / sizeof(T)).
+// Element vector of a 16-byte chunk.
+template <typename T> struct Vec16;
+template <> struct Vec16<bf16> { typedef bf16x8 type; };
+template <> struct Vec16<float> { typedef f32x4 type; };
+
+// E x E transpose of 16-byte rows (E = 16 / sizeof(T)), in registers.  Native
+// vector types throughout, so nothing is placed in scratch memory.
 template <typename T, int E>
-__device__ __forceinline__ void transpose_tile(const Chunk16 (&in)[E], Chunk16 (&out)[E]) {
-  const T* a = (const T*)in;
-  T* o = (T*)out;
+__device__ __forceinline__ void transpose_tile(const i32x4 (&in)[E], i32x4 (&out)[E]) {
+  typedef typename Vec16<T>::type V;
+  V a[E], o[E];
 #pragma unroll
-  for (int r = 0; r < E; ++r)
+  for (int r = 0; r < E; ++r) a[r] = __builtin_bit_cast(V, in[r]);
 #pragma unroll
-    for (int c = 0; c < E; ++c) o[c * E + r] = a[r * E + c];
+  for (int c = 0; c < E; ++c)
+#pragma unroll
+    for (int r = 0; r < E; ++r) o[c][r] = a[r][c];
+#pragma unroll
+  for (int c = 0; c < E; ++c) out[c] = __builtin_bit_cast(i32x4, o[c]);
 }
 
 template <typename T, int D, int R>
@@ -228,13 +238,13 @@ __global__ __launch_bounds__(256, 2) void attn_kvouter_kernel(AttnParams p) {
       constexpr int VU = (VT + 255) / 256;
       const T* ksrc = (const T*)p.k + kv0;
       const T* vsrc = (const T*)p.v + kv0;
-      Chunk16 kx[KU];
-      Chunk16 vin[VU][E];
+      i32x4 kx[KU];
+      i32x4 vin[VU][E];
 #pragma unroll
       for (int u = 0; u < KU; ++u) {
         const int ch = threadIdx.x + u * 256;
         const int row = ch / (D / E), col = ch - row * (D / E);
-        kx[u] = *(const Chunk16*)(ksrc + (int64_t)min(row, rows_ok - 1) * D + col * E);
+        kx[u] = *(const i32x4*)(ksrc + (int64_t)min(row, rows_ok - 1) * D + col * E);
       }
 #pragma unroll
       for (int u = 0; u < VU; ++u) {
@@ -242,16 +252,16 @@ __global__ __launch_bounds__(256, 2) void attn_kvouter_kernel(AttnParams p) {
         const int dg = tl % (D / E), kg = tl / (D / E);
 #pragma unroll
         for (int r = 0; r < E; ++r)
-          vin[u][r] = *(const Chunk16*)(vsrc + (int64_t)min(kg * E + r, rows_ok - 1) * D + dg * E);
+          vin[u][r] = *(const i32x4*)(vsrc + (int64_t)min(kg * E + r, rows_ok - 1) * D + dg * E);
       }
       __builtin_amdgcn_sched_barrier(0);  // keep every staging load ahead of the first use
 #pragma unroll
       for (int u = 0; u < KU; ++u) {
         const int ch = threadIdx.x + u * 256;
         const int row = ch / (D / E), col = ch - row * (D / E);
-        Chunk16 x = kx[u];
-        if (row >= rows_ok) x = Chunk16{};
-        *(Chunk16*)&Ks[row * LDK + col * E] = x;
+        i32x4 x = kx[u];
+        if (row >= rows_ok) x = i32x4{};
+        *(i32x4*)&Ks[row * LDK + col * E] = x;
       }
 #pragma unroll
       for (int u = 0; u < VU; ++u) {
@@ -260,14 +270,14 @@ __global__ __launch_bounds__(256, 2) void attn_kvouter_kernel(AttnParams p) {
         const int dg = tl % (D / E), kg = tl / (D / E);
 #pragma unroll
         for (int r = 0; r < E; ++r)
-          if (kg * E + r >= rows_ok) vin[u][r] = Chunk16{};
-        Chunk16 outc[E];
+          if (kg * E + r >= rows_ok) vin[u][r] = i32x4{};
+        i32x4 outc[E];
         transpose_tile<T, E>(vin[u], outc);
 #pragma unroll
         for (int r = 0; r < E; ++r) {  // rows are 8-byte aligned: two 8-byte stores
           uint2* dst = (uint2*)&Vt[(dg * E + r) * LDV + kg * E];
-          dst[0] = make_uint2(outc[r].w[0], outc[r].w[1]);
-          dst[1] = make_uint2(outc[r].w[2], outc[r].w[3]);
+          dst[0] = make_uint2((uint32_t)outc[r][0], (uint32_t)outc[r][1]);
+          dst[1] = make_uint2((uint32_t)outc[r][2], (uint32_t)outc[r][3]);
         }
       }
     }
@@ -454,7 +464,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnParams p) {
     }
     constexpr int VT = (D / E) * (kBlock / E);
     constexpr int VU = (VT + 255) / 256;
-    Chunk16 vin[VU][E];
+    i32x4 vin[VU][E];
     const T* vsrc = (const T*)p.v + kv0;
 #pragma unroll
     for (int u = 0; u < VU; ++u) {
@@ -462,7 +472,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnParams p) {
       const int dg = tl % (D / E), kg = tl / (D / E);
 #pragma unroll
       for (int r = 0; r < E; ++r)
-        vin[u][r] = *(const Chunk16*)(vsrc + (int64_t)min(kg * E + r, rows_ok - 1) * D + dg * E);
+        vin[u][r] = *(const i32x4*)(vsrc + (int64_t)min(kg * E + r, rows_ok - 1) * D + dg * E);
     }
     __builtin_amdgcn_sched_barrier(0);
 
@@ -474,11 +484,11 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnParams p) {
       const int dg = tl % (D / E), kg = tl / (D / E);
 #pragma unroll
       for (int r = 0; r < E; ++r)
-        if (kg * E + r >= rows_ok) vin[u][r] = Chunk16{};
-      Chunk16 outc[E];
+        if (kg * E + r >= rows_ok) vin[u][r] = i32x4{};
+      i32x4 outc[E];
       transpose_tile<T, E>(vin[u], outc);
 #pragma unroll
-      for (int r = 0; r < E; ++r) *(Chunk16*)&Vt[(dg * E + r) * LDV + kg * E] = outc[r];
+      for (int r = 0; r < E; ++r) *(i32x4*)&Vt[(dg * E + r) * LDV + kg * E] = outc[r];
     }
 
     // S^T for keys [32w, 32w + 32): lane (row l32, half h) holds keys 32w + c_row(j, h)
