@@ -587,24 +587,62 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnParams p) {
   const int32_t* srow = p.sel + (((int64_t)b * p.G + g) * p.S_q + i) * p.topk;
   const int64_t pbase = rowg * p.topk;
 
-  int cs[KMAX];
   float ls[KMAX];
-  Chunk16 x[KMAX];
-#pragma unroll
-  for (int s = 0; s < KMAX; ++s) {
-    const int sc = min(s, p.topk - 1);
-    cs[s] = srow[sc];
-    ls[s] = p.part_lse[(pbase + sc) * R + hh];
-    x[s] = __builtin_bit_cast(
-        Chunk16, __builtin_nontemporal_load((const i32x4*)((const T*)p.part_o + (pbase + sc) * (R * D) + ch * E)));
-  }
+  i32x4 x[KMAX];
   float mx = kNegInf;
+  if constexpr (STAGED) {
+    // A workgroup's rows share their selection rows and log-sum-exps: load those
+    // once into LDS instead of once per thread.
+    __shared__ int sel_s[RPW][KMAX];
+    __shared__ float lse_s[RPW][KMAX][R];
+    const int64_t row0 = (int64_t)blockIdx.x * RPW;
+    for (int e = threadIdx.x; e < RPW * KMAX; e += 256) {
+      const int lr = e / KMAX, s2 = e - lr * KMAX;
+      const int64_t rg = min(row0 + lr, rows_total - 1);
+      const int64_t rbi = rg / p.G;
+      const int rgg = (int)(rg - rbi * p.G);
+      const int ri = (int)(rbi % p.S_q), rb = (int)(rbi / p.S_q);
+      int c = -1;
+      if (s2 < p.topk) {
+        c = p.sel[(((int64_t)rb * p.G + rgg) * p.S_q + ri) * p.topk + s2];
+        if (!(c >= 0 && c < p.nb && (int64_t)c * kBlock <= p.q_offset + ri)) c = -1;
+      }
+      sel_s[lr][s2] = c;
+    }
+    for (int e = threadIdx.x; e < RPW * KMAX * R; e += 256) {
+      const int lr = e / (KMAX * R), rem = e - lr * (KMAX * R);
+      const int s2 = rem / R, hd = rem - s2 * R;
+      const int64_t rg = min(row0 + lr, rows_total - 1);
+      lse_s[lr][s2][hd] = s2 < p.topk ? p.part_lse[(rg * p.topk + s2) * R + hd] : 0.f;
+    }
+    __syncthreads();
+    const int lr = (int)(threadIdx.x / NCHT);
 #pragma unroll
-  for (int s = 0; s < KMAX; ++s) {
-    const int c = cs[s];
-    const bool used = s < p.topk && c >= 0 && c < p.nb && (int64_t)c * kBlock <= t;
-    ls[s] = used ? ls[s] : kNegInf;
-    mx = fmaxf(mx, ls[s]);
+    for (int s2 = 0; s2 < KMAX; ++s2) {
+      const int sc = min(s2, p.topk - 1);
+      x[s2] = __builtin_nontemporal_load((const i32x4*)((const T*)p.part_o + (pbase + sc) * (R * D) + ch * E));
+    }
+#pragma unroll
+    for (int s2 = 0; s2 < KMAX; ++s2) {
+      ls[s2] = sel_s[lr][s2] >= 0 ? lse_s[lr][s2][hh] : kNegInf;
+      mx = fmaxf(mx, ls[s2]);
+    }
+  } else {
+    int cs[KMAX];
+#pragma unroll
+    for (int s2 = 0; s2 < KMAX; ++s2) {
+      const int sc = min(s2, p.topk - 1);
+      cs[s2] = srow[sc];
+      ls[s2] = p.part_lse[(pbase + sc) * R + hh];
+      x[s2] = __builtin_nontemporal_load((const i32x4*)((const T*)p.part_o + (pbase + sc) * (R * D) + ch * E));
+    }
+#pragma unroll
+    for (int s2 = 0; s2 < KMAX; ++s2) {
+      const int c = cs[s2];
+      const bool used = s2 < p.topk && c >= 0 && c < p.nb && (int64_t)c * kBlock <= t;
+      ls[s2] = used ? ls[s2] : kNegInf;
+      mx = fmaxf(mx, ls[s2]);
+    }
   }
   float W = 0.f;
   float acc[E];
@@ -615,7 +653,7 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnParams p) {
     const bool used = ls[s] != kNegInf;
     const float w = used ? exp2f(ls[s] - mx) : 0.f;
     W += w;
-    const T* xv = (const T*)&x[s];
+    const typename Vec16<T>::type xv = __builtin_bit_cast(typename Vec16<T>::type, x[s]);
 #pragma unroll
     for (int e = 0; e < E; ++e) acc[e] += used ? w * to_f32(xv[e]) : 0.f;
   }
