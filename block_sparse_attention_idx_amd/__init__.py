@@ -10,12 +10,16 @@ Functions (same names as the C entry points):
 
 * ``index_select(q_idx, k_idx, topk, q_offset=0)`` -> sel int32 [B, G, S_q, k]
 * ``sparse_attn_fwd(q, k, v, sel, q_offset=0, scale=None, out_dtype=None,
-  return_lse=False)`` -> out [B, S_q, Hq, d] (and lse fp32 [B, Hq, S_q])
+  return_lse=False, k_scale=None, v_scale=None)`` -> out [B, S_q, Hq, d] (and
+  lse fp32 [B, Hq, S_q])
 * ``fwd(q, k, v, q_idx, k_idx, topk, q_offset=0, scale=None, out_dtype=None,
-  return_sel=False, return_lse=False)``
+  return_sel=False, return_lse=False, k_scale=None, v_scale=None)``
 
 Layouts: q [B,S_q,Hq,d], k/v [B,Hkv,S_k,d], q_idx [B,S_q,G,D_idx],
 k_idx [B,S_k,D_idx] with G = Hkv; all contiguous, on the GPU, fp32 or bf16.
+The caches k, v and k_idx may instead be ``torch.float8_e4m3fn`` tensors (OCP
+FP8 E4M3) next to bf16 q and q_idx; the keys and values attended to are then
+``k_scale * k`` and ``v_scale * v``.
 """
 from __future__ import annotations
 
@@ -31,6 +35,7 @@ __all__ = ["index_select", "sparse_attn_fwd", "fwd", "workspace_size", "MsaShape
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmsa.so")
 
 MSA_F32, MSA_BF16 = 0, 1
+CACHE_NATIVE, CACHE_FP8_E4M3 = 0, 1
 OP_INDEX_SELECT, OP_SPARSE_ATTN, OP_FWD = 0, 1, 2
 BLOCK_SIZE = 128
 
@@ -40,7 +45,7 @@ class MsaShape(ctypes.Structure):
         ("batch", ctypes.c_int32),
         ("q_len", ctypes.c_int32),
         ("kv_len", ctypes.c_int32),
-        ("pad0", ctypes.c_int32),
+        ("cache_format", ctypes.c_int32),
         ("q_offset", ctypes.c_int64),
         ("num_q_heads", ctypes.c_int32),
         ("num_kv_heads", ctypes.c_int32),
@@ -51,7 +56,9 @@ class MsaShape(ctypes.Structure):
         ("softmax_scale", ctypes.c_float),
         ("dtype", ctypes.c_int32),
         ("out_dtype", ctypes.c_int32),
-        ("pad1", ctypes.c_int32),
+        ("k_scale", ctypes.c_float),
+        ("v_scale", ctypes.c_float),
+        ("pad", ctypes.c_int32),
     ]
 
 
@@ -103,9 +110,9 @@ def _dtype_code(dt: torch.dtype) -> int:
 
 
 def make_shape(B, S_q, S_k, q_offset, Hq, Hkv, d, D_idx, topk, dtype, out_dtype=None, scale=None,
-               block_size=BLOCK_SIZE) -> MsaShape:
+               block_size=BLOCK_SIZE, cache_format=CACHE_NATIVE, k_scale=None, v_scale=None) -> MsaShape:
     s = MsaShape()
-    s.batch, s.q_len, s.kv_len, s.pad0 = B, S_q, S_k, 0
+    s.batch, s.q_len, s.kv_len, s.cache_format = B, S_q, S_k, cache_format
     s.q_offset = q_offset
     s.num_q_heads, s.num_kv_heads = Hq, Hkv
     s.head_dim, s.index_dim = d, D_idx
@@ -113,8 +120,21 @@ def make_shape(B, S_q, S_k, q_offset, Hq, Hkv, d, D_idx, topk, dtype, out_dtype=
     s.softmax_scale = 0.0 if scale is None else float(scale)
     s.dtype = _dtype_code(dtype)
     s.out_dtype = _dtype_code(out_dtype if out_dtype is not None else dtype)
-    s.pad1 = 0
+    s.k_scale = 0.0 if k_scale is None else float(k_scale)
+    s.v_scale = 0.0 if v_scale is None else float(v_scale)
+    s.pad = 0
     return s
+
+
+def _cache_format(q_dtype: torch.dtype, caches) -> int:
+    """Cache tensors share q's dtype, or are all float8_e4m3fn next to bf16 q."""
+    dts = {t.dtype for _, t in caches}
+    if dts == {q_dtype}:
+        return CACHE_NATIVE
+    if dts == {torch.float8_e4m3fn} and q_dtype == torch.bfloat16:
+        return CACHE_FP8_E4M3
+    names = ", ".join(f"{n} {t.dtype}" for n, t in caches)
+    raise ValueError(f"caches ({names}) must all have q's dtype {q_dtype}, or all be float8_e4m3fn with bf16 q")
 
 
 def _check(st: int):
@@ -164,12 +184,13 @@ def index_select(q_idx: torch.Tensor, k_idx: torch.Tensor, topk: int, q_offset: 
     """Per-group block selection, int32 [B, G, S_q, topk] (ascending ids, -1 padded)."""
     _need(q_idx, "q_idx", 4)
     dev = q_idx.device
-    _need(k_idx, "k_idx", 3, dev, q_idx.dtype)
+    _need(k_idx, "k_idx", 3, dev)
+    cf = _cache_format(q_idx.dtype, [("k_idx", k_idx)])
     B, S_q, G, D = q_idx.shape
     if k_idx.shape[0] != B or k_idx.shape[2] != D:
         raise ValueError("k_idx must be [B, S_k, D_idx] matching q_idx")
     S_k = k_idx.shape[1]
-    shape = make_shape(B, S_q, S_k, q_offset, G, G, 64, D, topk, q_idx.dtype)
+    shape = make_shape(B, S_q, S_k, q_offset, G, G, 64, D, topk, q_idx.dtype, cache_format=cf)
     if sel is None:
         sel = torch.empty((B, G, S_q, topk), dtype=torch.int32, device=dev)
     else:
@@ -184,12 +205,14 @@ def index_select(q_idx: torch.Tensor, k_idx: torch.Tensor, topk: int, q_offset: 
 
 def sparse_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sel: torch.Tensor, q_offset: int = 0,
                     scale: Optional[float] = None, out_dtype: Optional[torch.dtype] = None,
-                    return_lse: bool = False, workspace: Optional[torch.Tensor] = None):
+                    return_lse: bool = False, workspace: Optional[torch.Tensor] = None,
+                    k_scale: Optional[float] = None, v_scale: Optional[float] = None):
     """Exact softmax attention over the selected blocks."""
     _need(q, "q", 4)
     dev = q.device
-    _need(k, "k", 4, dev, q.dtype)
-    _need(v, "v", 4, dev, q.dtype)
+    _need(k, "k", 4, dev)
+    _need(v, "v", 4, dev)
+    cf = _cache_format(q.dtype, [("k", k), ("v", v)])
     _need(sel, "sel", 4, dev, torch.int32)
     B, S_q, Hq, d = q.shape
     Hkv, S_k = k.shape[1], k.shape[2]
@@ -198,7 +221,8 @@ def sparse_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sel: torc
     topk = sel.shape[3]
     if tuple(sel.shape[:3]) != (B, Hkv, S_q):
         raise ValueError("sel must be [B, G, S_q, topk]")
-    shape = make_shape(B, S_q, S_k, q_offset, Hq, Hkv, d, 32, topk, q.dtype, out_dtype, scale)
+    shape = make_shape(B, S_q, S_k, q_offset, Hq, Hkv, d, 32, topk, q.dtype, out_dtype, scale,
+                       cache_format=cf, k_scale=k_scale, v_scale=v_scale)
     out = torch.empty((B, S_q, Hq, d), dtype=out_dtype or q.dtype, device=dev)
     lse = torch.empty((B, Hq, S_q), dtype=torch.float32, device=dev) if return_lse else None
     ws = workspace if workspace is not None else _workspace(shape, OP_SPARSE_ATTN, dev)
@@ -211,12 +235,15 @@ def sparse_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sel: torc
 
 def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_idx: torch.Tensor, k_idx: torch.Tensor, topk: int,
         q_offset: int = 0, scale: Optional[float] = None, out_dtype: Optional[torch.dtype] = None,
-        return_sel: bool = False, return_lse: bool = False, workspace: Optional[torch.Tensor] = None):
+        return_sel: bool = False, return_lse: bool = False, workspace: Optional[torch.Tensor] = None,
+        k_scale: Optional[float] = None, v_scale: Optional[float] = None):
     """Index branch and main branch.  Returns out, plus sel and/or lse when asked."""
     _need(q, "q", 4)
     dev = q.device
-    for name, t, nd in (("k", k, 4), ("v", v, 4), ("q_idx", q_idx, 4), ("k_idx", k_idx, 3)):
-        _need(t, name, nd, dev, q.dtype)
+    _need(q_idx, "q_idx", 4, dev, q.dtype)
+    for name, t, nd in (("k", k, 4), ("v", v, 4), ("k_idx", k_idx, 3)):
+        _need(t, name, nd, dev)
+    cf = _cache_format(q.dtype, [("k", k), ("v", v), ("k_idx", k_idx)])
     B, S_q, Hq, d = q.shape
     Hkv, S_k = k.shape[1], k.shape[2]
     D = q_idx.shape[3]
@@ -224,7 +251,8 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_idx: torch.Tensor, 
         raise ValueError("k and v must be [B, Hkv, S_k, d] matching q")
     if tuple(q_idx.shape) != (B, S_q, Hkv, D) or tuple(k_idx.shape) != (B, S_k, D):
         raise ValueError("q_idx must be [B, S_q, Hkv, D_idx] and k_idx [B, S_k, D_idx]")
-    shape = make_shape(B, S_q, S_k, q_offset, Hq, Hkv, d, D, topk, q.dtype, out_dtype, scale)
+    shape = make_shape(B, S_q, S_k, q_offset, Hq, Hkv, d, D, topk, q.dtype, out_dtype, scale,
+                       cache_format=cf, k_scale=k_scale, v_scale=v_scale)
     out = torch.empty((B, S_q, Hq, d), dtype=out_dtype or q.dtype, device=dev)
     sel = torch.empty((B, Hkv, S_q, topk), dtype=torch.int32, device=dev) if return_sel else None
     lse = torch.empty((B, Hq, S_q), dtype=torch.float32, device=dev) if return_lse else None

@@ -26,6 +26,12 @@
 //   3. combine: per (token, head) the partial states of its slots are merged
 //      (weights 2^(lse_s - max)) into the output and the log-sum-exp.
 // With S_q small (decode) the gather is skipped: one item per selection entry.
+//
+// K and V may be stored as OCP FP8 E4M3 (storage type S = e4m3, compute type
+// T = bf16): staging widens them exactly to bf16, the per-tensor key scale is
+// folded into the softmax scale and the value scale is applied by the combine.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -177,9 +183,10 @@ __device__ __forceinline__ void transpose_tile(const i32x4 (&in)[E], i32x4 (&out
   for (int c = 0; c < E; ++c) out[c] = __builtin_bit_cast(i32x4, o[c]);
 }
 
-template <typename T, int D, int R>
+template <typename T, typename S, int D, int R>
 __global__ __launch_bounds__(256, 2) void attn_kvouter_kernel(AttnParams p) {
   using M = Mma<T>;
+  using IO = ChunkIO<T, S>;
   using frag = typename M::frag;
   constexpr int KPL = M::KPL, KSTEP = M::KSTEP, NKS = D / KSTEP;
   constexpr int E = 16 / (int)sizeof(T);  // elements per 16-byte chunk
@@ -236,15 +243,15 @@ __global__ __launch_bounds__(256, 2) void attn_kvouter_kernel(AttnParams p) {
       constexpr int KU = KCH / 256;
       constexpr int VT = (D / E) * (kBlock / E);
       constexpr int VU = (VT + 255) / 256;
-      const T* ksrc = (const T*)p.k + kv0;
-      const T* vsrc = (const T*)p.v + kv0;
-      i32x4 kx[KU];
-      i32x4 vin[VU][E];
+      const S* ksrc = (const S*)p.k + kv0;
+      const S* vsrc = (const S*)p.v + kv0;
+      typename IO::raw kx[KU];
+      typename IO::raw vin[VU][E];
 #pragma unroll
       for (int u = 0; u < KU; ++u) {
         const int ch = threadIdx.x + u * 256;
         const int row = ch / (D / E), col = ch - row * (D / E);
-        kx[u] = *(const i32x4*)(ksrc + (int64_t)min(row, rows_ok - 1) * D + col * E);
+        kx[u] = IO::load(ksrc + (int64_t)min(row, rows_ok - 1) * D + col * E);
       }
 #pragma unroll
       for (int u = 0; u < VU; ++u) {
@@ -252,14 +259,14 @@ __global__ __launch_bounds__(256, 2) void attn_kvouter_kernel(AttnParams p) {
         const int dg = tl % (D / E), kg = tl / (D / E);
 #pragma unroll
         for (int r = 0; r < E; ++r)
-          vin[u][r] = *(const i32x4*)(vsrc + (int64_t)min(kg * E + r, rows_ok - 1) * D + dg * E);
+          vin[u][r] = IO::load(vsrc + (int64_t)min(kg * E + r, rows_ok - 1) * D + dg * E);
       }
       __builtin_amdgcn_sched_barrier(0);  // keep every staging load ahead of the first use
 #pragma unroll
       for (int u = 0; u < KU; ++u) {
         const int ch = threadIdx.x + u * 256;
         const int row = ch / (D / E), col = ch - row * (D / E);
-        i32x4 x = kx[u];
+        i32x4 x = IO::widen(kx[u]);
         if (row >= rows_ok) x = i32x4{};
         *(i32x4*)&Ks[row * LDK + col * E] = x;
       }
@@ -268,11 +275,11 @@ __global__ __launch_bounds__(256, 2) void attn_kvouter_kernel(AttnParams p) {
         const int tl = threadIdx.x + u * 256;
         if (VT % 256 != 0 && tl >= VT) break;
         const int dg = tl % (D / E), kg = tl / (D / E);
+        i32x4 vw[E];
 #pragma unroll
-        for (int r = 0; r < E; ++r)
-          if (kg * E + r >= rows_ok) vin[u][r] = i32x4{};
+        for (int r = 0; r < E; ++r) vw[r] = kg * E + r < rows_ok ? IO::widen(vin[u][r]) : i32x4{};
         i32x4 outc[E];
-        transpose_tile<T, E>(vin[u], outc);
+        transpose_tile<T, E>(vw, outc);
 #pragma unroll
         for (int r = 0; r < E; ++r) {  // rows are 8-byte aligned: two 8-byte stores
           uint2* dst = (uint2*)&Vt[(dg * E + r) * LDV + kg * E];
@@ -414,9 +421,13 @@ __global__ __launch_bounds__(256, 2) void attn_kvouter_kernel(AttnParams p) {
 // the d-slice [32w, 32w + 32) of O^T = V^T P^T from the LDS copies of V^T and
 // P^T.  The partial state is written in the same lane-native layout as the
 // KV-outer kernel, so the combine is shared.
-template <typename T, int D, int R>
+template <typename T, typename S, int D, int R>
 __global__ __launch_bounds__(256) void attn_decode_kernel(AttnParams p) {
   using M = Mma<T>;
+  using IO = ChunkIO<T, S>;
+  // K fragments come straight from global memory: KPL elements of S per lane
+  constexpr bool kNative = std::is_same<S, T>::value;
+  typedef typename std::conditional<kNative, typename Mma<T>::frag, uint2>::type kraw;
   using frag = typename M::frag;
   constexpr int KPL = M::KPL, KSTEP = M::KSTEP, NKS = D / KSTEP;
   constexpr int E = 16 / (int)sizeof(T);
@@ -453,26 +464,27 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnParams p) {
     // loads: this wave's 32 K rows (A operand), the token's Q rows (B operand), and
     // this thread's share of V; all issued before any is used
     const int krow = min(wave * 32 + l32, rows_ok - 1);
-    const T* kp = (const T*)p.k + kv0 + (int64_t)krow * D;
+    const S* kp = (const S*)p.k + kv0 + (int64_t)krow * D;
     const int qh = l32 < R ? l32 : 0;  // rows past r repeat head 0 and are never stored
     const T* qp = (const T*)p.q + (((int64_t)b * p.S_q + i) * p.Hq + g * R + qh) * D;
-    frag ka[NKS], qb[NKS];
+    kraw ka[NKS];
+    frag qb[NKS];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      ka[ks] = *(const frag*)(kp + ks * KSTEP + h * KPL);
+      ka[ks] = *(const kraw*)(kp + ks * KSTEP + h * KPL);
       qb[ks] = *(const frag*)(qp + ks * KSTEP + h * KPL);
     }
     constexpr int VT = (D / E) * (kBlock / E);
     constexpr int VU = (VT + 255) / 256;
-    i32x4 vin[VU][E];
-    const T* vsrc = (const T*)p.v + kv0;
+    typename IO::raw vin[VU][E];
+    const S* vsrc = (const S*)p.v + kv0;
 #pragma unroll
     for (int u = 0; u < VU; ++u) {
       const int tl = min((int)threadIdx.x + u * 256, VT - 1);
       const int dg = tl % (D / E), kg = tl / (D / E);
 #pragma unroll
       for (int r = 0; r < E; ++r)
-        vin[u][r] = *(const i32x4*)(vsrc + (int64_t)min(kg * E + r, rows_ok - 1) * D + dg * E);
+        vin[u][r] = IO::load(vsrc + (int64_t)min(kg * E + r, rows_ok - 1) * D + dg * E);
     }
     __builtin_amdgcn_sched_barrier(0);
 
@@ -482,11 +494,11 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnParams p) {
       const int tl = threadIdx.x + u * 256;
       if (VT % 256 != 0 && tl >= VT) break;
       const int dg = tl % (D / E), kg = tl / (D / E);
+      i32x4 vw[E];
 #pragma unroll
-      for (int r = 0; r < E; ++r)
-        if (kg * E + r >= rows_ok) vin[u][r] = i32x4{};
+      for (int r = 0; r < E; ++r) vw[r] = kg * E + r < rows_ok ? IO::widen(vin[u][r]) : i32x4{};
       i32x4 outc[E];
-      transpose_tile<T, E>(vin[u], outc);
+      transpose_tile<T, E>(vw, outc);
 #pragma unroll
       for (int r = 0; r < E; ++r) *(i32x4*)&Vt[(dg * E + r) * LDV + kg * E] = outc[r];
     }
@@ -494,7 +506,12 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnParams p) {
     // S^T for keys [32w, 32w + 32): lane (row l32, half h) holds keys 32w + c_row(j, h)
     f32x16 sacc = f32x16{};
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) sacc = M::mma(ka[ks], qb[ks], sacc);
+    for (int ks = 0; ks < NKS; ++ks) {
+      frag a;
+      if constexpr (kNative) a = ka[ks];
+      else a = __builtin_bit_cast(frag, IO::widen(ka[ks]));
+      sacc = M::mma(a, qb[ks], sacc);
+    }
     if (lim < kBlock - 1) {
 #pragma unroll
       for (int j = 0; j < 16; ++j)
@@ -657,7 +674,7 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnParams p) {
 #pragma unroll
     for (int e = 0; e < E; ++e) acc[e] += used ? w * to_f32(xv[e]) : 0.f;
   }
-  const float inv = 1.0f / W;
+  const float inv = p.v_scale / W;  // the value cache's dequantisation scale (1 if none)
   const int r0 = (q * E) % 16, dt = (q * E) / 16;
   if constexpr (STAGED) {
     TO* srow_o = ostage + (int)(threadIdx.x / NCHT) * (R * D) + hh * D;
@@ -693,7 +710,7 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnParams p) {
     p.lse[((int64_t)b * p.Hq + g * R + hh) * p.S_q + i] = (mx + log2f(W)) * 0.69314718055994531f;
 }
 
-template <typename T, int D, int R>
+template <typename T, typename S, int D, int R>
 static hipError_t launch_attn_t(const AttnParams& p, hipStream_t s, const KernelTimer* tm) {
   const int64_t entries = (int64_t)p.B * p.G * p.S_q * p.topk;
   if (!p.direct) {
@@ -716,9 +733,9 @@ static hipError_t launch_attn_t(const AttnParams& p, hipStream_t s, const Kernel
   }
   timer_start(tm, kKernAttention, s);
   if (p.direct)
-    hipLaunchKernelGGL((attn_decode_kernel<T, D, R>), dim3(p.grid_decode), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((attn_decode_kernel<T, S, D, R>), dim3(p.grid_decode), dim3(256), 0, s, p);
   else
-    hipLaunchKernelGGL((attn_kvouter_kernel<T, D, R>), dim3(p.grid), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((attn_kvouter_kernel<T, S, D, R>), dim3(p.grid), dim3(256), 0, s, p);
   timer_stop(tm, kKernAttention, s);
   timer_start(tm, kKernCombine, s);
   constexpr int E = 16 / (int)sizeof(T);
@@ -735,28 +752,31 @@ static hipError_t launch_attn_t(const AttnParams& p, hipStream_t s, const Kernel
   return hipGetLastError();
 }
 
-template <typename T, int D>
+template <typename T, typename S, int D>
 static hipError_t launch_attn_d(const AttnParams& p, hipStream_t s, const KernelTimer* tm) {
   switch (p.r) {
-    case 1: return launch_attn_t<T, D, 1>(p, s, tm);
-    case 2: return launch_attn_t<T, D, 2>(p, s, tm);
-    case 4: return launch_attn_t<T, D, 4>(p, s, tm);
-    case 8: return launch_attn_t<T, D, 8>(p, s, tm);
-    case 16: return launch_attn_t<T, D, 16>(p, s, tm);
-    case 32: return launch_attn_t<T, D, 32>(p, s, tm);
+    case 1: return launch_attn_t<T, S, D, 1>(p, s, tm);
+    case 2: return launch_attn_t<T, S, D, 2>(p, s, tm);
+    case 4: return launch_attn_t<T, S, D, 4>(p, s, tm);
+    case 8: return launch_attn_t<T, S, D, 8>(p, s, tm);
+    case 16: return launch_attn_t<T, S, D, 16>(p, s, tm);
+    case 32: return launch_attn_t<T, S, D, 32>(p, s, tm);
   }
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_sparse_attention(const AttnParams& p, bool bf16_inputs, hipStream_t s, const KernelTimer* tm) {
-  if (bf16_inputs) {
-    if (p.d == 64) return launch_attn_d<bf16, 64>(p, s, tm);
-    if (p.d == 128) return launch_attn_d<bf16, 128>(p, s, tm);
-  } else {
-    if (p.d == 64) return launch_attn_d<float, 64>(p, s, tm);
-    if (p.d == 128) return launch_attn_d<float, 128>(p, s, tm);
-  }
+template <typename T, typename S>
+static hipError_t launch_attn_s(const AttnParams& p, hipStream_t s, const KernelTimer* tm) {
+  if (p.d == 64) return launch_attn_d<T, S, 64>(p, s, tm);
+  if (p.d == 128) return launch_attn_d<T, S, 128>(p, s, tm);
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_sparse_attention(const AttnParams& p, bool bf16_inputs, bool fp8_cache, hipStream_t s,
+                                   const KernelTimer* tm) {
+  if (fp8_cache) return bf16_inputs ? launch_attn_s<bf16, e4m3>(p, s, tm) : hipErrorInvalidValue;
+  if (bf16_inputs) return launch_attn_s<bf16, bf16>(p, s, tm);
+  return launch_attn_s<float, float>(p, s, tm);
 }
 
 }  // namespace msa

@@ -64,4 +64,43 @@ struct alignas(16) Chunk16 {
   uint32_t w[4];
 };
 
+// One OCP FP8 E4M3 (e4m3fn) value as stored in a KV or index-key cache: sign,
+// 4 exponent bits (bias 7), 3 mantissa bits; no infinities, NaN = 0x7f / 0xff.
+struct e4m3 {
+  uint8_t bits;
+};
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Four e4m3 values (one 32-bit word, lowest byte first) as four bf16 values
+// (two 32-bit words).  Every e4m3 value, subnormals included, is a bf16 value,
+// so the conversion (v_cvt_scalef32_pk_bf16_fp8 with scale 1) is exact.
+__device__ __forceinline__ uint2 e4m3x4_to_bf16(uint32_t w) {
+  const bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+  const bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
+  return make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+}
+
+// A run of E = 16 / sizeof(T) consecutive cache elements of storage type S,
+// loaded raw and later widened to one 16-byte chunk of T.  For S == T that is a
+// plain 16-byte load; for e4m3 (T = bf16) an 8-byte load converted exactly.
+// Loads and conversions are separate steps so that a kernel can issue all its
+// loads before the first conversion waits on one.
+template <typename T, typename S>
+struct ChunkIO {
+  typedef i32x4 raw;
+  __device__ static __forceinline__ raw load(const S* p) { return *(const i32x4*)p; }
+  __device__ static __forceinline__ i32x4 widen(raw x) { return x; }
+};
+
+template <>
+struct ChunkIO<bf16, e4m3> {
+  typedef uint2 raw;
+  __device__ static __forceinline__ raw load(const e4m3* p) { return *(const uint2*)p; }
+  __device__ static __forceinline__ i32x4 widen(raw x) {
+    const uint2 a = e4m3x4_to_bf16(x.x), b = e4m3x4_to_bf16(x.y);
+    return i32x4{(int)a.x, (int)a.y, (int)b.x, (int)b.y};
+  }
+};
+
 }  // namespace msa

@@ -22,11 +22,16 @@
 // block, sorts ascending and pads with -1; with a single split the index kernel
 // does that itself.
 //
+// Index keys stored as OCP FP8 E4M3 (S = e4m3) are widened exactly to bf16 as
+// they are staged, so the scores are the same as for the bf16 values they hold.
+//
 // Exactness: with integer-valued inputs every score is an integer of
 // magnitude <= D * max|q| * max|k| < 2^24, so fp32 MFMA accumulation is exact in
 // any order, and ties are broken by block index exactly as the definition says.
 // Only full blocks before the local block are ranked (block c < L ends at or
 // before t), so no causal mask is needed inside the ranked blocks.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -52,7 +57,7 @@ __device__ __forceinline__ bool ranks_before(float s1, int i1, float s2, int i2)
   return s1 > s2 || (s1 == s2 && i1 < i2);
 }
 
-template <typename T, int DI, int CAP, int RT>
+template <typename T, typename S, int DI, int CAP, int RT>
 __global__ __launch_bounds__(256, 2) void index_topk_kernel(IndexParams p) {
   using M = Mma<T>;
   using frag = typename M::frag;
@@ -61,7 +66,10 @@ __global__ __launch_bounds__(256, 2) void index_topk_kernel(IndexParams p) {
   constexpr int LDW = DI + PAD;  // LDS pitch (elements): rows 16 B apart in bank space
   constexpr int ROWS_WAVE = 32 * RT;
   constexpr int ROWS_WG = 4 * ROWS_WAVE;
-  constexpr int CH_PER_ROW = DI * (int)sizeof(T) / 16;
+  // staging: 16-byte chunks of k_idx in its storage type S; a chunk holds SE
+  // keys' elements and widens to SE / (16 / sizeof(T)) chunks of T in LDS
+  constexpr int SE = 16 / (int)sizeof(S);
+  constexpr int CH_PER_ROW = DI / SE;
   constexpr int CH_PER_THREAD = kBlock * CH_PER_ROW / 256;
   static_assert(CH_PER_THREAD >= 1 && (kBlock * CH_PER_ROW) % 256 == 0, "staging split");
   constexpr int KS_BYTES = 2 * kBlock * LDW * (int)sizeof(T);
@@ -118,13 +126,26 @@ __global__ __launch_bounds__(256, 2) void index_topk_kernel(IndexParams p) {
       li[rt][j] = -1;
     }
 
-  const char* kbase = (const char*)p.k_idx + (int64_t)b * p.S_k * DI * (int64_t)sizeof(T);
+  const char* kbase = (const char*)p.k_idx + (int64_t)b * p.S_k * DI * (int64_t)sizeof(S);
   // K tiles are prefetched two blocks ahead: `pre` holds block c + 1 (stored to
   // LDS after block c is scored), `pre2` is in flight for block c + 2.  Native
   // vector types keep both in registers.
   i32x4 pre[CH_PER_THREAD], pre2[CH_PER_THREAD];
   auto kblock = [&](int c) {
-    return (const i32x4*)(kbase + (int64_t)c * kBlock * DI * (int64_t)sizeof(T));
+    return (const i32x4*)(kbase + (int64_t)c * kBlock * DI * (int64_t)sizeof(S));
+  };
+  // one staged chunk into the LDS tile: row-major, SE elements from column col
+  auto stage = [&](T* tile, int ch, i32x4 x) {
+    const int row = ch / CH_PER_ROW, col = ch - row * CH_PER_ROW;
+    T* dst = &tile[row * LDW + col * SE];
+    if constexpr (std::is_same<S, T>::value) {
+      *(i32x4*)dst = x;
+    } else {
+      const uint2 a = e4m3x4_to_bf16((uint32_t)x[0]), b2 = e4m3x4_to_bf16((uint32_t)x[1]);
+      const uint2 c2 = e4m3x4_to_bf16((uint32_t)x[2]), d2 = e4m3x4_to_bf16((uint32_t)x[3]);
+      *(i32x4*)dst = i32x4{(int)a.x, (int)a.y, (int)b2.x, (int)b2.y};
+      *(i32x4*)(dst + 8) = i32x4{(int)c2.x, (int)c2.y, (int)d2.x, (int)d2.y};
+    }
   };
   if (has_blocks) {
     const i32x4* src = kblock(c_begin);
@@ -136,11 +157,7 @@ __global__ __launch_bounds__(256, 2) void index_topk_kernel(IndexParams p) {
       for (int u = 0; u < CH_PER_THREAD; ++u) pre2[u] = src1[threadIdx.x + u * 256];
     }
 #pragma unroll
-    for (int u = 0; u < CH_PER_THREAD; ++u) {
-      const int ch = threadIdx.x + u * 256;
-      const int row = ch / CH_PER_ROW, col = ch - row * CH_PER_ROW;
-      *(i32x4*)((char*)&Ks[row * LDW] + col * 16) = pre[u];
-    }
+    for (int u = 0; u < CH_PER_THREAD; ++u) stage(Ks, threadIdx.x + u * 256, pre[u]);
 #pragma unroll
     for (int u = 0; u < CH_PER_THREAD; ++u) pre[u] = pre2[u];
   }
@@ -181,11 +198,7 @@ __global__ __launch_bounds__(256, 2) void index_topk_kernel(IndexParams p) {
     }
     if (has_next) {
 #pragma unroll
-      for (int u = 0; u < CH_PER_THREAD; ++u) {
-        const int ch = threadIdx.x + u * 256;
-        const int row = ch / CH_PER_ROW, col = ch - row * CH_PER_ROW;
-        *(i32x4*)((char*)&Ks[(buf ^ 1) * (kBlock * LDW) + row * LDW] + col * 16) = pre[u];
-      }
+      for (int u = 0; u < CH_PER_THREAD; ++u) stage(Ks + (buf ^ 1) * (kBlock * LDW), threadIdx.x + u * 256, pre[u]);
 #pragma unroll
       for (int u = 0; u < CH_PER_THREAD; ++u) pre[u] = pre2[u];
     }
@@ -354,12 +367,12 @@ __global__ __launch_bounds__(256) void topk_merge_kernel(IndexParams p) {
   else if (lane < p.topk) out[lane] = -1;
 }
 
-template <typename T, int DI, int CAP>
+template <typename T, typename S, int DI, int CAP>
 static hipError_t launch_index_t(const IndexParams& p, hipStream_t s, const KernelTimer* tm) {
   timer_start(tm, kKernIndexScore, s);
   constexpr int RT = CAP <= 15 ? 2 : 1;
   static_assert(4 * 32 * RT == index_rows_per_wg(CAP + 1), "host and kernel agree on the row tile");
-  hipLaunchKernelGGL((index_topk_kernel<T, DI, CAP, RT>), dim3(p.grid_per_xcd * 8), dim3(256), 0, s, p);
+  hipLaunchKernelGGL((index_topk_kernel<T, S, DI, CAP, RT>), dim3(p.grid_per_xcd * 8), dim3(256), 0, s, p);
   timer_stop(tm, kKernIndexScore, s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -372,28 +385,27 @@ static hipError_t launch_index_t(const IndexParams& p, hipStream_t s, const Kern
   return hipGetLastError();
 }
 
-template <typename T, int DI>
+template <typename T, typename S, int DI>
 static hipError_t launch_index_d(const IndexParams& p, hipStream_t s, const KernelTimer* tm) {
-  if (p.topk <= 16) return launch_index_t<T, DI, 15>(p, s, tm);
-  return launch_index_t<T, DI, 31>(p, s, tm);
+  if (p.topk <= 16) return launch_index_t<T, S, DI, 15>(p, s, tm);
+  return launch_index_t<T, S, DI, 31>(p, s, tm);
 }
 
-hipError_t launch_index_select(const IndexParams& p, bool bf16_inputs, int index_dim, hipStream_t s,
-                               const KernelTimer* tm) {
-  if (bf16_inputs) {
-    switch (index_dim) {
-      case 32: return launch_index_d<bf16, 32>(p, s, tm);
-      case 64: return launch_index_d<bf16, 64>(p, s, tm);
-      case 128: return launch_index_d<bf16, 128>(p, s, tm);
-    }
-  } else {
-    switch (index_dim) {
-      case 32: return launch_index_d<float, 32>(p, s, tm);
-      case 64: return launch_index_d<float, 64>(p, s, tm);
-      case 128: return launch_index_d<float, 128>(p, s, tm);
-    }
+template <typename T, typename S>
+static hipError_t launch_index_s(const IndexParams& p, int index_dim, hipStream_t s, const KernelTimer* tm) {
+  switch (index_dim) {
+    case 32: return launch_index_d<T, S, 32>(p, s, tm);
+    case 64: return launch_index_d<T, S, 64>(p, s, tm);
+    case 128: return launch_index_d<T, S, 128>(p, s, tm);
   }
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_index_select(const IndexParams& p, bool bf16_inputs, bool fp8_keys, int index_dim, hipStream_t s,
+                               const KernelTimer* tm) {
+  if (fp8_keys) return bf16_inputs ? launch_index_s<bf16, e4m3>(p, index_dim, s, tm) : hipErrorInvalidValue;
+  if (bf16_inputs) return launch_index_s<bf16, bf16>(p, index_dim, s, tm);
+  return launch_index_s<float, float>(p, index_dim, s, tm);
 }
 
 }  // namespace msa

@@ -47,7 +47,8 @@ struct IndexParams {
 constexpr int index_row_tiles(int topk) { return topk <= 16 ? 2 : 1; }
 constexpr int index_rows_per_wg(int topk) { return 4 * 32 * index_row_tiles(topk); }
 
-hipError_t launch_index_select(const IndexParams& p, bool bf16_inputs, int index_dim, hipStream_t s,
+// fp8_keys: k_idx holds OCP FP8 E4M3 values (q_idx bf16).
+hipError_t launch_index_select(const IndexParams& p, bool bf16_inputs, bool fp8_keys, int index_dim, hipStream_t s,
                                const KernelTimer* timer);
 
 // Main branch (attn.hip).
@@ -78,10 +79,13 @@ struct AttnParams {
   int64_t n_direct;    // B * G * S_q * topk when direct
   int grid;            // persistent grid size of the attention kernel
   int grid_decode;     // persistent grid size of the decode-form attention kernel
-  float scale_log2;    // softmax scale * log2(e)
+  float scale_log2;    // softmax scale * key scale * log2(e)
+  float v_scale;       // dequantisation scale of the value cache (1 if none)
   int out_f32;         // output dtype: 1 fp32, 0 input dtype
 };
 
-hipError_t launch_sparse_attention(const AttnParams& p, bool bf16_inputs, hipStream_t s, const KernelTimer* timer);
+// fp8_cache: k and v hold OCP FP8 E4M3 values (q and the partial states bf16).
+hipError_t launch_sparse_attention(const AttnParams& p, bool bf16_inputs, bool fp8_cache, hipStream_t s,
+                                   const KernelTimer* timer);
 
 }  // namespace msa

@@ -43,10 +43,17 @@ bool is_pow2_upto32(int r) { return r == 1 || r == 2 || r == 4 || r == 8 || r ==
 
 int elem_bytes(int dtype) { return dtype == MSA_F32 ? 4 : 2; }
 
+bool fp8_cache(const msa_shape* s) { return s->cache_format == MSA_CACHE_FP8_E4M3; }
+
+bool scale_ok(float x) { return std::isfinite(x) && x >= 0.0f; }
+
 // Shape checks shared by every op.  'op' selects the op-specific ones.
 msa_status check_shape(const msa_shape* s, int op) {
   if (!s) return fail(MSA_ERR_INVALID, "shape is NULL");
-  if (s->pad0 != 0 || s->pad1 != 0) return fail(MSA_ERR_INVALID, "msa_shape padding fields must be 0");
+  static_assert(sizeof(msa_shape) == 72, "msa_shape layout");
+  if (s->pad != 0) return fail(MSA_ERR_INVALID, "msa_shape padding field must be 0");
+  if (s->cache_format != MSA_CACHE_NATIVE && s->cache_format != MSA_CACHE_FP8_E4M3)
+    return fail(MSA_ERR_INVALID, "unknown cache_format %d", s->cache_format);
   if (s->batch < 1) return fail(MSA_ERR_INVALID, "batch must be >= 1 (got %d)", s->batch);
   if (s->q_len < 0) return fail(MSA_ERR_INVALID, "q_len must be >= 0 (got %d)", s->q_len);
   if (s->kv_len < 1) return fail(MSA_ERR_INVALID, "kv_len must be >= 1 (got %d)", s->kv_len);
@@ -65,11 +72,15 @@ msa_status check_shape(const msa_shape* s, int op) {
   if (s->dtype != MSA_F32 && s->dtype != MSA_BF16) return fail(MSA_ERR_INVALID, "unknown dtype %d", s->dtype);
   if (s->out_dtype != MSA_F32 && s->out_dtype != MSA_BF16)
     return fail(MSA_ERR_INVALID, "unknown out_dtype %d", s->out_dtype);
-  if (!std::isfinite(s->softmax_scale) || s->softmax_scale < 0.0f)
+  if (!scale_ok(s->softmax_scale))
     return fail(MSA_ERR_INVALID, "softmax_scale must be finite and >= 0 (0 selects 1/sqrt(head_dim))");
+  if (!scale_ok(s->k_scale) || !scale_ok(s->v_scale))
+    return fail(MSA_ERR_INVALID, "k_scale and v_scale must be finite and >= 0 (0 means 1)");
 
   if (s->block_size != msa::kBlock)
     return fail(MSA_ERR_UNSUPPORTED, "block_size %d: only 128 is built", s->block_size);
+  if (fp8_cache(s) && s->dtype != MSA_BF16)
+    return fail(MSA_ERR_UNSUPPORTED, "FP8 caches are built for bf16 queries only");
   if (s->topk > 32) return fail(MSA_ERR_UNSUPPORTED, "topk %d: at most 32 is built", s->topk);
   if (s->q_len >= (1 << 25)) return fail(MSA_ERR_UNSUPPORTED, "q_len must be < 2^25");
   if ((int64_t)s->batch * s->num_kv_heads * ceil_div(s->kv_len, msa::kBlock) >= (1LL << 31))
@@ -173,7 +184,9 @@ AttnPlan plan_attn(const msa_shape* s) {
   p.grid = kAttnGrid;
   p.grid_decode = 768;  // 3 workgroups per CU (44 KiB of LDS each)
   const float scale = s->softmax_scale != 0.0f ? s->softmax_scale : 1.0f / std::sqrt((float)s->head_dim);
-  p.scale_log2 = scale * 1.4426950408889634f;
+  const float kscale = s->k_scale != 0.0f ? s->k_scale : 1.0f;
+  p.scale_log2 = scale * kscale * 1.4426950408889634f;
+  p.v_scale = s->v_scale != 0.0f ? s->v_scale : 1.0f;
   p.out_f32 = s->out_dtype == MSA_F32 ? 1 : 0;
 
   const size_t nbk = (size_t)p.nbuckets + 1;
@@ -242,7 +255,7 @@ msa_status hip_status(hipError_t e, const char* what) {
 
 extern "C" {
 
-const char* msa_version(void) { return "0.1.0"; }
+const char* msa_version(void) { return "0.2.0"; }
 
 msa_status msa_set_kernel_timer(int kernel, void* start_event, void* stop_event) {
   if (kernel < MSA_KERNEL_NONE || kernel > MSA_KERNEL_COMBINE)
@@ -290,7 +303,8 @@ msa_status msa_index_select(const msa_shape* s, const void* q_idx, const void* k
   if ((st = check_ws(ws, ws_bytes, ip.bytes)) != MSA_OK) return st;
   bind_index(ip, (char*)ws, q_idx, k_idx, sel);
   clear_stale_hip_error();
-  return hip_status(msa::launch_index_select(ip.p, s->dtype == MSA_BF16, s->index_dim, (hipStream_t)stream, timer()),
+  return hip_status(msa::launch_index_select(ip.p, s->dtype == MSA_BF16, fp8_cache(s), s->index_dim,
+                                             (hipStream_t)stream, timer()),
                     "index select launch");
 }
 
@@ -311,7 +325,8 @@ msa_status msa_sparse_attn_fwd(const msa_shape* s, const void* q, const void* k,
   ap.p.out = out;
   ap.p.lse = lse;
   clear_stale_hip_error();
-  return hip_status(msa::launch_sparse_attention(ap.p, s->dtype == MSA_BF16, (hipStream_t)stream, timer()),
+  return hip_status(msa::launch_sparse_attention(ap.p, s->dtype == MSA_BF16, fp8_cache(s), (hipStream_t)stream,
+                                                 timer()),
                     "sparse attention launch");
 }
 
@@ -333,7 +348,8 @@ msa_status msa_fwd(const msa_shape* s, const void* q, const void* k, const void*
   bind_index(ip, scratch, q_idx, k_idx, sel);
   hipStream_t hs = (hipStream_t)stream;
   clear_stale_hip_error();
-  st = hip_status(msa::launch_index_select(ip.p, s->dtype == MSA_BF16, s->index_dim, hs, timer()), "index select launch");
+  st = hip_status(msa::launch_index_select(ip.p, s->dtype == MSA_BF16, fp8_cache(s), s->index_dim, hs, timer()),
+                  "index select launch");
   if (st != MSA_OK) return st;
   bind_attn(ap, scratch);
   ap.p.q = q;
@@ -342,7 +358,8 @@ msa_status msa_fwd(const msa_shape* s, const void* q, const void* k, const void*
   ap.p.sel = sel;
   ap.p.out = out;
   ap.p.lse = lse;
-  return hip_status(msa::launch_sparse_attention(ap.p, s->dtype == MSA_BF16, hs, timer()), "sparse attention launch");
+  return hip_status(msa::launch_sparse_attention(ap.p, s->dtype == MSA_BF16, fp8_cache(s), hs, timer()),
+                    "sparse attention launch");
 }
 
 }  // extern "C"

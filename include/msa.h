@@ -24,7 +24,7 @@
  *    union, keys and values of KV head g.
  *
  * Layouts (all dense, contiguous, row-major; e = 4 bytes for MSA_F32, 2 for
- * MSA_BF16):
+ * MSA_BF16, 1 for FP8 caches):
  *    q, out   [B, S_q, Hq, d]
  *    k, v     [B, Hkv, S_k, d]       one (head, block) is a contiguous span
  *    q_idx    [B, S_q, G, D_idx]     G = Hkv index-query heads
@@ -47,12 +47,23 @@
  * last failing call of the calling thread.  Device faults surface at the
  * caller's synchronisation.
  *
+ * Caches in FP8.  The pages list FP8 among the precisions of the MSA
+ * inference kernel (aiforradalom.online page "MiniMax új eljárása
+ * 28-szorosára csökkenti az AI-figyelem számítási igényét", section
+ * "Elérhetőség"), without fixing a format.  Here, with cache_format =
+ * MSA_CACHE_FP8_E4M3, k, v and k_idx hold OCP FP8 E4M3 (e4m3fn) bytes while
+ * q, q_idx and the output stay in dtype (which must be MSA_BF16).  The keys
+ * and values attended to are k_scale * k and v_scale * v (per-tensor
+ * dequantisation scales).  Index keys are used as stored: a positive common
+ * scale would not change any ranking, so none is taken.
+ *
  * Supported on the GPU: block_size == 128; 1 <= topk <= 32; head_dim in
  * {64, 128}; index_dim in {32, 64, 128}; r = Hq / Hkv in {1, 2, 4, 8, 16,
- * 32}; dtype MSA_F32 or MSA_BF16 (the same for q, k, v, q_idx, k_idx);
- * out_dtype MSA_F32 or the input dtype.  Other values give
- * MSA_ERR_UNSUPPORTED.  Selections are exact when the index inputs make every
- * index score exactly representable in fp32 (for example small integers).
+ * 32}; dtype MSA_F32 or MSA_BF16 (the same for q, k, v, q_idx, k_idx unless
+ * the caches are FP8); out_dtype MSA_F32 or the input dtype.  Other values
+ * give MSA_ERR_UNSUPPORTED.  Selections are exact when the index inputs make
+ * every index score exactly representable in fp32 (for example small
+ * integers).
  */
 #ifndef MSA_H_
 #define MSA_H_
@@ -74,11 +85,17 @@ typedef enum {
 
 typedef enum { MSA_F32 = 0, MSA_BF16 = 1 } msa_dtype;
 
+/* Element format of the caches k, v and k_idx. */
+typedef enum {
+  MSA_CACHE_NATIVE = 0,   /* the same dtype as q                                */
+  MSA_CACHE_FP8_E4M3 = 1  /* OCP FP8 E4M3 bytes; requires dtype == MSA_BF16      */
+} msa_cache_format;
+
 typedef struct {
   int32_t batch;        /* B: sequences                                         */
   int32_t q_len;        /* S_q: query rows per sequence (0 = nothing to do)     */
   int32_t kv_len;       /* S_k: cached tokens per sequence, >= q_offset + S_q   */
-  int32_t pad0;         /* must be 0                                            */
+  int32_t cache_format; /* msa_cache_format of k, v and k_idx                   */
   int64_t q_offset;     /* absolute position of query row 0 (every sequence)    */
   int32_t num_q_heads;  /* Hq                                                   */
   int32_t num_kv_heads; /* Hkv = G, also the number of index-query heads        */
@@ -87,10 +104,12 @@ typedef struct {
   int32_t block_size;   /* Bk                                                   */
   int32_t topk;         /* k: blocks per (query, group), local block included   */
   float softmax_scale;  /* main-branch scale; 0 means 1/sqrt(d)                 */
-  int32_t dtype;        /* msa_dtype of q, k, v, q_idx, k_idx                   */
+  int32_t dtype;        /* msa_dtype of q and q_idx (and of the native caches)  */
   int32_t out_dtype;    /* msa_dtype of out                                     */
-  int32_t pad1;         /* must be 0                                            */
-} msa_shape;
+  float k_scale;        /* keys attended to are k_scale * k; 0 means 1          */
+  float v_scale;        /* values attended to are v_scale * v; 0 means 1        */
+  int32_t pad;          /* must be 0                                            */
+} msa_shape;            /* 72 bytes                                             */
 
 enum { MSA_OP_INDEX_SELECT = 0, MSA_OP_SPARSE_ATTN = 1, MSA_OP_FWD = 2 };
 
@@ -147,7 +166,7 @@ const char* msa_status_string(msa_status status);
 /* Thread-local description of the last failing call on this thread ("" if none). */
 const char* msa_last_error(void);
 
-/* Library version, e.g. "0.1.0". */
+/* Library version, e.g. "0.2.0". */
 const char* msa_version(void);
 
 #ifdef __cplusplus

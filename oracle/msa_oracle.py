@@ -41,6 +41,14 @@ the design notes of the repository):
 
 Index scores are computed in float64; with integer-valued index inputs every
 partial sum is an integer far below 2**53, so they are exact.
+
+FP8 caches.  The pages list FP8 among the MSA inference kernel's precisions
+(the Hungarian page, section "Elérhetőség") without naming a format; the
+reading taken is OCP FP8 E4M3 (e4m3fn) storage for k, v and k_idx with
+per-tensor dequantisation scales for k and v.  ``e4m3_to_f64`` decodes such
+bytes exactly from the OCP 8-bit floating point specification (OFP8, E4M3
+encoding) and ``dequantize_e4m3`` applies a scale; the attention itself is the
+same definition applied to the decoded values.
 """
 from __future__ import annotations
 
@@ -50,6 +58,8 @@ from typing import Iterable, Optional, Sequence, Tuple
 import numpy as np
 
 __all__ = [
+    "e4m3_to_f64",
+    "dequantize_e4m3",
     "block_maxima",
     "select_from_maxima",
     "index_select",
@@ -62,6 +72,33 @@ __all__ = [
 
 def _f64(x) -> np.ndarray:
     return np.asarray(x, dtype=np.float64)
+
+
+# ---------------------------------------------------------------------------
+# FP8 cache values
+# ---------------------------------------------------------------------------
+
+def e4m3_to_f64(codes) -> np.ndarray:
+    """Exact value of each OCP FP8 E4M3 code (uint8).
+
+    Bit layout s eeee mmm, exponent bias 7.  e = 0 encodes the subnormals
+    (-1)^s * m * 2^-9; otherwise the value is (-1)^s * (1 + m/8) * 2^(e-7).
+    The format has no infinities; the two codes with e = 15 and m = 7 are NaN,
+    so the largest finite magnitude is 1.75 * 2^8 = 448.
+    """
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    negative = (c >> 7) == 1
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0))
+    mag = np.where((e == 15) & ((c & 0x7) == 7), np.nan, mag)
+    return np.where(negative, -mag, mag)
+
+
+def dequantize_e4m3(codes, scale: float = 1.0) -> np.ndarray:
+    """scale * value of each E4M3 code, in float64.  The product of a 4-bit
+    significand and a float32 scale fits in 53 bits, so it is exact."""
+    return e4m3_to_f64(codes) * np.float64(np.float32(scale))
 
 
 # ---------------------------------------------------------------------------

@@ -15,6 +15,11 @@ MSA attention vs Minimax's Reference"):
 * The index query/key tensors hold small integers drawn uniformly from an
   inclusive range (-8..8 for the fp32 workload, -4..4 otherwise), stored exactly
   in the workload dtype, so every index score is an exact integer in fp32.
+* FP8 caches (``cache="fp8"``): K and V are the same standard-normal fp32 draws
+  divided by the per-tensor dequantisation scale (``k_scale``, ``v_scale``),
+  clamped to the E4M3 range +-448 and rounded to OCP FP8 E4M3 by torch's cast;
+  the integer index keys are stored exactly in E4M3.  Q and the index queries
+  stay bf16.
 
 Two generators exist:
 
@@ -40,6 +45,8 @@ import torch
 SEED_ROOT = 0x4D5341  # "MSA"
 
 TENSOR_IDS = {"q": 0, "k": 1, "v": 2, "q_idx": 3, "k_idx": 4}
+CACHE_TENSORS = ("k", "v", "k_idx")
+E4M3_MAX = 448.0
 
 
 @dataclasses.dataclass(frozen=True)
@@ -60,6 +67,9 @@ class Shape:
     dtype: str = "bf16"  # "f32" or "bf16"
     idx_lo: int = -4
     idx_hi: int = 4
+    cache: str = "native"  # "native" (k, v, k_idx in dtype) or "fp8" (OCP E4M3)
+    k_scale: float = 1.0   # dequantisation scales of an fp8 k / v cache
+    v_scale: float = 1.0
 
     @property
     def groups(self) -> int:
@@ -68,6 +78,15 @@ class Shape:
     @property
     def torch_dtype(self) -> torch.dtype:
         return torch.float32 if self.dtype == "f32" else torch.bfloat16
+
+    @property
+    def fp8(self) -> bool:
+        return self.cache == "fp8"
+
+    def tensor_dtype(self, name: str) -> torch.dtype:
+        if self.fp8 and name in CACHE_TENSORS:
+            return torch.float8_e4m3fn
+        return self.torch_dtype
 
     def replace(self, **kw) -> "Shape":
         return dataclasses.replace(self, **kw)
@@ -80,6 +99,8 @@ WORKLOADS: Dict[int, Shape] = {
     3: Shape(2, 32768, 32768, 0, 64, 4, 128, 128, 16),
     4: Shape(64, 1, 131072, 131071, 64, 4, 128, 128, 16),
     5: Shape(1, 4096, 1048576, 1044480, 64, 4, 128, 128, 16),
+    # the decode workload with its caches in FP8 (scales ~ 6 sigma / 448)
+    6: Shape(64, 1, 131072, 131071, 64, 4, 128, 128, 16, cache="fp8", k_scale=6.0 / 448, v_scale=5.5 / 448),
 }
 
 WORKLOAD_NAMES = {
@@ -88,6 +109,7 @@ WORKLOAD_NAMES = {
     3: "prefill_32k_b2_bf16",
     4: "decode_128k_b64_bf16",
     5: "chunked_prefill_1m_q4096_bf16",
+    6: "decode_128k_b64_fp8",
 }
 
 
@@ -107,6 +129,14 @@ def _per_seq_shape(s: Shape, tensor: str):
     raise KeyError(tensor)
 
 
+def _to_storage(s: Shape, tensor: str, x: torch.Tensor) -> torch.Tensor:
+    """fp32 draws to the tensor's storage dtype (fp8 caches: scaled, clamped)."""
+    if s.fp8 and tensor in ("k", "v"):
+        scale = s.k_scale if tensor == "k" else s.v_scale
+        x = (x / scale).clamp_(-E4M3_MAX, E4M3_MAX)
+    return x.to(s.tensor_dtype(tensor))
+
+
 def _host_draw(s: Shape, workload: int, tensor: str, b: int) -> torch.Tensor:
     rng = np.random.Generator(np.random.PCG64(_seed(workload, tensor, b)))
     shp = _per_seq_shape(s, tensor)
@@ -114,7 +144,7 @@ def _host_draw(s: Shape, workload: int, tensor: str, b: int) -> torch.Tensor:
         x = rng.standard_normal(size=shp, dtype=np.float32)
     else:
         x = rng.integers(s.idx_lo, s.idx_hi + 1, size=shp, dtype=np.int32).astype(np.float32)
-    return torch.from_numpy(x).to(s.torch_dtype)
+    return _to_storage(s, tensor, torch.from_numpy(x))
 
 
 def host_inputs(s: Shape, workload: int = 0) -> Dict[str, torch.Tensor]:
@@ -132,11 +162,10 @@ def _device_seed(workload: int, tensor: str, b: int) -> int:
 
 def device_inputs(s: Shape, workload: int, device="cuda") -> Dict[str, torch.Tensor]:
     """All five inputs generated on the device (Philox), per sequence."""
-    dt = s.torch_dtype
     out = {}
     for name in ("q", "k", "v", "q_idx", "k_idx"):
         shp = _per_seq_shape(s, name)
-        t = torch.empty((s.batch,) + shp, dtype=dt, device=device)
+        t = torch.empty((s.batch,) + shp, dtype=s.tensor_dtype(name), device=device)
         for b in range(s.batch):
             g = torch.Generator(device=device)
             g.manual_seed(_device_seed(workload, name, b))
@@ -147,21 +176,20 @@ def device_inputs(s: Shape, workload: int, device="cuda") -> Dict[str, torch.Ten
                 step = 1 << 28
                 for o in range(0, n, step):
                     m = min(step, n - o)
-                    flat[o:o + m].copy_(torch.randn(m, generator=g, device=device,
-                                                    dtype=torch.float32).to(dt))
+                    flat[o:o + m].copy_(_to_storage(s, name, torch.randn(m, generator=g, device=device,
+                                                                         dtype=torch.float32)))
             else:
-                t[b].copy_(torch.randint(s.idx_lo, s.idx_hi + 1, shp, generator=g,
-                                         device=device, dtype=torch.int32).to(dt))
+                t[b].copy_(_to_storage(s, name, torch.randint(s.idx_lo, s.idx_hi + 1, shp, generator=g,
+                                                              device=device, dtype=torch.int32).float()))
         out[name] = t
     return out
 
 
 def host_bytes(s: Shape) -> int:
     e = 4 if s.dtype == "f32" else 2
-    n = (2 * s.batch * s.q_len * s.num_q_heads * s.head_dim
-         + 2 * s.batch * s.num_kv_heads * s.kv_len * s.head_dim
-         + s.batch * s.q_len * s.groups * s.index_dim + s.batch * s.kv_len * s.index_dim)
-    return n * e
+    ec = 1 if s.fp8 else e
+    return (e * (2 * s.batch * s.q_len * s.num_q_heads * s.head_dim + s.batch * s.q_len * s.groups * s.index_dim)
+            + ec * (2 * s.batch * s.num_kv_heads * s.kv_len * s.head_dim + s.batch * s.kv_len * s.index_dim))
 
 
 def inputs_for(s: Shape, workload: int = 0, device: Optional[str] = None,
@@ -177,13 +205,21 @@ def inputs_for(s: Shape, workload: int = 0, device: Optional[str] = None,
 
 
 def as_f64(t) -> np.ndarray:
-    """Exact upcast of a stored fp32/bf16 tensor (or array) to a float64 array."""
+    """Exact upcast of a stored fp32/bf16 tensor (or array) to a float64 array.
+    FP8 tensors are refused: their bytes go to the oracle's decoder (codes())."""
     if isinstance(t, torch.Tensor):
         t = t.detach().to("cpu")
+        if t.dtype == torch.float8_e4m3fn:
+            raise TypeError("fp8 tensor: pass codes(t) to the oracle's e4m3 decoder")
         if t.dtype == torch.bfloat16:
             t = t.float()
         return t.numpy().astype(np.float64)
     return np.asarray(t, dtype=np.float64)
+
+
+def codes(t: torch.Tensor) -> np.ndarray:
+    """The raw bytes of an fp8 tensor as a uint8 array of the same shape."""
+    return t.detach().to("cpu").view(torch.uint8).numpy()
 
 
 def n_blocks(kv_len: int, block_size: int = 128) -> int:

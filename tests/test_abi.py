@@ -34,9 +34,15 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_struct_layout_matches_header():
-    assert ctypes.sizeof(msa.MsaShape) == 64
+    assert ctypes.sizeof(msa.MsaShape) == 72
+    assert msa.MsaShape.cache_format.offset == 12
     assert msa.MsaShape.q_offset.offset == 16
     assert msa.MsaShape.softmax_scale.offset == 48
+    assert msa.MsaShape.k_scale.offset == 60
+    assert msa.MsaShape.v_scale.offset == 64
+    assert msa.MsaShape.pad.offset == 68
+    text = open(HEADER).read()
+    assert "MSA_CACHE_NATIVE = 0" in text and "MSA_CACHE_FP8_E4M3 = 1" in text
 
 
 def _shape(wid=2, **kw):
@@ -60,7 +66,8 @@ def _fwd(sh, ws=None, ws_bytes=0, **ptrs):
 @pytest.mark.parametrize("field,value,status", [
     ("batch", 0, -1), ("q_len", -1, -1), ("kv_len", 0, -1), ("q_offset", -5, -1), ("kv_len", 100, -1),
     ("num_q_heads", 62, -1), ("num_kv_heads", 0, -1), ("topk", 0, -1), ("block_size", 0, -1),
-    ("dtype", 7, -1), ("out_dtype", 9, -1), ("pad0", 1, -1), ("pad1", 3, -1), ("head_dim", 0, -1),
+    ("dtype", 7, -1), ("out_dtype", 9, -1), ("cache_format", 2, -1), ("cache_format", -1, -1), ("pad", 3, -1),
+    ("head_dim", 0, -1),
     ("block_size", 64, -2), ("topk", 33, -2), ("head_dim", 96, -2), ("index_dim", 48, -2),
     ("num_q_heads", 12, -2),
 ])
@@ -81,11 +88,20 @@ def test_null_pointers_rejected():
     assert L.msa_sparse_attn_fwd(ctypes.byref(sh), FAKE, FAKE, FAKE, None, FAKE, None, None, 0, None) == -1
 
 
+@pytest.mark.parametrize("field", ["softmax_scale", "k_scale", "v_scale"])
 @pytest.mark.parametrize("scale", [float("nan"), float("inf"), -0.5])
-def test_bad_scale_rejected(scale):
+def test_bad_scale_rejected(field, scale):
     sh = _shape()
-    sh.softmax_scale = scale
+    setattr(sh, field, scale)
     assert _fwd(sh) == -1
+
+
+def test_fp8_caches_need_bf16_queries():
+    sh = _shape(1, cache_format=1)  # the fp32 workload
+    assert _fwd(sh) == -2
+    assert "FP8" in msa.lib().msa_last_error().decode()
+    sh = _shape(2, cache_format=1)
+    assert msa.workspace_size(sh, msa.OP_FWD) == msa.workspace_size(_shape(2), msa.OP_FWD)
 
 
 def test_workspace_checks():
@@ -132,3 +148,15 @@ def test_python_layer_rejects_cpu_tensors():
     q = torch.zeros(1, 4, 2, 64)
     with pytest.raises(ValueError):
         msa.sparse_attn_fwd(q, q, q, torch.zeros(1, 2, 4, 1, dtype=torch.int32))
+
+
+def test_python_cache_format_rules():
+    import torch
+    bf, f8 = torch.bfloat16, torch.float8_e4m3fn
+    t = lambda dt: torch.zeros(1, dtype=dt)
+    assert msa._cache_format(bf, [("k", t(bf)), ("v", t(bf))]) == msa.CACHE_NATIVE
+    assert msa._cache_format(bf, [("k", t(f8)), ("v", t(f8)), ("k_idx", t(f8))]) == msa.CACHE_FP8_E4M3
+    with pytest.raises(ValueError):  # mixed caches
+        msa._cache_format(bf, [("k", t(f8)), ("v", t(bf))])
+    with pytest.raises(ValueError):  # fp8 next to fp32 queries
+        msa._cache_format(torch.float32, [("k", t(f8)), ("v", t(f8))])

@@ -470,3 +470,62 @@ def test_synth_inputs_are_exact_and_seeded():
     assert c["q"].dtype == torch.bfloat16
     ki = synth.as_f64(c["k_idx"])
     assert (ki == np.round(ki)).all() and ki.min() >= -4 and ki.max() <= 4
+
+
+# --- FP8 (OCP E4M3) cache values -------------------------------------------
+# The pages list FP8 among the inference kernel's precisions (Hungarian page,
+# "Elérhetőség"); the format read into that is OCP FP8 E4M3 (e4m3fn).  The
+# decoder is pinned to torch's own float8_e4m3fn conversion and to the special
+# values the OCP OFP8 specification fixes for E4M3.
+
+def test_e4m3_decoder_matches_torch_on_every_code():
+    codes = np.arange(256, dtype=np.uint8)
+    mine = orc.e4m3_to_f64(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(mine, ref, equal_nan=True)
+    assert np.array_equal(np.signbit(mine), np.signbit(ref))
+
+
+def test_e4m3_special_values():
+    v = orc.e4m3_to_f64(np.arange(256, dtype=np.uint8))
+    assert v[0x7E] == 448.0 and v[0xFE] == -448.0          # largest finite magnitude
+    assert v[0x08] == 2.0 ** -6                             # smallest normal
+    assert v[0x07] == 7 * 2.0 ** -9 and v[0x01] == 2.0 ** -9  # subnormals
+    assert v[0x00] == 0.0 and not np.signbit(v[0x00])
+    assert v[0x80] == 0.0 and np.signbit(v[0x80])
+    assert np.isnan(v[0x7F]) and np.isnan(v[0xFF])          # the only NaNs, no infinities
+    assert np.isfinite(v[[c for c in range(256) if c not in (0x7F, 0xFF)]]).all()
+    assert v[0x38] == 1.0 and v[0x3C] == 1.5 and v[0xB8] == -1.0
+    # sign-magnitude order: positive codes increase strictly, negatives mirror them
+    pos = v[0x00:0x7F]
+    assert (np.diff(pos) > 0).all()
+    assert np.array_equal(v[0x80:0xFF], -pos)
+
+
+def test_e4m3_dequantize_is_exact():
+    from fractions import Fraction
+    codes = np.arange(0, 0x7F, dtype=np.uint8)
+    for scale in (1.0, 6.0 / 448, 0.0123, 3.0):
+        s32 = float(np.float32(scale))
+        got = orc.dequantize_e4m3(codes, scale)
+        for c, g in zip(codes[::7], got[::7]):
+            assert Fraction(g) == Fraction(float(orc.e4m3_to_f64(c))) * Fraction(s32)
+
+
+def test_synth_fp8_caches():
+    s = synth.Shape(2, 5, 700, 300, 8, 2, 64, 32, 4, cache="fp8", k_scale=0.02, v_scale=0.05)
+    x = synth.host_inputs(s, 9)
+    for n in ("k", "v", "k_idx"):
+        assert x[n].dtype == torch.float8_e4m3fn
+    for n in ("q", "q_idx"):
+        assert x[n].dtype == torch.bfloat16
+    ki = orc.e4m3_to_f64(synth.codes(x["k_idx"]))
+    assert set(np.unique(ki)) <= set(range(-4, 5))  # integers stored exactly
+    # the same seeded draws as the bf16 recipe, divided by the scale before rounding
+    ref = synth.host_inputs(s.replace(cache="native", dtype="f32", idx_lo=-4, idx_hi=4), 9)
+    kv = orc.e4m3_to_f64(synth.codes(x["k"]))
+    assert np.array_equal(ki, synth.as_f64(ref["k_idx"]))
+    rel = np.abs(kv * 0.02 - synth.as_f64(ref["k"])) / np.maximum(np.abs(synth.as_f64(ref["k"])), 2.0 ** -6 * 0.02)
+    assert rel.max() <= 2.0 ** -4 + 1e-12  # round to nearest with a 3-bit mantissa
+    with pytest.raises(TypeError):
+        synth.as_f64(x["k"])
