@@ -11,7 +11,8 @@ FLOPs, the masked half of the local block and the skipped blocks excluded).
 algorithmic FLOPs per launch over its own average duration, timed with HIP
 events recorded around that kernel on the stream it runs on.  The decode
 workload (64 sequences x 128K cache) is reported beside it in GB/s of
-algorithmic HBM bytes.  ``cpu_baseline`` times the fp64 CPU oracle on a bounded
+algorithmic HBM bytes, with bf16 caches (``decode``) and with FP8 E4M3 caches
+(``decode_fp8``).  ``cpu_baseline`` times the fp64 CPU oracle on a bounded
 sample of query rows of the same workload.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--decode-steps 50]
@@ -88,7 +89,8 @@ def algorithmic_work(s: synth.Shape):
 
     main:  4*d*Hq*B * sum_i [(n_sel(t)-1)*Bk + (t mod Bk) + 1], n_sel = min(k, L+1)
     index: 2*D_idx*G*B * sum_i L(t)*Bk           (only full blocks before L are scored)
-    bytes: B*[S_k*D_idx*e + G*n_sel*Bk*d*e*2 + 2*Hq*d*e + G*D_idx*e + 4*G*k]
+    bytes: B*[S_k*D_idx*c + G*n_sel*Bk*d*c*2 + 2*Hq*d*e + G*D_idx*e + 4*G*k]
+           (e bytes per query/output element, c per cache element: 1 for FP8 caches)
     """
     t = s.q_offset + np.arange(s.q_len, dtype=np.int64)
     L = t // s.block_size
@@ -97,8 +99,9 @@ def algorithmic_work(s: synth.Shape):
     flop_main = 4.0 * s.head_dim * s.num_q_heads * s.batch * float(toks.sum())
     flop_index = 2.0 * s.index_dim * s.groups * s.batch * float((L * s.block_size).sum())
     e = 2 if s.dtype == "bf16" else 4
+    c = 1 if s.fp8 else e
     nsel_last = int(n_sel[-1])
-    bytes_dec = s.batch * (s.kv_len * s.index_dim * e + s.groups * nsel_last * s.block_size * s.head_dim * e * 2
+    bytes_dec = s.batch * (s.kv_len * s.index_dim * c + s.groups * nsel_last * s.block_size * s.head_dim * c * 2
                            + 2 * s.num_q_heads * s.head_dim * e + s.groups * s.index_dim * e + 4 * s.groups * s.topk)
     return flop_main, flop_index, float(bytes_dec)
 
@@ -113,7 +116,9 @@ class Runner:
         self.out = torch.empty((s.batch, s.q_len, s.num_q_heads, s.head_dim), dtype=s.torch_dtype, device=dev)
         self.sel = torch.empty((s.batch, s.groups, s.q_len, s.topk), dtype=torch.int32, device=dev)
         self.shape = msa.make_shape(s.batch, s.q_len, s.kv_len, s.q_offset, s.num_q_heads, s.num_kv_heads,
-                                    s.head_dim, s.index_dim, s.topk, s.torch_dtype)
+                                    s.head_dim, s.index_dim, s.topk, s.torch_dtype,
+                                    cache_format=msa.CACHE_FP8_E4M3 if s.fp8 else msa.CACHE_NATIVE,
+                                    k_scale=s.k_scale if s.fp8 else None, v_scale=s.v_scale if s.fp8 else None)
         n = msa.workspace_size(self.shape, msa.OP_FWD)
         self.ws_raw = torch.empty(n + 256, dtype=torch.uint8, device=dev)
         off = (-self.ws_raw.data_ptr()) % 256
@@ -132,23 +137,25 @@ class Runner:
             raise RuntimeError(self.L.msa_last_error().decode())
 
     def time_steps(self, steps, warmup, timed_kernel=None):
-        """Returns (ms per step, list of per-step ms of timed_kernel or None)."""
+        """Returns (ms per step, list of per-step ms of timed_kernel or None).  The
+        per-step times of the last call are kept in self.step_ms."""
         for _ in range(warmup):
             self.step()
         torch.cuda.synchronize()
         ev = HipEvents() if timed_kernel else None
         kev = [(ev.create(), ev.create()) for _ in range(steps)] if timed_kernel else None
-        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
         torch.cuda.synchronize()
-        t0.record(self.stream)
+        marks[0].record(self.stream)
         for i in range(steps):
             if kev:
                 self.L.msa_set_kernel_timer(KERNELS[timed_kernel], kev[i][0], kev[i][1])
             self.step()
-        t1.record(self.stream)
+            marks[i + 1].record(self.stream)
         torch.cuda.synchronize()
         self.L.msa_set_kernel_timer(0, None, None)
-        total = t0.elapsed_time(t1)
+        total = marks[0].elapsed_time(marks[-1])
+        self.step_ms = [marks[i].elapsed_time(marks[i + 1]) for i in range(steps)]
         per_kernel = None
         if kev:
             per_kernel = [ev.elapsed_ms(a, b) for a, b in kev]
@@ -164,6 +171,41 @@ class Runner:
             if all(k is not None for k in ks):  # kernels this shape does not launch are left out
                 res[name] = float(np.median(ks))
         return res
+
+
+def step_stats(step_ms):
+    return {"ms_p50": round(float(np.median(step_ms)), 4), "ms_p99": round(float(np.percentile(step_ms, 99)), 4)}
+
+
+def decode_leg(msa, wid: int, args):
+    """One decode workload: GB/s of algorithmic bytes, and the k_idx scan kernel
+    (the index kernel) against the HBM roofline."""
+    sd = synth.WORKLOADS[wid]
+    name = synth.WORKLOAD_NAMES[wid]
+    _, _, dec_bytes = algorithmic_work(sd)
+    print(f"[bench] {name}: generating inputs", file=sys.stderr, flush=True)
+    drun = Runner(msa, sd, wid)
+    dms, idx_ms = drun.time_steps(args.decode_steps, args.warmup, "index_score")
+    stats = step_stats(drun.step_ms)
+    dk = {} if args.no_breakdown else drun.kernel_breakdown()
+    gbs = dec_bytes / (dms * 1e-3) / 1e9
+    idx_avg = float(np.mean(idx_ms))
+    kidx_bytes = float(sd.batch * sd.kv_len * sd.index_dim * (1 if sd.fp8 else 2))
+    profile = "index_topk_decode_128k_b64_fp8_hbm.md" if sd.fp8 else "index_topk_decode_128k_b64_hbm.md"
+    res = {
+        "workload": name, "value": round(gbs, 1), "unit": "GB/s",
+        "ms_per_step": round(dms, 4), **stats, "steps": args.decode_steps, "bytes_per_step": dec_bytes,
+        "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+        "roofline": {"bound": "hbm", "kernel": "index_topk", "achieved": round(kidx_bytes / (idx_avg * 1e-3) / 1e9, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(kidx_bytes / (idx_avg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                     "bytes_per_launch": kidx_bytes, "avg_launch_ms": round(idx_avg, 4),
+                     "traffic": recorded_traffic(profile, "index_topk.hip", "traffic_read_bytes_per_launch")},
+        "kernels_ms": {k: round(v, 4) for k, v in dk.items()},
+    }
+    del drun
+    torch.cuda.empty_cache()
+    return res
 
 
 def cpu_baseline(s: synth.Shape, x, out_gpu, sel_gpu, budget_s: float):
@@ -253,6 +295,7 @@ def main():
     run = Runner(msa, s, wid)
     print("[bench] timing msa_fwd", file=sys.stderr, flush=True)
     ms, attn_ms = run.time_steps(args.steps, args.warmup, "attention")
+    stats = step_stats(run.step_ms)
     kern = {} if args.no_breakdown else run.kernel_breakdown()
     attn_avg = float(np.mean(attn_ms))
     value = (flop_main + flop_index) / (ms * 1e-3) / 1e12
@@ -265,6 +308,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        **stats,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -280,7 +324,11 @@ def main():
                      if wid == 3 else None,
                      "traffic_unit": "bytes", "flop_per_launch": flop_main, "avg_launch_ms": round(attn_avg, 4)},
         "work": {"flop_main": flop_main, "flop_index": flop_index,
-                 "index_tflops": round(flop_index / (kern["index_score"] * 1e-3) / 1e12, 2) if kern else None},
+                 "index_tflops": round(flop_index / (kern["index_score"] * 1e-3) / 1e12, 2) if kern else None,
+                 # the main branch alone (what msa_sparse_attn_fwd runs): gather + attention + combine
+                 "sparse_attn_tflops": round(flop_main / (sum(kern.get(k, 0.0) for k in ("gather", "attention",
+                                                                                            "combine")) * 1e-3) / 1e12, 2)
+                 if kern else None},
         "kernels_ms": {k: round(v, 4) for k, v in kern.items()},
     }
     print(f"[bench] {ms:.3f} ms/step, attention {attn_avg:.3f} ms", file=sys.stderr, flush=True)
@@ -313,29 +361,8 @@ def main():
             torch.cuda.empty_cache()
 
     if not args.no_decode:
-        sd = synth.WORKLOADS[4]
-        _, _, dec_bytes = algorithmic_work(sd)
-        print("[bench] decode_128k_b64: generating inputs", file=sys.stderr, flush=True)
-        drun = Runner(msa, sd, 4)
-        dms, idx_ms = drun.time_steps(args.decode_steps, args.warmup, "index_score")
-        dk = {} if args.no_breakdown else drun.kernel_breakdown()
-        gbs = dec_bytes / (dms * 1e-3) / 1e9
-        idx_avg = float(np.mean(idx_ms))
-        kidx_bytes = float(sd.batch * sd.kv_len * sd.index_dim * 2)
-        result["decode"] = {
-            "workload": synth.WORKLOAD_NAMES[4], "value": round(gbs, 1), "unit": "GB/s",
-            "ms_per_step": round(dms, 4), "steps": args.decode_steps, "bytes_per_step": dec_bytes,
-            "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
-            "roofline": {"bound": "hbm", "kernel": "index_topk", "achieved": round(kidx_bytes / (idx_avg * 1e-3) / 1e9, 1),
-                         "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": round(kidx_bytes / (idx_avg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-                         "bytes_per_launch": kidx_bytes, "avg_launch_ms": round(idx_avg, 4),
-                         "traffic": recorded_traffic("index_topk_decode_128k_b64_hbm.md", "index_topk.hip",
-                                                     "traffic_read_bytes_per_launch")},
-            "kernels_ms": {k: round(v, 4) for k, v in dk.items()},
-        }
-        del drun
-        torch.cuda.empty_cache()
+        result["decode"] = decode_leg(msa, 4, args)
+        result["decode_fp8"] = decode_leg(msa, 6, args)
     print(json.dumps(result))
 
 

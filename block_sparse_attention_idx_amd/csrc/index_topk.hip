@@ -57,6 +57,40 @@ __device__ __forceinline__ bool ranks_before(float s1, int i1, float s2, int i2)
   return s1 > s2 || (s1 == s2 && i1 < i2);
 }
 
+// One (row, key split) result: with several splits the merged list goes to
+// the partial lists for topk_merge_kernel; with one split the first min(k-1, L)
+// entries are the selection, and the local block and -1 padding are added
+// with the ids in ascending order.
+template <int CAP>
+__device__ __forceinline__ void emit_row(const IndexParams& p, int b, int n, int split, int L, const float (&ms)[CAP],
+                                         const int (&mi)[CAP]) {
+  if (p.nsplit > 1) {
+    const int64_t rowg = (int64_t)b * p.rows_per_b + n;
+    float* ds = p.part_s + (rowg * p.nsplit + split) * CAP;
+    int32_t* di = p.part_i + (rowg * p.nsplit + split) * CAP;
+#pragma unroll
+    for (int j = 0; j < CAP; ++j) {
+      ds[j] = ms[j];
+      di[j] = mi[j];
+    }
+    return;
+  }
+  const int take = min(p.topk - 1, L);
+  const int i = n / p.G, g = n - (n / p.G) * p.G;
+  int32_t* out = p.sel + (((int64_t)b * p.G + g) * p.S_q + i) * p.topk;
+#pragma unroll
+  for (int j = 0; j < CAP; ++j) {
+    if (j < take) {
+      int r = 0;
+#pragma unroll
+      for (int m = 0; m < CAP; ++m) r += (m < take && mi[m] < mi[j]) ? 1 : 0;
+      out[r] = mi[j];
+    }
+  }
+  out[take] = L;
+  for (int j = take + 1; j < p.topk; ++j) out[j] = -1;
+}
+
 template <typename T, typename S, int DI, int CAP, int RT>
 __global__ __launch_bounds__(256, 2) void index_topk_kernel(IndexParams p) {
   using M = Mma<T>;
@@ -260,35 +294,168 @@ __global__ __launch_bounds__(256, 2) void index_topk_kernel(IndexParams p) {
         ia += take_a ? 1 : 0;
         ib += take_a ? 0 : 1;
       }
-      if (p.nsplit > 1) {
-        const int64_t rowg = (int64_t)b * p.rows_per_b + n;
-        float* ds = p.part_s + (rowg * p.nsplit + split) * CAP;
-        int32_t* di = p.part_i + (rowg * p.nsplit + split) * CAP;
+      emit_row<CAP>(p, b, n, split, rowL[rt], ms, mi);
+    }
+  }
+}
+
+// Few rows per sequence (S_q * G <= 32, e.g. decode).  One 32-row tile holds
+// all of a sequence's (row, group) pairs, so rather than four waves sharing a
+// staged block, each wave takes whole blocks of the unit's key range (wave w:
+// blocks c_begin + w, c_begin + w + 4, ...).  K fragments are read straight from
+// global memory as the MFMA A operand, one 32-key tile ahead of their use, with
+// no LDS staging and no barrier in the block loop.  Every lane reads 16 bytes
+// per load: for e4m3 keys that is two k-steps, so the reduction dimension is
+// taken in the order d = 32 p + 16 h + 8 (ks % 2) + e (p = ks / 2) for both
+// operands; any order common to K and Q gives the same dot products.  As in the kernel above the
+// two lane halves of a wave rank alternate blocks of its sequence; the 4 x 2
+// lists of a row are merged through LDS at the end.
+template <typename T, typename S, int DI, int CAP>
+__global__ __launch_bounds__(256, 2) void index_topk_small_kernel(IndexParams p) {
+  using M = Mma<T>;
+  using frag = typename M::frag;
+  constexpr int KPL = M::KPL, KSTEP = M::KSTEP, NKS = DI / KSTEP;
+  constexpr bool kNative = std::is_same<S, T>::value;
+  // one lane's 16-byte share of a K tile per load: one k-step of native keys,
+  // two k-steps of e4m3 keys
+  typedef typename std::conditional<kNative, frag, i32x4>::type kraw;
+  static_assert(kNative || (sizeof(S) == 1 && KPL == 8 && NKS % 2 == 0), "e4m3 keys come as 16-byte runs");
+  constexpr int NKR = kNative ? NKS : NKS / 2;  // loads per lane per tile
+  // element offset of k-step ks, lane half h (16 elements per 16 bytes of e4m3)
+  auto koff = [](int ks, int hh) { return kNative ? ks * KSTEP + hh * KPL : (ks / 2) * 32 + hh * 16 + (ks % 2) * 8; };
+  constexpr int NL = 8;  // lists per row: 4 waves x 2 lane halves
+  static_assert(NL * CAP * 32 * 8 <= 65536, "list merge fits the static LDS");
+  __shared__ float xs[NL * CAP * 32];
+  __shared__ int xi[NL * CAP * 32];
+
+  const int lin = blockIdx.x;
+  const int logical = (lin & 7) * p.grid_per_xcd + (lin >> 3);
+  if (logical >= p.nunits) return;
+  const int split = logical / p.B;
+  const int b = logical - split * p.B;
+  const int Lmax = (int)((p.q_offset + (p.rows_per_b - 1) / p.G) / kBlock);
+  const int c_begin = split * p.chunk;
+  const int c_end = min(c_begin + p.chunk, Lmax);
+  if (c_begin >= c_end && p.nsplit > 1) return;  // a single split still writes rows with L = 0
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int h = lane >> 5, l32 = lane & 31;
+  const bool rvalid = l32 < p.rows_per_b;
+  const int nc = rvalid ? l32 : p.rows_per_b - 1;  // invalid rows read a valid row
+  const int rowL = (int)((p.q_offset + nc / p.G) / kBlock);
+  frag qf[NKS];
+  {
+    const T* qrow = (const T*)p.q_idx + ((int64_t)b * p.rows_per_b + nc) * DI;
 #pragma unroll
-        for (int j = 0; j < CAP; ++j) {
-          ds[j] = ms[j];
-          di[j] = mi[j];
-        }
+    for (int ks = 0; ks < NKS; ++ks) qf[ks] = *(const frag*)(qrow + koff(ks, h));
+  }
+  float ls[CAP];
+  int li[CAP];
+#pragma unroll
+  for (int j = 0; j < CAP; ++j) {
+    ls[j] = kNegInf;
+    li[j] = -1;
+  }
+
+  // this wave's blocks: c_begin + wave + 4 j for j < nbw, read as 4 nbw tiles of 32 keys
+  const int nbw = c_end - c_begin > wave ? (c_end - c_begin - wave + 3) / 4 : 0;
+  const int ntl = 4 * nbw;
+  const S* kb = (const S*)p.k_idx + (int64_t)b * p.S_k * DI;
+  // tile tl of the wave; tl past the end re-reads the last one (just read, so from L2)
+  auto load_tile = [&](kraw (&a)[NKR], int tl) {
+    const int tc = min(tl, ntl - 1);
+    const int c = c_begin + wave + 4 * (tc / 4);
+    const S* src = kb + ((int64_t)c * kBlock + (tc % 4) * 32 + l32) * DI;
+#pragma unroll
+    for (int u = 0; u < NKR; ++u) a[u] = *(const kraw*)(src + koff(kNative ? u : 2 * u, h));
+  };
+  // this lane's max over its 16 keys of the tile
+  auto tile_max = [&](const kraw (&a)[NKR]) {
+    f32x16 acc = f32x16{};
+#pragma unroll
+    for (int u = 0; u < NKR; ++u) {
+      if constexpr (kNative) {
+        acc = M::mma(a[u], qf[u], acc);
       } else {
-        // the only split: the first min(k-1, L) entries are the selection; add
-        // the local block, order ids ascending, pad with -1
-        const int L = rowL[rt];
-        const int take = min(p.topk - 1, L);
-        const int i = n / p.G, g = n - (n / p.G) * p.G;
-        int32_t* out = p.sel + (((int64_t)b * p.G + g) * p.S_q + i) * p.topk;
-#pragma unroll
-        for (int j = 0; j < CAP; ++j) {
-          if (j < take) {
-            int r = 0;
-#pragma unroll
-            for (int m = 0; m < CAP; ++m) r += (m < take && mi[m] < mi[j]) ? 1 : 0;
-            out[r] = mi[j];
-          }
-        }
-        out[take] = L;
-        for (int j = take + 1; j < p.topk; ++j) out[j] = -1;
+        const uint2 w0 = e4m3x4_to_bf16((uint32_t)a[u][0]), w1 = e4m3x4_to_bf16((uint32_t)a[u][1]);
+        const uint2 w2 = e4m3x4_to_bf16((uint32_t)a[u][2]), w3 = e4m3x4_to_bf16((uint32_t)a[u][3]);
+        acc = M::mma(__builtin_bit_cast(frag, i32x4{(int)w0.x, (int)w0.y, (int)w1.x, (int)w1.y}), qf[2 * u], acc);
+        acc = M::mma(__builtin_bit_cast(frag, i32x4{(int)w2.x, (int)w2.y, (int)w3.x, (int)w3.y}), qf[2 * u + 1], acc);
       }
     }
+    float m = acc[0];
+#pragma unroll
+    for (int j = 1; j < 16; ++j) m = fmaxf(m, acc[j]);
+    return m;
+  };
+
+  float pm = kNegInf, pmA = kNegInf;
+  auto process = [&](const kraw (&a)[NKR], int tl) {
+    pm = fmaxf(pm, tile_max(a));
+    if (tl % 4 != 3) return;  // the block continues in the next tile
+    const int j = tl / 4;
+    const float full = fmaxf(pm, __shfl_xor(pm, 32));
+    pm = kNegInf;
+    // blocks pair up: half 0 ranks the wave's even blocks, half 1 the odd ones
+    const bool second = (j & 1) != 0;
+    if (!second) pmA = full;
+    if (second || j + 1 == nbw) {
+      const int c = c_begin + wave + 4 * j;
+      const float mine = h ? (second ? full : kNegInf) : pmA;
+      const int cc = (h || !second) ? c : c - 4;
+      const float x = (rvalid && cc < rowL) ? mine : kNegInf;
+      list_insert<CAP>(ls, li, x, cc);
+    }
+  };
+  if (nbw > 0) {
+    kraw ta[NKR], tb[NKR];
+    load_tile(ta, 0);
+    for (int tl = 0; tl < ntl; tl += 2) {  // ntl is a multiple of 4
+      load_tile(tb, tl + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      process(ta, tl);
+      load_tile(ta, tl + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      process(tb, tl + 1);
+    }
+  }
+
+  // merge the 8 lists of each row through LDS: [list][CAP][32 rows]
+#pragma unroll
+  for (int j = 0; j < CAP; ++j) {
+    const int o = ((wave * 2 + h) * CAP + j) * 32 + l32;
+    xs[o] = ls[j];
+    xi[o] = li[j];
+  }
+  __syncthreads();
+  if (wave == 0 && h == 0 && rvalid) {
+    int pos[NL];
+#pragma unroll
+    for (int w = 0; w < NL; ++w) pos[w] = 0;
+    float ms[CAP];
+    int mi[CAP];
+#pragma unroll
+    for (int j = 0; j < CAP; ++j) {
+      float bs = kNegInf;
+      int bi = -1, bw = -1;
+#pragma unroll
+      for (int w = 0; w < NL; ++w) {
+        const int o = (w * CAP + min(pos[w], CAP - 1)) * 32 + l32;
+        const float s2 = xs[o];
+        const int i2 = pos[w] < CAP ? xi[o] : -1;
+        // empty entries (id -1) rank last; block ids are unique across the lists
+        if (i2 >= 0 && (bi < 0 || ranks_before(s2, i2, bs, bi))) {
+          bs = s2;
+          bi = i2;
+          bw = w;
+        }
+      }
+      ms[j] = bs;
+      mi[j] = bi;
+#pragma unroll
+      for (int w = 0; w < NL; ++w) pos[w] += (w == bw) ? 1 : 0;
+    }
+    emit_row<CAP>(p, b, l32, split, rowL, ms, mi);
   }
 }
 
@@ -372,7 +539,15 @@ static hipError_t launch_index_t(const IndexParams& p, hipStream_t s, const Kern
   timer_start(tm, kKernIndexScore, s);
   constexpr int RT = CAP <= 15 ? 2 : 1;
   static_assert(4 * 32 * RT == index_rows_per_wg(CAP + 1), "host and kernel agree on the row tile");
-  hipLaunchKernelGGL((index_topk_kernel<T, S, DI, CAP, RT>), dim3(p.grid_per_xcd * 8), dim3(256), 0, s, p);
+  bool small_done = false;
+  if constexpr (sizeof(T) == 2) {  // the few-row form is built for bf16 queries
+    if (p.small) {
+      hipLaunchKernelGGL((index_topk_small_kernel<T, S, DI, CAP>), dim3(p.grid_per_xcd * 8), dim3(256), 0, s, p);
+      small_done = true;
+    }
+  }
+  if (!small_done)
+    hipLaunchKernelGGL((index_topk_kernel<T, S, DI, CAP, RT>), dim3(p.grid_per_xcd * 8), dim3(256), 0, s, p);
   timer_stop(tm, kKernIndexScore, s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

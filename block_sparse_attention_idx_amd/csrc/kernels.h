@@ -40,7 +40,12 @@ struct IndexParams {
   int nsplit, chunk;   // key-block splits and blocks per split
   int nunits;          // ntile_total * nsplit
   int grid_per_xcd;    // ceil(nunits / 8)
+  int small;           // 1: bf16 queries and rows_per_b <= kIndexSmallRows, one unit per (sequence, split)
 };
+
+// At most this many (row, group) pairs per sequence: the index kernel's
+// few-row form (each wave ranks whole blocks on its own).
+constexpr int kIndexSmallRows = 32;
 
 // Index rows per workgroup: 4 waves x 32 rows x RT row tiles, RT = 2 for lists
 // of up to 15 entries (k <= 16), 1 for the longer lists of k <= 32.

@@ -123,15 +123,18 @@ IndexPlan plan_index(const msa_shape* s) {
   p.topk = s->topk;
   p.q_offset = s->q_offset;
   p.rows_per_b = s->q_len * s->num_kv_heads;
-  p.ntile = (int)ceil_div(p.rows_per_b, msa::index_rows_per_wg(s->topk));
+  p.small = p.rows_per_b <= msa::kIndexSmallRows && s->dtype == MSA_BF16 ? 1 : 0;
+  p.ntile = p.small ? 1 : (int)ceil_div(p.rows_per_b, msa::index_rows_per_wg(s->topk));
   p.ntile_total = p.B * p.ntile;
   const int64_t Lmax = s->q_len > 0 ? (s->q_offset + s->q_len - 1) / msa::kBlock : 0;
   // Enough row tiles to fill the GPU: one unit per tile, no merge.  Otherwise
-  // split the key blocks so that about kIndexTargetUnits units exist.
+  // split the key blocks so that about kIndexTargetUnits units exist (at least
+  // 16 blocks per unit, 8 in the few-row form where 4 waves share a unit's
+  // blocks, and at most 128 splits for the merge).
   int64_t chunk = std::max<int64_t>(1, Lmax), nsplit = 1;
   if (Lmax > 0 && p.ntile_total < kIndexMinTiles) {
     const int64_t want = std::max<int64_t>(1, ceil_div(kIndexTargetUnits, std::max(1, p.ntile_total)));
-    chunk = std::max<int64_t>({16, ceil_div(Lmax, want), ceil_div(Lmax, 128)});
+    chunk = std::max<int64_t>({p.small ? 8 : 16, ceil_div(Lmax, want), ceil_div(Lmax, 128)});
     nsplit = ceil_div(Lmax, chunk);
   }
   p.chunk = (int)chunk;
