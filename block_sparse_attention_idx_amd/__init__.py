@@ -20,6 +20,12 @@ k_idx [B,S_k,D_idx] with G = Hkv; all contiguous, on the GPU, fp32 or bf16.
 The caches k, v and k_idx may instead be ``torch.float8_e4m3fn`` tensors (OCP
 FP8 E4M3) next to bf16 q and q_idx; the keys and values attended to are then
 ``k_scale * k`` and ``v_scale * v``.
+
+Caches of unequal length, optionally paged (``index_select_kvcache``,
+``sparse_attn_fwd_kvcache``, ``fwd_kvcache``): ``seq_lens`` int32 [B] gives the
+tokens of each sequence (query row i of sequence b sits at
+``seq_lens[b] - S_q + i``); with ``page_table`` int32 [B, max_pages] the caches
+are pools of 128-token pages, k/v [P, Hkv, 128, d] and k_idx [P, 128, D_idx].
 """
 from __future__ import annotations
 
@@ -29,8 +35,9 @@ from typing import Optional
 
 import torch
 
-__all__ = ["index_select", "sparse_attn_fwd", "fwd", "workspace_size", "MsaShape", "lib", "LIB_PATH",
-           "MsaError", "OP_INDEX_SELECT", "OP_SPARSE_ATTN", "OP_FWD"]
+__all__ = ["index_select", "sparse_attn_fwd", "fwd", "index_select_kvcache", "sparse_attn_fwd_kvcache",
+           "fwd_kvcache", "workspace_size", "MsaShape", "MsaKvCache", "lib", "LIB_PATH", "MsaError",
+           "OP_INDEX_SELECT", "OP_SPARSE_ATTN", "OP_FWD"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmsa.so")
 
@@ -59,6 +66,15 @@ class MsaShape(ctypes.Structure):
         ("k_scale", ctypes.c_float),
         ("v_scale", ctypes.c_float),
         ("pad", ctypes.c_int32),
+    ]
+
+
+class MsaKvCache(ctypes.Structure):
+    _fields_ = [
+        ("seq_lens", ctypes.c_void_p),
+        ("page_table", ctypes.c_void_p),
+        ("max_pages", ctypes.c_int32),
+        ("num_pages", ctypes.c_int32),
     ]
 
 
@@ -97,6 +113,15 @@ def lib() -> ctypes.CDLL:
         L.msa_version.restype = ctypes.c_char_p
         L.msa_set_kernel_timer.argtypes = [ctypes.c_int, vp, vp]
         L.msa_set_kernel_timer.restype = ctypes.c_int
+        cp = ctypes.POINTER(MsaKvCache)
+        L.msa_workspace_size_kvcache.argtypes = [shp, cp, ctypes.c_int]
+        L.msa_workspace_size_kvcache.restype = sz
+        L.msa_index_select_kvcache.argtypes = [shp, cp, vp, vp, vp, vp, sz, vp]
+        L.msa_index_select_kvcache.restype = ctypes.c_int
+        L.msa_sparse_attn_fwd_kvcache.argtypes = [shp, cp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.msa_sparse_attn_fwd_kvcache.restype = ctypes.c_int
+        L.msa_fwd_kvcache.argtypes = [shp, cp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.msa_fwd_kvcache.restype = ctypes.c_int
         _LIB = L
     return _LIB
 
@@ -170,13 +195,17 @@ def workspace_size(shape: MsaShape, op: int) -> int:
     return int(lib().msa_workspace_size(ctypes.byref(shape), op))
 
 
-def _workspace(shape: MsaShape, op: int, device) -> Optional[torch.Tensor]:
-    n = workspace_size(shape, op)
+def _aligned(n: int, device) -> Optional[torch.Tensor]:
+    """A 256-byte aligned device buffer of n bytes (None for 0)."""
     if n == 0:
         return None
     ws = torch.empty(n + 256, dtype=torch.uint8, device=device)
     off = (-ws.data_ptr()) % 256
     return ws[off:off + n]
+
+
+def _workspace(shape: MsaShape, op: int, device) -> Optional[torch.Tensor]:
+    return _aligned(workspace_size(shape, op), device)
 
 
 def index_select(q_idx: torch.Tensor, k_idx: torch.Tensor, topk: int, q_offset: int = 0,
@@ -260,6 +289,161 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_idx: torch.Tensor, 
     L = lib()
     st = L.msa_fwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(q_idx), _ptr(k_idx), _ptr(out), _ptr(sel),
                    _ptr(lse), _ptr(ws), 0 if ws is None else ws.numel(), _stream(dev))
+    _check(st)
+    res = [out]
+    if return_sel:
+        res.append(sel)
+    if return_lse:
+        res.append(lse)
+    return res[0] if len(res) == 1 else tuple(res)
+
+
+# ---- caches of unequal length, optionally paged ----------------------------
+
+def _kv_cache(B: int, dev, seq_lens, page_table, num_pages: int):
+    """The MsaKvCache descriptor (or None) and its max_pages."""
+    if seq_lens is None and page_table is None:
+        return None, 0
+    c = MsaKvCache()
+    if seq_lens is not None:
+        _need(seq_lens, "seq_lens", 1, dev, torch.int32)
+        if seq_lens.shape[0] != B:
+            raise ValueError(f"seq_lens must have {B} entries")
+        c.seq_lens = seq_lens.data_ptr()
+    max_pages = 0
+    if page_table is not None:
+        _need(page_table, "page_table", 2, dev, torch.int32)
+        if page_table.shape[0] != B:
+            raise ValueError(f"page_table must have {B} rows")
+        max_pages = page_table.shape[1]
+        c.page_table = page_table.data_ptr()
+        c.max_pages, c.num_pages = max_pages, num_pages
+    return c, max_pages
+
+
+def _kv_geometry(k: torch.Tensor, k_idx: Optional[torch.Tensor], B: int, page_table, kv_len):
+    """(Hkv, kv_len, num_pages) of dense [B, Hkv, S_k, d] or paged [P, Hkv, 128, d] caches."""
+    if page_table is not None:
+        P, Hkv, blk = k.shape[0], k.shape[1], k.shape[2]
+        if blk != BLOCK_SIZE:
+            raise ValueError(f"paged k/v must be [P, Hkv, {BLOCK_SIZE}, d]")
+        if k_idx is not None and (k_idx.shape[0] != P or k_idx.shape[1] != BLOCK_SIZE):
+            raise ValueError(f"paged k_idx must be [P, {BLOCK_SIZE}, D_idx]")
+        return Hkv, (kv_len if kv_len is not None else page_table.shape[1] * BLOCK_SIZE), P
+    if k.shape[0] != B:
+        raise ValueError("dense k/v must be [B, Hkv, S_k, d]")
+    if k_idx is not None and k_idx.shape[:2] != (B, k.shape[2]):
+        raise ValueError("dense k_idx must be [B, S_k, D_idx]")
+    return k.shape[1], k.shape[2], 0
+
+
+def index_select_kvcache(q_idx: torch.Tensor, k_idx: torch.Tensor, topk: int, seq_lens=None, page_table=None,
+                         kv_len: Optional[int] = None, q_offset: int = 0, sel: Optional[torch.Tensor] = None,
+                         workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """index_select over caches of unequal length and/or in pages."""
+    _need(q_idx, "q_idx", 4)
+    dev = q_idx.device
+    _need(k_idx, "k_idx", 3, dev)
+    cf = _cache_format(q_idx.dtype, [("k_idx", k_idx)])
+    B, S_q, G, D = q_idx.shape
+    if k_idx.shape[2] != D:
+        raise ValueError("k_idx must end in D_idx like q_idx")
+    if page_table is not None:
+        P = k_idx.shape[0]
+        if k_idx.shape[1] != BLOCK_SIZE:
+            raise ValueError(f"paged k_idx must be [P, {BLOCK_SIZE}, D_idx]")
+        S_k = kv_len if kv_len is not None else page_table.shape[1] * BLOCK_SIZE
+    else:
+        P = 0
+        if k_idx.shape[0] != B:
+            raise ValueError("dense k_idx must be [B, S_k, D_idx]")
+        S_k = k_idx.shape[1]
+    cache, _ = _kv_cache(B, dev, seq_lens, page_table, P)
+    shape = make_shape(B, S_q, S_k, q_offset, G, G, 64, D, topk, q_idx.dtype, cache_format=cf)
+    if sel is None:
+        sel = torch.empty((B, G, S_q, topk), dtype=torch.int32, device=dev)
+    else:
+        _need(sel, "sel", 4, dev, torch.int32)
+    L = lib()
+    cref = ctypes.byref(cache) if cache is not None else None
+    if workspace is None:
+        n = int(L.msa_workspace_size_kvcache(ctypes.byref(shape), cref, OP_INDEX_SELECT))
+        workspace = _aligned(n, dev)
+    st = L.msa_index_select_kvcache(ctypes.byref(shape), cref, _ptr(q_idx), _ptr(k_idx), _ptr(sel),
+                                    _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream(dev))
+    _check(st)
+    return sel
+
+
+def sparse_attn_fwd_kvcache(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sel: torch.Tensor, seq_lens=None,
+                            page_table=None, kv_len: Optional[int] = None, q_offset: int = 0,
+                            scale: Optional[float] = None, out_dtype: Optional[torch.dtype] = None,
+                            return_lse: bool = False, k_scale: Optional[float] = None,
+                            v_scale: Optional[float] = None, workspace: Optional[torch.Tensor] = None):
+    """sparse_attn_fwd over caches of unequal length and/or in pages."""
+    _need(q, "q", 4)
+    dev = q.device
+    _need(k, "k", 4, dev)
+    _need(v, "v", 4, dev)
+    cf = _cache_format(q.dtype, [("k", k), ("v", v)])
+    _need(sel, "sel", 4, dev, torch.int32)
+    B, S_q, Hq, d = q.shape
+    if tuple(v.shape) != tuple(k.shape) or k.shape[3] != d:
+        raise ValueError("k and v must match and end in d")
+    Hkv, S_k, P = _kv_geometry(k, None, B, page_table, kv_len)
+    topk = sel.shape[3]
+    if tuple(sel.shape[:3]) != (B, Hkv, S_q):
+        raise ValueError("sel must be [B, G, S_q, topk]")
+    cache, _ = _kv_cache(B, dev, seq_lens, page_table, P)
+    shape = make_shape(B, S_q, S_k, q_offset, Hq, Hkv, d, 32, topk, q.dtype, out_dtype, scale,
+                       cache_format=cf, k_scale=k_scale, v_scale=v_scale)
+    out = torch.empty((B, S_q, Hq, d), dtype=out_dtype or q.dtype, device=dev)
+    lse = torch.empty((B, Hq, S_q), dtype=torch.float32, device=dev) if return_lse else None
+    L = lib()
+    cref = ctypes.byref(cache) if cache is not None else None
+    if workspace is None:
+        n = int(L.msa_workspace_size_kvcache(ctypes.byref(shape), cref, OP_SPARSE_ATTN))
+        workspace = _aligned(n, dev)
+    st = L.msa_sparse_attn_fwd_kvcache(ctypes.byref(shape), cref, _ptr(q), _ptr(k), _ptr(v), _ptr(sel), _ptr(out),
+                                       _ptr(lse), _ptr(workspace), 0 if workspace is None else workspace.numel(),
+                                       _stream(dev))
+    _check(st)
+    return (out, lse) if return_lse else out
+
+
+def fwd_kvcache(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_idx: torch.Tensor, k_idx: torch.Tensor,
+                topk: int, seq_lens=None, page_table=None, kv_len: Optional[int] = None, q_offset: int = 0,
+                scale: Optional[float] = None, out_dtype: Optional[torch.dtype] = None, return_sel: bool = False,
+                return_lse: bool = False, k_scale: Optional[float] = None, v_scale: Optional[float] = None,
+                workspace: Optional[torch.Tensor] = None):
+    """fwd over caches of unequal length and/or in pages."""
+    _need(q, "q", 4)
+    dev = q.device
+    _need(q_idx, "q_idx", 4, dev, q.dtype)
+    for name, t, nd in (("k", k, 4), ("v", v, 4), ("k_idx", k_idx, 3)):
+        _need(t, name, nd, dev)
+    cf = _cache_format(q.dtype, [("k", k), ("v", v), ("k_idx", k_idx)])
+    B, S_q, Hq, d = q.shape
+    if tuple(v.shape) != tuple(k.shape) or k.shape[3] != d:
+        raise ValueError("k and v must match and end in d")
+    Hkv, S_k, P = _kv_geometry(k, k_idx, B, page_table, kv_len)
+    D = q_idx.shape[3]
+    if tuple(q_idx.shape) != (B, S_q, Hkv, D) or k_idx.shape[2] != D:
+        raise ValueError("q_idx must be [B, S_q, Hkv, D_idx] and k_idx end in D_idx")
+    cache, _ = _kv_cache(B, dev, seq_lens, page_table, P)
+    shape = make_shape(B, S_q, S_k, q_offset, Hq, Hkv, d, D, topk, q.dtype, out_dtype, scale,
+                       cache_format=cf, k_scale=k_scale, v_scale=v_scale)
+    out = torch.empty((B, S_q, Hq, d), dtype=out_dtype or q.dtype, device=dev)
+    sel = torch.empty((B, Hkv, S_q, topk), dtype=torch.int32, device=dev) if return_sel else None
+    lse = torch.empty((B, Hq, S_q), dtype=torch.float32, device=dev) if return_lse else None
+    L = lib()
+    cref = ctypes.byref(cache) if cache is not None else None
+    if workspace is None:
+        n = int(L.msa_workspace_size_kvcache(ctypes.byref(shape), cref, OP_FWD))
+        workspace = _aligned(n, dev)
+    st = L.msa_fwd_kvcache(ctypes.byref(shape), cref, _ptr(q), _ptr(k), _ptr(v), _ptr(q_idx), _ptr(k_idx),
+                           _ptr(out), _ptr(sel), _ptr(lse), _ptr(workspace),
+                           0 if workspace is None else workspace.numel(), _stream(dev))
     _check(st)
     res = [out]
     if return_sel:

@@ -232,10 +232,15 @@ __global__ __launch_bounds__(256, 2) void attn_kvouter_kernel(AttnParams p) {
       b = bg / p.G;
     }
 
+    // an unmapped page, or a block past the end of the cache: nothing to attend (uniform)
+    const int slen = cache_len(p.cm, p.S_k, b);
+    const int64_t kv0 = block_offset(p.cm, p.S_k, p.G, D, b, g, c);
+    if (kv0 < 0 || (int64_t)c * kBlock >= slen) continue;
+    const int64_t qo = first_pos(p.cm, p.q_offset, p.S_q, p.S_k, b);
+
     __syncthreads();  // the previous item is done with the LDS tiles
     {
-      const int64_t kv0 = (((int64_t)b * p.G + g) * p.S_k + (int64_t)c * kBlock) * D;
-      const int rows_ok = (int)min((int64_t)kBlock, (int64_t)p.S_k - (int64_t)c * kBlock);
+      const int rows_ok = (int)min((int64_t)kBlock, (int64_t)slen - (int64_t)c * kBlock);
       // Every load below is unconditional (rows past the cache end re-read its
       // last row and are zeroed afterwards), so all of them are in flight at once.
       constexpr int KCH = kBlock * D / E;
@@ -298,7 +303,7 @@ __global__ __launch_bounds__(256, 2) void attn_kvouter_kernel(AttnParams p) {
       const int32_t entry = in_list ? (toks ? toks[tslot] : direct_tok) : 0;
       const int i = entry >> 6, slot = entry & 63;
       // keys of this block visible to the row: index within block <= lim
-      const int64_t rel = p.q_offset + i - key0;  // query position relative to the block
+      const int64_t rel = qo + i - key0;  // query position relative to the block
       const bool rv = in_list && rel >= 0;        // a block after the query is skipped
       const int lim = (!rv || rel >= kBlock) ? kBlock : (int)rel;
       const int hh = l32 % R;
@@ -455,11 +460,13 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnParams p) {
     const int g = (int)(bg % p.G);
     const int b = (int)(bg / p.G);
     const int64_t key0 = (int64_t)c * kBlock;
-    const int64_t rel = p.q_offset + i - key0;
-    if (rel < 0) continue;  // a block after the query: nothing visible (uniform)
+    const int slen = cache_len(p.cm, p.S_k, b);
+    const int64_t rel = first_pos(p.cm, p.q_offset, p.S_q, p.S_k, b) + i - key0;
+    if (rel < 0 || key0 >= slen) continue;  // a block after the query: nothing visible (uniform)
+    const int64_t kv0 = block_offset(p.cm, p.S_k, p.G, D, b, g, c);
+    if (kv0 < 0) continue;  // an unmapped page is never read; the combine skips it too
     const int lim = rel >= kBlock ? kBlock : (int)rel;
-    const int rows_ok = (int)min((int64_t)kBlock, (int64_t)p.S_k - key0);
-    const int64_t kv0 = (((int64_t)b * p.G + g) * p.S_k + key0) * D;
+    const int rows_ok = (int)min((int64_t)kBlock, (int64_t)slen - key0);
 
     // loads: this wave's 32 K rows (A operand), the token's Q rows (B operand), and
     // this thread's share of V; all issued before any is used
@@ -600,7 +607,7 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnParams p) {
   const int i = (int)(bi % p.S_q);
   const int b = (int)(bi / p.S_q);
   const int hh = ch % R, h = (ch / R) & 1, q = ch / (2 * R);
-  const int64_t t = p.q_offset + i;
+  const int64_t t = first_pos(p.cm, p.q_offset, p.S_q, p.S_k, b) + i;
   const int32_t* srow = p.sel + (((int64_t)b * p.G + g) * p.S_q + i) * p.topk;
   const int64_t pbase = rowg * p.topk;
 
@@ -622,7 +629,8 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnParams p) {
       int c = -1;
       if (s2 < p.topk) {
         c = p.sel[(((int64_t)rb * p.G + rgg) * p.S_q + ri) * p.topk + s2];
-        if (!(c >= 0 && c < p.nb && (int64_t)c * kBlock <= p.q_offset + ri)) c = -1;
+        const int64_t rt = first_pos(p.cm, p.q_offset, p.S_q, p.S_k, rb) + ri;
+        if (!(c >= 0 && c < p.nb && (int64_t)c * kBlock <= rt && block_mapped(p.cm, rb, c))) c = -1;
       }
       sel_s[lr][s2] = c;
     }
@@ -656,7 +664,7 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnParams p) {
 #pragma unroll
     for (int s2 = 0; s2 < KMAX; ++s2) {
       const int c = cs[s2];
-      const bool used = s2 < p.topk && c >= 0 && c < p.nb && (int64_t)c * kBlock <= t;
+      const bool used = s2 < p.topk && c >= 0 && c < p.nb && (int64_t)c * kBlock <= t && block_mapped(p.cm, b, c);
       ls[s2] = used ? ls[s2] : kNegInf;
       mx = fmaxf(mx, ls[s2]);
     }
@@ -674,7 +682,9 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnParams p) {
 #pragma unroll
     for (int e = 0; e < E; ++e) acc[e] += used ? w * to_f32(xv[e]) : 0.f;
   }
-  const float inv = p.v_scale / W;  // the value cache's dequantisation scale (1 if none)
+  // the value cache's dequantisation scale (1 if none); a row that sees no key
+  // (it precedes its cache) gets zeros and lse = -inf
+  const float inv = W > 0.f ? p.v_scale / W : 0.f;
   const int r0 = (q * E) % 16, dt = (q * E) / 16;
   if constexpr (STAGED) {
     TO* srow_o = ostage + (int)(threadIdx.x / NCHT) * (R * D) + hh * D;

@@ -75,9 +75,13 @@ __device__ __forceinline__ void emit_row(const IndexParams& p, int b, int n, int
     }
     return;
   }
-  const int take = min(p.topk - 1, L);
   const int i = n / p.G, g = n - (n / p.G) * p.G;
   int32_t* out = p.sel + (((int64_t)b * p.G + g) * p.S_q + i) * p.topk;
+  if (L < 0) {  // a row before the start of its cache selects nothing
+    for (int j = 0; j < p.topk; ++j) out[j] = -1;
+    return;
+  }
+  const int take = min(p.topk - 1, L);
 #pragma unroll
   for (int j = 0; j < CAP; ++j) {
     if (j < take) {
@@ -126,7 +130,8 @@ __global__ __launch_bounds__(256, 2) void index_topk_kernel(IndexParams p) {
   const int tile = tg - b * p.ntile;
   const int n_first = tile * ROWS_WG;
   const int n_last = min(n_first + ROWS_WG, p.rows_per_b) - 1;
-  const int Lmax = (int)((p.q_offset + n_last / p.G) / kBlock);
+  const int64_t qo = first_pos(p.cm, p.q_offset, p.S_q, p.S_k, b);
+  const int Lmax = max(local_block(qo + n_last / p.G), 0);
   const int c_begin = split * p.chunk;
   const int c_end = min(c_begin + p.chunk, Lmax);
   const bool has_blocks = c_begin < c_end;
@@ -144,7 +149,7 @@ __global__ __launch_bounds__(256, 2) void index_topk_kernel(IndexParams p) {
     const int n = n_first + wave * ROWS_WAVE + rt * 32 + l32;
     rvalid[rt] = n < p.rows_per_b;
     const int nc = rvalid[rt] ? n : p.rows_per_b - 1;  // invalid rows read a valid row
-    rowL[rt] = (int)((p.q_offset + nc / p.G) / kBlock);
+    rowL[rt] = local_block(qo + nc / p.G);
     const T* qrow = (const T*)p.q_idx + ((int64_t)b * p.rows_per_b + nc) * DI;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) qf[rt][ks] = *(const frag*)(qrow + ks * KSTEP + h * KPL);
@@ -160,13 +165,14 @@ __global__ __launch_bounds__(256, 2) void index_topk_kernel(IndexParams p) {
       li[rt][j] = -1;
     }
 
-  const char* kbase = (const char*)p.k_idx + (int64_t)b * p.S_k * DI * (int64_t)sizeof(S);
+  const S* kpool = (const S*)p.k_idx;
   // K tiles are prefetched two blocks ahead: `pre` holds block c + 1 (stored to
   // LDS after block c is scored), `pre2` is in flight for block c + 2.  Native
   // vector types keep both in registers.
   i32x4 pre[CH_PER_THREAD], pre2[CH_PER_THREAD];
-  auto kblock = [&](int c) {
-    return (const i32x4*)(kbase + (int64_t)c * kBlock * DI * (int64_t)sizeof(S));
+  auto kblock = [&](int c) {  // an unmapped page is read from the pool start and scored -inf
+    const int64_t o = block_offset(p.cm, p.S_k, 1, DI, b, 0, c);
+    return (const i32x4*)(kpool + (o < 0 ? 0 : o));
   };
   // one staged chunk into the LDS tile: row-major, SE elements from column col
   auto stage = [&](T* tile, int ch, i32x4 x) {
@@ -228,6 +234,10 @@ __global__ __launch_bounds__(256, 2) void index_topk_kernel(IndexParams p) {
         for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
           for (int j = 0; j < 16; ++j) pm[rt] = fmaxf(pm[rt], acc[rt][j]);
+      }
+      if (!block_mapped(p.cm, b, c)) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) pm[rt] = kNegInf;
       }
     }
     if (has_next) {
@@ -333,7 +343,8 @@ __global__ __launch_bounds__(256, 2) void index_topk_small_kernel(IndexParams p)
   if (logical >= p.nunits) return;
   const int split = logical / p.B;
   const int b = logical - split * p.B;
-  const int Lmax = (int)((p.q_offset + (p.rows_per_b - 1) / p.G) / kBlock);
+  const int64_t qo = first_pos(p.cm, p.q_offset, p.S_q, p.S_k, b);
+  const int Lmax = max(local_block(qo + (p.rows_per_b - 1) / p.G), 0);
   const int c_begin = split * p.chunk;
   const int c_end = min(c_begin + p.chunk, Lmax);
   if (c_begin >= c_end && p.nsplit > 1) return;  // a single split still writes rows with L = 0
@@ -342,7 +353,7 @@ __global__ __launch_bounds__(256, 2) void index_topk_small_kernel(IndexParams p)
   const int h = lane >> 5, l32 = lane & 31;
   const bool rvalid = l32 < p.rows_per_b;
   const int nc = rvalid ? l32 : p.rows_per_b - 1;  // invalid rows read a valid row
-  const int rowL = (int)((p.q_offset + nc / p.G) / kBlock);
+  const int rowL = local_block(qo + nc / p.G);
   frag qf[NKS];
   {
     const T* qrow = (const T*)p.q_idx + ((int64_t)b * p.rows_per_b + nc) * DI;
@@ -360,12 +371,14 @@ __global__ __launch_bounds__(256, 2) void index_topk_small_kernel(IndexParams p)
   // this wave's blocks: c_begin + wave + 4 j for j < nbw, read as 4 nbw tiles of 32 keys
   const int nbw = c_end - c_begin > wave ? (c_end - c_begin - wave + 3) / 4 : 0;
   const int ntl = 4 * nbw;
-  const S* kb = (const S*)p.k_idx + (int64_t)b * p.S_k * DI;
-  // tile tl of the wave; tl past the end re-reads the last one (just read, so from L2)
+  const S* kpool = (const S*)p.k_idx;
+  // tile tl of the wave; tl past the end re-reads the last one (just read, so from
+  // L2); an unmapped page is read from the pool start and scored -inf
   auto load_tile = [&](kraw (&a)[NKR], int tl) {
     const int tc = min(tl, ntl - 1);
     const int c = c_begin + wave + 4 * (tc / 4);
-    const S* src = kb + ((int64_t)c * kBlock + (tc % 4) * 32 + l32) * DI;
+    const int64_t o = block_offset(p.cm, p.S_k, 1, DI, b, 0, c);
+    const S* src = kpool + (o < 0 ? 0 : o) + ((tc % 4) * 32 + l32) * DI;
 #pragma unroll
     for (int u = 0; u < NKR; ++u) a[u] = *(const kraw*)(src + koff(kNative ? u : 2 * u, h));
   };
@@ -394,8 +407,9 @@ __global__ __launch_bounds__(256, 2) void index_topk_small_kernel(IndexParams p)
     pm = fmaxf(pm, tile_max(a));
     if (tl % 4 != 3) return;  // the block continues in the next tile
     const int j = tl / 4;
-    const float full = fmaxf(pm, __shfl_xor(pm, 32));
+    float full = fmaxf(pm, __shfl_xor(pm, 32));
     pm = kNegInf;
+    if (!block_mapped(p.cm, b, c_begin + wave + 4 * j)) full = kNegInf;
     // blocks pair up: half 0 ranks the wave's even blocks, half 1 the odd ones
     const bool second = (j & 1) != 0;
     if (!second) pmA = full;
@@ -474,7 +488,12 @@ __global__ __launch_bounds__(256) void topk_merge_kernel(IndexParams p) {
   const int b = (int)(row / p.rows_per_b);
   const int n = (int)(row - (int64_t)b * p.rows_per_b);
   const int i = n / p.G, g = n - (n / p.G) * p.G;
-  const int L = (int)((p.q_offset + i) / kBlock);
+  const int L = local_block(first_pos(p.cm, p.q_offset, p.S_q, p.S_k, b) + i);
+  int32_t* out = p.sel + (((int64_t)b * p.G + g) * p.S_q + i) * p.topk;
+  if (L < 0) {  // a row before the start of its cache selects nothing
+    if (lane < p.topk) out[lane] = -1;
+    return;
+  }
   const int nl = L > 0 ? (L + p.chunk - 1) / p.chunk : 0;
   const int take = min(p.topk - 1, L);
 
@@ -528,7 +547,6 @@ __global__ __launch_bounds__(256) void topk_merge_kernel(IndexParams p) {
     const int w = __shfl(mywin, m);
     rank += (w < mywin) ? 1 : 0;
   }
-  int32_t* out = p.sel + (((int64_t)b * p.G + g) * p.S_q + i) * p.topk;
   if (lane < take) out[rank] = mywin;
   else if (lane == take) out[take] = L;
   else if (lane < p.topk) out[lane] = -1;

@@ -25,6 +25,46 @@ inline void timer_stop(const KernelTimer* t, int which, hipStream_t s) {
 
 enum { kKernIndexScore = 1, kKernTopkMerge = 2, kKernGather = 3, kKernAttention = 4, kKernCombine = 5 };
 
+// Where the caches (k, v, k_idx) of each sequence live.  Without a length
+// table every sequence holds S_k tokens and its query row 0 sits at q_offset;
+// with one, sequence b holds seq_lens[b] tokens (clamped to [0, S_k]) and its
+// query row i sits at seq_lens[b] - S_q + i.  Without a page table a cache is
+// a dense [B, H, S_k, W] tensor; with one it is a pool [num_pages, H, 128, W]
+// and logical block c of sequence b is page pages[b * max_pages + c].
+struct CacheMap {
+  const int32_t* seq_lens;  // [B] or null
+  const int32_t* pages;     // [B, max_pages] or null
+  int max_pages, num_pages;
+};
+
+__device__ __forceinline__ int cache_len(const CacheMap& m, int S_k, int b) {
+  return m.seq_lens ? min(max(m.seq_lens[b], 0), S_k) : S_k;
+}
+
+// Absolute position of query row 0 of sequence b (negative: leading rows see no key).
+__device__ __forceinline__ int64_t first_pos(const CacheMap& m, int64_t q_offset, int S_q, int S_k, int b) {
+  return m.seq_lens ? (int64_t)cache_len(m, S_k, b) - S_q : q_offset;
+}
+
+// Local block of position t; -1 for a row before the cache start.
+__device__ __forceinline__ int local_block(int64_t t) { return t >= 0 ? (int)(t / kBlock) : -1; }
+
+// Element offset of token 0 of logical block c, head hidx, of sequence b in a
+// cache of H heads and W elements per token; -1 when its page id is out of range.
+__device__ __forceinline__ int64_t block_offset(const CacheMap& m, int S_k, int H, int W, int b, int hidx, int c) {
+  if (!m.pages) return (((int64_t)b * H + hidx) * S_k + (int64_t)c * kBlock) * W;
+  const int pg = m.pages[(int64_t)b * m.max_pages + c];
+  if (pg < 0 || pg >= m.num_pages) return -1;
+  return (((int64_t)pg * H + hidx) * kBlock) * W;
+}
+
+// Whether block c of sequence b can be read (always, without a page table).
+__device__ __forceinline__ bool block_mapped(const CacheMap& m, int b, int c) {
+  if (!m.pages) return true;
+  const int pg = m.pages[(int64_t)b * m.max_pages + c];
+  return pg >= 0 && pg < m.num_pages;
+}
+
 // Index branch (index_topk.hip).
 struct IndexParams {
   const void* q_idx;   // [B, S_q, G, D]
@@ -32,6 +72,7 @@ struct IndexParams {
   float* part_s;       // [B*S_q*G, nsplit, CAP] partial top-list scores
   int32_t* part_i;     // same shape: block ids (-1 = empty)
   int32_t* sel;        // [B, G, S_q, topk]
+  CacheMap cm;
   int64_t q_offset;
   int B, S_q, S_k, G, topk;
   int rows_per_b;      // S_q * G
@@ -64,6 +105,7 @@ struct AttnParams {
   const int32_t* sel;  // [B, G, S_q, topk]
   void* out;           // [B, S_q, Hq, d]
   float* lse;          // [B, Hq, S_q] or null
+  CacheMap cm;
   // query gather (bucket = (b, g, c))
   int32_t* counts;     // [nbuckets]
   int32_t* offsets;    // [nbuckets + 1]

@@ -105,6 +105,43 @@ msa_status check_shape(const msa_shape* s, int op) {
   return MSA_OK;
 }
 
+// ---- caches ---------------------------------------------------------------
+
+msa_status check_cache(const msa_shape* s, const msa_kv_cache* c) {
+  if (!c) return MSA_OK;
+  if (c->seq_lens && s->q_offset != 0)
+    return fail(MSA_ERR_INVALID, "q_offset must be 0 when seq_lens is given (positions come from the lengths)");
+  if (c->page_table) {
+    if (c->max_pages < 1 || c->num_pages < 1)
+      return fail(MSA_ERR_INVALID, "max_pages and num_pages must be >= 1 with a page table");
+    if ((int64_t)s->kv_len > (int64_t)c->max_pages * msa::kBlock)
+      return fail(MSA_ERR_INVALID, "kv_len (%d) exceeds max_pages * 128 (%lld)", s->kv_len,
+                  (long long)c->max_pages * msa::kBlock);
+    if ((int64_t)s->batch * c->max_pages >= (1LL << 31))
+      return fail(MSA_ERR_UNSUPPORTED, "batch * max_pages exceeds 2^31");
+  }
+  return MSA_OK;
+}
+
+msa::CacheMap cache_map(const msa_kv_cache* c) {
+  msa::CacheMap m{};
+  if (c) {
+    m.seq_lens = c->seq_lens;
+    m.pages = c->page_table;
+    if (c->page_table) {
+      m.max_pages = c->max_pages;
+      m.num_pages = c->num_pages;
+    }
+  }
+  return m;
+}
+
+// The largest position a query row can have: the bound the launch plans use.
+int64_t max_pos(const msa_shape* s, const msa_kv_cache* c) {
+  if (c && c->seq_lens) return (int64_t)s->kv_len - 1;
+  return s->q_offset + s->q_len - 1;
+}
+
 // ---- index plan -----------------------------------------------------------
 
 struct IndexPlan {
@@ -113,9 +150,10 @@ struct IndexPlan {
   size_t bytes;  // workspace for the partial lists
 };
 
-IndexPlan plan_index(const msa_shape* s) {
+IndexPlan plan_index(const msa_shape* s, const msa_kv_cache* cache) {
   IndexPlan ip{};
   msa::IndexParams& p = ip.p;
+  p.cm = cache_map(cache);
   p.B = s->batch;
   p.S_q = s->q_len;
   p.S_k = s->kv_len;
@@ -126,7 +164,7 @@ IndexPlan plan_index(const msa_shape* s) {
   p.small = p.rows_per_b <= msa::kIndexSmallRows && s->dtype == MSA_BF16 ? 1 : 0;
   p.ntile = p.small ? 1 : (int)ceil_div(p.rows_per_b, msa::index_rows_per_wg(s->topk));
   p.ntile_total = p.B * p.ntile;
-  const int64_t Lmax = s->q_len > 0 ? (s->q_offset + s->q_len - 1) / msa::kBlock : 0;
+  const int64_t Lmax = s->q_len > 0 ? max_pos(s, cache) / msa::kBlock : 0;
   // Enough row tiles to fill the GPU: one unit per tile, no merge.  Otherwise
   // split the key blocks so that about kIndexTargetUnits units exist (at least
   // 16 blocks per unit, 8 in the few-row form where 4 waves share a unit's
@@ -164,9 +202,10 @@ struct AttnPlan {
   size_t bytes;
 };
 
-AttnPlan plan_attn(const msa_shape* s) {
+AttnPlan plan_attn(const msa_shape* s, const msa_kv_cache* cache) {
   AttnPlan ap{};
   msa::AttnParams& p = ap.p;
+  p.cm = cache_map(cache);
   p.B = s->batch;
   p.S_q = s->q_len;
   p.S_k = s->kv_len;
@@ -179,7 +218,7 @@ AttnPlan plan_attn(const msa_shape* s) {
   p.nb = (int)ceil_div(s->kv_len, msa::kBlock);
   p.nbuckets = p.B * p.G * p.nb;
   p.tpi = kTokensPerItem;
-  const int64_t Lmax = s->q_len > 0 ? (s->q_offset + s->q_len - 1) / msa::kBlock : 0;
+  const int64_t Lmax = s->q_len > 0 ? max_pos(s, cache) / msa::kBlock : 0;
   // queries per (b, g, block) on average; below 2 the gather buys nothing
   const double per_bucket = (double)s->q_len * std::min<int64_t>(s->topk, Lmax + 1) / (double)(Lmax + 1);
   p.direct = per_bucket < 2.0 ? 1 : 0;
@@ -284,25 +323,28 @@ const char* msa_status_string(msa_status st) {
 
 const char* msa_last_error(void) { return g_last_error.c_str(); }
 
-size_t msa_workspace_size(const msa_shape* s, int op) {
+size_t msa_workspace_size_kvcache(const msa_shape* s, const msa_kv_cache* cache, int op) {
   const std::string saved = g_last_error;
   size_t r = 0;
-  if (op >= MSA_OP_INDEX_SELECT && op <= MSA_OP_FWD && check_shape(s, op) == MSA_OK && s->q_len > 0) {
-    if (op == MSA_OP_INDEX_SELECT) r = plan_index(s).bytes;
-    else if (op == MSA_OP_SPARSE_ATTN) r = plan_attn(s).bytes;
-    else r = sel_bytes(s) + std::max(plan_index(s).bytes, plan_attn(s).bytes);
+  if (op >= MSA_OP_INDEX_SELECT && op <= MSA_OP_FWD && check_shape(s, op) == MSA_OK &&
+      check_cache(s, cache) == MSA_OK && s->q_len > 0) {
+    if (op == MSA_OP_INDEX_SELECT) r = plan_index(s, cache).bytes;
+    else if (op == MSA_OP_SPARSE_ATTN) r = plan_attn(s, cache).bytes;
+    else r = sel_bytes(s) + std::max(plan_index(s, cache).bytes, plan_attn(s, cache).bytes);
   }
   g_last_error = saved;
   return r;
 }
 
-msa_status msa_index_select(const msa_shape* s, const void* q_idx, const void* k_idx, int32_t* sel, void* ws,
-                            size_t ws_bytes, void* stream) {
+size_t msa_workspace_size(const msa_shape* s, int op) { return msa_workspace_size_kvcache(s, nullptr, op); }
+
+msa_status msa_index_select_kvcache(const msa_shape* s, const msa_kv_cache* cache, const void* q_idx,
+                                    const void* k_idx, int32_t* sel, void* ws, size_t ws_bytes, void* stream) {
   msa_status st = check_shape(s, MSA_OP_INDEX_SELECT);
-  if (st != MSA_OK) return st;
+  if (st != MSA_OK || (st = check_cache(s, cache)) != MSA_OK) return st;
   if (!q_idx || !k_idx || !sel) return fail(MSA_ERR_INVALID, "q_idx, k_idx and sel must be non-NULL");
   if (s->q_len == 0) return MSA_OK;
-  IndexPlan ip = plan_index(s);
+  IndexPlan ip = plan_index(s, cache);
   if ((st = check_ws(ws, ws_bytes, ip.bytes)) != MSA_OK) return st;
   bind_index(ip, (char*)ws, q_idx, k_idx, sel);
   clear_stale_hip_error();
@@ -311,14 +353,19 @@ msa_status msa_index_select(const msa_shape* s, const void* q_idx, const void* k
                     "index select launch");
 }
 
-msa_status msa_sparse_attn_fwd(const msa_shape* s, const void* q, const void* k, const void* v,
-                               const int32_t* sel, void* out, float* lse, void* ws, size_t ws_bytes,
-                               void* stream) {
+msa_status msa_index_select(const msa_shape* s, const void* q_idx, const void* k_idx, int32_t* sel, void* ws,
+                            size_t ws_bytes, void* stream) {
+  return msa_index_select_kvcache(s, nullptr, q_idx, k_idx, sel, ws, ws_bytes, stream);
+}
+
+msa_status msa_sparse_attn_fwd_kvcache(const msa_shape* s, const msa_kv_cache* cache, const void* q, const void* k,
+                                       const void* v, const int32_t* sel, void* out, float* lse, void* ws,
+                                       size_t ws_bytes, void* stream) {
   msa_status st = check_shape(s, MSA_OP_SPARSE_ATTN);
-  if (st != MSA_OK) return st;
+  if (st != MSA_OK || (st = check_cache(s, cache)) != MSA_OK) return st;
   if (!q || !k || !v || !sel || !out) return fail(MSA_ERR_INVALID, "q, k, v, sel and out must be non-NULL");
   if (s->q_len == 0) return MSA_OK;
-  AttnPlan ap = plan_attn(s);
+  AttnPlan ap = plan_attn(s, cache);
   if ((st = check_ws(ws, ws_bytes, ap.bytes)) != MSA_OK) return st;
   bind_attn(ap, (char*)ws);
   ap.p.q = q;
@@ -333,16 +380,21 @@ msa_status msa_sparse_attn_fwd(const msa_shape* s, const void* q, const void* k,
                     "sparse attention launch");
 }
 
-msa_status msa_fwd(const msa_shape* s, const void* q, const void* k, const void* v, const void* q_idx,
-                   const void* k_idx, void* out, int32_t* sel_out, float* lse, void* ws, size_t ws_bytes,
-                   void* stream) {
+msa_status msa_sparse_attn_fwd(const msa_shape* s, const void* q, const void* k, const void* v, const int32_t* sel,
+                               void* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  return msa_sparse_attn_fwd_kvcache(s, nullptr, q, k, v, sel, out, lse, ws, ws_bytes, stream);
+}
+
+msa_status msa_fwd_kvcache(const msa_shape* s, const msa_kv_cache* cache, const void* q, const void* k,
+                           const void* v, const void* q_idx, const void* k_idx, void* out, int32_t* sel_out,
+                           float* lse, void* ws, size_t ws_bytes, void* stream) {
   msa_status st = check_shape(s, MSA_OP_FWD);
-  if (st != MSA_OK) return st;
+  if (st != MSA_OK || (st = check_cache(s, cache)) != MSA_OK) return st;
   if (!q || !k || !v || !q_idx || !k_idx || !out)
     return fail(MSA_ERR_INVALID, "q, k, v, q_idx, k_idx and out must be non-NULL");
   if (s->q_len == 0) return MSA_OK;
-  IndexPlan ip = plan_index(s);
-  AttnPlan ap = plan_attn(s);
+  IndexPlan ip = plan_index(s, cache);
+  AttnPlan ap = plan_attn(s, cache);
   const size_t need = sel_bytes(s) + std::max(ip.bytes, ap.bytes);
   if ((st = check_ws(ws, ws_bytes, need)) != MSA_OK) return st;
   char* w = (char*)ws;
@@ -363,6 +415,12 @@ msa_status msa_fwd(const msa_shape* s, const void* q, const void* k, const void*
   ap.p.lse = lse;
   return hip_status(msa::launch_sparse_attention(ap.p, s->dtype == MSA_BF16, fp8_cache(s), hs, timer()),
                     "sparse attention launch");
+}
+
+msa_status msa_fwd(const msa_shape* s, const void* q, const void* k, const void* v, const void* q_idx,
+                   const void* k_idx, void* out, int32_t* sel_out, float* lse, void* ws, size_t ws_bytes,
+                   void* stream) {
+  return msa_fwd_kvcache(s, nullptr, q, k, v, q_idx, k_idx, out, sel_out, lse, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

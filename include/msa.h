@@ -143,6 +143,53 @@ msa_status msa_fwd(const msa_shape* shape, const void* q, const void* k, const v
                    const void* q_idx, const void* k_idx, void* out, int32_t* sel_out,
                    float* lse, void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- Caches of unequal length, optionally paged -------------------------
+ *
+ * Serving batches hold KV caches that grow and differ in length (snilld.dk
+ * page, sections "POC målinger og miljø" and "Implementering i produktion":
+ * batches of 1-4 sequences at 4k-128k contexts, growing KV caches in long
+ * conversations).  The *_kvcache calls take the same shape plus this
+ * descriptor:
+ *
+ *  - seq_lens (device int32 [B], or NULL): sequence b holds seq_lens[b] tokens
+ *    (values are clamped to [0, kv_len]) and its query row i sits at
+ *    t = seq_lens[b] - q_len + i; shape->q_offset must then be 0.  Rows with
+ *    t < 0 precede their cache: their selection is all -1, their output 0 and
+ *    their lse -inf.  NULL: every sequence holds kv_len tokens and row i sits
+ *    at q_offset + i, as in the plain calls.
+ *  - page_table (device int32 [B, max_pages], or NULL): the caches are pools of
+ *    128-token pages, k and v [num_pages, Hkv, 128, d] and k_idx
+ *    [num_pages, 128, D_idx]; logical block c (tokens [128c, 128c + 128)) of
+ *    sequence b is page page_table[b * max_pages + c].  kv_len, the longest
+ *    cache, must be <= max_pages * 128.  Page ids outside [0, num_pages) are
+ *    never read: such a block is neither ranked nor attended.  NULL: the caches
+ *    are dense, k and v [B, Hkv, kv_len, d] and k_idx [B, kv_len, D_idx].
+ *
+ * Selections hold logical block ids.  Everything else (dtypes, FP8 caches,
+ * scales, workspace rules, errors) is as for the plain calls, which are the
+ * *_kvcache calls with cache == NULL. */
+typedef struct {
+  const int32_t* seq_lens;   /* [B] device, or NULL                               */
+  const int32_t* page_table; /* [B, max_pages] device, or NULL                    */
+  int32_t max_pages;         /* columns of page_table (ignored without one)       */
+  int32_t num_pages;         /* pages in each pool (ignored without a page table) */
+} msa_kv_cache;
+
+/* Workspace for the *_kvcache calls (it depends on whether lengths are given). */
+size_t msa_workspace_size_kvcache(const msa_shape* shape, const msa_kv_cache* cache, int op);
+
+msa_status msa_index_select_kvcache(const msa_shape* shape, const msa_kv_cache* cache, const void* q_idx,
+                                    const void* k_idx, int32_t* sel, void* workspace, size_t workspace_bytes,
+                                    void* stream);
+
+msa_status msa_sparse_attn_fwd_kvcache(const msa_shape* shape, const msa_kv_cache* cache, const void* q,
+                                       const void* k, const void* v, const int32_t* sel, void* out, float* lse,
+                                       void* workspace, size_t workspace_bytes, void* stream);
+
+msa_status msa_fwd_kvcache(const msa_shape* shape, const msa_kv_cache* cache, const void* q, const void* k,
+                           const void* v, const void* q_idx, const void* k_idx, void* out, int32_t* sel_out,
+                           float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Kernels of the forward path, for msa_set_kernel_timer. */
 typedef enum {
   MSA_KERNEL_NONE = 0,

@@ -49,6 +49,14 @@ per-tensor dequantisation scales for k and v.  ``e4m3_to_f64`` decodes such
 bytes exactly from the OCP 8-bit floating point specification (OFP8, E4M3
 encoding) and ``dequantize_e4m3`` applies a scale; the attention itself is the
 same definition applied to the decoded values.
+
+Caches of unequal length.  Serving batches hold caches that differ in length
+and grow (the snilld.dk page, sections "POC målinger og miljø" and
+"Implementering i produktion").  ``msa_forward_varlen`` applies the same
+definition per sequence, with the queries at the last S_q positions of each
+cache; a row before the start of its cache (t < 0) sees no key, and the reading
+taken is: no selection (-1 only), output 0, lse -inf.  ``page_gather`` reads a
+sequence's cache out of a pool of 128-token pages.
 """
 from __future__ import annotations
 
@@ -58,6 +66,8 @@ from typing import Iterable, Optional, Sequence, Tuple
 import numpy as np
 
 __all__ = [
+    "page_gather",
+    "msa_forward_varlen",
     "e4m3_to_f64",
     "dequantize_e4m3",
     "block_maxima",
@@ -273,3 +283,57 @@ def dense_causal_attention(q, k, v, q_offset: int = 0, scale: Optional[float] = 
                 out[b, i, g * r:(g + 1) * r] = o
                 lse[b, g * r:(g + 1) * r, i] = ls
     return out, lse
+
+
+# ---------------------------------------------------------------------------
+# Caches of unequal length, paged caches
+# ---------------------------------------------------------------------------
+
+def page_gather(pool, pages, n_tokens: int, block_size: int = 128) -> np.ndarray:
+    """The first n_tokens tokens of one sequence's cache, read out of a page pool.
+
+    pool:  [P, H, Bk, W] (keys or values) or [P, Bk, W] (index keys)
+    pages: the sequence's page ids; logical block c (tokens [c*Bk, (c+1)*Bk)) is
+           page pages[c]
+    returns [H, n_tokens, W] or [n_tokens, W]
+    """
+    pool = np.asarray(pool)
+    nb = -(-int(n_tokens) // block_size)
+    axis = 1 if pool.ndim == 4 else 0
+    if nb == 0:
+        shape = list(pool.shape[1:])
+        shape[axis] = 0
+        return np.zeros(shape, dtype=pool.dtype)
+    full = np.concatenate([pool[int(pages[c])] for c in range(nb)], axis=axis)
+    return full[:, :n_tokens] if axis == 1 else full[:n_tokens]
+
+
+def msa_forward_varlen(q, k_seqs, v_seqs, q_idx, k_idx_seqs, topk: int, block_size: int = 128,
+                       scale: Optional[float] = None):
+    """MSA forward over a batch of caches of unequal length.
+
+    q: [B, S_q, Hq, d]; q_idx: [B, S_q, G, D_idx]; for each sequence b,
+    k_seqs[b] and v_seqs[b] are [G, n_b, d] and k_idx_seqs[b] is [n_b, D_idx]:
+    its n_b cached tokens.  Query row i of sequence b sits at t = n_b - S_q + i.
+    Rows with t < 0 precede their cache: selection all -1, output 0, lse -inf.
+    Returns (out [B, S_q, Hq, d], sel [B, G, S_q, topk], lse [B, Hq, S_q]).
+    """
+    q = np.asarray(q)
+    q_idx = np.asarray(q_idx)
+    B, S_q, Hq, d = q.shape
+    G = q_idx.shape[2]
+    out = np.zeros((B, S_q, Hq, d))
+    sel = np.full((B, G, S_q, topk), -1, dtype=np.int32)
+    lse = np.full((B, Hq, S_q), -np.inf)
+    for b in range(B):
+        n = int(np.asarray(k_idx_seqs[b]).shape[0])
+        i0 = max(0, S_q - n)  # the first row at a position >= 0
+        if i0 >= S_q:
+            continue
+        o, sl, ls = msa_forward(q[b:b + 1, i0:], np.asarray(k_seqs[b])[None], np.asarray(v_seqs[b])[None],
+                                q_idx[b:b + 1, i0:], np.asarray(k_idx_seqs[b])[None], topk,
+                                n - S_q + i0, block_size, scale)
+        out[b, i0:] = o[0]
+        sel[b, :, i0:] = sl[0]
+        lse[b, :, i0:] = ls[0]
+    return out, sel, lse

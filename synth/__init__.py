@@ -101,7 +101,14 @@ WORKLOADS: Dict[int, Shape] = {
     5: Shape(1, 4096, 1048576, 1044480, 64, 4, 128, 128, 16),
     # the decode workload with its caches in FP8 (scales ~ 6 sigma / 448)
     6: Shape(64, 1, 131072, 131071, 64, 4, 128, 128, 16, cache="fp8", k_scale=6.0 / 448, v_scale=5.5 / 448),
+    # decode over 64 caches of unequal length in a shuffled page pool (PAGED below);
+    # kv_len is the longest possible cache, positions come from the lengths
+    7: Shape(64, 1, 131072, 0, 64, 4, 128, 128, 16),
 }
+
+# Paged workloads: cache lengths log-uniform over [lo, hi] (seeded by the
+# workload id), pages shuffled in a pool with `spare` pages of no sequence.
+PAGED = {7: dict(lo=4096, hi=131072, spare=64)}
 
 WORKLOAD_NAMES = {
     1: "prefill_1k_fp32",
@@ -110,6 +117,7 @@ WORKLOAD_NAMES = {
     4: "decode_128k_b64_bf16",
     5: "chunked_prefill_1m_q4096_bf16",
     6: "decode_128k_b64_fp8",
+    7: "decode_paged_varlen_b64_bf16",
 }
 
 
@@ -160,10 +168,11 @@ def _device_seed(workload: int, tensor: str, b: int) -> int:
     return int(ss.generate_state(1, dtype=np.uint64)[0] & ((1 << 63) - 1))
 
 
-def device_inputs(s: Shape, workload: int, device="cuda") -> Dict[str, torch.Tensor]:
-    """All five inputs generated on the device (Philox), per sequence."""
+def device_inputs(s: Shape, workload: int, device="cuda", names=("q", "k", "v", "q_idx", "k_idx")
+                  ) -> Dict[str, torch.Tensor]:
+    """The inputs (all five by default) generated on the device (Philox), per sequence."""
     out = {}
-    for name in ("q", "k", "v", "q_idx", "k_idx"):
+    for name in names:
         shp = _per_seq_shape(s, name)
         t = torch.empty((s.batch,) + shp, dtype=s.tensor_dtype(name), device=device)
         for b in range(s.batch):
@@ -215,6 +224,96 @@ def as_f64(t) -> np.ndarray:
             t = t.float()
         return t.numpy().astype(np.float64)
     return np.asarray(t, dtype=np.float64)
+
+
+# ---- caches of unequal length, paged caches ---------------------------------
+
+POOL_MARK = 0x504F4F4C  # "POOL": seed word of a whole page pool
+
+
+def varlen_lengths(batch: int, lo: int, hi: int, seed: int) -> np.ndarray:
+    """Seeded cache lengths, log-uniform over [lo, hi] (int32 [batch])."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([SEED_ROOT, 0x4C454E, seed])))
+    x = np.exp(rng.uniform(np.log(lo), np.log(hi + 1), size=batch)).astype(np.int64)
+    return np.clip(x, lo, hi).astype(np.int32)
+
+
+def page_table_for(seq_lens, max_pages: int, spare: int = 0, seed: int = 0, block_size: int = 128):
+    """A shuffled page pool: the logical blocks of every sequence get distinct
+    pages in random order; entries past a sequence's blocks are -1.  ``spare``
+    pages belong to no sequence.  Returns (table int32 [B, max_pages], num_pages)."""
+    need = [-(-int(n) // block_size) for n in seq_lens]
+    if max(need, default=0) > max_pages:
+        raise ValueError("a sequence needs more than max_pages pages")
+    P = sum(need) + spare
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([SEED_ROOT, 0x504147, seed])))
+    perm = rng.permutation(P).astype(np.int32)
+    table = np.full((len(need), max_pages), -1, dtype=np.int32)
+    o = 0
+    for b, nb in enumerate(need):
+        table[b, :nb] = perm[o:o + nb]
+        o += nb
+    return table, P
+
+
+def _pool_shape(s: Shape, tensor: str, num_pages: int):
+    if tensor in ("k", "v"):
+        return (num_pages, s.num_kv_heads, s.block_size, s.head_dim)
+    return (num_pages, s.block_size, s.index_dim)
+
+
+def paged_inputs(s: Shape, num_pages: int, workload: int = 0, device: Optional[str] = None) -> Dict[str, torch.Tensor]:
+    """q and q_idx per sequence as in host_inputs; k, v [P, Hkv, 128, d] and
+    k_idx [P, 128, D_idx] page pools, each drawn whole from one generator seeded
+    by (workload, tensor, POOL_MARK), with the value recipes of the dense caches.
+    On the host (PCG64) without a device, on the device (Philox) with one."""
+    out = {}
+    for name in ("q", "q_idx"):
+        if device is None:
+            out[name] = torch.stack([_host_draw(s, workload, name, b) for b in range(s.batch)])
+        else:
+            out[name] = device_inputs_one(s, workload, name, device)
+    for name in ("k", "v", "k_idx"):
+        shp = _pool_shape(s, name, num_pages)
+        ss = np.random.SeedSequence([SEED_ROOT, workload, TENSOR_IDS[name], POOL_MARK])
+        if device is None:
+            rng = np.random.Generator(np.random.PCG64(ss))
+            if name == "k_idx":
+                x = rng.integers(s.idx_lo, s.idx_hi + 1, size=shp, dtype=np.int32).astype(np.float32)
+            else:
+                x = rng.standard_normal(size=shp, dtype=np.float32)
+            out[name] = _to_storage(s, name, torch.from_numpy(x))
+        else:
+            g = torch.Generator(device=device)
+            g.manual_seed(int(ss.generate_state(1, dtype=np.uint64)[0] & ((1 << 63) - 1)))
+            t = torch.empty(shp, dtype=s.tensor_dtype(name), device=device)
+            flat = t.view(-1)
+            step = 1 << 28
+            for o in range(0, flat.numel(), step):
+                m = min(step, flat.numel() - o)
+                if name == "k_idx":
+                    x = torch.randint(s.idx_lo, s.idx_hi + 1, (m,), generator=g, device=device,
+                                      dtype=torch.int32).float()
+                else:
+                    x = torch.randn(m, generator=g, device=device, dtype=torch.float32)
+                flat[o:o + m].copy_(_to_storage(s, name, x))
+            out[name] = t
+    return out
+
+
+def paged_workload(workload: int, device: Optional[str] = None):
+    """Inputs of a paged workload: (inputs, seq_lens int32 [B], page_table int32
+    [B, kv_len / 128], num_pages)."""
+    s = WORKLOADS[workload]
+    cfg = PAGED[workload]
+    lens = varlen_lengths(s.batch, cfg["lo"], cfg["hi"], seed=workload)
+    table, P = page_table_for(lens, s.kv_len // s.block_size, cfg["spare"], seed=workload)
+    return paged_inputs(s, P, workload, device), lens, table, P
+
+
+def device_inputs_one(s: Shape, workload: int, name: str, device) -> torch.Tensor:
+    """One per-sequence input (q or q_idx) drawn on the device as in device_inputs."""
+    return device_inputs(s, workload, device, names=(name,))[name]
 
 
 def codes(t: torch.Tensor) -> np.ndarray:

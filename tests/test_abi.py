@@ -160,3 +160,29 @@ def test_python_cache_format_rules():
         msa._cache_format(bf, [("k", t(f8)), ("v", t(bf))])
     with pytest.raises(ValueError):  # fp8 next to fp32 queries
         msa._cache_format(torch.float32, [("k", t(f8)), ("v", t(f8))])
+
+
+def test_kvcache_descriptor_checks():
+    L = msa.lib()
+    sh = _shape(4)  # the 128K decode shape: q_offset 131071
+    c = msa.MsaKvCache()
+    c.seq_lens = 0x2000  # never dereferenced: validation fails or nothing is launched
+    args = lambda cache: (ctypes.byref(sh), ctypes.byref(cache), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None,
+                          None, 0, None)
+    assert L.msa_fwd_kvcache(*args(c)) == -1  # lengths given but q_offset != 0
+    assert "q_offset" in L.msa_last_error().decode()
+    sh.q_offset = 0
+    c.page_table = 0x3000
+    c.max_pages, c.num_pages = 0, 10
+    assert L.msa_fwd_kvcache(*args(c)) == -1  # a page table needs max_pages >= 1
+    c.max_pages = 1023  # 1023 * 128 < kv_len 131072
+    assert L.msa_fwd_kvcache(*args(c)) == -1
+    assert "max_pages" in L.msa_last_error().decode()
+    c.max_pages = 1024
+    assert L.msa_fwd_kvcache(*args(c)) == -3  # valid: now only the workspace is missing
+    # with lengths, the plan bounds positions by kv_len, not by q_offset + q_len
+    # (q_offset 0 and one query row: without lengths there is no block to rank)
+    need_var = L.msa_workspace_size_kvcache(ctypes.byref(sh), ctypes.byref(c), msa.OP_INDEX_SELECT)
+    need_fixed = L.msa_workspace_size_kvcache(ctypes.byref(sh), None, msa.OP_INDEX_SELECT)
+    assert need_var > 0 and need_fixed == 0
+    assert L.msa_workspace_size_kvcache(ctypes.byref(sh), None, msa.OP_FWD) == msa.workspace_size(sh, msa.OP_FWD)

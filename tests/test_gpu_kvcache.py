@@ -1,0 +1,196 @@
+"""GPU parity for caches of unequal length and paged caches (the *_kvcache calls).
+
+Each sequence's cache is read back on the host (dense slices, or
+oracle.page_gather over the page pool) and the oracle runs msa_forward_varlen on
+it.  Selections must match bit for bit, outputs within the bf16 tolerance
+(max-abs 2e-2), lse within 1e-3; rows that precede their cache must give -1
+selections, zero output and lse = -inf.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import msa_oracle as orc
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-2
+
+
+def _msa():
+    import block_sparse_attention_idx_amd as msa
+    msa.lib()
+    return msa
+
+
+def _f64(s: synth.Shape, name: str, t: torch.Tensor) -> np.ndarray:
+    if s.fp8 and name in ("k", "v", "k_idx"):
+        scale = {"k": s.k_scale, "v": s.v_scale, "k_idx": 1.0}[name]
+        return orc.dequantize_e4m3(synth.codes(t), scale)
+    return synth.as_f64(t)
+
+
+def _compare(out, sel, lse, ref_out, ref_sel, ref_lse):
+    sg = sel.cpu().numpy()
+    bad = np.argwhere((sg != ref_sel).any(axis=-1))
+    assert bad.size == 0, f"{len(bad)} selection rows differ, first {bad[:5].tolist()}"
+    og = out.float().cpu().numpy()
+    err = float(np.abs(og - ref_out).max())
+    assert err <= TOL, err
+    lg = lse.cpu().numpy()
+    assert np.array_equal(np.isneginf(lg), np.isneginf(ref_lse))
+    fin = np.isfinite(ref_lse)
+    assert float(np.abs(lg[fin] - ref_lse[fin]).max(initial=0.0)) <= 1e-3
+
+
+def _scales(s):
+    return dict(k_scale=s.k_scale, v_scale=s.v_scale) if s.fp8 else {}
+
+
+DENSE_CASES = [
+    # (lens, S_q, Hq, Hkv, d, D, k, cache)
+    ([1, 700, 2999, 3000, 1500], 1, 64, 4, 128, 128, 16, "native"),     # decode
+    ([2, 130, 2048, 3000], 4, 32, 4, 128, 64, 8, "native"),             # speculative rows; one precedes its cache
+    ([1, 700, 2999, 3000, 1500], 1, 64, 4, 128, 128, 32, "fp8"),
+]
+
+
+@pytest.mark.parametrize("case", DENSE_CASES, ids=lambda c: f"{c[0]}-{c[1]}-{c[6]}-{c[7]}")
+def test_dense_varlen(case):
+    msa = _msa()
+    lens, S_q, Hq, Hkv, d, D, k, cache = case
+    alloc = max(lens) + 17
+    s = synth.Shape(len(lens), S_q, alloc, 0, Hq, Hkv, d, D, k, cache=cache,
+                    k_scale=0.03 if cache == "fp8" else 1.0, v_scale=0.02 if cache == "fp8" else 1.0)
+    print(f"dense varlen {case}", flush=True)
+    xh = synth.host_inputs(s, 41 + k)
+    x = {n: t.cuda() for n, t in xh.items()}
+    sl = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    out, sel, lse = msa.fwd_kvcache(x["q"], x["k"], x["v"], x["q_idx"], x["k_idx"], k, seq_lens=sl,
+                                    return_sel=True, return_lse=True, **_scales(s))
+    torch.cuda.synchronize()
+    f = {n: _f64(s, n, t) for n, t in xh.items()}
+    ks = [f["k"][b, :, :n] for b, n in enumerate(lens)]
+    vs = [f["v"][b, :, :n] for b, n in enumerate(lens)]
+    kis = [f["k_idx"][b, :n] for b, n in enumerate(lens)]
+    ref = orc.msa_forward_varlen(f["q"], ks, vs, f["q_idx"], kis, k)
+    _compare(out, sel, lse, *ref)
+
+
+PAGED_CASES = [
+    # (lens, S_q, Hq, Hkv, d, D, k, cache, spare)
+    ([130, 4000, 1, 2048, 5000, 777], 1, 64, 4, 128, 128, 16, "native", 7),
+    ([130, 4000, 1, 2048, 5000, 777], 1, 64, 4, 128, 128, 16, "fp8", 3),
+    ([4096, 129, 3000, 5120], 2, 16, 2, 64, 32, 8, "native", 0),
+    ([5000, 333, 4097], 1, 32, 4, 128, 128, 32, "native", 11),
+    ([1000, 2600], 300, 32, 2, 128, 128, 8, "native", 5),    # a chunk of 300 rows: the gathered path
+    ([2600, 1800, 700], 200, 16, 4, 128, 64, 12, "fp8", 2),
+]
+
+
+def _paged(case, seed):
+    lens, S_q, Hq, Hkv, d, D, k, cache, spare = case
+    max_pages = -(-max(lens) // 128) + 2
+    s = synth.Shape(len(lens), S_q, max_pages * 128, 0, Hq, Hkv, d, D, k, cache=cache,
+                    k_scale=0.04 if cache == "fp8" else 1.0, v_scale=0.03 if cache == "fp8" else 1.0)
+    table, P = synth.page_table_for(lens, max_pages, spare, seed)
+    xh = synth.paged_inputs(s, P, seed)
+    return s, table, P, xh
+
+
+def _paged_oracle(s, lens, table, xh):
+    f = {n: _f64(s, n, t) for n, t in xh.items()}
+    ks = [orc.page_gather(f["k"], table[b], n) for b, n in enumerate(lens)]
+    vs = [orc.page_gather(f["v"], table[b], n) for b, n in enumerate(lens)]
+    kis = [orc.page_gather(f["k_idx"], table[b], n) for b, n in enumerate(lens)]
+    return orc.msa_forward_varlen(f["q"], ks, vs, f["q_idx"], kis, s.topk)
+
+
+@pytest.mark.parametrize("case", PAGED_CASES, ids=lambda c: f"{len(c[0])}seq-{c[1]}-{c[6]}-{c[7]}")
+def test_paged(case):
+    msa = _msa()
+    lens = case[0]
+    print(f"paged {case}", flush=True)
+    s, table, P, xh = _paged(case, 60 + case[1] + case[6])
+    x = {n: t.cuda() for n, t in xh.items()}
+    sl = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    pt = torch.from_numpy(table).cuda()
+    out, sel, lse = msa.fwd_kvcache(x["q"], x["k"], x["v"], x["q_idx"], x["k_idx"], s.topk, seq_lens=sl,
+                                    page_table=pt, return_sel=True, return_lse=True, **_scales(s))
+    torch.cuda.synchronize()
+    _compare(out, sel, lse, *_paged_oracle(s, lens, table, xh))
+    # the two branches on their own give the same
+    sel2 = msa.index_select_kvcache(x["q_idx"], x["k_idx"], s.topk, seq_lens=sl, page_table=pt)
+    out2 = msa.sparse_attn_fwd_kvcache(x["q"], x["k"], x["v"], sel2, seq_lens=sl, page_table=pt, **_scales(s))
+    torch.cuda.synchronize()
+    assert torch.equal(sel2, sel) and torch.equal(out2, out)
+
+
+def test_equal_lengths_match_the_plain_call():
+    msa = _msa()
+    s = synth.Shape(3, 4, 2000, 1996, 32, 4, 128, 128, 16)
+    x = {n: t.cuda() for n, t in synth.host_inputs(s, 8).items()}
+    a = msa.fwd(x["q"], x["k"], x["v"], x["q_idx"], x["k_idx"], 16, q_offset=1996, return_sel=True, return_lse=True)
+    sl = torch.full((3,), 2000, dtype=torch.int32, device="cuda")
+    b = msa.fwd_kvcache(x["q"], x["k"], x["v"], x["q_idx"], x["k_idx"], 16, seq_lens=sl, return_sel=True,
+                        return_lse=True)
+    torch.cuda.synchronize()
+    for u, w in zip(a, b):
+        assert torch.equal(u, w)
+
+
+def test_unmapped_pages_are_skipped_safely():
+    # sequence 0: a middle block's page id is negative; sequence 1: its local
+    # block's page id is past the pool.  Neither is read; the other sequences are
+    # unaffected and every output stays finite.
+    msa = _msa()
+    case = ([4000, 3000, 2500, 900], 1, 64, 4, 128, 128, 16, "native", 4)
+    lens = case[0]
+    s, table, P, xh = _paged(case, 77)
+    ref = _paged_oracle(s, lens, table, xh)
+    bad = table.copy()
+    bad[0, 5] = -5
+    L1 = (lens[1] - 1) // 128
+    bad[1, L1] = 10 ** 6
+    x = {n: t.cuda() for n, t in xh.items()}
+    out, sel, lse = msa.fwd_kvcache(x["q"], x["k"], x["v"], x["q_idx"], x["k_idx"], s.topk,
+                                    seq_lens=torch.tensor(lens, dtype=torch.int32, device="cuda"),
+                                    page_table=torch.from_numpy(bad).cuda(), return_sel=True, return_lse=True)
+    torch.cuda.synchronize()
+    og, sg, lg = out.float().cpu().numpy(), sel.cpu().numpy(), lse.cpu().numpy()
+    assert np.isfinite(og).all() and np.isfinite(lg).all()
+    assert not (sg[0] == 5).any()           # the unmapped block is never ranked
+    assert (sg[1, :, 0] == L1).any(axis=-1).all()  # the local block is still listed (it is forced)
+    for b in (2, 3):
+        assert np.array_equal(sg[b], ref[1][b])
+        assert float(np.abs(og[b] - ref[0][b]).max()) <= TOL
+
+
+def test_paged_decode_workload_sampled():
+    msa = _msa()
+    wid = 7
+    s = synth.WORKLOADS[wid]
+    print(f"workload {synth.WORKLOAD_NAMES[wid]}: inputs", flush=True)
+    x, lens, table, P = synth.paged_workload(wid, device="cuda")
+    sl = torch.from_numpy(lens).cuda()
+    pt = torch.from_numpy(table).cuda()
+    out, sel = msa.fwd_kvcache(x["q"], x["k"], x["v"], x["q_idx"], x["k_idx"], s.topk, seq_lens=sl, page_table=pt,
+                               kv_len=s.kv_len, return_sel=True)
+    torch.cuda.synchronize()
+    print("  forward done", flush=True)
+    picks = [int(np.argmin(lens)), int(np.argmax(lens)), 17]
+    pools = {n: x[n] for n in ("k", "v", "k_idx")}
+    f = {}
+    for n in ("k", "v", "k_idx"):  # only the picked sequences' pages come back to the host
+        f[n] = []
+        for b in picks:
+            nb = -(-int(lens[b]) // 128)
+            pg = torch.from_numpy(table[b, :nb].astype(np.int64)).cuda()
+            f[n].append(orc.page_gather(_f64(s, n, pools[n].index_select(0, pg).cpu()), np.arange(nb), int(lens[b])))
+    q = _f64(s, "q", x["q"][picks].cpu())
+    qi = _f64(s, "q_idx", x["q_idx"][picks].cpu())
+    ref_out, ref_sel, _ = orc.msa_forward_varlen(q, f["k"], f["v"], qi, f["k_idx"], s.topk)
+    assert np.array_equal(sel[picks].cpu().numpy(), ref_sel)
+    err = float(np.abs(out[picks].float().cpu().numpy() - ref_out).max())
+    print(f"  max abs err {err:.3e}", flush=True)
+    assert err <= TOL

@@ -529,3 +529,77 @@ def test_synth_fp8_caches():
     assert rel.max() <= 2.0 ** -4 + 1e-12  # round to nearest with a 3-bit mantissa
     with pytest.raises(TypeError):
         synth.as_f64(x["k"])
+
+
+# --- caches of unequal length and paged caches --------------------------------
+
+def test_page_gather_inverts_a_scatter():
+    rng = np.random.default_rng(3)
+    for n in (1, 127, 128, 129, 700):
+        nb = -(-n // 128)
+        dense_kv = rng.standard_normal((2, nb * 128, 8))
+        dense_ki = rng.standard_normal((nb * 128, 4))
+        P = nb + 5
+        pages = rng.permutation(P)[:nb]
+        pool_kv = rng.standard_normal((P, 2, 128, 8))
+        pool_ki = rng.standard_normal((P, 128, 4))
+        for c in range(nb):  # plain scatter of block c into page pages[c]
+            pool_kv[pages[c]] = dense_kv[:, c * 128:(c + 1) * 128]
+            pool_ki[pages[c]] = dense_ki[c * 128:(c + 1) * 128]
+        assert np.array_equal(orc.page_gather(pool_kv, pages, n), dense_kv[:, :n])
+        assert np.array_equal(orc.page_gather(pool_ki, pages, n), dense_ki[:n])
+    assert orc.page_gather(np.zeros((3, 2, 128, 8)), [], 0).shape == (2, 0, 8)
+
+
+def _varlen_case(seed, lens, S_q, G=2, r=2, d=16, D=8, lo=-4, hi=4):
+    rng = np.random.default_rng(seed)
+    B = len(lens)
+    q = rng.standard_normal((B, S_q, G * r, d))
+    qi = rng.integers(lo, hi + 1, (B, S_q, G, D)).astype(np.float64)
+    ks = [rng.standard_normal((G, n, d)) for n in lens]
+    vs = [rng.standard_normal((G, n, d)) for n in lens]
+    kis = [rng.integers(lo, hi + 1, (n, D)).astype(np.float64) for n in lens]
+    return q, ks, vs, qi, kis
+
+
+def test_varlen_equal_lengths_is_the_plain_forward():
+    lens, S_q, k = [300, 300, 300], 5, 2
+    q, ks, vs, qi, kis = _varlen_case(1, lens, S_q)
+    out, sel, lse = orc.msa_forward_varlen(q, ks, vs, qi, kis, k, block_size=32)
+    ro, rs, rl = orc.msa_forward(q, np.stack(ks), np.stack(vs), qi, np.stack(kis), k, 300 - S_q, 32)
+    assert np.array_equal(sel, rs)
+    assert np.allclose(out, ro, atol=1e-12) and np.allclose(lse, rl, atol=1e-12)
+
+
+def test_varlen_rows_before_the_cache():
+    # sequence 1 holds 2 tokens but has 5 query rows: rows 0..2 precede it
+    lens, S_q, k = [90, 2, 33], 5, 3
+    q, ks, vs, qi, kis = _varlen_case(2, lens, S_q)
+    out, sel, lse = orc.msa_forward_varlen(q, ks, vs, qi, kis, k, block_size=16)
+    assert (sel[1, :, :3] == -1).all() and (out[1, :3] == 0).all() and np.isneginf(lse[1, :, :3]).all()
+    ro, rs, rl = orc.msa_forward(q[1:2, 3:], ks[1][None], vs[1][None], qi[1:2, 3:], kis[1][None], k, 0, 16)
+    assert np.array_equal(sel[1, :, 3:], rs[0]) and np.allclose(out[1, 3:], ro[0]) and np.allclose(lse[1, :, 3:], rl[0])
+    assert sel[1, 0, 3].tolist() == [0, -1, -1]  # position 0: the local block only
+
+
+def test_varlen_positions_against_torch_sdpa():
+    # k at least the number of blocks: every row is dense causal attention over
+    # its own cache with the query at position n_b - S_q + i
+    lens, S_q, Bk = [40, 7, 64, 3], 4, 16
+    q, ks, vs, qi, kis = _varlen_case(5, lens, S_q)
+    out, sel, lse = orc.msa_forward_varlen(q, ks, vs, qi, kis, topk=8, block_size=Bk)
+    G, r, d = 2, 2, 16
+    for b, n in enumerate(lens):
+        for i in range(S_q):
+            t = n - S_q + i
+            if t < 0:
+                continue
+            for h in range(G * r):
+                g = h // r
+                qh = torch.from_numpy(q[b, i, h]).view(1, 1, 1, d)
+                kk = torch.from_numpy(ks[b][g, :t + 1]).view(1, 1, t + 1, d)
+                vv = torch.from_numpy(vs[b][g, :t + 1]).view(1, 1, t + 1, d)
+                ref = F.scaled_dot_product_attention(qh, kk, vv).view(d).numpy()
+                assert np.allclose(out[b, i, h], ref, atol=1e-12)
+                s_ = (ks[b][g, :t + 1] @ q[b, i, h]) / math.sqrt(d)
+                assert abs(lse[b, h, i] - (s_.max() + math.log(np.exp(s_ - s_.max()).sum()))) < 1e-12
