@@ -11,8 +11,9 @@ FLOPs, the masked half of the local block and the skipped blocks excluded).
 algorithmic FLOPs per launch over its own average duration, timed with HIP
 events recorded around that kernel on the stream it runs on.  The decode
 workload (64 sequences x 128K cache) is reported beside it in GB/s of
-algorithmic HBM bytes, with bf16 caches (``decode``) and with FP8 E4M3 caches
-(``decode_fp8``).  ``cpu_baseline`` times the fp64 CPU oracle on a bounded
+algorithmic HBM bytes, with bf16 caches (``decode``), with FP8 E4M3 caches
+(``decode_fp8``) and over 64 caches of unequal length (4K-128K tokens) in a
+shuffled page pool (``decode_paged``).  ``cpu_baseline`` times the fp64 CPU oracle on a bounded
 sample of query rows of the same workload.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--decode-steps 50]
@@ -106,12 +107,36 @@ def algorithmic_work(s: synth.Shape):
     return flop_main, flop_index, float(bytes_dec)
 
 
+def paged_decode_bytes(s: synth.Shape, lens) -> float:
+    """Algorithmic bytes of one decode step over caches of lengths ``lens``: the
+    decode formula with S_k replaced by each sequence's own length."""
+    e = 2 if s.dtype == "bf16" else 4
+    c = 1 if s.fp8 else e
+    total = 0
+    for n in np.asarray(lens, dtype=np.int64):
+        n_sel = min(s.topk, (int(n) - 1) // s.block_size + 1)
+        total += (int(n) * s.index_dim * c + s.groups * n_sel * s.block_size * s.head_dim * c * 2
+                  + 2 * s.num_q_heads * s.head_dim * e + s.groups * s.index_dim * e + 4 * s.groups * s.topk)
+    return float(total)
+
+
 class Runner:
-    """One workload on the GPU: inputs, outputs and workspace allocated once."""
+    """One workload on the GPU: inputs, outputs and workspace allocated once.
+    Paged workloads run msa_fwd_kvcache over their page pool."""
 
     def __init__(self, msa, s: synth.Shape, wid: int):
         self.msa, self.s = msa, s
-        self.x = synth.inputs_for(s, wid, device="cuda")
+        self.cache = None
+        if wid in synth.PAGED:
+            self.x, self.lens, table, P = synth.paged_workload(wid, device="cuda")
+            self.seq_lens = torch.from_numpy(self.lens).cuda()
+            self.table = torch.from_numpy(table).cuda()
+            self.cache = msa.MsaKvCache()
+            self.cache.seq_lens = self.seq_lens.data_ptr()
+            self.cache.page_table = self.table.data_ptr()
+            self.cache.max_pages, self.cache.num_pages = table.shape[1], P
+        else:
+            self.x = synth.inputs_for(s, wid, device="cuda")
         dev = self.x["q"].device
         self.out = torch.empty((s.batch, s.q_len, s.num_q_heads, s.head_dim), dtype=s.torch_dtype, device=dev)
         self.sel = torch.empty((s.batch, s.groups, s.q_len, s.topk), dtype=torch.int32, device=dev)
@@ -119,20 +144,21 @@ class Runner:
                                     s.head_dim, s.index_dim, s.topk, s.torch_dtype,
                                     cache_format=msa.CACHE_FP8_E4M3 if s.fp8 else msa.CACHE_NATIVE,
                                     k_scale=s.k_scale if s.fp8 else None, v_scale=s.v_scale if s.fp8 else None)
-        n = msa.workspace_size(self.shape, msa.OP_FWD)
+        self.L = msa.lib()
+        cref = ctypes.byref(self.cache) if self.cache is not None else None
+        n = self.L.msa_workspace_size_kvcache(ctypes.byref(self.shape), cref, msa.OP_FWD)
         self.ws_raw = torch.empty(n + 256, dtype=torch.uint8, device=dev)
         off = (-self.ws_raw.data_ptr()) % 256
         self.ws = self.ws_raw[off:off + n]
-        self.L = msa.lib()
         self.stream = torch.cuda.current_stream(dev)
-        self.args = [ctypes.byref(self.shape)] + [ctypes.c_void_p(self.x[n_].data_ptr())
-                                                   for n_ in ("q", "k", "v", "q_idx", "k_idx")]
+        self.args = [ctypes.byref(self.shape), cref] + [ctypes.c_void_p(self.x[n_].data_ptr())
+                                                         for n_ in ("q", "k", "v", "q_idx", "k_idx")]
         self.args += [ctypes.c_void_p(self.out.data_ptr()), ctypes.c_void_p(self.sel.data_ptr()), None,
                       ctypes.c_void_p(self.ws.data_ptr()), ctypes.c_size_t(self.ws.numel()),
                       ctypes.c_void_p(self.stream.cuda_stream)]
 
     def step(self):
-        st = self.L.msa_fwd(*self.args)
+        st = self.L.msa_fwd_kvcache(*self.args)
         if st != 0:
             raise RuntimeError(self.L.msa_last_error().decode())
 
@@ -182,16 +208,19 @@ def decode_leg(msa, wid: int, args):
     (the index kernel) against the HBM roofline."""
     sd = synth.WORKLOADS[wid]
     name = synth.WORKLOAD_NAMES[wid]
-    _, _, dec_bytes = algorithmic_work(sd)
     print(f"[bench] {name}: generating inputs", file=sys.stderr, flush=True)
     drun = Runner(msa, sd, wid)
+    paged = drun.cache is not None
+    dec_bytes = paged_decode_bytes(sd, drun.lens) if paged else algorithmic_work(sd)[2]
     dms, idx_ms = drun.time_steps(args.decode_steps, args.warmup, "index_score")
     stats = step_stats(drun.step_ms)
     dk = {} if args.no_breakdown else drun.kernel_breakdown()
     gbs = dec_bytes / (dms * 1e-3) / 1e9
     idx_avg = float(np.mean(idx_ms))
-    kidx_bytes = float(sd.batch * sd.kv_len * sd.index_dim * (1 if sd.fp8 else 2))
-    profile = "index_topk_decode_128k_b64_fp8_hbm.md" if sd.fp8 else "index_topk_decode_128k_b64_hbm.md"
+    kidx_tokens = int(np.sum(drun.lens, dtype=np.int64)) if paged else sd.batch * sd.kv_len
+    kidx_bytes = float(kidx_tokens * sd.index_dim * (1 if sd.fp8 else 2))
+    profile = {4: "index_topk_decode_128k_b64_hbm.md", 6: "index_topk_decode_128k_b64_fp8_hbm.md",
+               7: "index_topk_decode_paged_varlen_b64_hbm.md"}[wid]
     res = {
         "workload": name, "value": round(gbs, 1), "unit": "GB/s",
         "ms_per_step": round(dms, 4), **stats, "steps": args.decode_steps, "bytes_per_step": dec_bytes,
@@ -203,6 +232,8 @@ def decode_leg(msa, wid: int, args):
                      "traffic": recorded_traffic(profile, "index_topk.hip", "traffic_read_bytes_per_launch")},
         "kernels_ms": {k: round(v, 4) for k, v in dk.items()},
     }
+    if paged:
+        res["cache_tokens"] = {"total": kidx_tokens, "min": int(drun.lens.min()), "max": int(drun.lens.max())}
     del drun
     torch.cuda.empty_cache()
     return res
@@ -363,6 +394,7 @@ def main():
     if not args.no_decode:
         result["decode"] = decode_leg(msa, 4, args)
         result["decode_fp8"] = decode_leg(msa, 6, args)
+        result["decode_paged"] = decode_leg(msa, 7, args)
     print(json.dumps(result))
 
 

@@ -95,6 +95,62 @@ __device__ __forceinline__ void emit_row(const IndexParams& p, int b, int n, int
   for (int j = take + 1; j < p.topk; ++j) out[j] = -1;
 }
 
+// The unit (row tile tg = b * ntile + tile, key split) of workgroup lin, or
+// false when it has none.  With a unit list (sequences of their own lengths)
+// the units holding work come first.  Otherwise, with key splits, hardware
+// hands consecutive workgroup ids to the 8 XCDs in turn, so the order gives
+// each XCD a contiguous run of units (one key range, many row tiles) whose
+// k_idx range stays in its L2; without splits, heavy_first puts the tiles with
+// the most causal blocks first.
+__device__ __forceinline__ bool unit_of(const IndexParams& p, int lin, bool heavy_first, int& tg, int& split) {
+  if (p.units) {
+    if (lin >= *p.unit_count) return false;
+    const int u = p.units[lin];
+    split = u & 127;
+    tg = u >> 7;
+    return true;
+  }
+  const int logical = (p.nsplit > 1 || !heavy_first) ? (lin & 7) * p.grid_per_xcd + (lin >> 3) : p.nunits - 1 - lin;
+  if (logical < 0 || logical >= p.nunits) return false;
+  split = logical / p.ntile_total;
+  tg = logical - split * p.ntile_total;
+  return true;
+}
+
+// Unit list for sequences of their own lengths: per row tile, one unit per key
+// split that holds blocks before the tile's last local block (one unit when
+// there is a single split, which also writes rows without blocks), packed in
+// tile order by one workgroup (a scan over per-thread counts).
+__global__ __launch_bounds__(1024) void index_units_kernel(IndexParams p) {
+  __shared__ int32_t s_cnt[1024];
+  const int n = p.ntile_total;
+  const int per = (n + 1023) / 1024;
+  const int lo = min(n, (int)threadIdx.x * per), hi = min(n, lo + per);
+  auto count = [&](int tg) {
+    if (p.nsplit == 1) return 1;
+    const int b = tg / p.ntile, tile = tg - b * p.ntile;
+    const int n_last = min((tile + 1) * p.rows_wg, p.rows_per_b) - 1;
+    const int L = local_block(first_pos(p.cm, p.q_offset, p.S_q, p.S_k, b) + n_last / p.G);
+    return L > 0 ? (L + p.chunk - 1) / p.chunk : 0;
+  };
+  int mine = 0;
+  for (int tg = lo; tg < hi; ++tg) mine += count(tg);
+  s_cnt[threadIdx.x] = mine;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int a = (int)threadIdx.x >= off ? s_cnt[threadIdx.x - off] : 0;
+    __syncthreads();
+    s_cnt[threadIdx.x] += a;
+    __syncthreads();
+  }
+  int o = s_cnt[threadIdx.x] - mine;
+  for (int tg = lo; tg < hi; ++tg) {
+    const int k = count(tg);
+    for (int sp = 0; sp < k; ++sp) p.units[o++] = (tg << 7) | sp;
+  }
+  if (threadIdx.x == 1023) *p.unit_count = s_cnt[1023];
+}
+
 template <typename T, typename S, int DI, int CAP, int RT>
 __global__ __launch_bounds__(256, 2) void index_topk_kernel(IndexParams p) {
   using M = Mma<T>;
@@ -116,16 +172,8 @@ __global__ __launch_bounds__(256, 2) void index_topk_kernel(IndexParams p) {
   __shared__ __align__(16) char smem[SMEM];
   T* Ks = (T*)smem;  // [2][kBlock * LDW]
 
-  // Unit order.  With key splits, hardware hands consecutive workgroup ids to
-  // the 8 XCDs in turn, so each XCD gets a contiguous run of units (one key
-  // range, many row tiles) and the k_idx range it streams stays in its L2.
-  // Without splits (one unit per row tile), the tiles with the most causal
-  // blocks go first, spread over all XCDs.
-  const int lin = blockIdx.x;
-  const int logical = p.nsplit > 1 ? (lin & 7) * p.grid_per_xcd + (lin >> 3) : p.nunits - 1 - lin;
-  if (logical < 0 || logical >= p.nunits) return;
-  const int split = logical / p.ntile_total;
-  const int tg = logical - split * p.ntile_total;
+  int tg, split;
+  if (!unit_of(p, blockIdx.x, true, tg, split)) return;
   const int b = tg / p.ntile;
   const int tile = tg - b * p.ntile;
   const int n_first = tile * ROWS_WG;
@@ -338,11 +386,8 @@ __global__ __launch_bounds__(256, 2) void index_topk_small_kernel(IndexParams p)
   __shared__ float xs[NL * CAP * 32];
   __shared__ int xi[NL * CAP * 32];
 
-  const int lin = blockIdx.x;
-  const int logical = (lin & 7) * p.grid_per_xcd + (lin >> 3);
-  if (logical >= p.nunits) return;
-  const int split = logical / p.B;
-  const int b = logical - split * p.B;
+  int b, split;  // one row tile per sequence: the tile is the sequence
+  if (!unit_of(p, blockIdx.x, false, b, split)) return;
   const int64_t qo = first_pos(p.cm, p.q_offset, p.S_q, p.S_k, b);
   const int Lmax = max(local_block(qo + (p.rows_per_b - 1) / p.G), 0);
   const int c_begin = split * p.chunk;
@@ -372,12 +417,23 @@ __global__ __launch_bounds__(256, 2) void index_topk_small_kernel(IndexParams p)
   const int nbw = c_end - c_begin > wave ? (c_end - c_begin - wave + 3) / 4 : 0;
   const int ntl = 4 * nbw;
   const S* kpool = (const S*)p.k_idx;
+  // Paged caches: lane j holds the page id of the wave's block j, read before
+  // the block loop so that no tile load waits on a page-table read (blocks past
+  // the 64th of a wave, in caches beyond 4M tokens, read the table directly).
+  const bool paged = p.cm.pages != nullptr;
+  const int pg_lane = paged && lane < nbw ? p.cm.pages[(int64_t)b * p.cm.max_pages + c_begin + wave + 4 * lane] : 0;
+  // element offset of the wave's block j, or -1 when its page is unmapped
+  auto blk_off = [&](int j) -> int64_t {
+    const int c = c_begin + wave + 4 * j;
+    if (!paged) return ((int64_t)b * p.S_k + (int64_t)c * kBlock) * DI;
+    const int pg = j < 64 ? __builtin_amdgcn_readlane(pg_lane, j) : p.cm.pages[(int64_t)b * p.cm.max_pages + c];
+    return pg >= 0 && pg < p.cm.num_pages ? (int64_t)pg * kBlock * DI : -1;
+  };
   // tile tl of the wave; tl past the end re-reads the last one (just read, so from
   // L2); an unmapped page is read from the pool start and scored -inf
   auto load_tile = [&](kraw (&a)[NKR], int tl) {
     const int tc = min(tl, ntl - 1);
-    const int c = c_begin + wave + 4 * (tc / 4);
-    const int64_t o = block_offset(p.cm, p.S_k, 1, DI, b, 0, c);
+    const int64_t o = blk_off(tc / 4);
     const S* src = kpool + (o < 0 ? 0 : o) + ((tc % 4) * 32 + l32) * DI;
 #pragma unroll
     for (int u = 0; u < NKR; ++u) a[u] = *(const kraw*)(src + koff(kNative ? u : 2 * u, h));
@@ -409,7 +465,7 @@ __global__ __launch_bounds__(256, 2) void index_topk_small_kernel(IndexParams p)
     const int j = tl / 4;
     float full = fmaxf(pm, __shfl_xor(pm, 32));
     pm = kNegInf;
-    if (!block_mapped(p.cm, b, c_begin + wave + 4 * j)) full = kNegInf;
+    if (blk_off(j) < 0) full = kNegInf;
     // blocks pair up: half 0 ranks the wave's even blocks, half 1 the odd ones
     const bool second = (j & 1) != 0;
     if (!second) pmA = full;
@@ -555,6 +611,7 @@ __global__ __launch_bounds__(256) void topk_merge_kernel(IndexParams p) {
 template <typename T, typename S, int DI, int CAP>
 static hipError_t launch_index_t(const IndexParams& p, hipStream_t s, const KernelTimer* tm) {
   timer_start(tm, kKernIndexScore, s);
+  if (p.units) hipLaunchKernelGGL(index_units_kernel, dim3(1), dim3(1024), 0, s, p);
   constexpr int RT = CAP <= 15 ? 2 : 1;
   static_assert(4 * 32 * RT == index_rows_per_wg(CAP + 1), "host and kernel agree on the row tile");
   bool small_done = false;

@@ -82,6 +82,11 @@ struct IndexParams {
   int nunits;          // ntile_total * nsplit
   int grid_per_xcd;    // ceil(nunits / 8)
   int small;           // 1: bf16 queries and rows_per_b <= kIndexSmallRows, one unit per (sequence, split)
+  int rows_wg;         // (row, group) pairs per row tile
+  // With per-sequence lengths: the units that hold work, packed as
+  // (row tile << 7) | split by index_units_kernel, and their number.  Null otherwise.
+  int32_t* units;
+  int32_t* unit_count;
 };
 
 // At most this many (row, group) pairs per sequence: the index kernel's

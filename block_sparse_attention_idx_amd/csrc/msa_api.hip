@@ -33,6 +33,7 @@ constexpr size_t kAlign = 256;
 constexpr int kTokensPerItem = 128;
 constexpr int kAttnGrid = 512;      // persistent attention grid: 2 workgroups per CU
 constexpr int kIndexTargetUnits = 2048;
+constexpr int64_t kIndexVarlenChunk = 16;  // key blocks per unit when sequences have their own lengths
 constexpr int kIndexMinTiles = 512;  // row tiles that fill 256 CUs without key splits
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -120,6 +121,8 @@ msa_status check_cache(const msa_shape* s, const msa_kv_cache* c) {
     if ((int64_t)s->batch * c->max_pages >= (1LL << 31))
       return fail(MSA_ERR_UNSUPPORTED, "batch * max_pages exceeds 2^31");
   }
+  if (c->seq_lens && (int64_t)s->batch * ((int64_t)s->q_len * s->num_kv_heads / 128 + 1) >= (1LL << 24))
+    return fail(MSA_ERR_UNSUPPORTED, "batch * row tiles exceeds 2^24 with seq_lens");
   return MSA_OK;
 }
 
@@ -147,7 +150,9 @@ int64_t max_pos(const msa_shape* s, const msa_kv_cache* c) {
 struct IndexPlan {
   msa::IndexParams p;
   int cap;
-  size_t bytes;  // workspace for the partial lists
+  size_t off_s, off_i, off_units, off_count;  // partial lists, unit list (0 when unused)
+  bool lists, unit_list;
+  size_t bytes;
 };
 
 IndexPlan plan_index(const msa_shape* s, const msa_kv_cache* cache) {
@@ -162,17 +167,23 @@ IndexPlan plan_index(const msa_shape* s, const msa_kv_cache* cache) {
   p.q_offset = s->q_offset;
   p.rows_per_b = s->q_len * s->num_kv_heads;
   p.small = p.rows_per_b <= msa::kIndexSmallRows && s->dtype == MSA_BF16 ? 1 : 0;
-  p.ntile = p.small ? 1 : (int)ceil_div(p.rows_per_b, msa::index_rows_per_wg(s->topk));
+  p.rows_wg = p.small ? p.rows_per_b : msa::index_rows_per_wg(s->topk);
+  p.ntile = (int)ceil_div(p.rows_per_b, p.rows_wg);
   p.ntile_total = p.B * p.ntile;
   const int64_t Lmax = s->q_len > 0 ? max_pos(s, cache) / msa::kBlock : 0;
   // Enough row tiles to fill the GPU: one unit per tile, no merge.  Otherwise
   // split the key blocks so that about kIndexTargetUnits units exist (at least
   // 16 blocks per unit, 8 in the few-row form where 4 waves share a unit's
   // blocks, and at most 128 splits for the merge).
+  // With per-sequence lengths the work per sequence is unknown here: a fixed,
+  // small chunk keeps short caches from leaving most units idle, and a unit
+  // list built on the device packs the units that hold work first.
   int64_t chunk = std::max<int64_t>(1, Lmax), nsplit = 1;
   if (Lmax > 0 && p.ntile_total < kIndexMinTiles) {
+    const int64_t min_chunk = p.small ? 8 : 16;
     const int64_t want = std::max<int64_t>(1, ceil_div(kIndexTargetUnits, std::max(1, p.ntile_total)));
-    chunk = std::max<int64_t>({p.small ? 8 : 16, ceil_div(Lmax, want), ceil_div(Lmax, 128)});
+    const bool varlen = cache && cache->seq_lens;
+    chunk = std::max<int64_t>({min_chunk, varlen ? kIndexVarlenChunk : ceil_div(Lmax, want), ceil_div(Lmax, 128)});
     nsplit = ceil_div(Lmax, chunk);
   }
   p.chunk = (int)chunk;
@@ -181,14 +192,30 @@ IndexPlan plan_index(const msa_shape* s, const msa_kv_cache* cache) {
   p.grid_per_xcd = (int)ceil_div(p.nunits, 8);
   ip.cap = s->topk <= 16 ? 15 : 31;
   const size_t entries = (size_t)p.B * p.rows_per_b * p.nsplit * ip.cap;
-  ip.bytes = p.nsplit > 1 ? 2 * align_up(entries * 4) : 0;
+  size_t off = 0;
+  ip.lists = p.nsplit > 1;
+  if (ip.lists) {
+    ip.off_s = off;
+    off += align_up(entries * 4);
+    ip.off_i = off;
+    off += align_up(entries * 4);
+  }
+  ip.unit_list = cache && cache->seq_lens;  // work per sequence known only on the device
+  if (ip.unit_list) {
+    ip.off_units = off;
+    off += align_up((size_t)p.nunits * 4);
+    ip.off_count = off;
+    off += align_up(4);
+  }
+  ip.bytes = off;
   return ip;
 }
 
 void bind_index(IndexPlan& ip, char* ws, const void* q_idx, const void* k_idx, int32_t* sel) {
-  const size_t half = ip.bytes / 2;
-  ip.p.part_s = (float*)ws;
-  ip.p.part_i = (int32_t*)(ws + half);
+  ip.p.part_s = ip.lists ? (float*)(ws + ip.off_s) : nullptr;
+  ip.p.part_i = ip.lists ? (int32_t*)(ws + ip.off_i) : nullptr;
+  ip.p.units = ip.unit_list ? (int32_t*)(ws + ip.off_units) : nullptr;
+  ip.p.unit_count = ip.unit_list ? (int32_t*)(ws + ip.off_count) : nullptr;
   ip.p.q_idx = q_idx;
   ip.p.k_idx = k_idx;
   ip.p.sel = sel;
