@@ -40,6 +40,7 @@ METRIC = "MSA fwd TFLOP/s (prefill 32K/128K) + decode KV GB/s, % of MI355X roofl
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 KERNELS = {"index_score": 1, "topk_merge": 2, "gather": 3, "attention": 4, "combine": 5}
+KL_KERNELS = {"kl_teacher": 6, "kl_combine": 7}
 
 
 class HipEvents:
@@ -189,6 +190,48 @@ class Runner:
                 ev.destroy(a)
                 ev.destroy(b)
         return total / steps, per_kernel
+
+    def kl_teacher(self, steps=10, warmup=2):
+        """Time msa_kl_teacher_fwd on this workload's selection and lse: (ms per call,
+        per-kernel ms).  One forward with lse first provides them."""
+        s, msa = self.s, self.msa
+        dev = self.x["q"].device
+        lse = torch.empty((s.batch, s.num_q_heads, s.q_len), dtype=torch.float32, device=dev)
+        fa = list(self.args)
+        fa[9] = ctypes.c_void_p(lse.data_ptr())
+        if self.L.msa_fwd_kvcache(*fa) != 0:
+            raise RuntimeError(self.L.msa_last_error().decode())
+        kl = torch.empty((s.batch, s.groups, s.q_len), dtype=torch.float32, device=dev)
+        cref = ctypes.byref(self.cache) if self.cache is not None else None
+        ka = [ctypes.byref(self.shape), cref] + [ctypes.c_void_p(self.x[n].data_ptr()) for n in ("q", "k", "q_idx", "k_idx")]
+        ka += [ctypes.c_void_p(self.sel.data_ptr()), ctypes.c_void_p(lse.data_ptr()), ctypes.c_float(1.0),
+               ctypes.c_void_p(kl.data_ptr()), None, ctypes.c_void_p(self.ws.data_ptr()),
+               ctypes.c_size_t(self.ws.numel()), ctypes.c_void_p(self.stream.cuda_stream)]
+
+        def call():
+            if self.L.msa_kl_teacher_fwd_kvcache(*ka) != 0:
+                raise RuntimeError(self.L.msa_last_error().decode())
+        for _ in range(warmup):
+            call()
+        torch.cuda.synchronize()
+        ev = HipEvents()
+        per = {}
+        for name, kid in KL_KERNELS.items():
+            a, b = ev.create(), ev.create()
+            self.L.msa_set_kernel_timer(kid, a, b)
+            call()
+            torch.cuda.synchronize()
+            self.L.msa_set_kernel_timer(0, None, None)
+            per[name] = ev.elapsed_ms(a, b)
+            ev.destroy(a)
+            ev.destroy(b)
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record(self.stream)
+        for _ in range(steps):
+            call()
+        t1.record(self.stream)
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / steps, per
 
     def kernel_breakdown(self, steps=3):
         res = {}
@@ -363,6 +406,14 @@ def main():
         "kernels_ms": {k: round(v, 4) for k, v in kern.items()},
     }
     print(f"[bench] {ms:.3f} ms/step, attention {attn_avg:.3f} ms", file=sys.stderr, flush=True)
+    if not args.no_extra:
+        # the KL-alignment teacher on the same workload: QK^T again (half the main
+        # FLOPs) plus the index scores over the same tokens
+        flop_kl = flop_main * (0.5 + s.index_dim * s.groups / (2.0 * s.head_dim * s.num_q_heads))
+        kms, kper = run.kl_teacher()
+        result["kl_teacher"] = {"ms": round(kms, 4), "tflops": round(flop_kl / (kms * 1e-3) / 1e12, 2),
+                                "frac_of_mfma_peak": round(flop_kl / (kms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                                "flop": flop_kl, "kernels_ms": {k: round(v, 4) for k, v in kper.items() if v}}
 
     if not args.no_cpu:
         print("[bench] cpu baseline (oracle on sampled rows)", file=sys.stderr, flush=True)

@@ -36,14 +36,14 @@ from typing import Optional
 import torch
 
 __all__ = ["index_select", "sparse_attn_fwd", "fwd", "index_select_kvcache", "sparse_attn_fwd_kvcache",
-           "fwd_kvcache", "workspace_size", "MsaShape", "MsaKvCache", "lib", "LIB_PATH", "MsaError",
-           "OP_INDEX_SELECT", "OP_SPARSE_ATTN", "OP_FWD"]
+           "fwd_kvcache", "kl_teacher_fwd", "kl_teacher_fwd_kvcache", "workspace_size", "MsaShape", "MsaKvCache",
+           "lib", "LIB_PATH", "MsaError", "OP_INDEX_SELECT", "OP_SPARSE_ATTN", "OP_FWD", "OP_KL_TEACHER"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmsa.so")
 
 MSA_F32, MSA_BF16 = 0, 1
 CACHE_NATIVE, CACHE_FP8_E4M3 = 0, 1
-OP_INDEX_SELECT, OP_SPARSE_ATTN, OP_FWD = 0, 1, 2
+OP_INDEX_SELECT, OP_SPARSE_ATTN, OP_FWD, OP_KL_TEACHER = 0, 1, 2, 3
 BLOCK_SIZE = 128
 
 
@@ -122,6 +122,11 @@ def lib() -> ctypes.CDLL:
         L.msa_sparse_attn_fwd_kvcache.restype = ctypes.c_int
         L.msa_fwd_kvcache.argtypes = [shp, cp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.msa_fwd_kvcache.restype = ctypes.c_int
+        fl = ctypes.c_float
+        L.msa_kl_teacher_fwd.argtypes = [shp, vp, vp, vp, vp, vp, vp, fl, vp, vp, vp, sz, vp]
+        L.msa_kl_teacher_fwd.restype = ctypes.c_int
+        L.msa_kl_teacher_fwd_kvcache.argtypes = [shp, cp, vp, vp, vp, vp, vp, vp, fl, vp, vp, vp, sz, vp]
+        L.msa_kl_teacher_fwd_kvcache.restype = ctypes.c_int
         _LIB = L
     return _LIB
 
@@ -451,3 +456,57 @@ def fwd_kvcache(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_idx: torch.
     if return_lse:
         res.append(lse)
     return res[0] if len(res) == 1 else tuple(res)
+
+
+# ---- KL-alignment teacher (forward only) ------------------------------------
+
+def kl_teacher_fwd_kvcache(q: torch.Tensor, k: torch.Tensor, q_idx: torch.Tensor, k_idx: torch.Tensor,
+                           sel: torch.Tensor, lse: torch.Tensor, seq_lens=None, page_table=None,
+                           kv_len: Optional[int] = None, q_offset: int = 0, scale: Optional[float] = None,
+                           index_scale: float = 1.0, k_scale: Optional[float] = None, return_idx_lse: bool = False,
+                           workspace: Optional[torch.Tensor] = None):
+    """KL(group-averaged main distribution || index distribution) per (b, g, i),
+    fp32 [B, G, S_q], from the forward's selection and lse; with return_idx_lse
+    also the index log-sum-exp over the same tokens."""
+    _need(q, "q", 4)
+    dev = q.device
+    _need(q_idx, "q_idx", 4, dev, q.dtype)
+    _need(k, "k", 4, dev)
+    _need(k_idx, "k_idx", 3, dev)
+    cf = _cache_format(q.dtype, [("k", k), ("k_idx", k_idx)])
+    _need(sel, "sel", 4, dev, torch.int32)
+    _need(lse, "lse", 3, dev, torch.float32)
+    B, S_q, Hq, d = q.shape
+    if k.shape[3] != d:
+        raise ValueError("k must end in d")
+    Hkv, S_k, P = _kv_geometry(k, k_idx, B, page_table, kv_len)
+    D = q_idx.shape[3]
+    if tuple(q_idx.shape) != (B, S_q, Hkv, D) or k_idx.shape[2] != D:
+        raise ValueError("q_idx must be [B, S_q, Hkv, D_idx] and k_idx end in D_idx")
+    topk = sel.shape[3]
+    if tuple(sel.shape[:3]) != (B, Hkv, S_q) or tuple(lse.shape) != (B, Hq, S_q):
+        raise ValueError("sel must be [B, G, S_q, topk] and lse [B, Hq, S_q]")
+    cache, _ = _kv_cache(B, dev, seq_lens, page_table, P)
+    shape = make_shape(B, S_q, S_k, q_offset, Hq, Hkv, d, D, topk, q.dtype, None, scale,
+                       cache_format=cf, k_scale=k_scale)
+    kl = torch.empty((B, Hkv, S_q), dtype=torch.float32, device=dev)
+    ilse = torch.empty((B, Hkv, S_q), dtype=torch.float32, device=dev) if return_idx_lse else None
+    L = lib()
+    cref = ctypes.byref(cache) if cache is not None else None
+    if workspace is None:
+        n = int(L.msa_workspace_size_kvcache(ctypes.byref(shape), cref, OP_KL_TEACHER))
+        workspace = _aligned(n, dev)
+    st = L.msa_kl_teacher_fwd_kvcache(ctypes.byref(shape), cref, _ptr(q), _ptr(k), _ptr(q_idx), _ptr(k_idx),
+                                      _ptr(sel), _ptr(lse), float(index_scale), _ptr(kl), _ptr(ilse),
+                                      _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream(dev))
+    _check(st)
+    return (kl, ilse) if return_idx_lse else kl
+
+
+def kl_teacher_fwd(q, k, q_idx, k_idx, sel, lse, q_offset: int = 0, scale: Optional[float] = None,
+                   index_scale: float = 1.0, k_scale: Optional[float] = None, return_idx_lse: bool = False,
+                   workspace: Optional[torch.Tensor] = None):
+    """kl_teacher_fwd_kvcache over dense caches of kv_len tokens each."""
+    return kl_teacher_fwd_kvcache(q, k, q_idx, k_idx, sel, lse, q_offset=q_offset, scale=scale,
+                                  index_scale=index_scale, k_scale=k_scale, return_idx_lse=return_idx_lse,
+                                  workspace=workspace)

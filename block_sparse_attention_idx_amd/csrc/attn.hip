@@ -720,8 +720,7 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnParams p) {
     p.lse[((int64_t)b * p.Hq + g * R + hh) * p.S_q + i] = (mx + log2f(W)) * 0.69314718055994531f;
 }
 
-template <typename T, typename S, int D, int R>
-static hipError_t launch_attn_t(const AttnParams& p, hipStream_t s, const KernelTimer* tm) {
+void launch_gather(const AttnParams& p, hipStream_t s, const KernelTimer* tm) {
   const int64_t entries = (int64_t)p.B * p.G * p.S_q * p.topk;
   if (!p.direct) {
     timer_start(tm, kKernGather, s);
@@ -741,6 +740,11 @@ static hipError_t launch_attn_t(const AttnParams& p, hipStream_t s, const Kernel
       hipLaunchKernelGGL(gather_scatter_kernel, dim3((unsigned)((entries + 255) / 256)), dim3(256), 0, s, p);
     timer_stop(tm, kKernGather, s);
   }
+}
+
+template <typename T, typename S, int D, int R>
+static hipError_t launch_attn_t(const AttnParams& p, hipStream_t s, const KernelTimer* tm) {
+  launch_gather(p, s, tm);
   timer_start(tm, kKernAttention, s);
   if (p.direct)
     hipLaunchKernelGGL((attn_decode_kernel<T, S, D, R>), dim3(p.grid_decode), dim3(256), 0, s, p);

@@ -23,7 +23,8 @@ inline void timer_stop(const KernelTimer* t, int which, hipStream_t s) {
   if (t && t->which == which) (void)hipEventRecord(t->stop, s);
 }
 
-enum { kKernIndexScore = 1, kKernTopkMerge = 2, kKernGather = 3, kKernAttention = 4, kKernCombine = 5 };
+enum { kKernIndexScore = 1, kKernTopkMerge = 2, kKernGather = 3, kKernAttention = 4, kKernCombine = 5,
+       kKernKlTeacher = 6, kKernKlCombine = 7 };
 
 // Where the caches (k, v, k_idx) of each sequence live.  Without a length
 // table every sequence holds S_k tokens and its query row 0 sits at q_offset;
@@ -139,5 +140,24 @@ struct AttnParams {
 // fp8_cache: k and v hold OCP FP8 E4M3 values (q and the partial states bf16).
 hipError_t launch_sparse_attention(const AttnParams& p, bool bf16_inputs, bool fp8_cache, hipStream_t s,
                                    const KernelTimer* timer);
+
+// Query gather of the KV-outer kernels (nothing when p.direct).
+void launch_gather(const AttnParams& p, hipStream_t s, const KernelTimer* timer);
+
+// KL-alignment teacher (kl.hip): the main branch's token sets and work items,
+// plus the index tensors, the main branch's lse and the outputs.
+struct KlParams {
+  const void* q_idx;   // [B, S_q, G, D_idx]
+  const void* k_idx;   // [B, S_k, D_idx] (or a page pool)
+  const float* lse;    // [B, Hq, S_q] main-branch log-sum-exp (natural log)
+  float index_scale;   // multiplies the raw index scores before their softmax
+  int index_dim;
+  float* part;         // [B, S_q, G, topk, 3]: per block sum pbar (log pbar - s), max s, sum exp(s - max)
+  float* kl;           // [B, G, S_q]
+  float* idx_lse;      // [B, G, S_q] or null
+};
+
+hipError_t launch_kl_teacher(const AttnParams& p, const KlParams& kp, bool bf16_inputs, bool fp8_cache,
+                             hipStream_t s, const KernelTimer* timer);
 
 }  // namespace msa

@@ -1,0 +1,365 @@
+// KL-alignment teacher of MSA on gfx950, forward only.
+//
+// Method (snilld.dk page "MiniMax lancerer MSA", section "Træning og
+// stabilisering"; Hungarian page "MiniMax új eljárása …", section "A
+// betanítás és a kernel-optimalizáció"): Top-k cannot be differentiated, so a
+// KL loss trains the index branch to follow the main branch.  The teacher is
+// the main branch's attention distribution over the selected tokens, averaged
+// over the heads of the GQA group; the student is the softmax of the index
+// scores over the same tokens.  Per (b, g, i), with s_j the index scores times
+// index_scale:
+//   KL = sum_j pbar(j) (log pbar(j) - log q(j)),   q = softmax(s)
+//      = sum_j pbar(j) (log pbar(j) - s_j) + lse(s).
+// With the main branch's log-sum-exp given, pbar(j) needs no second softmax
+// pass, so every selected block contributes additive terms: its sum of
+// pbar (log pbar - s), plus the max and the exp-sum of its index scores.
+//
+// Work items and token lists are those of the main branch (the same gather).
+// Per item the block's K and index keys are staged in LDS, and passes of 4
+// waves x 32 (token, head) rows recompute S^T = K Q^T and the index scores
+// S_idx^T = K_idx Q_idx^T (each row with its token's index query) on 32x32
+// MFMA tiles.  The r heads of a token sit in r adjacent lanes; their
+// probabilities are summed by a butterfly that leaves lane hh of the group
+// owning 64 / r of its half's keys, so each logarithm is taken once per key,
+// not once per head.
+#include <type_traits>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace msa {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.69314718055994531f;
+
+// The 64 scores of a lane (4 key tiles x 16 registers) as one vector value:
+// selecting between its elements by a lane-dependent condition then stays a
+// register select (an array indexed that way would be placed in memory).
+typedef float f32x64 __attribute__((ext_vector_type(64)));
+
+// Butterfly over the R lanes of a token (offsets O = R/2, R/4, ..., 1): at each
+// step a lane keeps the upper or lower half of its N values by bit O of hh.
+// sum() adds the partner's other half, pick() only selects.  Afterwards lane
+// hh holds, in x[0, 64 / R), slots [hh * 64 / R, (hh + 1) * 64 / R).
+template <int O, int N>
+struct Butterfly {
+  __device__ static __forceinline__ void sum(f32x64& x, int hh) {
+    const bool up = (hh & O) != 0;
+#pragma unroll
+    for (int k = 0; k < N / 2; ++k) {
+      const float lo = x[k], hi = x[k + N / 2];
+      x[k] = (up ? hi : lo) + __shfl_xor(up ? lo : hi, O);
+    }
+    Butterfly<O / 2, N / 2>::sum(x, hh);
+  }
+  __device__ static __forceinline__ void pick(f32x64& x, int hh) {
+    const bool up = (hh & O) != 0;
+#pragma unroll
+    for (int k = 0; k < N / 2; ++k) {
+      const float lo = x[k], hi = x[k + N / 2];
+      x[k] = up ? hi : lo;
+    }
+    Butterfly<O / 2, N / 2>::pick(x, hh);
+  }
+};
+
+template <int N>
+struct Butterfly<0, N> {
+  __device__ static __forceinline__ void sum(f32x64&, int) {}
+  __device__ static __forceinline__ void pick(f32x64&, int) {}
+};
+
+// Reductions over all lanes of one token: its R lanes in both halves.
+template <int R>
+__device__ __forceinline__ float token_sum(float x) {
+#pragma unroll
+  for (int o = 1; o < R; o <<= 1) x += __shfl_xor(x, o);
+  return x + __shfl_xor(x, 32);
+}
+
+template <int R>
+__device__ __forceinline__ float token_max(float x) {
+#pragma unroll
+  for (int o = 1; o < R; o <<= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return fmaxf(x, __shfl_xor(x, 32));
+}
+
+template <typename T, typename S, int D, int R, int DI>
+__global__ __launch_bounds__(256, 2) void kl_teacher_kernel(AttnParams p, KlParams kp) {
+  using M = Mma<T>;
+  using IO = ChunkIO<T, S>;
+  using frag = typename M::frag;
+  constexpr int KPL = M::KPL, KSTEP = M::KSTEP, NKS = D / KSTEP, NKI = DI / KSTEP;
+  constexpr int E = 16 / (int)sizeof(T);  // elements per 16-byte chunk of T
+  constexpr int LDK = D + E, LDI = DI + E;
+  constexpr int TPW = 32 / R, TPP = 4 * TPW;
+  constexpr int NV = 64;      // score registers per lane: 4 key tiles x 16
+  constexpr int NK = NV / R;  // keys a lane owns after the head butterfly
+  __shared__ __align__(16) T Ks[kBlock * LDK];
+  __shared__ __align__(16) T KIs[kBlock * LDI];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int h = lane >> 5, l32 = lane & 31;
+  const int hh = l32 % R;
+  const int64_t total = p.direct ? p.n_direct : (int64_t)*p.n_items;
+  const float sl2 = p.scale_log2;  // main scale (key scale included) in log2 units
+
+  for (int64_t item = blockIdx.x; item < total; item += gridDim.x) {
+    int b, g, c, ntok;
+    const int32_t* toks;
+    int32_t direct_tok = 0;
+    if (p.direct) {
+      c = p.sel[item];
+      if (c < 0 || c >= p.nb) continue;  // uniform across the workgroup
+      const int slot = (int)(item % p.topk);
+      const int64_t rest = item / p.topk;
+      const int i = (int)(rest % p.S_q);
+      const int64_t bg = rest / p.S_q;
+      g = (int)(bg % p.G);
+      b = (int)(bg / p.G);
+      direct_tok = (i << 6) | slot;
+      toks = nullptr;
+      ntok = 1;
+    } else {
+      const int bk = p.item_bucket[item];
+      const int start = (int)(item - p.item_off[bk]) * p.tpi;
+      ntok = min(p.tpi, p.counts[bk] - start);
+      toks = p.entries + p.offsets[bk] + start;
+      c = bk % p.nb;
+      const int bg = bk / p.nb;
+      g = bg % p.G;
+      b = bg / p.G;
+    }
+    // an unmapped page, or a block past the end of the cache: nothing to score (uniform)
+    const int slen = cache_len(p.cm, p.S_k, b);
+    const int64_t kv0 = block_offset(p.cm, p.S_k, p.G, D, b, g, c);
+    const int64_t ki0 = block_offset(p.cm, p.S_k, 1, DI, b, 0, c);
+    if (kv0 < 0 || ki0 < 0 || (int64_t)c * kBlock >= slen) continue;
+    const int64_t qo = first_pos(p.cm, p.q_offset, p.S_q, p.S_k, b);
+
+    __syncthreads();  // the previous item is done with the LDS tiles
+    {
+      // K and the index keys of the block; rows past the cache end re-read its
+      // last row and are zeroed; every load is issued before any is stored
+      const int rows_ok = (int)min((int64_t)kBlock, (int64_t)slen - (int64_t)c * kBlock);
+      constexpr int KU = kBlock * D / E / 256, IU = kBlock * DI / E / 256;
+      static_assert(KU >= 1 && IU >= 1 && (kBlock * DI / E) % 256 == 0, "staging covers the block");
+      const S* ksrc = (const S*)p.k + kv0;
+      const S* isrc = (const S*)kp.k_idx + ki0;
+      typename IO::raw kx[KU], ix[IU];
+#pragma unroll
+      for (int u = 0; u < KU; ++u) {
+        const int ch = threadIdx.x + u * 256;
+        const int row = ch / (D / E), col = ch - row * (D / E);
+        kx[u] = IO::load(ksrc + (int64_t)min(row, rows_ok - 1) * D + col * E);
+      }
+#pragma unroll
+      for (int u = 0; u < IU; ++u) {
+        const int ch = threadIdx.x + u * 256;
+        const int row = ch / (DI / E), col = ch - row * (DI / E);
+        ix[u] = IO::load(isrc + (int64_t)min(row, rows_ok - 1) * DI + col * E);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int u = 0; u < KU; ++u) {
+        const int ch = threadIdx.x + u * 256;
+        const int row = ch / (D / E), col = ch - row * (D / E);
+        *(i32x4*)&Ks[row * LDK + col * E] = row < rows_ok ? IO::widen(kx[u]) : i32x4{};
+      }
+#pragma unroll
+      for (int u = 0; u < IU; ++u) {
+        const int ch = threadIdx.x + u * 256;
+        const int row = ch / (DI / E), col = ch - row * (DI / E);
+        *(i32x4*)&KIs[row * LDI + col * E] = row < rows_ok ? IO::widen(ix[u]) : i32x4{};
+      }
+    }
+    __syncthreads();
+
+    const int64_t key0 = (int64_t)c * kBlock;
+    for (int p0 = 0; p0 < ntok; p0 += TPP) {
+      if (p0 + wave * TPW >= ntok) continue;  // this wave has no rows in this pass
+      const int tslot = p0 + wave * TPW + l32 / R;
+      const bool in_list = tslot < ntok;
+      const int32_t entry = in_list ? (toks ? toks[tslot] : direct_tok) : 0;
+      const int i = entry >> 6, slot = entry & 63;
+      const int64_t rel = qo + i - key0;  // query position relative to the block
+      const bool rv = in_list && rel >= 0;
+      const int lim = (!rv || rel >= kBlock) ? kBlock - 1 : (int)rel;  // last visible key
+      const bool masked = __any(lim < kBlock - 1);  // the causal mask only bites in a local block
+      const int head = g * R + hh;
+
+      // teacher: this head's probabilities exp(scale q.k - lse), 0 where masked
+      f32x64 pv;
+      {
+        frag qf[NKS];
+        const T* qrow = (const T*)p.q + (((int64_t)b * p.S_q + i) * p.Hq + head) * D;
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) qf[ks] = *(const frag*)(qrow + ks * KSTEP + h * KPL);
+        const float lse2 = kp.lse[((int64_t)b * p.Hq + head) * p.S_q + i] * kLog2e;
+        __builtin_amdgcn_sched_barrier(0);
+        f32x16 sacc[4];
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) sacc[kt] = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+          for (int kt = 0; kt < 4; ++kt) {
+            const frag a = *(const frag*)&Ks[(kt * 32 + l32) * LDK + ks * KSTEP + h * KPL];
+            sacc[kt] = M::mma(a, qf[ks], sacc[kt]);
+          }
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) pv[kt * 16 + j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][j], sl2, -lse2));
+        if (masked) {
+#pragma unroll
+          for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+              if (kt * 32 + c_row(j, h) > lim) pv[kt * 16 + j] = 0.f;
+        }
+      }
+      Butterfly<R / 2, NV>::sum(pv, hh);  // pv[0, NK): sums over the token's heads
+
+      // student: the token's index scores (times index_scale), -inf where masked
+      f32x64 sv;
+      {
+        frag qif[NKI];
+        const T* qirow = (const T*)kp.q_idx + (((int64_t)b * p.S_q + i) * p.G + g) * DI;
+#pragma unroll
+        for (int ks = 0; ks < NKI; ++ks) qif[ks] = *(const frag*)(qirow + ks * KSTEP + h * KPL);
+        __builtin_amdgcn_sched_barrier(0);
+        f32x16 siacc[4];
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) siacc[kt] = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < NKI; ++ks)
+#pragma unroll
+          for (int kt = 0; kt < 4; ++kt) {
+            const frag a = *(const frag*)&KIs[(kt * 32 + l32) * LDI + ks * KSTEP + h * KPL];
+            siacc[kt] = M::mma(a, qif[ks], siacc[kt]);
+          }
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) sv[kt * 16 + j] = siacc[kt][j] * kp.index_scale;
+        if (masked) {
+#pragma unroll
+          for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+              if (kt * 32 + c_row(j, h) > lim) sv[kt * 16 + j] = kNegInf;
+        }
+      }
+      Butterfly<R / 2, NV>::pick(sv, hh);
+
+      // this lane's keys, then the token's totals over its lanes
+      float ent = 0.f, smax = kNegInf;
+#pragma unroll
+      for (int k = 0; k < NK; ++k) {
+        const float pb = pv[k] * (1.0f / R);
+        ent += pb > 0.f ? pb * (__builtin_amdgcn_logf(pb) * kLn2 - sv[k]) : 0.f;
+        smax = fmaxf(smax, sv[k]);
+      }
+      ent = token_sum<R>(ent);
+      smax = token_max<R>(smax);
+      float sexp = 0.f;
+      if (smax != kNegInf) {
+#pragma unroll
+        for (int k = 0; k < NK; ++k) sexp += __builtin_amdgcn_exp2f((sv[k] - smax) * kLog2e);
+      }
+      sexp = token_sum<R>(sexp);
+      if (rv && hh == 0 && h == 0) {
+        const int64_t ptok = (((int64_t)b * p.S_q + i) * p.G + g) * p.topk + slot;
+        kp.part[ptok * 3 + 0] = ent;
+        kp.part[ptok * 3 + 1] = smax;
+        kp.part[ptok * 3 + 2] = sexp;
+      }
+    }
+  }
+}
+
+// One thread per (b, g, i): the block terms of the row's visible selected
+// blocks give KL = sum ent + lse_idx, lse_idx = m + log sum_s l_s e^(m_s - m).
+// A row that sees no block gets KL = 0 and lse_idx = -inf.
+__global__ __launch_bounds__(256) void kl_combine_kernel(AttnParams p, KlParams kp) {
+  const int64_t row = (int64_t)blockIdx.x * 256 + threadIdx.x;  // (b * G + g) * S_q + i
+  if (row >= (int64_t)p.B * p.G * p.S_q) return;
+  const int i = (int)(row % p.S_q);
+  const int64_t bg = row / p.S_q;
+  const int g = (int)(bg % p.G);
+  const int b = (int)(bg / p.G);
+  const int64_t t = first_pos(p.cm, p.q_offset, p.S_q, p.S_k, b) + i;
+  const int32_t* srow = p.sel + row * p.topk;
+  const float* part = kp.part + ((((int64_t)b * p.S_q + i) * p.G + g) * p.topk) * 3;
+  float ent = 0.f, m = kNegInf;
+  for (int s = 0; s < p.topk; ++s) {
+    const int c = srow[s];
+    if (c < 0 || c >= p.nb || (int64_t)c * kBlock > t || !block_mapped(p.cm, b, c)) continue;
+    ent += part[s * 3 + 0];
+    m = fmaxf(m, part[s * 3 + 1]);
+  }
+  float l = 0.f;
+  if (m != kNegInf) {
+    for (int s = 0; s < p.topk; ++s) {
+      const int c = srow[s];
+      if (c < 0 || c >= p.nb || (int64_t)c * kBlock > t || !block_mapped(p.cm, b, c)) continue;
+      l += part[s * 3 + 2] * __builtin_amdgcn_exp2f((part[s * 3 + 1] - m) * kLog2e);
+    }
+  }
+  const float lse = m != kNegInf ? m + __builtin_amdgcn_logf(l) * kLn2 : kNegInf;
+  kp.kl[row] = m != kNegInf ? ent + lse : 0.f;
+  if (kp.idx_lse) kp.idx_lse[row] = lse;
+}
+
+template <typename T, typename S, int D, int R, int DI>
+static hipError_t launch_kl_t(const AttnParams& p, const KlParams& kp, hipStream_t s, const KernelTimer* tm) {
+  launch_gather(p, s, tm);
+  timer_start(tm, kKernKlTeacher, s);
+  hipLaunchKernelGGL((kl_teacher_kernel<T, S, D, R, DI>), dim3(p.grid), dim3(256), 0, s, p, kp);
+  timer_stop(tm, kKernKlTeacher, s);
+  timer_start(tm, kKernKlCombine, s);
+  const int64_t rows = (int64_t)p.B * p.G * p.S_q;
+  hipLaunchKernelGGL(kl_combine_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, s, p, kp);
+  timer_stop(tm, kKernKlCombine, s);
+  return hipGetLastError();
+}
+
+template <typename T, typename S, int D, int R>
+static hipError_t launch_kl_r(const AttnParams& p, const KlParams& kp, hipStream_t s, const KernelTimer* tm) {
+  switch (kp.index_dim) {
+    case 32: return launch_kl_t<T, S, D, R, 32>(p, kp, s, tm);
+    case 64: return launch_kl_t<T, S, D, R, 64>(p, kp, s, tm);
+    case 128: return launch_kl_t<T, S, D, R, 128>(p, kp, s, tm);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <typename T, typename S, int D>
+static hipError_t launch_kl_d(const AttnParams& p, const KlParams& kp, hipStream_t s, const KernelTimer* tm) {
+  switch (p.r) {
+    case 1: return launch_kl_r<T, S, D, 1>(p, kp, s, tm);
+    case 2: return launch_kl_r<T, S, D, 2>(p, kp, s, tm);
+    case 4: return launch_kl_r<T, S, D, 4>(p, kp, s, tm);
+    case 8: return launch_kl_r<T, S, D, 8>(p, kp, s, tm);
+    case 16: return launch_kl_r<T, S, D, 16>(p, kp, s, tm);
+    case 32: return launch_kl_r<T, S, D, 32>(p, kp, s, tm);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <typename T, typename S>
+static hipError_t launch_kl_s(const AttnParams& p, const KlParams& kp, hipStream_t s, const KernelTimer* tm) {
+  if (p.d == 64) return launch_kl_d<T, S, 64>(p, kp, s, tm);
+  if (p.d == 128) return launch_kl_d<T, S, 128>(p, kp, s, tm);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_kl_teacher(const AttnParams& p, const KlParams& kp, bool bf16_inputs, bool fp8_cache,
+                             hipStream_t s, const KernelTimer* tm) {
+  if (fp8_cache) return bf16_inputs ? launch_kl_s<bf16, e4m3>(p, kp, s, tm) : hipErrorInvalidValue;
+  if (bf16_inputs) return launch_kl_s<bf16, bf16>(p, kp, s, tm);
+  return launch_kl_s<float, float>(p, kp, s, tm);
+}
+
+}  // namespace msa

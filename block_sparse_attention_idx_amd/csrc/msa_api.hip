@@ -86,13 +86,15 @@ msa_status check_shape(const msa_shape* s, int op) {
   if (s->q_len >= (1 << 25)) return fail(MSA_ERR_UNSUPPORTED, "q_len must be < 2^25");
   if ((int64_t)s->batch * s->num_kv_heads * ceil_div(s->kv_len, msa::kBlock) >= (1LL << 31))
     return fail(MSA_ERR_UNSUPPORTED, "batch * kv heads * blocks exceeds 2^31");
-  if (op == MSA_OP_INDEX_SELECT || op == MSA_OP_FWD) {
+  const bool index_op = op == MSA_OP_INDEX_SELECT || op == MSA_OP_FWD || op == MSA_OP_KL_TEACHER;
+  const bool attn_op = op == MSA_OP_SPARSE_ATTN || op == MSA_OP_FWD || op == MSA_OP_KL_TEACHER;
+  if (index_op) {
     if (s->index_dim != 32 && s->index_dim != 64 && s->index_dim != 128)
       return fail(MSA_ERR_UNSUPPORTED, "index_dim %d: built for 32, 64, 128", s->index_dim);
     if ((int64_t)s->q_len * s->num_kv_heads * s->batch >= (1LL << 31))
       return fail(MSA_ERR_UNSUPPORTED, "batch * q_len * groups exceeds 2^31");
   }
-  if (op == MSA_OP_SPARSE_ATTN || op == MSA_OP_FWD) {
+  if (attn_op) {
     if (s->head_dim != 64 && s->head_dim != 128)
       return fail(MSA_ERR_UNSUPPORTED, "head_dim %d: built for 64 and 128", s->head_dim);
     const int r = s->num_q_heads / s->num_kv_heads;
@@ -329,7 +331,7 @@ extern "C" {
 const char* msa_version(void) { return "0.2.0"; }
 
 msa_status msa_set_kernel_timer(int kernel, void* start_event, void* stop_event) {
-  if (kernel < MSA_KERNEL_NONE || kernel > MSA_KERNEL_COMBINE)
+  if (kernel < MSA_KERNEL_NONE || kernel > MSA_KERNEL_KL_COMBINE)
     return fail(MSA_ERR_INVALID, "unknown kernel id %d", kernel);
   if (kernel == MSA_KERNEL_NONE || !start_event || !stop_event) {
     g_timer = {0, nullptr, nullptr};
@@ -355,10 +357,10 @@ const char* msa_last_error(void) { return g_last_error.c_str(); }
 size_t msa_workspace_size_kvcache(const msa_shape* s, const msa_kv_cache* cache, int op) {
   const std::string saved = g_last_error;
   size_t r = 0;
-  if (op >= MSA_OP_INDEX_SELECT && op <= MSA_OP_FWD && check_shape(s, op) == MSA_OK &&
+  if (op >= MSA_OP_INDEX_SELECT && op <= MSA_OP_KL_TEACHER && check_shape(s, op) == MSA_OK &&
       check_cache(s, cache) == MSA_OK && s->q_len > 0) {
     if (op == MSA_OP_INDEX_SELECT) r = plan_index(s, cache).bytes;
-    else if (op == MSA_OP_SPARSE_ATTN) r = plan_attn(s, cache).bytes;
+    else if (op == MSA_OP_SPARSE_ATTN || op == MSA_OP_KL_TEACHER) r = plan_attn(s, cache).bytes;
     else r = sel_bytes(s) + std::max(plan_index(s, cache).bytes, plan_attn(s, cache).bytes);
   }
   g_last_error = saved;
@@ -444,6 +446,37 @@ msa_status msa_fwd_kvcache(const msa_shape* s, const msa_kv_cache* cache, const 
   ap.p.lse = lse;
   return hip_status(msa::launch_sparse_attention(ap.p, s->dtype == MSA_BF16, fp8_cache(s), hs, timer()),
                     "sparse attention launch");
+}
+
+msa_status msa_kl_teacher_fwd_kvcache(const msa_shape* s, const msa_kv_cache* cache, const void* q, const void* k,
+                                      const void* q_idx, const void* k_idx, const int32_t* sel, const float* lse,
+                                      float index_scale, float* kl, float* idx_lse, void* ws, size_t ws_bytes,
+                                      void* stream) {
+  msa_status st = check_shape(s, MSA_OP_KL_TEACHER);
+  if (st != MSA_OK || (st = check_cache(s, cache)) != MSA_OK) return st;
+  if (!q || !k || !q_idx || !k_idx || !sel || !lse || !kl)
+    return fail(MSA_ERR_INVALID, "q, k, q_idx, k_idx, sel, lse and kl must be non-NULL");
+  if (!std::isfinite(index_scale)) return fail(MSA_ERR_INVALID, "index_scale must be finite");
+  if (s->q_len == 0) return MSA_OK;
+  AttnPlan ap = plan_attn(s, cache);
+  if ((st = check_ws(ws, ws_bytes, ap.bytes)) != MSA_OK) return st;
+  bind_attn(ap, (char*)ws);
+  ap.p.q = q;
+  ap.p.k = k;
+  ap.p.sel = sel;
+  // the per-block terms take the place of the partial outputs (3 floats per
+  // (token, group, slot) against r * d values)
+  msa::KlParams kp{q_idx, k_idx, lse, index_scale, s->index_dim, (float*)ap.p.part_o, kl, idx_lse};
+  clear_stale_hip_error();
+  return hip_status(msa::launch_kl_teacher(ap.p, kp, s->dtype == MSA_BF16, fp8_cache(s), (hipStream_t)stream, timer()),
+                    "KL teacher launch");
+}
+
+msa_status msa_kl_teacher_fwd(const msa_shape* s, const void* q, const void* k, const void* q_idx, const void* k_idx,
+                              const int32_t* sel, const float* lse, float index_scale, float* kl, float* idx_lse,
+                              void* ws, size_t ws_bytes, void* stream) {
+  return msa_kl_teacher_fwd_kvcache(s, nullptr, q, k, q_idx, k_idx, sel, lse, index_scale, kl, idx_lse, ws, ws_bytes,
+                                    stream);
 }
 
 msa_status msa_fwd(const msa_shape* s, const void* q, const void* k, const void* v, const void* q_idx,

@@ -111,7 +111,7 @@ typedef struct {
   int32_t pad;          /* must be 0                                            */
 } msa_shape;            /* 72 bytes                                             */
 
-enum { MSA_OP_INDEX_SELECT = 0, MSA_OP_SPARSE_ATTN = 1, MSA_OP_FWD = 2 };
+enum { MSA_OP_INDEX_SELECT = 0, MSA_OP_SPARSE_ATTN = 1, MSA_OP_FWD = 2, MSA_OP_KL_TEACHER = 3 };
 
 /* Bytes of workspace the given op needs for this shape (0 when the shape is
  * invalid or unsupported; the call itself then reports why).  The same shape
@@ -190,6 +190,35 @@ msa_status msa_fwd_kvcache(const msa_shape* shape, const msa_kv_cache* cache, co
                            const void* v, const void* q_idx, const void* k_idx, void* out, int32_t* sel_out,
                            float* lse, void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- KL-alignment teacher (forward only) ---------------------------------
+ *
+ * Top-k is not differentiable, so MSA trains the index branch with a KL loss
+ * towards the main branch; the teacher is the main distribution over the
+ * selected tokens averaged over the heads of the GQA group (snilld.dk page,
+ * section "Træning og stabilisering"; Hungarian page, section "A betanítás és
+ * a kernel-optimalizáció").  For each (b, g, i), with T the tokens the main
+ * branch attends to (the visible tokens of the selected blocks):
+ *    pbar(j)  = mean over the r heads h of group g of softmax_T(scale * q_h . k_j)
+ *    log q(j) = log_softmax_T(index_scale * q_idx[b,i,g,:] . k_idx[b,j,:])
+ *    kl[b,g,i]      = sum_{j in T} pbar(j) * (log pbar(j) - log q(j))   (natural log)
+ *    idx_lse[b,g,i] = log sum_{j in T} exp(index_scale * q_idx . k_idx_j)
+ * sel and lse are those of the forward (msa_fwd's sel_out and lse, or any
+ * selection with the main branch's lse for it); the teacher then needs no
+ * second softmax pass.  kl and idx_lse are fp32 [B, G, S_q]; idx_lse may be
+ * NULL.  A row that sees no token gets kl = 0 and idx_lse = -inf.
+ * index_scale must be finite (1 keeps the raw scores the selection ranks).
+ * The shape, caches, FP8 format and k_scale are as for the main branch
+ * (v_scale is not used); workspace: msa_workspace_size(shape,
+ * MSA_OP_KL_TEACHER). */
+msa_status msa_kl_teacher_fwd(const msa_shape* shape, const void* q, const void* k, const void* q_idx,
+                              const void* k_idx, const int32_t* sel, const float* lse, float index_scale,
+                              float* kl, float* idx_lse, void* workspace, size_t workspace_bytes, void* stream);
+
+msa_status msa_kl_teacher_fwd_kvcache(const msa_shape* shape, const msa_kv_cache* cache, const void* q,
+                                      const void* k, const void* q_idx, const void* k_idx, const int32_t* sel,
+                                      const float* lse, float index_scale, float* kl, float* idx_lse,
+                                      void* workspace, size_t workspace_bytes, void* stream);
+
 /* Kernels of the forward path, for msa_set_kernel_timer. */
 typedef enum {
   MSA_KERNEL_NONE = 0,
@@ -197,7 +226,9 @@ typedef enum {
   MSA_KERNEL_TOPK_MERGE = 2,  /* merge of the partial lists, local block, -1 pad   */
   MSA_KERNEL_GATHER = 3,      /* query gather: histogram, scan, scatter (4 launches) */
   MSA_KERNEL_ATTENTION = 4,   /* KV-outer sparse attention (partial states)         */
-  MSA_KERNEL_COMBINE = 5      /* merge of the partial states into out and lse       */
+  MSA_KERNEL_COMBINE = 5,     /* merge of the partial states into out and lse       */
+  MSA_KERNEL_KL_TEACHER = 6,  /* KL teacher: per-block terms                        */
+  MSA_KERNEL_KL_COMBINE = 7   /* KL teacher: per-row totals                         */
 } msa_kernel;
 
 /* Profiling hook.  For the calling thread, every later msa_* call records

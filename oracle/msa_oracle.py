@@ -57,6 +57,15 @@ definition per sequence, with the queries at the last S_q positions of each
 cache; a row before the start of its cache (t < 0) sees no key, and the reading
 taken is: no selection (-1 only), output 0, lse -inf.  ``page_gather`` reads a
 sequence's cache out of a pool of 128-token pages.
+
+KL-alignment teacher (forward only).  Top-k is not differentiable, so a KL loss
+trains the index branch to match the main branch; the teacher is the main
+distribution over the selected tokens, averaged over the group's heads (the
+snilld.dk page, "Træning og stabilisering"; the Hungarian page, "A betanítás és
+a kernel-optimalizáció").  Readings taken in ``kl_teacher``: both distributions
+are over the tokens the main branch attends to; the index distribution is the
+softmax of the raw index scores (times an optional index_scale, 1 by default);
+the loss is KL(teacher || index) in natural log.
 """
 from __future__ import annotations
 
@@ -66,6 +75,7 @@ from typing import Iterable, Optional, Sequence, Tuple
 import numpy as np
 
 __all__ = [
+    "kl_teacher",
     "page_gather",
     "msa_forward_varlen",
     "e4m3_to_f64",
@@ -337,3 +347,50 @@ def msa_forward_varlen(q, k_seqs, v_seqs, q_idx, k_idx_seqs, topk: int, block_si
         sel[b, :, i0:] = sl[0]
         lse[b, :, i0:] = ls[0]
     return out, sel, lse
+
+
+# ---------------------------------------------------------------------------
+# KL-alignment teacher (forward)
+# ---------------------------------------------------------------------------
+
+def kl_teacher(q, k, q_idx, k_idx, sel, q_offset: int = 0, block_size: int = 128,
+               scale: Optional[float] = None, index_scale: float = 1.0,
+               rows: Optional[Sequence[Tuple[int, int]]] = None):
+    """KL divergence of the index distribution from the group-averaged main one.
+
+    For each (b, g, i) with T the tokens the main branch attends to (token_set):
+      teacher  pbar(j) = mean over the r heads h of group g of softmax_T(scale * q_h . k_j)
+      index    log qi(j) = log_softmax_T(index_scale * q_idx[b, i, g] . k_idx[b, j])
+      kl       = sum_j pbar(j) * (log pbar(j) - log qi(j))     (0 log 0 = 0)
+    Returns (kl [B, G, S_q], idx_lse [B, G, S_q]) in float64, idx_lse being the
+    log-sum-exp of index_scale * scores over T.  A row with an empty T (before
+    the start of its cache) gets kl = 0 and idx_lse = -inf; rows not listed in
+    ``rows`` (when given) are NaN.
+    """
+    q, k, q_idx, k_idx, sel = (np.asarray(a) for a in (q, k, q_idx, k_idx, sel))
+    B, S_q, Hq, d = q.shape
+    G = k.shape[1]
+    r = Hq // G
+    if scale is None or scale == 0.0:
+        scale = 1.0 / math.sqrt(d)
+    kl = np.full((B, G, S_q), np.nan)
+    ilse = np.full((B, G, S_q), np.nan)
+    todo = [(b, i) for b in range(B) for i in range(S_q)] if rows is None else rows
+    for b, i in todo:
+        t = q_offset + i
+        for g in range(G):
+            T = token_set(sel[b, g, i], t, block_size)
+            if T.size == 0:
+                kl[b, g, i], ilse[b, g, i] = 0.0, -np.inf
+                continue
+            s = scale * (_f64(q[b, i, g * r:(g + 1) * r]) @ _f64(k[b, g, T]).T)   # [r, n]
+            p = np.exp(s - s.max(axis=1, keepdims=True))
+            p /= p.sum(axis=1, keepdims=True)
+            pbar = p.mean(axis=0)
+            si = index_scale * (_f64(k_idx[b, T]) @ _f64(q_idx[b, i, g]))            # [n]
+            m = si.max()
+            lse = m + math.log(np.exp(si - m).sum())
+            plogp = np.where(pbar > 0, pbar * np.log(np.where(pbar > 0, pbar, 1.0)), 0.0)
+            kl[b, g, i] = float(plogp.sum() - (pbar * (si - lse)).sum())
+            ilse[b, g, i] = lse
+    return kl, ilse

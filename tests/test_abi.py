@@ -186,3 +186,18 @@ def test_kvcache_descriptor_checks():
     need_fixed = L.msa_workspace_size_kvcache(ctypes.byref(sh), None, msa.OP_INDEX_SELECT)
     assert need_var > 0 and need_fixed == 0
     assert L.msa_workspace_size_kvcache(ctypes.byref(sh), None, msa.OP_FWD) == msa.workspace_size(sh, msa.OP_FWD)
+
+
+def test_kl_teacher_checks():
+    L = msa.lib()
+    sh = _shape(2)
+    args = lambda **kw: [ctypes.byref(sh)] + [kw.get(n, FAKE) for n in ("q", "k", "q_idx", "k_idx", "sel", "lse")] + \
+        [ctypes.c_float(kw.get("isc", 1.0)), kw.get("kl", FAKE), None, kw.get("ws", None), kw.get("wsb", 0), None]
+    for name in ("q", "k", "q_idx", "k_idx", "sel", "lse", "kl"):
+        assert L.msa_kl_teacher_fwd(*args(**{name: None})) == -1, name
+    assert L.msa_kl_teacher_fwd(*args(isc=float("nan"))) == -1
+    assert "index_scale" in L.msa_last_error().decode()
+    assert L.msa_kl_teacher_fwd(*args()) == -3  # valid: only the workspace is missing
+    need = msa.workspace_size(sh, msa.OP_KL_TEACHER)
+    assert need == msa.workspace_size(sh, msa.OP_SPARSE_ATTN) > 0
+    assert msa.lib().msa_set_kernel_timer(7, None, None) == 0 and msa.lib().msa_set_kernel_timer(8, None, None) == -1

@@ -603,3 +603,81 @@ def test_varlen_positions_against_torch_sdpa():
                 assert np.allclose(out[b, i, h], ref, atol=1e-12)
                 s_ = (ks[b][g, :t + 1] @ q[b, i, h]) / math.sqrt(d)
                 assert abs(lse[b, h, i] - (s_.max() + math.log(np.exp(s_ - s_.max()).sum()))) < 1e-12
+
+
+# --- KL-alignment teacher (forward) --------------------------------------------
+# Teacher: the main distribution over the selected tokens averaged over the
+# group's heads (snilld page, "Træning og stabilisering"); student: the softmax
+# of the index scores over the same tokens; loss KL(teacher || student).
+
+def _kl_case(seed, B=2, S_q=40, S_k=200, qo=160, G=2, r=4, d=16, D=8, k=3, Bk=32):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, S_q, G * r, d))
+    kk = rng.standard_normal((B, G, S_k, d))
+    qi = rng.integers(-3, 4, (B, S_q, G, D)).astype(np.float64)
+    ki = rng.integers(-3, 4, (B, S_k, D)).astype(np.float64)
+    sel = orc.index_select(qi, ki, k, qo, Bk)
+    return q, kk, qi, ki, sel, qo, Bk
+
+
+def test_kl_teacher_against_torch_kl_div():
+    q, kk, qi, ki, sel, qo, Bk = _kl_case(1)
+    kl, ilse = orc.kl_teacher(q, kk, qi, ki, sel, qo, Bk, index_scale=0.7)
+    B, S_q, Hq, d = q.shape
+    G, r = kk.shape[1], Hq // kk.shape[1]
+    S_k = kk.shape[2]
+    for b in range(B):
+        for g in range(G):
+            # dense masks from the selection, softmaxes and KL by torch primitives
+            mask = torch.zeros(S_q, S_k, dtype=torch.bool)
+            for i in range(S_q):
+                for c in sel[b, g, i]:
+                    if c >= 0:
+                        mask[i, c * Bk:min((c + 1) * Bk, qo + i + 1)] = True
+            s = torch.einsum("ihd,jd->hij", torch.from_numpy(q[b, :, g * r:(g + 1) * r]),
+                             torch.from_numpy(kk[b, g])) / math.sqrt(d)
+            pbar = torch.softmax(s.masked_fill(~mask, -math.inf), dim=-1).mean(0)
+            si = 0.7 * (torch.from_numpy(qi[b, :, g]) @ torch.from_numpy(ki[b]).T)
+            logq = torch.log_softmax(si.masked_fill(~mask, -math.inf), dim=-1)
+            ref = F.kl_div(logq.masked_fill(~mask, 0.0), pbar, reduction="none").sum(-1)
+            assert np.allclose(kl[b, g], ref.numpy(), atol=1e-12, rtol=1e-10)
+            assert np.allclose(ilse[b, g], torch.logsumexp(si.masked_fill(~mask, -math.inf), -1).numpy(), atol=1e-12)
+
+
+def test_kl_teacher_closed_forms():
+    q, kk, qi, ki, sel, qo, Bk = _kl_case(2, r=1, D=16)
+    d = q.shape[3]
+    # index scores equal to the main scores: the index distribution is the teacher, KL = 0
+    qi2 = q[:, :, :, :] / math.sqrt(d)        # r = 1: one head per group, q_idx = scale * q
+    ki2 = kk[:, 0]                             # G = 2 groups share the index key: use group 0 only
+    kl, _ = orc.kl_teacher(q[:, :, :1], kk[:, :1], qi2[:, :, :1], ki2, sel[:, :1], qo, Bk)
+    assert np.abs(kl).max() < 1e-12
+    # a uniform teacher (q = 0): KL = lse(s) - mean(s) - log n over the token set
+    q0 = np.zeros_like(q)
+    kl, ilse = orc.kl_teacher(q0, kk, qi, ki, sel, qo, Bk)
+    for b, g, i in [(0, 0, 0), (1, 1, 39), (0, 1, 17)]:
+        T = orc.token_set(sel[b, g, i], qo + i, Bk)
+        si = ki[b, T] @ qi[b, i, g]
+        m = si.max()
+        lse = m + math.log(np.exp(si - m).sum())
+        assert abs(kl[b, g, i] - (lse - si.mean() - math.log(len(T)))) < 1e-12
+        assert abs(ilse[b, g, i] - lse) < 1e-12
+    # index_scale -> 0: a uniform student, KL = sum pbar log pbar + log n >= 0
+    kl, _ = orc.kl_teacher(q, kk, qi, ki, sel, qo, Bk, index_scale=0.0)
+    assert (kl > -1e-12).all()
+
+
+def test_kl_teacher_invariants():
+    q, kk, qi, ki, sel, qo, Bk = _kl_case(3)
+    kl, _ = orc.kl_teacher(q, kk, qi, ki, sel, qo, Bk)
+    assert (kl >= -1e-12).all()  # Gibbs' inequality
+    # identical heads in a group: the teacher is that head's own distribution
+    qs = np.repeat(q[:, :, ::4], 4, axis=2)   # r = 4: every head equal to the group's first
+    kl_rep, _ = orc.kl_teacher(qs, kk, qi, ki, sel, qo, Bk)
+    kl_one, _ = orc.kl_teacher(q[:, :, ::4], kk, qi, ki, sel, qo, Bk)
+    assert np.allclose(kl_rep, kl_one, atol=1e-12)
+    # rows before their cache (empty token set): 0 and -inf
+    sel2 = sel.copy()
+    sel2[0, 0, 5] = -1
+    kl2, ilse2 = orc.kl_teacher(q, kk, qi, ki, sel2, qo, Bk)
+    assert kl2[0, 0, 5] == 0.0 and np.isneginf(ilse2[0, 0, 5])
