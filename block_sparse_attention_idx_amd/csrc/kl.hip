@@ -37,10 +37,27 @@ constexpr float kLn2 = 0.69314718055994531f;
 // register select (an array indexed that way would be placed in memory).
 typedef float f32x64 __attribute__((ext_vector_type(64)));
 
-// Butterfly over the R lanes of a token (offsets O = R/2, R/4, ..., 1): at each
+// The partner of a lane at butterfly step O (lanes of a token are R aligned,
+// consecutive lanes): lanes differing in bit 0 or bit 1 (quad permutes), lanes
+// i and 7 - i of each 8 (half-row mirror) and i and 15 - i of each 16 (row
+// mirror) -- all DPP moves, full-rate VALU with no LDS round trip -- and lanes
+// 16 apart (a lane permute).  Each pairs lanes whose bit O differs and whose
+// higher bits agree, which is all a butterfly needs.
+template <int O>
+__device__ __forceinline__ float partner(float x) {
+  const int v = __builtin_bit_cast(int, x);
+  if constexpr (O == 1) return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false));
+  else if constexpr (O == 2) return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false));
+  else if constexpr (O == 4) return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false));
+  else if constexpr (O == 8) return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false));
+  else return __shfl_xor(x, O);
+}
+
+// Butterfly over the R lanes of a token (steps O = R/2, R/4, ..., 1): at each
 // step a lane keeps the upper or lower half of its N values by bit O of hh.
-// sum() adds the partner's other half, pick() only selects.  Afterwards lane
-// hh holds, in x[0, 64 / R), slots [hh * 64 / R, (hh + 1) * 64 / R).
+// sum() adds the partner's copy of the kept half, pick() only selects.
+// Afterwards each lane holds 64 / R of the slots in x[0, 64 / R), every slot
+// held by one lane of the token, and pick() leaves the same slots as sum().
 template <int O, int N>
 struct Butterfly {
   __device__ static __forceinline__ void sum(f32x64& x, int hh) {
@@ -48,7 +65,8 @@ struct Butterfly {
 #pragma unroll
     for (int k = 0; k < N / 2; ++k) {
       const float lo = x[k], hi = x[k + N / 2];
-      x[k] = (up ? hi : lo) + __shfl_xor(up ? lo : hi, O);
+      const float slo = lo + partner<O>(lo), shi = hi + partner<O>(hi);
+      x[k] = up ? shi : slo;
     }
     Butterfly<O / 2, N / 2>::sum(x, hh);
   }
@@ -69,19 +87,18 @@ struct Butterfly<0, N> {
   __device__ static __forceinline__ void pick(f32x64&, int) {}
 };
 
-// Reductions over all lanes of one token: its R lanes in both halves.
-template <int R>
+// Reductions over all lanes of one token: its R lanes (steps 1, 2, 4, ...: each
+// step joins two groups already reduced) in both halves.
+template <int R, int O = 1>
 __device__ __forceinline__ float token_sum(float x) {
-#pragma unroll
-  for (int o = 1; o < R; o <<= 1) x += __shfl_xor(x, o);
-  return x + __shfl_xor(x, 32);
+  if constexpr (O < R) return token_sum<R, 2 * O>(x + partner<O>(x));
+  else return x + __shfl_xor(x, 32);
 }
 
-template <int R>
+template <int R, int O = 1>
 __device__ __forceinline__ float token_max(float x) {
-#pragma unroll
-  for (int o = 1; o < R; o <<= 1) x = fmaxf(x, __shfl_xor(x, o));
-  return fmaxf(x, __shfl_xor(x, 32));
+  if constexpr (O < R) return token_max<R, 2 * O>(fmaxf(x, partner<O>(x)));
+  else return fmaxf(x, __shfl_xor(x, 32));
 }
 
 template <typename T, typename S, int D, int R, int DI>
@@ -97,6 +114,7 @@ __global__ __launch_bounds__(256, 2) void kl_teacher_kernel(AttnParams p, KlPara
   constexpr int NK = NV / R;  // keys a lane owns after the head butterfly
   __shared__ __align__(16) T Ks[kBlock * LDK];
   __shared__ __align__(16) T KIs[kBlock * LDI];
+  __shared__ int32_t ent_s[kBlock];  // the item's token entries ((row << 6) | slot)
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int h = lane >> 5, l32 = lane & 31;
@@ -138,6 +156,7 @@ __global__ __launch_bounds__(256, 2) void kl_teacher_kernel(AttnParams p, KlPara
     const int64_t qo = first_pos(p.cm, p.q_offset, p.S_q, p.S_k, b);
 
     __syncthreads();  // the previous item is done with the LDS tiles
+    if ((int)threadIdx.x < ntok) ent_s[threadIdx.x] = toks ? toks[threadIdx.x] : direct_tok;
     {
       // K and the index keys of the block; rows past the cache end re-read its
       // last row and are zeroed; every load is issued before any is stored
@@ -176,27 +195,32 @@ __global__ __launch_bounds__(256, 2) void kl_teacher_kernel(AttnParams p, KlPara
     __syncthreads();
 
     const int64_t key0 = (int64_t)c * kBlock;
-    for (int p0 = 0; p0 < ntok; p0 += TPP) {
-      if (p0 + wave * TPW >= ntok) continue;  // this wave has no rows in this pass
-      const int tslot = p0 + wave * TPW + l32 / R;
-      const bool in_list = tslot < ntok;
-      const int32_t entry = in_list ? (toks ? toks[tslot] : direct_tok) : 0;
-      const int i = entry >> 6, slot = entry & 63;
+    const int head = g * R + hh;
+    // A wave's rows of pass ps: the token entry (from LDS), its Q row, index
+    // query row and main lse; loaded one pass ahead of their use.  Rows past
+    // the token list read token 0's (valid) rows and are never stored.
+    auto load_rows = [&](int ps, frag (&qf)[NKS], frag (&qif)[NKI], float& lse2, int32_t& entry) {
+      const int tslot = ps * TPP + wave * TPW + l32 / R;
+      entry = tslot < ntok ? ent_s[tslot] : -1;
+      const int i = entry >= 0 ? entry >> 6 : 0;
+      const T* qrow = (const T*)p.q + (((int64_t)b * p.S_q + i) * p.Hq + head) * D;
+      const T* qirow = (const T*)kp.q_idx + (((int64_t)b * p.S_q + i) * p.G + g) * DI;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) qf[ks] = *(const frag*)(qrow + ks * KSTEP + h * KPL);
+#pragma unroll
+      for (int ks = 0; ks < NKI; ++ks) qif[ks] = *(const frag*)(qirow + ks * KSTEP + h * KPL);
+      lse2 = kp.lse[((int64_t)b * p.Hq + head) * p.S_q + i] * kLog2e;
+    };
+    auto pass = [&](const frag (&qf)[NKS], const frag (&qif)[NKI], float lse2, int32_t entry) {
+      const int i = entry >= 0 ? entry >> 6 : 0, slot = entry & 63;
       const int64_t rel = qo + i - key0;  // query position relative to the block
-      const bool rv = in_list && rel >= 0;
+      const bool rv = entry >= 0 && rel >= 0;
       const int lim = (!rv || rel >= kBlock) ? kBlock - 1 : (int)rel;  // last visible key
       const bool masked = __any(lim < kBlock - 1);  // the causal mask only bites in a local block
-      const int head = g * R + hh;
 
-      // teacher: this head's probabilities exp(scale q.k - lse), 0 where masked
+      // teacher: this head's probabilities exp(scale q.k - lse)
       f32x64 pv;
       {
-        frag qf[NKS];
-        const T* qrow = (const T*)p.q + (((int64_t)b * p.S_q + i) * p.Hq + head) * D;
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) qf[ks] = *(const frag*)(qrow + ks * KSTEP + h * KPL);
-        const float lse2 = kp.lse[((int64_t)b * p.Hq + head) * p.S_q + i] * kLog2e;
-        __builtin_amdgcn_sched_barrier(0);
         f32x16 sacc[4];
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) sacc[kt] = f32x16{};
@@ -211,24 +235,12 @@ __global__ __launch_bounds__(256, 2) void kl_teacher_kernel(AttnParams p, KlPara
         for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
           for (int j = 0; j < 16; ++j) pv[kt * 16 + j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][j], sl2, -lse2));
-        if (masked) {
-#pragma unroll
-          for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-            for (int j = 0; j < 16; ++j)
-              if (kt * 32 + c_row(j, h) > lim) pv[kt * 16 + j] = 0.f;
-        }
       }
       Butterfly<R / 2, NV>::sum(pv, hh);  // pv[0, NK): sums over the token's heads
 
-      // student: the token's index scores (times index_scale), -inf where masked
+      // student: the token's index scores times index_scale
       f32x64 sv;
       {
-        frag qif[NKI];
-        const T* qirow = (const T*)kp.q_idx + (((int64_t)b * p.S_q + i) * p.G + g) * DI;
-#pragma unroll
-        for (int ks = 0; ks < NKI; ++ks) qif[ks] = *(const frag*)(qirow + ks * KSTEP + h * KPL);
-        __builtin_amdgcn_sched_barrier(0);
         f32x16 siacc[4];
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) siacc[kt] = f32x16{};
@@ -243,15 +255,22 @@ __global__ __launch_bounds__(256, 2) void kl_teacher_kernel(AttnParams p, KlPara
         for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
           for (int j = 0; j < 16; ++j) sv[kt * 16 + j] = siacc[kt][j] * kp.index_scale;
-        if (masked) {
-#pragma unroll
-          for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-            for (int j = 0; j < 16; ++j)
-              if (kt * 32 + c_row(j, h) > lim) sv[kt * 16 + j] = kNegInf;
-        }
       }
       Butterfly<R / 2, NV>::pick(sv, hh);
+      // Lane hh now holds register slots hh * NK + k (slot s: key tile s / 16,
+      // register s % 16).  The heads of a token share its visibility limit, so
+      // the causal mask of a local block applies here, after the head sums.
+      if (masked) {
+#pragma unroll
+        for (int k = 0; k < NK; ++k) {
+          const int sl = hh * NK + k;
+          const int key = (sl >> 4) * 32 + c_row(sl & 15, h);
+          if (key > lim) {
+            pv[k] = 0.f;
+            sv[k] = kNegInf;
+          }
+        }
+      }
 
       // this lane's keys, then the token's totals over its lanes
       float ent = 0.f, smax = kNegInf;
@@ -274,6 +293,24 @@ __global__ __launch_bounds__(256, 2) void kl_teacher_kernel(AttnParams p, KlPara
         kp.part[ptok * 3 + 0] = ent;
         kp.part[ptok * 3 + 1] = smax;
         kp.part[ptok * 3 + 2] = sexp;
+      }
+    };
+
+    const int npass = wave * TPW < ntok ? (ntok - wave * TPW + TPP - 1) / TPP : 0;
+    if (npass > 0) {
+      frag qfA[NKS], qiA[NKI], qfB[NKS], qiB[NKI];
+      float lseA, lseB;
+      int32_t entA, entB;
+      load_rows(0, qfA, qiA, lseA, entA);
+      for (int ps = 0; ps < npass; ps += 2) {
+        load_rows(ps + 1, qfB, qiB, lseB, entB);
+        __builtin_amdgcn_sched_barrier(0);
+        pass(qfA, qiA, lseA, entA);
+        if (ps + 1 < npass) {
+          load_rows(ps + 2, qfA, qiA, lseA, entA);
+          __builtin_amdgcn_sched_barrier(0);
+          pass(qfB, qiB, lseB, entB);
+        }
       }
     }
   }
