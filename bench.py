@@ -41,6 +41,7 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 KERNELS = {"index_score": 1, "topk_merge": 2, "gather": 3, "attention": 4, "combine": 5}
 KL_KERNELS = {"kl_teacher": 6, "kl_combine": 7}
+BWD_KERNELS = {"bwd": 8, "bwd_combine": 9}
 
 
 class HipEvents:
@@ -233,6 +234,56 @@ class Runner:
         torch.cuda.synchronize()
         return t0.elapsed_time(t1) / steps, per
 
+    def backward(self, steps=5, warmup=1):
+        """Time msa_sparse_attn_bwd on this workload (selection, output and lse
+        from one forward; a seeded bf16 output gradient): (ms per call, per-kernel ms)."""
+        s, msa = self.s, self.msa
+        dev = self.x["q"].device
+        lse = torch.empty((s.batch, s.num_q_heads, s.q_len), dtype=torch.float32, device=dev)
+        fa = list(self.args)
+        fa[9] = ctypes.c_void_p(lse.data_ptr())
+        if self.L.msa_fwd_kvcache(*fa) != 0:
+            raise RuntimeError(self.L.msa_last_error().decode())
+        g = torch.Generator(device=dev)
+        g.manual_seed(11)
+        dout = torch.randn(self.out.shape, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        dq = torch.empty(self.out.shape, dtype=torch.float32, device=dev)
+        dk = torch.empty(self.x["k"].shape, dtype=torch.float32, device=dev)
+        dv = torch.empty_like(dk)
+        n = msa.workspace_size(self.shape, msa.OP_SPARSE_ATTN_BWD)
+        wsr = torch.empty(n + 256, dtype=torch.uint8, device=dev)
+        ws = wsr[(-wsr.data_ptr()) % 256:][:n]
+        ptr = lambda t: ctypes.c_void_p(t.data_ptr())
+        ba = [ctypes.byref(self.shape), ptr(self.x["q"]), ptr(self.x["k"]), ptr(self.x["v"]), ptr(self.sel),
+              ptr(self.out), ptr(lse), ptr(dout), ptr(dq), ptr(dk), ptr(dv), ptr(ws), ctypes.c_size_t(n),
+              ctypes.c_void_p(self.stream.cuda_stream)]
+
+        def call():
+            if self.L.msa_sparse_attn_bwd(*ba) != 0:
+                raise RuntimeError(self.L.msa_last_error().decode())
+        for _ in range(warmup):
+            call()
+        torch.cuda.synchronize()
+        ev = HipEvents()
+        per = {}
+        for name, kid in BWD_KERNELS.items():
+            a, b = ev.create(), ev.create()
+            self.L.msa_set_kernel_timer(kid, a, b)
+            call()
+            torch.cuda.synchronize()
+            self.L.msa_set_kernel_timer(0, None, None)
+            per[name] = ev.elapsed_ms(a, b)
+            ev.destroy(a)
+            ev.destroy(b)
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record(self.stream)
+        for _ in range(steps):
+            call()
+        t1.record(self.stream)
+        torch.cuda.synchronize()
+        del ws, wsr, dq, dk, dv, dout
+        return t0.elapsed_time(t1) / steps, per
+
     def kernel_breakdown(self, steps=3):
         res = {}
         for name in KERNELS:
@@ -414,6 +465,12 @@ def main():
         result["kl_teacher"] = {"ms": round(kms, 4), "tflops": round(flop_kl / (kms * 1e-3) / 1e12, 2),
                                 "frac_of_mfma_peak": round(flop_kl / (kms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                                 "flop": flop_kl, "kernels_ms": {k: round(v, 4) for k, v in kper.items() if v}}
+        # the main branch's backward: S, dP, dV, dK and dQ products, 10 d FLOP per (row, key)
+        flop_bwd = 2.5 * flop_main
+        bms, bper = run.backward()
+        result["backward"] = {"ms": round(bms, 4), "tflops": round(flop_bwd / (bms * 1e-3) / 1e12, 2),
+                              "frac_of_mfma_peak": round(flop_bwd / (bms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                              "flop": flop_bwd, "kernels_ms": {k: round(v, 4) for k, v in bper.items() if v}}
 
     if not args.no_cpu:
         print("[bench] cpu baseline (oracle on sampled rows)", file=sys.stderr, flush=True)

@@ -37,13 +37,14 @@ import torch
 
 __all__ = ["index_select", "sparse_attn_fwd", "fwd", "index_select_kvcache", "sparse_attn_fwd_kvcache",
            "fwd_kvcache", "kl_teacher_fwd", "kl_teacher_fwd_kvcache", "workspace_size", "MsaShape", "MsaKvCache",
-           "lib", "LIB_PATH", "MsaError", "OP_INDEX_SELECT", "OP_SPARSE_ATTN", "OP_FWD", "OP_KL_TEACHER"]
+           "lib", "LIB_PATH", "MsaError", "OP_INDEX_SELECT", "OP_SPARSE_ATTN", "OP_FWD", "OP_KL_TEACHER",
+           "sparse_attn_bwd", "OP_SPARSE_ATTN_BWD"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmsa.so")
 
 MSA_F32, MSA_BF16 = 0, 1
 CACHE_NATIVE, CACHE_FP8_E4M3 = 0, 1
-OP_INDEX_SELECT, OP_SPARSE_ATTN, OP_FWD, OP_KL_TEACHER = 0, 1, 2, 3
+OP_INDEX_SELECT, OP_SPARSE_ATTN, OP_FWD, OP_KL_TEACHER, OP_SPARSE_ATTN_BWD = 0, 1, 2, 3, 4
 BLOCK_SIZE = 128
 
 
@@ -127,6 +128,8 @@ def lib() -> ctypes.CDLL:
         L.msa_kl_teacher_fwd.restype = ctypes.c_int
         L.msa_kl_teacher_fwd_kvcache.argtypes = [shp, cp, vp, vp, vp, vp, vp, vp, fl, vp, vp, vp, sz, vp]
         L.msa_kl_teacher_fwd_kvcache.restype = ctypes.c_int
+        L.msa_sparse_attn_bwd.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.msa_sparse_attn_bwd.restype = ctypes.c_int
         _LIB = L
     return _LIB
 
@@ -510,3 +513,38 @@ def kl_teacher_fwd(q, k, q_idx, k_idx, sel, lse, q_offset: int = 0, scale: Optio
     return kl_teacher_fwd_kvcache(q, k, q_idx, k_idx, sel, lse, q_offset=q_offset, scale=scale,
                                   index_scale=index_scale, k_scale=k_scale, return_idx_lse=return_idx_lse,
                                   workspace=workspace)
+
+
+# ---- backward of the main branch ------------------------------------------------
+
+def sparse_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sel: torch.Tensor, out: torch.Tensor,
+                    lse: torch.Tensor, dout: torch.Tensor, q_offset: int = 0, scale: Optional[float] = None,
+                    workspace: Optional[torch.Tensor] = None):
+    """Gradients (dq, dk, dv), fp32, of sparse_attn_fwd's output for the output
+    gradient dout, the selection held constant; out and lse are the forward's."""
+    _need(q, "q", 4, dtype=torch.bfloat16)
+    dev = q.device
+    for name, t in (("k", k), ("v", v), ("out", out), ("dout", dout)):
+        _need(t, name, 4, dev, torch.bfloat16)
+    _need(sel, "sel", 4, dev, torch.int32)
+    _need(lse, "lse", 3, dev, torch.float32)
+    B, S_q, Hq, d = q.shape
+    Hkv, S_k = k.shape[1], k.shape[2]
+    if tuple(k.shape) != (B, Hkv, S_k, d) or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("k and v must be [B, Hkv, S_k, d] matching q")
+    if tuple(out.shape) != tuple(q.shape) or tuple(dout.shape) != tuple(q.shape):
+        raise ValueError("out and dout must be shaped like q")
+    topk = sel.shape[3]
+    if tuple(sel.shape[:3]) != (B, Hkv, S_q) or tuple(lse.shape) != (B, Hq, S_q):
+        raise ValueError("sel must be [B, G, S_q, topk] and lse [B, Hq, S_q]")
+    shape = make_shape(B, S_q, S_k, q_offset, Hq, Hkv, d, 32, topk, torch.bfloat16, torch.bfloat16, scale)
+    dq = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    dk = torch.empty(k.shape, dtype=torch.float32, device=dev)
+    dv = torch.empty(v.shape, dtype=torch.float32, device=dev)
+    ws = workspace if workspace is not None else _workspace(shape, OP_SPARSE_ATTN_BWD, dev)
+    L = lib()
+    st = L.msa_sparse_attn_bwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(sel), _ptr(out), _ptr(lse),
+                               _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), 0 if ws is None else ws.numel(),
+                               _stream(dev))
+    _check(st)
+    return dq, dk, dv

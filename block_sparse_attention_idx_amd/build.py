@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libmsa.so")
-SOURCES = ["msa_api.hip", "index_topk.hip", "attn.hip", "kl.hip"]
+SOURCES = ["msa_api.hip", "index_topk.hip", "attn.hip", "kl.hip", "bwd.hip"]
 ARCH = "gfx950"
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"

@@ -162,27 +162,6 @@ __global__ __launch_bounds__(1024) void gather_scan_kernel(AttnParams p) {
   }
 }
 
-// Element vector of a 16-byte chunk.
-template <typename T> struct Vec16;
-template <> struct Vec16<bf16> { typedef bf16x8 type; };
-template <> struct Vec16<float> { typedef f32x4 type; };
-
-// E x E transpose of 16-byte rows (E = 16 / sizeof(T)), in registers.  Native
-// vector types throughout, so nothing is placed in scratch memory.
-template <typename T, int E>
-__device__ __forceinline__ void transpose_tile(const i32x4 (&in)[E], i32x4 (&out)[E]) {
-  typedef typename Vec16<T>::type V;
-  V a[E], o[E];
-#pragma unroll
-  for (int r = 0; r < E; ++r) a[r] = __builtin_bit_cast(V, in[r]);
-#pragma unroll
-  for (int c = 0; c < E; ++c)
-#pragma unroll
-    for (int r = 0; r < E; ++r) o[c][r] = a[r][c];
-#pragma unroll
-  for (int c = 0; c < E; ++c) out[c] = __builtin_bit_cast(i32x4, o[c]);
-}
-
 template <typename T, typename S, int D, int R>
 __global__ __launch_bounds__(256, 2) void attn_kvouter_kernel(AttnParams p) {
   using M = Mma<T>;

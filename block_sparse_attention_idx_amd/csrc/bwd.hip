@@ -1,0 +1,345 @@
+// Backward of the MSA main branch on gfx950 (the selection held constant).
+//
+// The pages name no backward kernel; MSA-PT / MSA-CPT training needs one
+// (snilld.dk page "MiniMax lancerer MSA", section "Træning og stabilisering").
+// Top-k is not differentiable, so the selection is a constant and each query
+// row gets the gradient of exact softmax attention over its token set:
+//   P = exp(scale S - lse), dP = dO V^T, Dsum = rowsum(dO o O),
+//   dS = P o (dP - Dsum), dQ = scale dS K, dK = scale dS^T Q, dV = P^T dO.
+//
+// KV-outer, like the forward: one work item per (b, g, block) bucket with every
+// query that selected the block, so the block's dK and dV accumulate over all
+// of them in registers and are written once, with no atomics.  Wave w owns the
+// block's keys [32w, 32w + 32) and keeps their K and V rows in registers as
+// MFMA B operands.  Passes of 32 rows ((token, head) pairs; the r heads of a
+// token adjacent) are shared by the 4 waves:
+//   S = Q K_w^T and dP = dO V_w^T put the wave's key in the lane and the rows in
+//   the registers -- directly the A operand of dV_w += P^T dO and
+//   dK_w += dS^T Q, whose B operands (dO, Q with rows as the reduction index)
+//   come from transposed tiles in LDS;
+//   dS goes to LDS ([row][key]) and wave w forms the d-slice [32w, 32w + 32) of
+//   dQ^T = K^T dS^T over all 128 keys (K^T staged once per item), stored as a
+//   bf16 partial per (token, slot) in the forward's lane-native layout and
+//   summed over the slots by bwd_dq_combine_kernel.
+#include "common.h"
+#include "kernels.h"
+
+namespace msa {
+
+constexpr float kLog2eB = 1.4426950408889634f;
+
+__global__ void bwd_zero_kernel(float* __restrict__ x, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) x[i] = 0.f;
+}
+
+// Dsum[b, h, i] = dO[b, i, h, :] . O[b, i, h, :] in fp32, one thread per row.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_dsum_kernel(AttnParams p, BwdParams bp) {
+  const int64_t row = (int64_t)blockIdx.x * 256 + threadIdx.x;  // (b * S_q + i) * Hq + h
+  if (row >= (int64_t)p.B * p.S_q * p.Hq) return;
+  const bf16x8* o = (const bf16x8*)((const bf16*)bp.out + row * D);
+  const bf16x8* g = (const bf16x8*)((const bf16*)bp.dout + row * D);
+  float acc = 0.f;
+#pragma unroll
+  for (int c = 0; c < D / 8; ++c) {
+    const bf16x8 a = o[c], b = g[c];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = __builtin_fmaf((float)a[e], (float)b[e], acc);
+  }
+  const int h = (int)(row % p.Hq);
+  const int64_t bi = row / p.Hq;
+  const int i = (int)(bi % p.S_q);
+  const int b = (int)(bi / p.S_q);
+  bp.dsum[((int64_t)b * p.Hq + h) * p.S_q + i] = acc;
+}
+
+template <int D, int R>
+__global__ __launch_bounds__(256, 1) void attn_bwd_kernel(AttnParams p, BwdParams bp) {
+  using T = bf16;
+  using M = Mma<T>;
+  using frag = M::frag;
+  constexpr int KPL = M::KPL, KSTEP = M::KSTEP, NKS = D / KSTEP;
+  constexpr int E = 8;               // bf16 elements per 16-byte chunk
+  constexpr int NDT = D / 32;        // 32-wide d tiles
+  constexpr int TPW = 32 / R;        // tokens per pass of 32 rows
+  constexpr int LDT = kBlock + 8;    // K^T pitch: [d][key]
+  constexpr int LDR = 32 + 8;        // Q^T, dO^T pitch: [d][row]
+  constexpr int LDS2 = kBlock + 8;   // dS pitch: [row][key]
+  __shared__ __align__(16) T Kt[D * LDT];
+  __shared__ __align__(16) T Qt[D * LDR];
+  __shared__ __align__(16) T Ot[D * LDR];
+  __shared__ __align__(16) T dSs[32 * LDS2];
+  __shared__ float lse_s[32], dsum_s[32];
+  __shared__ int lim_s[32];
+  __shared__ int32_t ent_s[32];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int h = lane >> 5, l32 = lane & 31;
+  const float sl2 = p.scale_log2;
+
+  for (int64_t item = blockIdx.x; item < (int64_t)*p.n_items; item += gridDim.x) {
+    const int bk = p.item_bucket[item];  // one item per bucket
+    const int ntok = p.counts[bk];
+    const int32_t* toks = p.entries + p.offsets[bk];
+    const int c = bk % p.nb;
+    const int bg = bk / p.nb;
+    const int g = bg % p.G, b = bg / p.G;
+    const int64_t key0 = (int64_t)c * kBlock;
+    if (key0 >= p.S_k) continue;  // uniform
+    const int64_t kv0 = (((int64_t)b * p.G + g) * p.S_k + key0) * D;
+    const int rows_ok = (int)min((int64_t)kBlock, (int64_t)p.S_k - key0);
+    const int64_t qo = p.q_offset;
+
+    // this wave's 32 keys: K and V rows as B operands (lane = key), for the whole item
+    const int kw = wave * 32 + l32;
+    frag kf[NKS], vf[NKS];
+    {
+      const T* kr = (const T*)p.k + kv0 + (int64_t)min(kw, rows_ok - 1) * D;
+      const T* vr = (const T*)p.v + kv0 + (int64_t)min(kw, rows_ok - 1) * D;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        kf[ks] = *(const frag*)(kr + ks * KSTEP + h * KPL);
+        vf[ks] = *(const frag*)(vr + ks * KSTEP + h * KPL);
+      }
+    }
+    __syncthreads();  // the previous item is done with the LDS tiles
+    {
+      // K^T [d][key] by 8 x 8 transposes; rows past the cache end are zero
+      constexpr int VT = (D / E) * (kBlock / E);
+      static_assert(VT % 256 == 0 || VT < 256, "K^T staging split");
+      for (int tl = threadIdx.x; tl < VT; tl += 256) {
+        const int dg = tl % (D / E), kg = tl / (D / E);
+        i32x4 in[E], outc[E];
+#pragma unroll
+        for (int r = 0; r < E; ++r) {
+          const int kr = kg * E + r;
+          in[r] = kr < rows_ok ? *(const i32x4*)((const T*)p.k + kv0 + (int64_t)kr * D + dg * E) : i32x4{};
+        }
+        transpose_tile<T, E>(in, outc);
+#pragma unroll
+        for (int r = 0; r < E; ++r) *(i32x4*)&Kt[(dg * E + r) * LDT + kg * E] = outc[r];
+      }
+    }
+
+    f32x16 dk_acc[NDT], dv_acc[NDT];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      dk_acc[dt] = f32x16{};
+      dv_acc[dt] = f32x16{};
+    }
+
+    for (int p0 = 0; p0 < ntok; p0 += TPW) {
+      __syncthreads();  // the previous pass is done with the pass tiles (and K^T is written)
+      // the pass's rows: row rr = token (p0 + rr / R), head rr % R
+      if (threadIdx.x < 32) {
+        const int rr = threadIdx.x;
+        const int tslot = p0 + rr / R;
+        const bool valid = tslot < ntok;
+        const int32_t entry = valid ? toks[tslot] : 0;
+        const int i = entry >> 6;
+        const int64_t rel = qo + i - key0;
+        const int head = g * R + rr % R;
+        // lim: the last visible key of the block, -1 when the row sees none of it
+        lim_s[rr] = (!valid || rel < 0) ? -1 : (rel >= kBlock ? kBlock - 1 : (int)rel);
+        ent_s[rr] = valid ? entry : -1;
+        lse_s[rr] = valid ? bp.lse[((int64_t)b * p.Hq + head) * p.S_q + i] * kLog2eB : 0.f;
+        dsum_s[rr] = valid ? bp.dsum[((int64_t)b * p.Hq + head) * p.S_q + i] : 0.f;
+      }
+      // Q^T and dO^T [d][row] by 8 x 8 transposes (threads [0, D/2) and [D/2, D))
+      if ((int)threadIdx.x < D) {
+        const bool is_o = (int)threadIdx.x >= D / 2;
+        const int tl = is_o ? threadIdx.x - D / 2 : threadIdx.x;
+        const int dg = tl % (D / E), rg = tl / (D / E);
+        const T* base = is_o ? (const T*)bp.dout : (const T*)p.q;
+        i32x4 in[E], outc[E];
+#pragma unroll
+        for (int r = 0; r < E; ++r) {
+          const int rr = rg * E + r;
+          const int tslot = min(p0 + rr / R, ntok - 1);  // rows past the list reuse a valid row
+          const int i = toks[tslot] >> 6;
+          in[r] = *(const i32x4*)(base + (((int64_t)b * p.S_q + i) * p.Hq + g * R + rr % R) * D + dg * E);
+        }
+        transpose_tile<T, E>(in, outc);
+        T* dst = is_o ? Ot : Qt;
+#pragma unroll
+        for (int r = 0; r < E; ++r) *(i32x4*)&dst[(dg * E + r) * LDR + rg * E] = outc[r];
+      }
+      __syncthreads();
+
+      // S = Q K_w^T and dP = dO V_w^T: lane = key kw, register j = row c_row(j, h)
+      f32x16 s = f32x16{}, dp = f32x16{};
+      {
+        const int tslot = min(p0 + l32 / R, ntok - 1);
+        const int i = toks[tslot] >> 6;
+        const int64_t roff = (((int64_t)b * p.S_q + i) * p.Hq + g * R + l32 % R) * D;
+        frag qa[NKS], oa[NKS];
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+          qa[ks] = *(const frag*)((const T*)p.q + roff + ks * KSTEP + h * KPL);
+          oa[ks] = *(const frag*)((const T*)bp.dout + roff + ks * KSTEP + h * KPL);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+          s = M::mma(qa[ks], kf[ks], s);
+          dp = M::mma(oa[ks], vf[ks], dp);
+        }
+      }
+      float pj[16], dsj[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int row = c_row(j, h);
+        const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[j], sl2, -lse_s[row]));
+        pj[j] = kw <= lim_s[row] ? e : 0.f;
+        dsj[j] = pj[j] * (dp[j] - dsum_s[row]);
+      }
+
+      // dV_w += P^T dO and dK_w += dS^T Q; step ks2 pairs reduction index h*8+e
+      // with row c_row(8 ks2 + e, h): two runs of four rows of the [d][row] tiles
+#pragma unroll
+      for (int ks2 = 0; ks2 < 2; ++ks2) {
+        frag pa, da;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          pa[e] = (bf16)pj[ks2 * 8 + e];
+          da[e] = (bf16)dsj[ks2 * 8 + e];
+        }
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          const T* orow = &Ot[(dt * 32 + l32) * LDR + ks2 * 16 + h * 4];
+          const T* qrow = &Qt[(dt * 32 + l32) * LDR + ks2 * 16 + h * 4];
+          const frag ob = __builtin_shufflevector(*(const bf16x4*)orow, *(const bf16x4*)(orow + 8), 0, 1, 2, 3, 4,
+                                                  5, 6, 7);
+          const frag qb = __builtin_shufflevector(*(const bf16x4*)qrow, *(const bf16x4*)(qrow + 8), 0, 1, 2, 3, 4,
+                                                  5, 6, 7);
+          dv_acc[dt] = M::mma(pa, ob, dv_acc[dt]);
+          dk_acc[dt] = M::mma(da, qb, dk_acc[dt]);
+        }
+      }
+
+      // dQ: dS to LDS [row][key], then wave w forms d-slice w of dQ^T = K^T dS^T
+#pragma unroll
+      for (int j = 0; j < 16; ++j) dSs[c_row(j, h) * LDS2 + kw] = (bf16)dsj[j];
+      __syncthreads();
+      if (wave < NDT) {
+        f32x16 dq = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < kBlock / KSTEP; ++ks) {
+          const frag a = *(const frag*)&Kt[(wave * 32 + l32) * LDT + ks * KSTEP + h * KPL];
+          const frag bb = *(const frag*)&dSs[l32 * LDS2 + ks * KSTEP + h * KPL];
+          dq = M::mma(a, bb, dq);
+        }
+        // lane = row l32 (its token and head), registers = d wave * 32 + c_row(j, h)
+        const int32_t entry = ent_s[l32];
+        if (entry >= 0 && lim_s[l32] >= 0) {
+          const int i = entry >> 6, slot = entry & 63, hh = l32 % R;
+          const int64_t ptok = (((int64_t)b * p.S_q + i) * p.G + g) * p.topk + slot;
+          T* po = (T*)p.part_o + ptok * (R * D);
+#pragma unroll
+          for (int qq = 0; qq < 2; ++qq) {  // chunks q = 2 wave + qq of the lane-native layout
+            const int q = wave * 2 + qq;
+            bf16x8 v;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = (bf16)dq[qq * 8 + e];
+            __builtin_nontemporal_store(__builtin_bit_cast(i32x4, v), (i32x4*)(po + ((q * 2 + h) * R + hh) * E));
+          }
+        }
+      }
+    }
+
+    // the block's dK (times the scale) and dV: lane = d, register j = key c_row(j, h)
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int kr = wave * 32 + c_row(j, h);
+        if (kr < rows_ok) {
+          const int64_t o = kv0 + (int64_t)kr * D + dt * 32 + l32;
+          bp.dk[o] = dk_acc[dt][j] * bp.scale;
+          bp.dv[o] = dv_acc[dt][j];
+        }
+      }
+  }
+}
+
+// dq[b, i, h, :] = scale * (sum over the row's visible selected blocks of the
+// partials); a thread per 16-byte chunk of the lane-native partial layout.
+template <int D, int R>
+__global__ __launch_bounds__(256) void bwd_dq_combine_kernel(AttnParams p, BwdParams bp) {
+  constexpr int E = 8;
+  constexpr int NCHT = D * R / E;  // chunks per (token, slot) partial
+  const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (u >= (int64_t)p.B * p.S_q * p.G * NCHT) return;
+  const int ch = (int)(u % NCHT);
+  const int64_t rowg = u / NCHT;  // (b * S_q + i) * G + g
+  const int g = (int)(rowg % p.G);
+  const int64_t bi = rowg / p.G;
+  const int i = (int)(bi % p.S_q);
+  const int b = (int)(bi / p.S_q);
+  const int hh = ch % R, h = (ch / R) & 1, q = ch / (2 * R);
+  const int64_t t = p.q_offset + i;
+  const int32_t* srow = p.sel + (((int64_t)b * p.G + g) * p.S_q + i) * p.topk;
+  float acc[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.f;
+  for (int s2 = 0; s2 < p.topk; ++s2) {
+    const int c = srow[s2];
+    if (c < 0 || c >= p.nb || (int64_t)c * kBlock > t) continue;
+    const bf16x8 x = __builtin_bit_cast(
+        bf16x8, __builtin_nontemporal_load((const i32x4*)((const bf16*)p.part_o + (rowg * p.topk + s2) * (R * D) + ch * E)));
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] += (float)x[e];
+  }
+  const int r0 = (q * E) % 16, dt = (q * E) / 16;
+  float* orow = bp.dq + (bi * p.Hq + g * R + hh) * D;
+#pragma unroll
+  for (int m = 0; m < E / 4; ++m) {
+    const int d0 = dt * 32 + (r0 / 4 + m) * 8 + 4 * h;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) orow[d0 + e] = acc[4 * m + e] * bp.scale;
+  }
+}
+
+template <int D, int R>
+static hipError_t launch_bwd_t(const AttnParams& p, const BwdParams& bp, hipStream_t s, const KernelTimer* tm) {
+  const int64_t rows = (int64_t)p.B * p.S_q * p.Hq;
+  const int64_t kvn = (int64_t)p.B * p.G * p.S_k * D;
+  timer_start(tm, kKernBwd, s);
+  hipLaunchKernelGGL((bwd_dsum_kernel<D>), dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, s, p, bp);
+  // blocks no query selected get zero gradients
+  hipLaunchKernelGGL(bwd_zero_kernel, dim3((unsigned)((kvn + 255) / 256)), dim3(256), 0, s, bp.dk, kvn);
+  hipLaunchKernelGGL(bwd_zero_kernel, dim3((unsigned)((kvn + 255) / 256)), dim3(256), 0, s, bp.dv, kvn);
+  timer_stop(tm, kKernBwd, s);
+  launch_gather(p, s, tm);
+  timer_start(tm, kKernBwd, s);
+  hipLaunchKernelGGL((attn_bwd_kernel<D, R>), dim3(p.grid), dim3(256), 0, s, p, bp);
+  timer_stop(tm, kKernBwd, s);
+  timer_start(tm, kKernBwdCombine, s);
+  const int64_t units = (int64_t)p.B * p.S_q * p.G * (D * R / 8);
+  hipLaunchKernelGGL((bwd_dq_combine_kernel<D, R>), dim3((unsigned)((units + 255) / 256)), dim3(256), 0, s, p, bp);
+  timer_stop(tm, kKernBwdCombine, s);
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_bwd_d(const AttnParams& p, const BwdParams& bp, hipStream_t s, const KernelTimer* tm) {
+  switch (p.r) {
+    case 1: return launch_bwd_t<D, 1>(p, bp, s, tm);
+    case 2: return launch_bwd_t<D, 2>(p, bp, s, tm);
+    case 4: return launch_bwd_t<D, 4>(p, bp, s, tm);
+    case 8: return launch_bwd_t<D, 8>(p, bp, s, tm);
+    case 16: return launch_bwd_t<D, 16>(p, bp, s, tm);
+    case 32: return launch_bwd_t<D, 32>(p, bp, s, tm);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_sparse_attention_bwd(const AttnParams& p, const BwdParams& bp, hipStream_t s,
+                                       const KernelTimer* tm) {
+  if (p.d == 64) return launch_bwd_d<64>(p, bp, s, tm);
+  if (p.d == 128) return launch_bwd_d<128>(p, bp, s, tm);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace msa

@@ -24,7 +24,7 @@ inline void timer_stop(const KernelTimer* t, int which, hipStream_t s) {
 }
 
 enum { kKernIndexScore = 1, kKernTopkMerge = 2, kKernGather = 3, kKernAttention = 4, kKernCombine = 5,
-       kKernKlTeacher = 6, kKernKlCombine = 7 };
+       kKernKlTeacher = 6, kKernKlCombine = 7, kKernBwd = 8, kKernBwdCombine = 9 };
 
 // Where the caches (k, v, k_idx) of each sequence live.  Without a length
 // table every sequence holds S_k tokens and its query row 0 sits at q_offset;
@@ -159,5 +159,22 @@ struct KlParams {
 
 hipError_t launch_kl_teacher(const AttnParams& p, const KlParams& kp, bool bf16_inputs, bool fp8_cache,
                              hipStream_t s, const KernelTimer* timer);
+
+// Backward of the main branch (bwd.hip): bf16 q, k, v, out and dout; fp32
+// gradients.  The gather runs with one work item per bucket (p.tpi covers any
+// bucket) and p.part_o holds the bf16 dQ partials.
+struct BwdParams {
+  const void* out;     // [B, S_q, Hq, d] forward output
+  const void* dout;    // [B, S_q, Hq, d] its gradient
+  const float* lse;    // [B, Hq, S_q] forward log-sum-exp (natural log)
+  float* dsum;         // [B, Hq, S_q] workspace: rowsum(dout * out)
+  float* dq;           // [B, S_q, Hq, d]
+  float* dk;           // [B, G, S_k, d]
+  float* dv;           // [B, G, S_k, d]
+  float scale;         // softmax scale (key scale included)
+};
+
+hipError_t launch_sparse_attention_bwd(const AttnParams& p, const BwdParams& bp, hipStream_t s,
+                                       const KernelTimer* timer);
 
 }  // namespace msa

@@ -87,7 +87,14 @@ msa_status check_shape(const msa_shape* s, int op) {
   if ((int64_t)s->batch * s->num_kv_heads * ceil_div(s->kv_len, msa::kBlock) >= (1LL << 31))
     return fail(MSA_ERR_UNSUPPORTED, "batch * kv heads * blocks exceeds 2^31");
   const bool index_op = op == MSA_OP_INDEX_SELECT || op == MSA_OP_FWD || op == MSA_OP_KL_TEACHER;
-  const bool attn_op = op == MSA_OP_SPARSE_ATTN || op == MSA_OP_FWD || op == MSA_OP_KL_TEACHER;
+  const bool attn_op = op == MSA_OP_SPARSE_ATTN || op == MSA_OP_FWD || op == MSA_OP_KL_TEACHER ||
+                       op == MSA_OP_SPARSE_ATTN_BWD;
+  if (op == MSA_OP_SPARSE_ATTN_BWD) {
+    if (s->dtype != MSA_BF16 || s->out_dtype != MSA_BF16 || fp8_cache(s))
+      return fail(MSA_ERR_UNSUPPORTED, "the backward is built for bf16 q, k, v, out and dout");
+    if ((s->k_scale != 0.0f && s->k_scale != 1.0f) || (s->v_scale != 0.0f && s->v_scale != 1.0f))
+      return fail(MSA_ERR_UNSUPPORTED, "the backward takes unscaled caches (k_scale, v_scale 0 or 1)");
+  }
   if (index_op) {
     if (s->index_dim != 32 && s->index_dim != 64 && s->index_dim != 128)
       return fail(MSA_ERR_UNSUPPORTED, "index_dim %d: built for 32, 64, 128", s->index_dim);
@@ -287,6 +294,41 @@ AttnPlan plan_attn(const msa_shape* s, const msa_kv_cache* cache) {
   return ap;
 }
 
+// Backward: the main branch's gather with one work item per bucket (tpi above
+// any bucket's size, no direct mode) and one workgroup per bucket, so that the
+// hardware's dispatch balances buckets of unequal size; plus rowsum(dO * O).
+AttnPlan plan_bwd(const msa_shape* s, size_t* off_dsum) {
+  msa_shape s2 = *s;
+  AttnPlan ap = plan_attn(&s2, nullptr);
+  msa::AttnParams& p = ap.p;
+  if (p.direct) {  // redo the layout with the gather regions
+    p.direct = 0;
+    const size_t nbk = (size_t)p.nbuckets + 1;
+    const size_t entries = (size_t)p.B * p.G * p.S_q * p.topk;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+      const size_t o = off;
+      off += align_up(bytes);
+      return o;
+    };
+    ap.off_counts = take(nbk * 4);
+    ap.off_offsets = take(nbk * 4);
+    ap.off_cursor = take(nbk * 4);
+    ap.off_item_off = take(nbk * 4);
+    ap.off_nitems = take(4);
+    ap.off_entries = take(entries * 4);
+    ap.off_items = take(((size_t)p.nbuckets + 1) * 4);
+    ap.off_po = take(entries * (size_t)p.r * p.d * 2);
+    ap.off_pl = take(entries * (size_t)p.r * 4);
+    ap.bytes = off;
+  }
+  p.tpi = 1 << 25;  // > any bucket (q_len < 2^25): one item per bucket
+  p.grid = p.nbuckets;
+  *off_dsum = ap.bytes;
+  ap.bytes += align_up((size_t)s->batch * s->num_q_heads * s->q_len * 4);
+  return ap;
+}
+
 void bind_attn(AttnPlan& ap, char* ws) {
   msa::AttnParams& p = ap.p;
   if (!p.direct) {
@@ -331,7 +373,7 @@ extern "C" {
 const char* msa_version(void) { return "0.2.0"; }
 
 msa_status msa_set_kernel_timer(int kernel, void* start_event, void* stop_event) {
-  if (kernel < MSA_KERNEL_NONE || kernel > MSA_KERNEL_KL_COMBINE)
+  if (kernel < MSA_KERNEL_NONE || kernel > MSA_KERNEL_BWD_COMBINE)
     return fail(MSA_ERR_INVALID, "unknown kernel id %d", kernel);
   if (kernel == MSA_KERNEL_NONE || !start_event || !stop_event) {
     g_timer = {0, nullptr, nullptr};
@@ -357,10 +399,14 @@ const char* msa_last_error(void) { return g_last_error.c_str(); }
 size_t msa_workspace_size_kvcache(const msa_shape* s, const msa_kv_cache* cache, int op) {
   const std::string saved = g_last_error;
   size_t r = 0;
-  if (op >= MSA_OP_INDEX_SELECT && op <= MSA_OP_KL_TEACHER && check_shape(s, op) == MSA_OK &&
+  if (op >= MSA_OP_INDEX_SELECT && op <= MSA_OP_SPARSE_ATTN_BWD && check_shape(s, op) == MSA_OK &&
       check_cache(s, cache) == MSA_OK && s->q_len > 0) {
     if (op == MSA_OP_INDEX_SELECT) r = plan_index(s, cache).bytes;
     else if (op == MSA_OP_SPARSE_ATTN || op == MSA_OP_KL_TEACHER) r = plan_attn(s, cache).bytes;
+    else if (op == MSA_OP_SPARSE_ATTN_BWD) {
+      size_t od = 0;
+      r = cache ? 0 : plan_bwd(s, &od).bytes;
+    }
     else r = sel_bytes(s) + std::max(plan_index(s, cache).bytes, plan_attn(s, cache).bytes);
   }
   g_last_error = saved;
@@ -477,6 +523,28 @@ msa_status msa_kl_teacher_fwd(const msa_shape* s, const void* q, const void* k, 
                               void* ws, size_t ws_bytes, void* stream) {
   return msa_kl_teacher_fwd_kvcache(s, nullptr, q, k, q_idx, k_idx, sel, lse, index_scale, kl, idx_lse, ws, ws_bytes,
                                     stream);
+}
+
+msa_status msa_sparse_attn_bwd(const msa_shape* s, const void* q, const void* k, const void* v, const int32_t* sel,
+                               const void* out, const float* lse, const void* dout, float* dq, float* dk, float* dv,
+                               void* ws, size_t ws_bytes, void* stream) {
+  msa_status st = check_shape(s, MSA_OP_SPARSE_ATTN_BWD);
+  if (st != MSA_OK) return st;
+  if (!q || !k || !v || !sel || !out || !lse || !dout || !dq || !dk || !dv)
+    return fail(MSA_ERR_INVALID, "q, k, v, sel, out, lse, dout, dq, dk and dv must be non-NULL");
+  if (s->q_len == 0) return MSA_OK;
+  size_t off_dsum = 0;
+  AttnPlan ap = plan_bwd(s, &off_dsum);
+  if ((st = check_ws(ws, ws_bytes, ap.bytes)) != MSA_OK) return st;
+  bind_attn(ap, (char*)ws);
+  ap.p.q = q;
+  ap.p.k = k;
+  ap.p.v = v;
+  ap.p.sel = sel;
+  const float scale = s->softmax_scale != 0.0f ? s->softmax_scale : 1.0f / std::sqrt((float)s->head_dim);
+  msa::BwdParams bp{out, dout, lse, (float*)((char*)ws + off_dsum), dq, dk, dv, scale};
+  clear_stale_hip_error();
+  return hip_status(msa::launch_sparse_attention_bwd(ap.p, bp, (hipStream_t)stream, timer()), "backward launch");
 }
 
 msa_status msa_fwd(const msa_shape* s, const void* q, const void* k, const void* v, const void* q_idx,

@@ -111,7 +111,8 @@ typedef struct {
   int32_t pad;          /* must be 0                                            */
 } msa_shape;            /* 72 bytes                                             */
 
-enum { MSA_OP_INDEX_SELECT = 0, MSA_OP_SPARSE_ATTN = 1, MSA_OP_FWD = 2, MSA_OP_KL_TEACHER = 3 };
+enum { MSA_OP_INDEX_SELECT = 0, MSA_OP_SPARSE_ATTN = 1, MSA_OP_FWD = 2, MSA_OP_KL_TEACHER = 3,
+       MSA_OP_SPARSE_ATTN_BWD = 4 };
 
 /* Bytes of workspace the given op needs for this shape (0 when the shape is
  * invalid or unsupported; the call itself then reports why).  The same shape
@@ -219,6 +220,26 @@ msa_status msa_kl_teacher_fwd_kvcache(const msa_shape* shape, const msa_kv_cache
                                       const float* lse, float index_scale, float* kl, float* idx_lse,
                                       void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- Backward of the main branch ------------------------------------------
+ *
+ * MSA-PT and MSA-CPT train the model with sparse attention (snilld.dk page,
+ * section "Træning og stabilisering"); the pages name no backward kernel.
+ * Top-k is not differentiable, so the selection is held constant and each
+ * query row gets the gradient of exact softmax attention over its token set T
+ * (as in msa_sparse_attn_fwd): with p = softmax_T(scale q.k), o = sum p v and
+ * the output gradient dO,
+ *    dV[b,g,j] += p_j dO,   dS_j = p_j (dO.v_j - dO.o),
+ *    dQ[b,i,h] = scale sum_j dS_j k_j,   dK[b,g,j] += scale dS_j q[b,i,h].
+ * Inputs: q, k, v, sel and the forward's out and lse (natural log), dout like
+ * out; all bf16 except lse.  Outputs dq [B, S_q, Hq, d], dk and dv
+ * [B, Hkv, S_k, d], fp32; keys no query attends get zero.  Built for
+ * dtype == out_dtype == MSA_BF16, native caches and k_scale, v_scale in
+ * {0, 1}; workspace: msa_workspace_size(shape, MSA_OP_SPARSE_ATTN_BWD). */
+msa_status msa_sparse_attn_bwd(const msa_shape* shape, const void* q, const void* k, const void* v,
+                               const int32_t* sel, const void* out, const float* lse, const void* dout,
+                               float* dq, float* dk, float* dv, void* workspace, size_t workspace_bytes,
+                               void* stream);
+
 /* Kernels of the forward path, for msa_set_kernel_timer. */
 typedef enum {
   MSA_KERNEL_NONE = 0,
@@ -228,7 +249,9 @@ typedef enum {
   MSA_KERNEL_ATTENTION = 4,   /* KV-outer sparse attention (partial states)         */
   MSA_KERNEL_COMBINE = 5,     /* merge of the partial states into out and lse       */
   MSA_KERNEL_KL_TEACHER = 6,  /* KL teacher: per-block terms                        */
-  MSA_KERNEL_KL_COMBINE = 7   /* KL teacher: per-row totals                         */
+  MSA_KERNEL_KL_COMBINE = 7,  /* KL teacher: per-row totals                         */
+  MSA_KERNEL_BWD = 8,         /* backward: block gradients and dQ partials          */
+  MSA_KERNEL_BWD_COMBINE = 9  /* backward: dQ partials summed                        */
 } msa_kernel;
 
 /* Profiling hook.  For the calling thread, every later msa_* call records

@@ -66,6 +66,11 @@ a kernel-optimalizáció").  Readings taken in ``kl_teacher``: both distribution
 are over the tokens the main branch attends to; the index distribution is the
 softmax of the raw index scores (times an optional index_scale, 1 by default);
 the loss is KL(teacher || index) in natural log.
+
+Backward of the main branch.  The pages name no backward kernel (MSA-PT and
+MSA-CPT training needs one).  ``sparse_attention_bwd`` is the gradient of the
+main branch with the selection held constant (Top-k is not differentiable):
+for each query row, the gradient of exact softmax attention over its token set.
 """
 from __future__ import annotations
 
@@ -75,6 +80,7 @@ from typing import Iterable, Optional, Sequence, Tuple
 import numpy as np
 
 __all__ = [
+    "sparse_attention_bwd",
     "kl_teacher",
     "page_gather",
     "msa_forward_varlen",
@@ -394,3 +400,52 @@ def kl_teacher(q, k, q_idx, k_idx, sel, q_offset: int = 0, block_size: int = 128
             kl[b, g, i] = float(plogp.sum() - (pbar * (si - lse)).sum())
             ilse[b, g, i] = lse
     return kl, ilse
+
+
+# ---------------------------------------------------------------------------
+# Backward of the main branch (selection held constant)
+# ---------------------------------------------------------------------------
+
+def sparse_attention_bwd(q, k, v, sel, dout, q_offset: int = 0, block_size: int = 128,
+                         scale: Optional[float] = None):
+    """Gradients of sparse_attention's output with respect to q, k and v.
+
+    For each (b, i, h) with token set T (token_set of its group's selection),
+    s_j = scale q.k_j, p = softmax_T(s), o = sum_j p_j v_j.  With the output
+    gradient dO = dout[b, i, h]:
+      dV[b, g, j] += p_j dO                    (j in T)
+      dP_j = dO . v_j,   Dsum = sum_j p_j dP_j  (= dO . o)
+      dS_j = p_j (dP_j - Dsum)
+      dQ[b, i, h] = scale sum_j dS_j k_j
+      dK[b, g, j] += scale dS_j q[b, i, h]
+    Returns (dq [B, S_q, Hq, d], dk [B, G, S_k, d], dv [B, G, S_k, d]) in float64.
+    """
+    q, k, v, sel, dout = (np.asarray(a) for a in (q, k, v, sel, dout))
+    B, S_q, Hq, d = q.shape
+    G = k.shape[1]
+    r = Hq // G
+    if scale is None or scale == 0.0:
+        scale = 1.0 / math.sqrt(d)
+    dq = np.zeros((B, S_q, Hq, d))
+    dk = np.zeros(k.shape)
+    dv = np.zeros(v.shape)
+    for b in range(B):
+        for i in range(S_q):
+            t = q_offset + i
+            for g in range(G):
+                T = token_set(sel[b, g, i], t, block_size)
+                if T.size == 0:
+                    continue
+                qh = _f64(q[b, i, g * r:(g + 1) * r])          # [r, d]
+                kt, vt = _f64(k[b, g, T]), _f64(v[b, g, T])      # [n, d]
+                do = _f64(dout[b, i, g * r:(g + 1) * r])         # [r, d]
+                s = scale * (qh @ kt.T)                          # [r, n]
+                p = np.exp(s - s.max(axis=1, keepdims=True))
+                p /= p.sum(axis=1, keepdims=True)
+                dp = do @ vt.T                                   # [r, n]
+                dsum = (p * dp).sum(axis=1, keepdims=True)
+                ds = p * (dp - dsum)
+                dq[b, i, g * r:(g + 1) * r] = scale * (ds @ kt)
+                np.add.at(dk[b, g], T, scale * (ds.T @ qh))
+                np.add.at(dv[b, g], T, p.T @ do)
+    return dq, dk, dv

@@ -200,4 +200,18 @@ def test_kl_teacher_checks():
     assert L.msa_kl_teacher_fwd(*args()) == -3  # valid: only the workspace is missing
     need = msa.workspace_size(sh, msa.OP_KL_TEACHER)
     assert need == msa.workspace_size(sh, msa.OP_SPARSE_ATTN) > 0
-    assert msa.lib().msa_set_kernel_timer(7, None, None) == 0 and msa.lib().msa_set_kernel_timer(8, None, None) == -1
+    assert msa.lib().msa_set_kernel_timer(9, None, None) == 0 and msa.lib().msa_set_kernel_timer(10, None, None) == -1
+
+
+def test_backward_checks():
+    L = msa.lib()
+    sh = _shape(2)  # bf16
+    args = lambda **kw: [ctypes.byref(sh)] + [kw.get(n, FAKE) for n in ("q", "k", "v", "sel", "out", "lse", "dout",
+                                                                      "dq", "dk", "dv")] + [None, 0, None]
+    for name in ("q", "k", "v", "sel", "out", "lse", "dout", "dq", "dk", "dv"):
+        assert L.msa_sparse_attn_bwd(*args(**{name: None})) == -1, name
+    assert L.msa_sparse_attn_bwd(*args()) == -3  # valid: only the workspace is missing
+    assert msa.workspace_size(sh, msa.OP_SPARSE_ATTN_BWD) > msa.workspace_size(sh, msa.OP_SPARSE_ATTN)
+    for field, value in (("dtype", 0), ("out_dtype", 0), ("cache_format", 1), ("k_scale", 0.5)):
+        bad = _shape(2, **{field: value})
+        assert L.msa_sparse_attn_bwd(ctypes.byref(bad), *args()[1:]) == -2, field

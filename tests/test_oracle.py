@@ -681,3 +681,70 @@ def test_kl_teacher_invariants():
     sel2[0, 0, 5] = -1
     kl2, ilse2 = orc.kl_teacher(q, kk, qi, ki, sel2, qo, Bk)
     assert kl2[0, 0, 5] == 0.0 and np.isneginf(ilse2[0, 0, 5])
+
+
+# --- backward of the main branch --------------------------------------------
+
+def test_sparse_attention_bwd_against_torch_autograd():
+    rng = np.random.default_rng(21)
+    B, S_q, S_k, qo, G, r, d, D, k, Bk = 2, 30, 160, 130, 2, 3, 8, 4, 3, 32
+    q = rng.standard_normal((B, S_q, G * r, d))
+    kk = rng.standard_normal((B, G, S_k, d))
+    vv = rng.standard_normal((B, G, S_k, d))
+    qi = rng.integers(-3, 4, (B, S_q, G, D)).astype(np.float64)
+    ki = rng.integers(-3, 4, (B, S_k, D)).astype(np.float64)
+    sel = orc.index_select(qi, ki, k, qo, Bk)
+    dout = rng.standard_normal((B, S_q, G * r, d))
+    dq, dk, dv = orc.sparse_attention_bwd(q, kk, vv, sel, dout, qo, Bk)
+    # torch: dense masked SDPA in fp64 with autograd, the mask from the selection
+    tq = torch.from_numpy(q).permute(0, 2, 1, 3).clone().requires_grad_(True)       # [B, Hq, S_q, d]
+    tk = torch.from_numpy(kk).clone().requires_grad_(True)                            # [B, G, S_k, d]
+    tv = torch.from_numpy(vv).clone().requires_grad_(True)
+    mask = torch.zeros(B, G * r, S_q, S_k, dtype=torch.bool)
+    for b in range(B):
+        for g in range(G):
+            for i in range(S_q):
+                for c in sel[b, g, i]:
+                    if c >= 0:
+                        mask[b, g * r:(g + 1) * r, i, c * Bk:min((c + 1) * Bk, qo + i + 1)] = True
+    out = F.scaled_dot_product_attention(tq, tk.repeat_interleave(r, dim=1), tv.repeat_interleave(r, dim=1),
+                                         attn_mask=mask)
+    out.backward(torch.from_numpy(dout).permute(0, 2, 1, 3))
+    assert np.allclose(dq, tq.grad.permute(0, 2, 1, 3).numpy(), atol=1e-12)
+    assert np.allclose(dk, tk.grad.numpy(), atol=1e-12)
+    assert np.allclose(dv, tv.grad.numpy(), atol=1e-12)
+
+
+def test_sparse_attention_bwd_closed_forms():
+    rng = np.random.default_rng(22)
+    B, S_q, S_k, G, r, d, Bk = 1, 6, 6, 1, 2, 4, 4
+    q = rng.standard_normal((B, S_q, r, d))
+    kk = rng.standard_normal((B, G, S_k, d))
+    vv = rng.standard_normal((B, G, S_k, d))
+    sel = np.full((B, G, S_q, 2), -1, dtype=np.int32)
+    sel[0, 0, :, 0] = 0
+    sel[0, 0, 4:, 1] = 1
+    # a zero output gradient gives zero gradients
+    z = orc.sparse_attention_bwd(q, kk, vv, sel, np.zeros_like(q), 0, Bk)
+    assert all(np.abs(x).max() == 0 for x in z)
+    # row 0 attends to key 0 alone: p = 1, so dq = 0 and dv[0] gets dO of that row
+    dout = np.zeros_like(q)
+    dout[0, 0] = rng.standard_normal((r, d))
+    dq, dk, dv = orc.sparse_attention_bwd(q, kk, vv, sel, dout, 0, Bk)
+    assert np.abs(dq).max() < 1e-15 and np.abs(dk).max() < 1e-15
+    assert np.allclose(dv[0, 0, 0], dout[0, 0].sum(axis=0)) and np.abs(dv[0, 0, 1:]).max() == 0
+    # the gradients are those of a linear functional: a central difference agrees
+    dout = rng.standard_normal(q.shape)
+    dq, dk, dv = orc.sparse_attention_bwd(q, kk, vv, sel, dout, 0, Bk)
+    f = lambda qq, k_, v_: float((orc.sparse_attention(qq, k_, v_, sel, 0, Bk)[0] * dout).sum())
+    eps = 1e-6
+    for (arr, grad, idx) in ((q, dq, (0, 5, 1, 2)), (kk, dk, (0, 0, 3, 1)), (vv, dv, (0, 0, 5, 0))):
+        a1, a2 = arr.copy(), arr.copy()
+        a1[idx] += eps
+        a2[idx] -= eps
+        args1 = [q, kk, vv]
+        args2 = [q, kk, vv]
+        which = 0 if arr is q else (1 if arr is kk else 2)
+        args1[which], args2[which] = a1, a2
+        num = (f(*args1) - f(*args2)) / (2 * eps)
+        assert abs(num - grad[idx]) < 1e-7
