@@ -12,7 +12,9 @@
 // of them in registers and are written once, with no atomics.  Wave w owns the
 // block's keys [32w, 32w + 32) and keeps their K and V rows in registers as
 // MFMA B operands.  Passes of 32 rows ((token, head) pairs; the r heads of a
-// token adjacent) are shared by the 4 waves:
+// token adjacent) are shared by the 4 waves; a pass's Q and dO rows are
+// fetched one pass ahead (the bucket's token entries sit in LDS) and written to
+// LDS both row-major and transposed:
 //   S = Q K_w^T and dP = dO V_w^T put the wave's key in the lane and the rows in
 //   the registers -- directly the A operand of dV_w += P^T dO and
 //   dK_w += dS^T Q, whose B operands (dO, Q with rows as the reduction index)
@@ -63,16 +65,24 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kernel(AttnParams p, BwdParam
   constexpr int E = 8;               // bf16 elements per 16-byte chunk
   constexpr int NDT = D / 32;        // 32-wide d tiles
   constexpr int TPW = 32 / R;        // tokens per pass of 32 rows
+  constexpr int CH = D / E;          // 16-byte chunks per row
+  constexpr int CPT = 32 * CH / 256; // chunks of a pass's Q (and dO) rows per thread
+  static_assert(CPT >= 1 && (32 * CH) % 256 == 0, "row staging split");
+  constexpr int ECH = 1024;          // token entries staged in LDS at a time
   constexpr int LDT = kBlock + 8;    // K^T pitch: [d][key]
+  constexpr int LDQ = D + 8;         // Q, dO pitch: [row][d]
   constexpr int LDR = 32 + 8;        // Q^T, dO^T pitch: [d][row]
   constexpr int LDS2 = kBlock + 8;   // dS pitch: [row][key]
   __shared__ __align__(16) T Kt[D * LDT];
+  __shared__ __align__(16) T Qr[32 * LDQ];
+  __shared__ __align__(16) T Or[32 * LDQ];
   __shared__ __align__(16) T Qt[D * LDR];
   __shared__ __align__(16) T Ot[D * LDR];
   __shared__ __align__(16) T dSs[32 * LDS2];
   __shared__ float lse_s[32], dsum_s[32];
   __shared__ int lim_s[32];
   __shared__ int32_t ent_s[32];
+  __shared__ int32_t tok_s[ECH];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int h = lane >> 5, l32 = lane & 31;
@@ -107,7 +117,6 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kernel(AttnParams p, BwdParam
     {
       // K^T [d][key] by 8 x 8 transposes; rows past the cache end are zero
       constexpr int VT = (D / E) * (kBlock / E);
-      static_assert(VT % 256 == 0 || VT < 256, "K^T staging split");
       for (int tl = threadIdx.x; tl < VT; tl += 256) {
         const int dg = tl % (D / E), kg = tl / (D / E);
         i32x4 in[E], outc[E];
@@ -121,6 +130,46 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kernel(AttnParams p, BwdParam
         for (int r = 0; r < E; ++r) *(i32x4*)&Kt[(dg * E + r) * LDT + kg * E] = outc[r];
       }
     }
+    // the bucket's token entries, ECH at a time from ent_base
+    int ent_base = 0;
+    auto stage_entries = [&](int base) {
+      for (int t = threadIdx.x; t < ECH; t += 256) tok_s[t] = base + t < ntok ? toks[base + t] : 0;
+    };
+    stage_entries(0);
+    __syncthreads();
+
+    // A pass's rows, fetched into registers one pass ahead: chunks of its Q and
+    // dO rows (row = token (p0 + row / R), head row % R) and, for threads < 32,
+    // row threadIdx.x's entry, lse, rowsum and visibility limit.
+    i32x4 qx[CPT], ox[CPT];
+    float lse_n = 0.f, dsum_n = 0.f;
+    int ent_n = -1, lim_n = -1;
+    auto fetch = [&](int p0) {
+#pragma unroll
+      for (int u = 0; u < CPT; ++u) {
+        const int ch = threadIdx.x + u * 256;
+        const int row = ch / CH, col = ch - row * CH;
+        const int tslot = min(p0 + row / R, ntok - 1);  // rows past the list reuse a valid row
+        const int i = tok_s[tslot - ent_base] >> 6;
+        const int64_t roff = (((int64_t)b * p.S_q + i) * p.Hq + g * R + row % R) * D + col * E;
+        qx[u] = *(const i32x4*)((const T*)p.q + roff);
+        ox[u] = *(const i32x4*)((const T*)bp.dout + roff);
+      }
+      if (threadIdx.x < 32) {
+        const int rr = threadIdx.x;
+        const int tslot = p0 + rr / R;
+        const bool valid = tslot < ntok;
+        const int32_t entry = valid ? tok_s[tslot - ent_base] : 0;
+        const int i = entry >> 6;
+        const int64_t rel = qo + i - key0;
+        const int64_t hrow = ((int64_t)b * p.Hq + g * R + rr % R) * p.S_q + i;
+        // lim: the last visible key of the block, -1 when the row sees none of it
+        lim_n = (!valid || rel < 0) ? -1 : (rel >= kBlock ? kBlock - 1 : (int)rel);
+        ent_n = valid ? entry : -1;
+        lse_n = valid ? bp.lse[hrow] * kLog2eB : 0.f;
+        dsum_n = valid ? bp.dsum[hrow] : 0.f;
+      }
+    };
 
     f32x16 dk_acc[NDT], dv_acc[NDT];
 #pragma unroll
@@ -129,62 +178,47 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kernel(AttnParams p, BwdParam
       dv_acc[dt] = f32x16{};
     }
 
+    fetch(0);
     for (int p0 = 0; p0 < ntok; p0 += TPW) {
-      __syncthreads();  // the previous pass is done with the pass tiles (and K^T is written)
-      // the pass's rows: row rr = token (p0 + rr / R), head rr % R
-      if (threadIdx.x < 32) {
-        const int rr = threadIdx.x;
-        const int tslot = p0 + rr / R;
-        const bool valid = tslot < ntok;
-        const int32_t entry = valid ? toks[tslot] : 0;
-        const int i = entry >> 6;
-        const int64_t rel = qo + i - key0;
-        const int head = g * R + rr % R;
-        // lim: the last visible key of the block, -1 when the row sees none of it
-        lim_s[rr] = (!valid || rel < 0) ? -1 : (rel >= kBlock ? kBlock - 1 : (int)rel);
-        ent_s[rr] = valid ? entry : -1;
-        lse_s[rr] = valid ? bp.lse[((int64_t)b * p.Hq + head) * p.S_q + i] * kLog2eB : 0.f;
-        dsum_s[rr] = valid ? bp.dsum[((int64_t)b * p.Hq + head) * p.S_q + i] : 0.f;
-      }
-      // Q^T and dO^T [d][row] by 8 x 8 transposes (threads [0, D/2) and [D/2, D))
-      if ((int)threadIdx.x < D) {
-        const bool is_o = (int)threadIdx.x >= D / 2;
-        const int tl = is_o ? threadIdx.x - D / 2 : threadIdx.x;
-        const int dg = tl % (D / E), rg = tl / (D / E);
-        const T* base = is_o ? (const T*)bp.dout : (const T*)p.q;
-        i32x4 in[E], outc[E];
+      __syncthreads();  // the previous pass is done with the pass tiles
+      // this pass's rows into LDS: row-major (A operands of S and dP) and
+      // transposed (B operands of dV and dK)
 #pragma unroll
-        for (int r = 0; r < E; ++r) {
-          const int rr = rg * E + r;
-          const int tslot = min(p0 + rr / R, ntok - 1);  // rows past the list reuse a valid row
-          const int i = toks[tslot] >> 6;
-          in[r] = *(const i32x4*)(base + (((int64_t)b * p.S_q + i) * p.Hq + g * R + rr % R) * D + dg * E);
+      for (int u = 0; u < CPT; ++u) {
+        const int ch = threadIdx.x + u * 256;
+        const int row = ch / CH, col = ch - row * CH;
+        *(i32x4*)&Qr[row * LDQ + col * E] = qx[u];
+        *(i32x4*)&Or[row * LDQ + col * E] = ox[u];
+        const bf16x8 qv = __builtin_bit_cast(bf16x8, qx[u]), ov = __builtin_bit_cast(bf16x8, ox[u]);
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          Qt[(col * E + e) * LDR + row] = qv[e];
+          Ot[(col * E + e) * LDR + row] = ov[e];
         }
-        transpose_tile<T, E>(in, outc);
-        T* dst = is_o ? Ot : Qt;
-#pragma unroll
-        for (int r = 0; r < E; ++r) *(i32x4*)&dst[(dg * E + r) * LDR + rg * E] = outc[r];
+      }
+      if (threadIdx.x < 32) {
+        lim_s[threadIdx.x] = lim_n;
+        ent_s[threadIdx.x] = ent_n;
+        lse_s[threadIdx.x] = lse_n;
+        dsum_s[threadIdx.x] = dsum_n;
+      }
+      const bool has_next = p0 + TPW < ntok;
+      if (has_next && p0 + 2 * TPW > ent_base + ECH) {  // the next pass needs the next entries
+        ent_base = p0 + TPW;
+        stage_entries(ent_base);
       }
       __syncthreads();
+      if (has_next) fetch(p0 + TPW);  // in flight during this pass
+      __builtin_amdgcn_sched_barrier(0);
 
       // S = Q K_w^T and dP = dO V_w^T: lane = key kw, register j = row c_row(j, h)
       f32x16 s = f32x16{}, dp = f32x16{};
-      {
-        const int tslot = min(p0 + l32 / R, ntok - 1);
-        const int i = toks[tslot] >> 6;
-        const int64_t roff = (((int64_t)b * p.S_q + i) * p.Hq + g * R + l32 % R) * D;
-        frag qa[NKS], oa[NKS];
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-          qa[ks] = *(const frag*)((const T*)p.q + roff + ks * KSTEP + h * KPL);
-          oa[ks] = *(const frag*)((const T*)bp.dout + roff + ks * KSTEP + h * KPL);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-          s = M::mma(qa[ks], kf[ks], s);
-          dp = M::mma(oa[ks], vf[ks], dp);
-        }
+      for (int ks = 0; ks < NKS; ++ks) {
+        const frag qa = *(const frag*)&Qr[l32 * LDQ + ks * KSTEP + h * KPL];
+        const frag oa = *(const frag*)&Or[l32 * LDQ + ks * KSTEP + h * KPL];
+        s = M::mma(qa, kf[ks], s);
+        dp = M::mma(oa, vf[ks], dp);
       }
       float pj[16], dsj[16];
 #pragma unroll
