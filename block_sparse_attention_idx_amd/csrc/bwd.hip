@@ -7,11 +7,14 @@
 //   P = exp(scale S - lse), dP = dO V^T, Dsum = rowsum(dO o O),
 //   dS = P o (dP - Dsum), dQ = scale dS K, dK = scale dS^T Q, dV = P^T dO.
 //
-// KV-outer, like the forward: one work item per (b, g, block) bucket with every
-// query that selected the block, so the block's dK and dV accumulate over all
-// of them in registers and are written once, with no atomics.  Wave w owns the
+// KV-outer, like the forward: a work item is a block with up to 512 of the
+// queries that selected it (the buckets of early blocks, visible to most
+// queries, are many times the mean); the block's dK and dV accumulate over the
+// item's queries in registers and are added to the (zeroed) outputs with fp32
+// atomics, so their summation order between items is not fixed.  Wave w owns the
 // block's keys [32w, 32w + 32) and keeps their K and V rows in registers as
-// MFMA B operands.  Passes of 32 rows ((token, head) pairs; the r heads of a
+// MFMA B operands (8 waves: waves w and w + 4 own the same keys and split d
+// between their dK / dV accumulators, so two waves fit on each SIMD).  Passes of 32 rows ((token, head) pairs; the r heads of a
 // token adjacent) are shared by the 4 waves; a pass's Q and dO rows are
 // fetched one pass ahead (the bucket's token entries sit in LDS) and written to
 // LDS both row-major and transposed:
@@ -57,7 +60,7 @@ __global__ __launch_bounds__(256) void bwd_dsum_kernel(AttnParams p, BwdParams b
 }
 
 template <int D, int R>
-__global__ __launch_bounds__(256, 1) void attn_bwd_kernel(AttnParams p, BwdParams bp) {
+__global__ __launch_bounds__(512, 1) void attn_bwd_kernel(AttnParams p, BwdParams bp) {
   using T = bf16;
   using M = Mma<T>;
   using frag = M::frag;
@@ -66,12 +69,14 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kernel(AttnParams p, BwdParam
   constexpr int NDT = D / 32;        // 32-wide d tiles
   constexpr int TPW = 32 / R;        // tokens per pass of 32 rows
   constexpr int CH = D / E;          // 16-byte chunks per row
-  constexpr int CPT = 32 * CH / 256; // chunks of a pass's Q (and dO) rows per thread
-  static_assert(CPT >= 1 && (32 * CH) % 256 == 0, "row staging split");
+  constexpr int NT = 512;            // 8 waves: wave w owns keys [32 (w % 4), +32) and half of d
+  constexpr int CPT = (32 * CH + NT - 1) / NT;  // chunks of a pass's Q (and dO) rows per thread
+  constexpr bool kAllStage = (32 * CH) % NT == 0;  // false (d = 64): threads past 32 * CH idle
+  constexpr int NDH = NDT / 2;       // d tiles of a wave's dK / dV
   constexpr int ECH = 1024;          // token entries staged in LDS at a time
   constexpr int LDT = kBlock + 8;    // K^T pitch: [d][key]
   constexpr int LDQ = D + 8;         // Q, dO pitch: [row][d]
-  constexpr int LDR = 32 + 8;        // Q^T, dO^T pitch: [d][row]
+  constexpr int LDR = 32 + 8;        // Q^T, dO^T pitch: [d][row], rows swizzled by d (tsw)
   constexpr int LDS2 = kBlock + 8;   // dS pitch: [row][key]
   __shared__ __align__(16) T Kt[D * LDT];
   __shared__ __align__(16) T Qr[32 * LDQ];
@@ -86,12 +91,19 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kernel(AttnParams p, BwdParam
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int h = lane >> 5, l32 = lane & 31;
+  const int kgrp = wave & 3, dh = wave >> 2;  // key group and d half
+  // Row position of row `row` in line d of the transposed tiles.  XOR with a
+  // multiple of 4 keeps the aligned runs of four rows the MFMA operands read
+  // contiguous, and spreads the 8-d column chunks written together over the
+  // LDS banks (with a plain layout all of them map to one bank).
+  auto tsw = [](int d, int row) { return row ^ (4 * ((d >> 3) & 7)); };
   const float sl2 = p.scale_log2;
 
   for (int64_t item = blockIdx.x; item < (int64_t)*p.n_items; item += gridDim.x) {
-    const int bk = p.item_bucket[item];  // one item per bucket
-    const int ntok = p.counts[bk];
-    const int32_t* toks = p.entries + p.offsets[bk];
+    const int bk = p.item_bucket[item];
+    const int start = (int)(item - p.item_off[bk]) * p.tpi;
+    const int ntok = min(p.tpi, p.counts[bk] - start);
+    const int32_t* toks = p.entries + p.offsets[bk] + start;
     const int c = bk % p.nb;
     const int bg = bk / p.nb;
     const int g = bg % p.G, b = bg / p.G;
@@ -102,7 +114,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kernel(AttnParams p, BwdParam
     const int64_t qo = p.q_offset;
 
     // this wave's 32 keys: K and V rows as B operands (lane = key), for the whole item
-    const int kw = wave * 32 + l32;
+    const int kw = kgrp * 32 + l32;
     frag kf[NKS], vf[NKS];
     {
       const T* kr = (const T*)p.k + kv0 + (int64_t)min(kw, rows_ok - 1) * D;
@@ -117,7 +129,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kernel(AttnParams p, BwdParam
     {
       // K^T [d][key] by 8 x 8 transposes; rows past the cache end are zero
       constexpr int VT = (D / E) * (kBlock / E);
-      for (int tl = threadIdx.x; tl < VT; tl += 256) {
+      for (int tl = threadIdx.x; tl < VT; tl += NT) {
         const int dg = tl % (D / E), kg = tl / (D / E);
         i32x4 in[E], outc[E];
 #pragma unroll
@@ -133,7 +145,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kernel(AttnParams p, BwdParam
     // the bucket's token entries, ECH at a time from ent_base
     int ent_base = 0;
     auto stage_entries = [&](int base) {
-      for (int t = threadIdx.x; t < ECH; t += 256) tok_s[t] = base + t < ntok ? toks[base + t] : 0;
+      for (int t = threadIdx.x; t < ECH; t += NT) tok_s[t] = base + t < ntok ? toks[base + t] : 0;
     };
     stage_entries(0);
     __syncthreads();
@@ -147,7 +159,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kernel(AttnParams p, BwdParam
     auto fetch = [&](int p0) {
 #pragma unroll
       for (int u = 0; u < CPT; ++u) {
-        const int ch = threadIdx.x + u * 256;
+        const int ch = min((int)threadIdx.x + u * NT, 32 * CH - 1);  // idle threads re-read the last chunk
         const int row = ch / CH, col = ch - row * CH;
         const int tslot = min(p0 + row / R, ntok - 1);  // rows past the list reuse a valid row
         const int i = tok_s[tslot - ent_base] >> 6;
@@ -171,11 +183,11 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kernel(AttnParams p, BwdParam
       }
     };
 
-    f32x16 dk_acc[NDT], dv_acc[NDT];
+    f32x16 dk_acc[NDH], dv_acc[NDH];  // d tiles dh * NDH + t
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
-      dk_acc[dt] = f32x16{};
-      dv_acc[dt] = f32x16{};
+    for (int t = 0; t < NDH; ++t) {
+      dk_acc[t] = f32x16{};
+      dv_acc[t] = f32x16{};
     }
 
     fetch(0);
@@ -185,15 +197,17 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kernel(AttnParams p, BwdParam
       // transposed (B operands of dV and dK)
 #pragma unroll
       for (int u = 0; u < CPT; ++u) {
-        const int ch = threadIdx.x + u * 256;
+        const int ch = threadIdx.x + u * NT;
+        if (!kAllStage && ch >= 32 * CH) break;
         const int row = ch / CH, col = ch - row * CH;
         *(i32x4*)&Qr[row * LDQ + col * E] = qx[u];
         *(i32x4*)&Or[row * LDQ + col * E] = ox[u];
         const bf16x8 qv = __builtin_bit_cast(bf16x8, qx[u]), ov = __builtin_bit_cast(bf16x8, ox[u]);
 #pragma unroll
         for (int e = 0; e < E; ++e) {
-          Qt[(col * E + e) * LDR + row] = qv[e];
-          Ot[(col * E + e) * LDR + row] = ov[e];
+          const int d = col * E + e;
+          Qt[d * LDR + tsw(d, row)] = qv[e];
+          Ot[d * LDR + tsw(d, row)] = ov[e];
         }
       }
       if (threadIdx.x < 32) {
@@ -240,21 +254,25 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kernel(AttnParams p, BwdParam
           da[e] = (bf16)dsj[ks2 * 8 + e];
         }
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-          const T* orow = &Ot[(dt * 32 + l32) * LDR + ks2 * 16 + h * 4];
-          const T* qrow = &Qt[(dt * 32 + l32) * LDR + ks2 * 16 + h * 4];
-          const frag ob = __builtin_shufflevector(*(const bf16x4*)orow, *(const bf16x4*)(orow + 8), 0, 1, 2, 3, 4,
-                                                  5, 6, 7);
-          const frag qb = __builtin_shufflevector(*(const bf16x4*)qrow, *(const bf16x4*)(qrow + 8), 0, 1, 2, 3, 4,
-                                                  5, 6, 7);
-          dv_acc[dt] = M::mma(pa, ob, dv_acc[dt]);
-          dk_acc[dt] = M::mma(da, qb, dk_acc[dt]);
+        for (int t = 0; t < NDH; ++t) {
+          const int dt = dh * NDH + t;
+          const int d = dt * 32 + l32;
+          const int lo = tsw(d, ks2 * 16 + h * 4), hi = tsw(d, ks2 * 16 + 8 + h * 4);
+          const frag ob = __builtin_shufflevector(*(const bf16x4*)&Ot[d * LDR + lo], *(const bf16x4*)&Ot[d * LDR + hi],
+                                                  0, 1, 2, 3, 4, 5, 6, 7);
+          const frag qb = __builtin_shufflevector(*(const bf16x4*)&Qt[d * LDR + lo], *(const bf16x4*)&Qt[d * LDR + hi],
+                                                  0, 1, 2, 3, 4, 5, 6, 7);
+          dv_acc[t] = M::mma(pa, ob, dv_acc[t]);
+          dk_acc[t] = M::mma(da, qb, dk_acc[t]);
         }
       }
 
-      // dQ: dS to LDS [row][key], then wave w forms d-slice w of dQ^T = K^T dS^T
+      // dQ: dS to LDS [row][key] (one copy per key group), then wave w < NDT
+      // forms d-slice w of dQ^T = K^T dS^T
+      if (dh == 0) {
 #pragma unroll
-      for (int j = 0; j < 16; ++j) dSs[c_row(j, h) * LDS2 + kw] = (bf16)dsj[j];
+        for (int j = 0; j < 16; ++j) dSs[c_row(j, h) * LDS2 + kw] = (bf16)dsj[j];
+      }
       __syncthreads();
       if (wave < NDT) {
         f32x16 dq = f32x16{};
@@ -284,14 +302,14 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kernel(AttnParams p, BwdParam
 
     // the block's dK (times the scale) and dV: lane = d, register j = key c_row(j, h)
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
+    for (int t = 0; t < NDH; ++t)
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        const int kr = wave * 32 + c_row(j, h);
+        const int kr = kgrp * 32 + c_row(j, h);
         if (kr < rows_ok) {
-          const int64_t o = kv0 + (int64_t)kr * D + dt * 32 + l32;
-          bp.dk[o] = dk_acc[dt][j] * bp.scale;
-          bp.dv[o] = dv_acc[dt][j];
+          const int64_t o = kv0 + (int64_t)kr * D + (dh * NDH + t) * 32 + l32;
+          atomicAdd(&bp.dk[o], dk_acc[t][j] * bp.scale);
+          atomicAdd(&bp.dv[o], dv_acc[t][j]);
         }
       }
   }
@@ -347,7 +365,7 @@ static hipError_t launch_bwd_t(const AttnParams& p, const BwdParams& bp, hipStre
   timer_stop(tm, kKernBwd, s);
   launch_gather(p, s, tm);
   timer_start(tm, kKernBwd, s);
-  hipLaunchKernelGGL((attn_bwd_kernel<D, R>), dim3(p.grid), dim3(256), 0, s, p, bp);
+  hipLaunchKernelGGL((attn_bwd_kernel<D, R>), dim3(p.grid), dim3(512), 0, s, p, bp);
   timer_stop(tm, kKernBwd, s);
   timer_start(tm, kKernBwdCombine, s);
   const int64_t units = (int64_t)p.B * p.S_q * p.G * (D * R / 8);

@@ -161,8 +161,8 @@ hipError_t launch_kl_teacher(const AttnParams& p, const KlParams& kp, bool bf16_
                              hipStream_t s, const KernelTimer* timer);
 
 // Backward of the main branch (bwd.hip): bf16 q, k, v, out and dout; fp32
-// gradients.  The gather runs with one work item per bucket (p.tpi covers any
-// bucket) and p.part_o holds the bf16 dQ partials.
+// gradients.  The gather cuts buckets into work items of p.tpi tokens and
+// p.part_o holds the bf16 dQ partials.
 struct BwdParams {
   const void* out;     // [B, S_q, Hq, d] forward output
   const void* dout;    // [B, S_q, Hq, d] its gradient
