@@ -151,11 +151,12 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_kernel(AttnParams p, BwdParam
     __syncthreads();
 
     // A pass's rows, fetched into registers one pass ahead: chunks of its Q and
-    // dO rows (row = token (p0 + row / R), head row % R) and, for threads < 32,
-    // row threadIdx.x's entry, lse, rowsum and visibility limit.
+    // dO rows (row = token (p0 + row / R), head row % R) and, in wave 0, row
+    // (lane % 32)'s entry with its raw lse and rowsum.  Nothing here consumes a
+    // loaded value, so no wait is placed before the pass's compute.
     i32x4 qx[CPT], ox[CPT];
     float lse_n = 0.f, dsum_n = 0.f;
-    int ent_n = -1, lim_n = -1;
+    int32_t ent_n = 0, pslot_n = 0;
     auto fetch = [&](int p0) {
 #pragma unroll
       for (int u = 0; u < CPT; ++u) {
@@ -167,19 +168,13 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_kernel(AttnParams p, BwdParam
         qx[u] = *(const i32x4*)((const T*)p.q + roff);
         ox[u] = *(const i32x4*)((const T*)bp.dout + roff);
       }
-      if (threadIdx.x < 32) {
-        const int rr = threadIdx.x;
-        const int tslot = p0 + rr / R;
-        const bool valid = tslot < ntok;
-        const int32_t entry = valid ? tok_s[tslot - ent_base] : 0;
-        const int i = entry >> 6;
-        const int64_t rel = qo + i - key0;
-        const int64_t hrow = ((int64_t)b * p.Hq + g * R + rr % R) * p.S_q + i;
-        // lim: the last visible key of the block, -1 when the row sees none of it
-        lim_n = (!valid || rel < 0) ? -1 : (rel >= kBlock ? kBlock - 1 : (int)rel);
-        ent_n = valid ? entry : -1;
-        lse_n = valid ? bp.lse[hrow] * kLog2eB : 0.f;
-        dsum_n = valid ? bp.dsum[hrow] : 0.f;
+      if (wave == 0) {
+        const int rr = lane & 31;
+        pslot_n = p0 + rr / R;
+        ent_n = tok_s[min(pslot_n, ntok - 1) - ent_base];
+        const int64_t hrow = ((int64_t)b * p.Hq + g * R + rr % R) * p.S_q + (ent_n >> 6);
+        lse_n = bp.lse[hrow];
+        dsum_n = bp.dsum[hrow];
       }
     };
 
@@ -211,10 +206,13 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_kernel(AttnParams p, BwdParam
         }
       }
       if (threadIdx.x < 32) {
-        lim_s[threadIdx.x] = lim_n;
-        ent_s[threadIdx.x] = ent_n;
-        lse_s[threadIdx.x] = lse_n;
-        dsum_s[threadIdx.x] = dsum_n;
+        const bool valid = pslot_n < ntok;
+        const int64_t rel = qo + (ent_n >> 6) - key0;
+        // lim: the last visible key of the block, -1 when the row sees none of it
+        lim_s[threadIdx.x] = (!valid || rel < 0) ? -1 : (rel >= kBlock ? kBlock - 1 : (int)rel);
+        ent_s[threadIdx.x] = valid ? ent_n : -1;
+        lse_s[threadIdx.x] = valid ? lse_n * kLog2eB : 0.f;
+        dsum_s[threadIdx.x] = valid ? dsum_n : 0.f;
       }
       const bool has_next = p0 + TPW < ntok;
       if (has_next && p0 + 2 * TPW > ent_base + ECH) {  // the next pass needs the next entries
