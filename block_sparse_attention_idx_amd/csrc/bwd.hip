@@ -59,6 +59,18 @@ __global__ __launch_bounds__(256) void bwd_dsum_kernel(AttnParams p, BwdParams b
   bp.dsum[((int64_t)b * p.Hq + h) * p.S_q + i] = acc;
 }
 
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// Transposing LDS read (gfx950): within each group of 16 lanes, lane i receives,
+// as element e, element i % 4 of the 8 bytes addressed by lane 4 e + i / 4 of
+// the group.  Pointing lane s of a group at 4 consecutive elements of row
+// r0 + s / 4, column c0 + 4 (s % 4) of a row-major tile hands lane i the column
+// c0 + i of rows r0 .. r0 + 3.
+__device__ __forceinline__ bf16x4 read_tr(const bf16* p) {
+  return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p)));
+}
+
 template <int D, int R>
 __global__ __launch_bounds__(512, 1) void attn_bwd_kernel(AttnParams p, BwdParams bp) {
   using T = bf16;
@@ -66,38 +78,61 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_kernel(AttnParams p, BwdParam
   using frag = M::frag;
   constexpr int KPL = M::KPL, KSTEP = M::KSTEP, NKS = D / KSTEP;
   constexpr int E = 8;               // bf16 elements per 16-byte chunk
-  constexpr int NDT = D / 32;        // 32-wide d tiles
+  constexpr int NDT = D / 32;        // 32-wide d tiles of dK / dV
   constexpr int TPW = 32 / R;        // tokens per pass of 32 rows
   constexpr int CH = D / E;          // 16-byte chunks per row
-  constexpr int NT = 512;            // 8 waves: wave w owns keys [32 (w % 4), +32) and half of d
+  constexpr int NT = 512;            // 8 waves
   constexpr int CPT = (32 * CH + NT - 1) / NT;  // chunks of a pass's Q (and dO) rows per thread
   constexpr bool kAllStage = (32 * CH) % NT == 0;  // false (d = 64): threads past 32 * CH idle
-  constexpr int NDH = NDT / 2;       // d tiles of a wave's dK / dV
-  constexpr int ECH = 1024;          // token entries staged in LDS at a time
-  constexpr int LDT = kBlock + 8;    // K^T pitch: [d][key]
-  constexpr int LDQ = D + 8;         // Q, dO pitch: [row][d]
-  constexpr int LDR = 32 + 8;        // Q^T, dO^T pitch: [d][row], rows swizzled by d (tsw)
-  constexpr int LDS2 = kBlock + 8;   // dS pitch: [row][key]
-  __shared__ __align__(16) T Kt[D * LDT];
-  __shared__ __align__(16) T Qr[32 * LDQ];
-  __shared__ __align__(16) T Or[32 * LDQ];
-  __shared__ __align__(16) T Qt[D * LDR];
-  __shared__ __align__(16) T Ot[D * LDR];
-  __shared__ __align__(16) T dSs[32 * LDS2];
-  __shared__ float lse_s[32], dsum_s[32];
-  __shared__ int lim_s[32];
-  __shared__ int32_t ent_s[32];
+  constexpr int ECH = kBwdTokensPerItem;  // an item's token entries, all staged in LDS
+  constexpr int NQT = D / 64;        // 16 x 16 dQ tiles per wave
+  constexpr int LDST = 32;           // dS^T pitch: [key][row]
+  __shared__ __align__(16) T Ks[kBlock * D];      // K [key][d]
+  __shared__ __align__(16) T Qr[2][32 * D];       // the pass's Q and dO rows [row][d], two passes
+  __shared__ __align__(16) T Or[2][32 * D];
+  __shared__ __align__(16) float Ps[4 * 4 * 64 * 4];  // P handed from S waves to dS waves
+  __shared__ __align__(16) T dSt[kBlock * LDST];  // dS^T [key][row]
+  __shared__ float lse_s[2][32], dsum_s[2][32];
+  __shared__ int lim_s[2][32];
+  __shared__ int32_t ent_s[2][32];
   __shared__ int32_t tok_s[ECH];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int h = lane >> 5, l32 = lane & 31;
-  const int kgrp = wave & 3, dh = wave >> 2;  // key group and d half
-  // Row position of row `row` in line d of the transposed tiles.  XOR with a
-  // multiple of 4 keeps the aligned runs of four rows the MFMA operands read
-  // contiguous, and spreads the 8-d column chunks written together over the
-  // LDS banks (with a plain layout all of them map to one bank).
-  auto tsw = [](int d, int row) { return row ^ (4 * ((d >> 3) & 7)); };
+  const int grp = lane >> 4, gl = lane & 15;  // 16-lane group and lane in it (transposing reads)
+  // Waves 0-3 (S waves) own keys [32 w, 32 w + 32): S = Q K_w^T, P, dV_w += P^T dO.
+  // Waves 4-7 (dS waves) own the same keys: dP = dO V_w^T, dS = P o (dP - Dsum),
+  // dK_w += dS^T Q.  All 8 form 16 x 16 tiles of dQ^T = K^T dS^T.
+  const bool sw_wave = wave < 4;
+  const int kgrp = wave & 3;
+  const int kw = kgrp * 32 + l32;
+  // 16-byte chunk c of row r of the [row][d] tiles (Q, dO, K) sits at chunk
+  // c ^ sw(r): 16 consecutive rows put one chunk in 16 distinct bank groups (the
+  // MFMA A-operand reads) and 4 consecutive rows put a run of 4 (2 for d = 64)
+  // chunks in distinct banks (the transposing reads).
+  auto sw = [](int r) { return CH == 16 ? (((r & 3) << 2) | ((r >> 2) & 3)) : (((r & 3) << 1) | ((r >> 2) & 1)); };
+  auto at = [&](int r, int col) { return r * D + ((((col >> 3) ^ sw(r))) << 3) + (col & 7); };
+  // dS^T: chunk c of key row k at c ^ 2 ((k >> 3) & 1), so rows k and k + 8 differ
+  auto at_ds = [](int k, int row) { return k * LDST + ((((row >> 3) ^ (((k >> 3) & 1) << 1))) << 3) + (row & 7); };
   const float sl2 = p.scale_log2;
+  // Per-lane element offsets of the transposing reads; the swizzles repeat every
+  // 16 rows of the [row][d] tiles and every 16 key rows of dS^T, so each read of
+  // a loop below is one of these plus a constant.
+  //  dV / dK B operands: row 4 (grp / 2) + gl / 4 (+ 8), d 32 t + 16 (grp % 2) + 4 (gl % 4)
+  int boff[NDT][2];
+#pragma unroll
+  for (int t = 0; t < NDT; ++t)
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+      boff[t][hf] = at(4 * (grp >> 1) + (gl >> 2) + 8 * hf, 32 * t + 16 * (grp & 1) + 4 * (gl & 3));
+  //  dQ: K^T from key rows 8 grp + gl / 4 (+ 4), d 16 d16 + 4 (gl % 4); dS^T from
+  //  the same key rows, rows 16 rt + 4 (gl % 4)
+  const int d16 = wave % (D / 16);
+  const int koff0 = at(8 * grp + (gl >> 2), 16 * d16 + 4 * (gl & 3));
+  const int koff4 = at(8 * grp + 4 + (gl >> 2), 16 * d16 + 4 * (gl & 3));
+  int doff[NQT];
+#pragma unroll
+  for (int u = 0; u < NQT; ++u) doff[u] = at_ds(8 * grp + (gl >> 2), 16 * ((wave + 8 * u) / (D / 16)) + 4 * (gl & 3));
 
   for (int64_t item = blockIdx.x; item < (int64_t)*p.n_items; item += gridDim.x) {
     const int bk = p.item_bucket[item];
@@ -113,47 +148,25 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_kernel(AttnParams p, BwdParam
     const int rows_ok = (int)min((int64_t)kBlock, (int64_t)p.S_k - key0);
     const int64_t qo = p.q_offset;
 
-    // this wave's 32 keys: K and V rows as B operands (lane = key), for the whole item
-    const int kw = kgrp * 32 + l32;
-    frag kf[NKS], vf[NKS];
+    // B operands of S (K rows) or dP (V rows) for the wave's keys, lane = key kw
+    frag kvf[NKS];
     {
-      const T* kr = (const T*)p.k + kv0 + (int64_t)min(kw, rows_ok - 1) * D;
-      const T* vr = (const T*)p.v + kv0 + (int64_t)min(kw, rows_ok - 1) * D;
+      const T* src = (const T*)(sw_wave ? p.k : p.v) + kv0 + (int64_t)min(kw, rows_ok - 1) * D;
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        kf[ks] = *(const frag*)(kr + ks * KSTEP + h * KPL);
-        vf[ks] = *(const frag*)(vr + ks * KSTEP + h * KPL);
-      }
+      for (int ks = 0; ks < NKS; ++ks) kvf[ks] = *(const frag*)(src + ks * KSTEP + h * KPL);
     }
-    __syncthreads();  // the previous item is done with the LDS tiles
-    {
-      // K^T [d][key] by 8 x 8 transposes; rows past the cache end are zero
-      constexpr int VT = (D / E) * (kBlock / E);
-      for (int tl = threadIdx.x; tl < VT; tl += NT) {
-        const int dg = tl % (D / E), kg = tl / (D / E);
-        i32x4 in[E], outc[E];
-#pragma unroll
-        for (int r = 0; r < E; ++r) {
-          const int kr = kg * E + r;
-          in[r] = kr < rows_ok ? *(const i32x4*)((const T*)p.k + kv0 + (int64_t)kr * D + dg * E) : i32x4{};
-        }
-        transpose_tile<T, E>(in, outc);
-#pragma unroll
-        for (int r = 0; r < E; ++r) *(i32x4*)&Kt[(dg * E + r) * LDT + kg * E] = outc[r];
-      }
+    __syncthreads();  // the previous item is done with every LDS tile
+    for (int ch = threadIdx.x; ch < kBlock * CH; ch += NT) {  // K, rows past the cache end zero
+      const int r = ch / CH, cc = ch - r * CH;
+      const i32x4 x = r < rows_ok ? *(const i32x4*)((const T*)p.k + kv0 + (int64_t)r * D + cc * E) : i32x4{};
+      *(i32x4*)&Ks[r * D + ((cc ^ sw(r)) << 3)] = x;
     }
-    // the bucket's token entries, ECH at a time from ent_base
-    int ent_base = 0;
-    auto stage_entries = [&](int base) {
-      for (int t = threadIdx.x; t < ECH; t += NT) tok_s[t] = base + t < ntok ? toks[base + t] : 0;
-    };
-    stage_entries(0);
+    for (int t = threadIdx.x; t < ECH; t += NT) tok_s[t] = t < ntok ? toks[t] : 0;
     __syncthreads();
 
-    // A pass's rows, fetched into registers one pass ahead: chunks of its Q and
-    // dO rows (row = token (p0 + row / R), head row % R) and, in wave 0, row
-    // (lane % 32)'s entry with its raw lse and rowsum.  Nothing here consumes a
-    // loaded value, so no wait is placed before the pass's compute.
+    // A pass's rows, fetched into registers two passes ahead of use: chunks of
+    // its Q and dO rows (row = token (p0 + row / R), head row % R) and, in wave
+    // 0, row (lane % 32)'s entry with its raw lse and rowsum.
     i32x4 qx[CPT], ox[CPT];
     float lse_n = 0.f, dsum_n = 0.f;
     int32_t ent_n = 0, pslot_n = 0;
@@ -162,8 +175,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_kernel(AttnParams p, BwdParam
       for (int u = 0; u < CPT; ++u) {
         const int ch = min((int)threadIdx.x + u * NT, 32 * CH - 1);  // idle threads re-read the last chunk
         const int row = ch / CH, col = ch - row * CH;
-        const int tslot = min(p0 + row / R, ntok - 1);  // rows past the list reuse a valid row
-        const int i = tok_s[tslot - ent_base] >> 6;
+        const int i = tok_s[min(p0 + row / R, ntok - 1)] >> 6;  // rows past the list reuse a valid row
         const int64_t roff = (((int64_t)b * p.S_q + i) * p.Hq + g * R + row % R) * D + col * E;
         qx[u] = *(const i32x4*)((const T*)p.q + roff);
         ox[u] = *(const i32x4*)((const T*)bp.dout + roff);
@@ -171,163 +183,188 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_kernel(AttnParams p, BwdParam
       if (wave == 0) {
         const int rr = lane & 31;
         pslot_n = p0 + rr / R;
-        ent_n = tok_s[min(pslot_n, ntok - 1) - ent_base];
+        ent_n = tok_s[min(pslot_n, ntok - 1)];
         const int64_t hrow = ((int64_t)b * p.Hq + g * R + rr % R) * p.S_q + (ent_n >> 6);
         lse_n = bp.lse[hrow];
         dsum_n = bp.dsum[hrow];
       }
     };
-
-    f32x16 dk_acc[NDH], dv_acc[NDH];  // d tiles dh * NDH + t
-#pragma unroll
-    for (int t = 0; t < NDH; ++t) {
-      dk_acc[t] = f32x16{};
-      dv_acc[t] = f32x16{};
-    }
-
-    fetch(0);
-    for (int p0 = 0; p0 < ntok; p0 += TPW) {
-      __syncthreads();  // the previous pass is done with the pass tiles
-      // this pass's rows into LDS: row-major (A operands of S and dP) and
-      // transposed (B operands of dV and dK)
+    // registers -> LDS buffer nb_
+    auto stage = [&](int nb_) {
 #pragma unroll
       for (int u = 0; u < CPT; ++u) {
         const int ch = threadIdx.x + u * NT;
         if (!kAllStage && ch >= 32 * CH) break;
         const int row = ch / CH, col = ch - row * CH;
-        *(i32x4*)&Qr[row * LDQ + col * E] = qx[u];
-        *(i32x4*)&Or[row * LDQ + col * E] = ox[u];
-        const bf16x8 qv = __builtin_bit_cast(bf16x8, qx[u]), ov = __builtin_bit_cast(bf16x8, ox[u]);
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-          const int d = col * E + e;
-          Qt[d * LDR + tsw(d, row)] = qv[e];
-          Ot[d * LDR + tsw(d, row)] = ov[e];
-        }
+        *(i32x4*)&Qr[nb_][row * D + ((col ^ sw(row)) << 3)] = qx[u];
+        *(i32x4*)&Or[nb_][row * D + ((col ^ sw(row)) << 3)] = ox[u];
       }
       if (threadIdx.x < 32) {
         const bool valid = pslot_n < ntok;
         const int64_t rel = qo + (ent_n >> 6) - key0;
         // lim: the last visible key of the block, -1 when the row sees none of it
-        lim_s[threadIdx.x] = (!valid || rel < 0) ? -1 : (rel >= kBlock ? kBlock - 1 : (int)rel);
-        ent_s[threadIdx.x] = valid ? ent_n : -1;
-        lse_s[threadIdx.x] = valid ? lse_n * kLog2eB : 0.f;
-        dsum_s[threadIdx.x] = valid ? dsum_n : 0.f;
+        lim_s[nb_][threadIdx.x] = (!valid || rel < 0) ? -1 : (rel >= kBlock ? kBlock - 1 : (int)rel);
+        ent_s[nb_][threadIdx.x] = valid ? ent_n : -1;
+        lse_s[nb_][threadIdx.x] = valid ? lse_n * kLog2eB : 0.f;
+        dsum_s[nb_][threadIdx.x] = valid ? dsum_n : 0.f;
       }
-      const bool has_next = p0 + TPW < ntok;
-      if (has_next && p0 + 2 * TPW > ent_base + ECH) {  // the next pass needs the next entries
-        ent_base = p0 + TPW;
-        stage_entries(ent_base);
-      }
-      __syncthreads();
-      if (has_next) fetch(p0 + TPW);  // in flight during this pass
-      __builtin_amdgcn_sched_barrier(0);
+    };
 
-      // S = Q K_w^T and dP = dO V_w^T: lane = key kw, register j = row c_row(j, h)
-      f32x16 s = f32x16{}, dp = f32x16{};
+    f32x16 acc[NDT];  // dV_w (S waves) or dK_w (dS waves): lane = d, register j = key c_row(j, h)
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        const frag qa = *(const frag*)&Qr[l32 * LDQ + ks * KSTEP + h * KPL];
-        const frag oa = *(const frag*)&Or[l32 * LDQ + ks * KSTEP + h * KPL];
-        s = M::mma(qa, kf[ks], s);
-        dp = M::mma(oa, vf[ks], dp);
-      }
-      float pj[16], dsj[16];
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int row = c_row(j, h);
-        const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[j], sl2, -lse_s[row]));
-        pj[j] = kw <= lim_s[row] ? e : 0.f;
-        dsj[j] = pj[j] * (dp[j] - dsum_s[row]);
-      }
+    for (int t = 0; t < NDT; ++t) acc[t] = f32x16{};
 
-      // dV_w += P^T dO and dK_w += dS^T Q; step ks2 pairs reduction index h*8+e
-      // with row c_row(8 ks2 + e, h): two runs of four rows of the [d][row] tiles
+    fetch(0);
+    stage(0);
+    if (TPW < ntok) fetch(TPW);
+    __syncthreads();
+    int buf = 0;
+    for (int p0 = 0; p0 < ntok; p0 += TPW, buf ^= 1) {
+      // the next pass's rows into the other buffer: its readers (the previous
+      // pass) finished before that pass's last barrier
+      if (p0 + TPW < ntok) {
+        stage(buf ^ 1);
+        if (p0 + 2 * TPW < ntok) fetch(p0 + 2 * TPW);  // in flight for the next two passes
+      }
+      const T* Qb = Qr[buf];
+      const T* Ob = Or[buf];
+
+      // S = Q K_w^T (S waves) or dP = dO V_w^T (dS waves): lane = key kw, register j = row c_row(j, h)
+      f32x16 s = f32x16{};
+      {
+        const T* A = sw_wave ? Qb : Ob;
 #pragma unroll
-      for (int ks2 = 0; ks2 < 2; ++ks2) {
-        frag pa, da;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          pa[e] = (bf16)pj[ks2 * 8 + e];
-          da[e] = (bf16)dsj[ks2 * 8 + e];
-        }
-#pragma unroll
-        for (int t = 0; t < NDH; ++t) {
-          const int dt = dh * NDH + t;
-          const int d = dt * 32 + l32;
-          const int lo = tsw(d, ks2 * 16 + h * 4), hi = tsw(d, ks2 * 16 + 8 + h * 4);
-          const frag ob = __builtin_shufflevector(*(const bf16x4*)&Ot[d * LDR + lo], *(const bf16x4*)&Ot[d * LDR + hi],
-                                                  0, 1, 2, 3, 4, 5, 6, 7);
-          const frag qb = __builtin_shufflevector(*(const bf16x4*)&Qt[d * LDR + lo], *(const bf16x4*)&Qt[d * LDR + hi],
-                                                  0, 1, 2, 3, 4, 5, 6, 7);
-          dv_acc[t] = M::mma(pa, ob, dv_acc[t]);
-          dk_acc[t] = M::mma(da, qb, dk_acc[t]);
+        for (int ks = 0; ks < NKS; ++ks) {
+          const frag a = *(const frag*)&A[at(l32, ks * KSTEP + h * KPL)];
+          s = M::mma(a, kvf[ks], s);
         }
       }
-
-      // dQ: dS to LDS [row][key] (one copy per key group), then wave w < NDT
-      // forms d-slice w of dQ^T = K^T dS^T
-      if (dh == 0) {
+      frag pa[2];  // P or dS in bf16: A operands of dV / dK, step ks2 pairs index h*8+e with row c_row(8 ks2 + e, h)
+      if (sw_wave) {
+        float pj[16];
 #pragma unroll
-        for (int j = 0; j < 16; ++j) dSs[c_row(j, h) * LDS2 + kw] = (bf16)dsj[j];
-      }
-      __syncthreads();
-      if (wave < NDT) {
-        f32x16 dq = f32x16{};
-#pragma unroll
-        for (int ks = 0; ks < kBlock / KSTEP; ++ks) {
-          const frag a = *(const frag*)&Kt[(wave * 32 + l32) * LDT + ks * KSTEP + h * KPL];
-          const frag bb = *(const frag*)&dSs[l32 * LDS2 + ks * KSTEP + h * KPL];
-          dq = M::mma(a, bb, dq);
+        for (int j = 0; j < 16; ++j) {
+          const int row = c_row(j, h);
+          const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[j], sl2, -lse_s[buf][row]));
+          pj[j] = kw <= lim_s[buf][row] ? e : 0.f;
         }
-        // lane = row l32 (its token and head), registers = d wave * 32 + c_row(j, h)
-        const int32_t entry = ent_s[l32];
-        if (entry >= 0 && lim_s[l32] >= 0) {
-          const int i = entry >> 6, slot = entry & 63, hh = l32 % R;
-          const int64_t ptok = (((int64_t)b * p.S_q + i) * p.G + g) * p.topk + slot;
-          T* po = (T*)p.part_o + ptok * (R * D);
 #pragma unroll
-          for (int qq = 0; qq < 2; ++qq) {  // chunks q = 2 wave + qq of the lane-native layout
-            const int q = wave * 2 + qq;
-            bf16x8 v;
+        for (int j4 = 0; j4 < 4; ++j4)
+          *(f32x4*)&Ps[((kgrp * 4 + j4) * 64 + lane) * 4] = f32x4{pj[4 * j4], pj[4 * j4 + 1], pj[4 * j4 + 2], pj[4 * j4 + 3]};
 #pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = (bf16)dq[qq * 8 + e];
-            __builtin_nontemporal_store(__builtin_bit_cast(i32x4, v), (i32x4*)(po + ((q * 2 + h) * R + hh) * E));
+        for (int ks2 = 0; ks2 < 2; ++ks2)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) pa[ks2][e] = (bf16)pj[ks2 * 8 + e];
+      }
+      __syncthreads();  // P is in LDS
+      if (!sw_wave) {
+        float dsj[16];
+#pragma unroll
+        for (int j4 = 0; j4 < 4; ++j4) {
+          const f32x4 pv = *(const f32x4*)&Ps[((kgrp * 4 + j4) * 64 + lane) * 4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int j = 4 * j4 + e;
+            dsj[j] = pv[e] * (s[j] - dsum_s[buf][c_row(j, h)]);
+          }
+        }
+#pragma unroll
+        for (int ks2 = 0; ks2 < 2; ++ks2)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) pa[ks2][e] = (bf16)dsj[ks2 * 8 + e];
+        // dS^T [key][row]: registers 4m .. 4m + 3 are rows 8m + 4h .. + 3
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+          *(bf16x4*)&dSt[at_ds(kw, 8 * m + 4 * h)] =
+              bf16x4{(bf16)dsj[4 * m], (bf16)dsj[4 * m + 1], (bf16)dsj[4 * m + 2], (bf16)dsj[4 * m + 3]};
+      }
+      // dV_w += P^T dO or dK_w += dS^T Q; B operands (rows as the reduction
+      // index) by transposing reads: rows 16 ks2 + 4 h' + 0..3 and + 8, with h'
+      // the half of the 16-lane group
+      {
+        const T* Bt = sw_wave ? Ob : Qb;
+#pragma unroll
+        for (int ks2 = 0; ks2 < 2; ++ks2)
+#pragma unroll
+          for (int t = 0; t < NDT; ++t) {
+            const frag bb = __builtin_shufflevector(read_tr(Bt + boff[t][0] + 16 * ks2 * D),
+                                                    read_tr(Bt + boff[t][1] + 16 * ks2 * D), 0, 1, 2, 3, 4, 5, 6, 7);
+            acc[t] = M::mma(pa[ks2], bb, acc[t]);
+          }
+      }
+      // this wave's dQ rows, read before the metadata buffer turns over
+      int32_t q_ent[NQT];
+      int q_lim[NQT];
+#pragma unroll
+      for (int u = 0; u < NQT; ++u) {
+        const int rt = (wave + 8 * u) / (D / 16);
+        q_ent[u] = ent_s[buf][16 * rt + gl];
+        q_lim[u] = lim_s[buf][16 * rt + gl];
+      }
+      __syncthreads();  // dS^T is in LDS
+
+      // dQ^T = K^T dS^T in 16 x 16 x 32 tiles: wave w takes d rows 16 (w % (D / 16))
+      // and row tiles (w + 8 u) / (D / 16); lane = row 16 rt + gl, registers = d 4 grp + j
+      {
+        f32x4 dq[NQT];
+#pragma unroll
+        for (int u = 0; u < NQT; ++u) dq[u] = f32x4{};
+#pragma unroll
+        for (int ks = 0; ks < kBlock / 32; ++ks) {
+          const frag a = __builtin_shufflevector(read_tr(Ks + koff0 + 32 * ks * D), read_tr(Ks + koff4 + 32 * ks * D),
+                                                 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+          for (int u = 0; u < NQT; ++u) {
+            const frag bb = __builtin_shufflevector(read_tr(dSt + doff[u] + 32 * ks * LDST),
+                                                    read_tr(dSt + doff[u] + (32 * ks + 4) * LDST), 0, 1, 2, 3, 4, 5, 6,
+                                                    7);
+            dq[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bb, dq[u], 0, 0, 0);
+          }
+        }
+        // partial per (token, slot): [head][d] bf16, 4 consecutive d per lane
+#pragma unroll
+        for (int u = 0; u < NQT; ++u) {
+          if (q_ent[u] >= 0 && q_lim[u] >= 0) {
+            const int rt = (wave + 8 * u) / (D / 16);
+            const int row = 16 * rt + gl;
+            const int i = q_ent[u] >> 6, slot = q_ent[u] & 63;
+            const int64_t ptok = (((int64_t)b * p.S_q + i) * p.G + g) * p.topk + slot;
+            T* po = (T*)p.part_o + (ptok * R + row % R) * D + 16 * d16 + 4 * grp;
+            *(bf16x4*)po = bf16x4{(bf16)dq[u][0], (bf16)dq[u][1], (bf16)dq[u][2], (bf16)dq[u][3]};
           }
         }
       }
     }
 
-    // the block's dK (times the scale) and dV: lane = d, register j = key c_row(j, h)
+    // the block's dV (S waves) or dK times the scale (dS waves): lane = d, register j = key c_row(j, h)
+    // (key kgrp * 32 + 4 h + c_row(j, 0), d 32 t + l32): one base per lane plus constants
+    float* dst = (sw_wave ? bp.dv : bp.dk) + kv0 + (int64_t)(kgrp * 32 + 4 * h) * D + l32;
+    const int lim_k = rows_ok - (kgrp * 32 + 4 * h);
+    const float f = sw_wave ? 1.f : bp.scale;
 #pragma unroll
-    for (int t = 0; t < NDH; ++t)
+    for (int t = 0; t < NDT; ++t)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int kr = kgrp * 32 + c_row(j, h);
-        if (kr < rows_ok) {
-          const int64_t o = kv0 + (int64_t)kr * D + (dh * NDH + t) * 32 + l32;
-          atomicAdd(&bp.dk[o], dk_acc[t][j] * bp.scale);
-          atomicAdd(&bp.dv[o], dv_acc[t][j]);
-        }
-      }
+      for (int j = 0; j < 16; ++j)
+        if (c_row(j, 0) < lim_k) atomicAdd(dst + c_row(j, 0) * D + t * 32, acc[t][j] * f);
   }
 }
 
 // dq[b, i, h, :] = scale * (sum over the row's visible selected blocks of the
-// partials); a thread per 16-byte chunk of the lane-native partial layout.
+// partials [head][d]); a thread per 16-byte chunk.
 template <int D, int R>
 __global__ __launch_bounds__(256) void bwd_dq_combine_kernel(AttnParams p, BwdParams bp) {
   constexpr int E = 8;
-  constexpr int NCHT = D * R / E;  // chunks per (token, slot) partial
+  constexpr int CPR = D / E;  // chunks per head row
   const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (u >= (int64_t)p.B * p.S_q * p.G * NCHT) return;
-  const int ch = (int)(u % NCHT);
-  const int64_t rowg = u / NCHT;  // (b * S_q + i) * G + g
+  if (u >= (int64_t)p.B * p.S_q * p.G * R * CPR) return;
+  const int ch = (int)(u % CPR);
+  const int64_t rest = u / CPR;
+  const int hh = (int)(rest % R);
+  const int64_t rowg = rest / R;  // (b * S_q + i) * G + g
   const int g = (int)(rowg % p.G);
   const int64_t bi = rowg / p.G;
   const int i = (int)(bi % p.S_q);
   const int b = (int)(bi / p.S_q);
-  const int hh = ch % R, h = (ch / R) & 1, q = ch / (2 * R);
   const int64_t t = p.q_offset + i;
   const int32_t* srow = p.sel + (((int64_t)b * p.G + g) * p.S_q + i) * p.topk;
   float acc[E];
@@ -337,18 +374,14 @@ __global__ __launch_bounds__(256) void bwd_dq_combine_kernel(AttnParams p, BwdPa
     const int c = srow[s2];
     if (c < 0 || c >= p.nb || (int64_t)c * kBlock > t) continue;
     const bf16x8 x = __builtin_bit_cast(
-        bf16x8, __builtin_nontemporal_load((const i32x4*)((const bf16*)p.part_o + (rowg * p.topk + s2) * (R * D) + ch * E)));
+        bf16x8, __builtin_nontemporal_load(
+                    (const i32x4*)((const bf16*)p.part_o + ((rowg * p.topk + s2) * R + hh) * D + ch * E)));
 #pragma unroll
     for (int e = 0; e < E; ++e) acc[e] += (float)x[e];
   }
-  const int r0 = (q * E) % 16, dt = (q * E) / 16;
-  float* orow = bp.dq + (bi * p.Hq + g * R + hh) * D;
-#pragma unroll
-  for (int m = 0; m < E / 4; ++m) {
-    const int d0 = dt * 32 + (r0 / 4 + m) * 8 + 4 * h;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) orow[d0 + e] = acc[4 * m + e] * bp.scale;
-  }
+  f32x4* orow = (f32x4*)(bp.dq + (bi * p.Hq + g * R + hh) * D + ch * E);
+  orow[0] = f32x4{acc[0], acc[1], acc[2], acc[3]} * bp.scale;
+  orow[1] = f32x4{acc[4], acc[5], acc[6], acc[7]} * bp.scale;
 }
 
 template <int D, int R>

@@ -31,7 +31,6 @@ msa_status fail(msa_status st, const char* fmt, ...) {
 
 constexpr size_t kAlign = 256;
 constexpr int kTokensPerItem = 128;
-constexpr int kBwdTokensPerItem = 512;  // backward work items (their dK, dV meet in fp32 atomics)
 constexpr int kAttnGrid = 512;      // persistent attention grid: 2 workgroups per CU
 constexpr int kIndexTargetUnits = 2048;
 constexpr int64_t kIndexVarlenChunk = 16;  // key blocks per unit when sequences have their own lengths
@@ -296,7 +295,7 @@ AttnPlan plan_attn(const msa_shape* s, const msa_kv_cache* cache) {
 }
 
 // Backward: the main branch's gather (never direct) with work items of
-// kBwdTokensPerItem tokens and one workgroup per possible item, dispatched as
+// msa::kBwdTokensPerItem tokens and one workgroup per possible item, dispatched as
 // slots free; plus rowsum(dO * O).
 AttnPlan plan_bwd(const msa_shape* s, size_t* off_dsum) {
   msa_shape s2 = *s;
@@ -318,12 +317,12 @@ AttnPlan plan_bwd(const msa_shape* s, size_t* off_dsum) {
     ap.off_item_off = take(nbk * 4);
     ap.off_nitems = take(4);
     ap.off_entries = take(entries * 4);
-    ap.off_items = take(((size_t)p.nbuckets + entries / kBwdTokensPerItem + 1) * 4);
+    ap.off_items = take(((size_t)p.nbuckets + entries / msa::kBwdTokensPerItem + 1) * 4);
     ap.off_po = take(entries * (size_t)p.r * p.d * 2);
     ap.off_pl = take(entries * (size_t)p.r * 4);
     ap.bytes = off;
   }
-  p.tpi = kBwdTokensPerItem;
+  p.tpi = msa::kBwdTokensPerItem;
   // items: at most one partial item per bucket plus entries / tpi full ones
   p.grid = (int)std::min<int64_t>((int64_t)p.nbuckets + (int64_t)p.B * p.G * p.S_q * p.topk / p.tpi + 1, 1 << 30);
   *off_dsum = ap.bytes;
