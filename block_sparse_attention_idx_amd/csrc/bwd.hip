@@ -164,13 +164,19 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_kernel(AttnParams p, BwdParam
     for (int t = threadIdx.x; t < ECH; t += NT) tok_s[t] = t < ntok ? toks[t] : 0;
     __syncthreads();
 
-    // A pass's rows, fetched into registers two passes ahead of use: chunks of
-    // its Q and dO rows (row = token (p0 + row / R), head row % R) and, in wave
-    // 0, row (lane % 32)'s entry with its raw lse and rowsum.
-    i32x4 qx[CPT], ox[CPT];
-    float lse_n = 0.f, dsum_n = 0.f;
-    int32_t ent_n = 0, pslot_n = 0;
-    auto fetch = [&](int p0) {
+    // A pass's rows, fetched into one of two register sets three passes before
+    // use and written to LDS one pass before: chunks of its Q and dO rows
+    // (row = token (p0 + row / R), head row % R) and, in wave 0, row (lane % 32)'s
+    // entry with its raw lse and rowsum.
+    struct Rows {
+      i32x4 qx[CPT], ox[CPT];
+      float lse_n, dsum_n;
+      int32_t ent_n, pslot_n;
+    };
+    Rows rw[2];
+    auto fetch = [&](int p0, Rows& r) {
+      i32x4* qx = r.qx;
+      i32x4* ox = r.ox;
 #pragma unroll
       for (int u = 0; u < CPT; ++u) {
         const int ch = min((int)threadIdx.x + u * NT, 32 * CH - 1);  // idle threads re-read the last chunk
@@ -182,15 +188,19 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_kernel(AttnParams p, BwdParam
       }
       if (wave == 0) {
         const int rr = lane & 31;
-        pslot_n = p0 + rr / R;
-        ent_n = tok_s[min(pslot_n, ntok - 1)];
-        const int64_t hrow = ((int64_t)b * p.Hq + g * R + rr % R) * p.S_q + (ent_n >> 6);
-        lse_n = bp.lse[hrow];
-        dsum_n = bp.dsum[hrow];
+        r.pslot_n = p0 + rr / R;
+        r.ent_n = tok_s[min(r.pslot_n, ntok - 1)];
+        const int64_t hrow = ((int64_t)b * p.Hq + g * R + rr % R) * p.S_q + (r.ent_n >> 6);
+        r.lse_n = bp.lse[hrow];
+        r.dsum_n = bp.dsum[hrow];
       }
     };
     // registers -> LDS buffer nb_
-    auto stage = [&](int nb_) {
+    auto stage = [&](int nb_, const Rows& r) {
+      const i32x4* qx = r.qx;
+      const i32x4* ox = r.ox;
+      const float lse_n = r.lse_n, dsum_n = r.dsum_n;
+      const int32_t ent_n = r.ent_n, pslot_n = r.pslot_n;
 #pragma unroll
       for (int u = 0; u < CPT; ++u) {
         const int ch = threadIdx.x + u * NT;
@@ -214,17 +224,59 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_kernel(AttnParams p, BwdParam
 #pragma unroll
     for (int t = 0; t < NDT; ++t) acc[t] = f32x16{};
 
-    fetch(0);
-    stage(0);
-    if (TPW < ntok) fetch(TPW);
+    // dQ^T = K^T dS^T of the previous pass in 16 x 16 x 32 tiles, issued between
+    // the next pass's S / dP products and its barrier (dS^T is rewritten only
+    // after that barrier): wave w takes d rows 16 (w % (D / 16)) and row tiles
+    // (w + 8 u) / (D / 16); lane = row 16 rt + gl, registers = d 4 grp + j
+    int32_t q_ent[NQT];
+    int q_lim[NQT];
+#pragma unroll
+    for (int u = 0; u < NQT; ++u) q_ent[u] = -1;
+    auto dq_pass = [&]() {
+      f32x4 dq[NQT];
+#pragma unroll
+      for (int u = 0; u < NQT; ++u) dq[u] = f32x4{};
+#pragma unroll
+      for (int ks = 0; ks < kBlock / 32; ++ks) {
+        const frag a = __builtin_shufflevector(read_tr(Ks + koff0 + 32 * ks * D), read_tr(Ks + koff4 + 32 * ks * D), 0,
+                                               1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+        for (int u = 0; u < NQT; ++u) {
+          const frag bb = __builtin_shufflevector(read_tr(dSt + doff[u] + 32 * ks * LDST),
+                                                  read_tr(dSt + doff[u] + (32 * ks + 4) * LDST), 0, 1, 2, 3, 4, 5, 6, 7);
+          dq[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bb, dq[u], 0, 0, 0);
+        }
+      }
+      // partial per (token, slot): [head][d] bf16, 4 consecutive d per lane
+#pragma unroll
+      for (int u = 0; u < NQT; ++u) {
+        if (q_ent[u] >= 0 && q_lim[u] >= 0) {
+          const int rt = (wave + 8 * u) / (D / 16);
+          const int row = 16 * rt + gl;
+          const int i = q_ent[u] >> 6, slot = q_ent[u] & 63;
+          const int64_t ptok = (((int64_t)b * p.S_q + i) * p.G + g) * p.topk + slot;
+          T* po = (T*)p.part_o + (ptok * R + row % R) * D + 16 * d16 + 4 * grp;
+          *(bf16x4*)po = bf16x4{(bf16)dq[u][0], (bf16)dq[u][1], (bf16)dq[u][2], (bf16)dq[u][3]};
+        }
+      }
+    };
+
+    fetch(0, rw[0]);
+    stage(0, rw[0]);
+    if (TPW < ntok) fetch(TPW, rw[1]);
+    if (2 * TPW < ntok) fetch(2 * TPW, rw[0]);
     __syncthreads();
-    int buf = 0;
-    for (int p0 = 0; p0 < ntok; p0 += TPW, buf ^= 1) {
-      // the next pass's rows into the other buffer: its readers (the previous
-      // pass) finished before that pass's last barrier
+    for (int p00 = 0; p00 < ntok; p00 += 2 * TPW)
+#pragma unroll
+    for (int buf = 0; buf < 2; ++buf) {  // pass p0 uses row buffer buf and refills register set buf ^ 1
+      const int p0 = p00 + buf * TPW;
+      if (p0 >= ntok) break;
+      // the next pass's rows into the other buffer (its readers, the previous
+      // pass, finished before that pass's last barrier); the register set
+      // freed refetches three passes ahead
       if (p0 + TPW < ntok) {
-        stage(buf ^ 1);
-        if (p0 + 2 * TPW < ntok) fetch(p0 + 2 * TPW);  // in flight for the next two passes
+        stage(buf ^ 1, rw[buf ^ 1]);
+        if (p0 + 3 * TPW < ntok) fetch(p0 + 3 * TPW, rw[buf ^ 1]);
       }
       const T* Qb = Qr[buf];
       const T* Ob = Or[buf];
@@ -239,6 +291,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_kernel(AttnParams p, BwdParam
           s = M::mma(a, kvf[ks], s);
         }
       }
+      if (p0 > 0) dq_pass();  // the previous pass's dQ, overlapping this pass's products
       frag pa[2];  // P or dS in bf16: A operands of dV / dK, step ks2 pairs index h*8+e with row c_row(8 ks2 + e, h)
       if (sw_wave) {
         float pj[16];
@@ -292,49 +345,16 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_kernel(AttnParams p, BwdParam
             acc[t] = M::mma(pa[ks2], bb, acc[t]);
           }
       }
-      // this wave's dQ rows, read before the metadata buffer turns over
-      int32_t q_ent[NQT];
-      int q_lim[NQT];
+      // this pass's dQ rows, read before the metadata buffer turns over
 #pragma unroll
       for (int u = 0; u < NQT; ++u) {
         const int rt = (wave + 8 * u) / (D / 16);
         q_ent[u] = ent_s[buf][16 * rt + gl];
         q_lim[u] = lim_s[buf][16 * rt + gl];
       }
-      __syncthreads();  // dS^T is in LDS
-
-      // dQ^T = K^T dS^T in 16 x 16 x 32 tiles: wave w takes d rows 16 (w % (D / 16))
-      // and row tiles (w + 8 u) / (D / 16); lane = row 16 rt + gl, registers = d 4 grp + j
-      {
-        f32x4 dq[NQT];
-#pragma unroll
-        for (int u = 0; u < NQT; ++u) dq[u] = f32x4{};
-#pragma unroll
-        for (int ks = 0; ks < kBlock / 32; ++ks) {
-          const frag a = __builtin_shufflevector(read_tr(Ks + koff0 + 32 * ks * D), read_tr(Ks + koff4 + 32 * ks * D),
-                                                 0, 1, 2, 3, 4, 5, 6, 7);
-#pragma unroll
-          for (int u = 0; u < NQT; ++u) {
-            const frag bb = __builtin_shufflevector(read_tr(dSt + doff[u] + 32 * ks * LDST),
-                                                    read_tr(dSt + doff[u] + (32 * ks + 4) * LDST), 0, 1, 2, 3, 4, 5, 6,
-                                                    7);
-            dq[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bb, dq[u], 0, 0, 0);
-          }
-        }
-        // partial per (token, slot): [head][d] bf16, 4 consecutive d per lane
-#pragma unroll
-        for (int u = 0; u < NQT; ++u) {
-          if (q_ent[u] >= 0 && q_lim[u] >= 0) {
-            const int rt = (wave + 8 * u) / (D / 16);
-            const int row = 16 * rt + gl;
-            const int i = q_ent[u] >> 6, slot = q_ent[u] & 63;
-            const int64_t ptok = (((int64_t)b * p.S_q + i) * p.G + g) * p.topk + slot;
-            T* po = (T*)p.part_o + (ptok * R + row % R) * D + 16 * d16 + 4 * grp;
-            *(bf16x4*)po = bf16x4{(bf16)dq[u][0], (bf16)dq[u][1], (bf16)dq[u][2], (bf16)dq[u][3]};
-          }
-        }
-      }
+      __syncthreads();  // dS^T is in LDS; the pass's row buffers are free
     }
+    dq_pass();  // the item's last pass
 
     // the block's dV (S waves) or dK times the scale (dS waves): lane = d, register j = key c_row(j, h)
     // (key kgrp * 32 + 4 h + c_row(j, 0), d 32 t + l32): one base per lane plus constants
