@@ -232,7 +232,9 @@ msa_status msa_kl_teacher_fwd_kvcache(const msa_shape* shape, const msa_kv_cache
  *    dQ[b,i,h] = scale sum_j dS_j k_j,   dK[b,g,j] += scale dS_j q[b,i,h].
  * Inputs: q, k, v, sel and the forward's out and lse (natural log), dout like
  * out; all bf16 except lse.  Outputs dq [B, S_q, Hq, d], dk and dv
- * [B, Hkv, S_k, d], fp32; keys no query attends get zero.  Built for
+ * [B, Hkv, S_k, d], fp32; keys no query attends get zero.  dk and dv sum the
+ * contributions of a block's query groups with fp32 atomics, so their last
+ * bits may differ between calls; dq is summed in a fixed order.  Built for
  * dtype == out_dtype == MSA_BF16, native caches and k_scale, v_scale in
  * {0, 1}; workspace: msa_workspace_size(shape, MSA_OP_SPARSE_ATTN_BWD). */
 msa_status msa_sparse_attn_bwd(const msa_shape* shape, const void* q, const void* k, const void* v,
