@@ -388,7 +388,7 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=50)
     ap.add_argument("--workload", type=int, default=3)
     ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--no-extra", action="store_true", help="skip the 8K and 1M-context prefill workloads")
+    ap.add_argument("--no-extra", action="store_true", help="skip the KL teacher, the backward and the 8K and 1M-context prefill workloads")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-breakdown", action="store_true", help="skip the per-kernel timing passes")

@@ -38,25 +38,30 @@ __global__ void bwd_zero_kernel(float* __restrict__ x, int64_t n) {
   if (i < n) x[i] = 0.f;
 }
 
-// Dsum[b, h, i] = dO[b, i, h, :] . O[b, i, h, :] in fp32, one thread per row.
+// Dsum[b, h, i] = dO[b, i, h, :] . O[b, i, h, :] in fp32: a lane per 16-byte
+// chunk (consecutive lanes read consecutive chunks), D / 8 lanes per row summed
+// by butterfly.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_dsum_kernel(AttnParams p, BwdParams bp) {
-  const int64_t row = (int64_t)blockIdx.x * 256 + threadIdx.x;  // (b * S_q + i) * Hq + h
-  if (row >= (int64_t)p.B * p.S_q * p.Hq) return;
-  const bf16x8* o = (const bf16x8*)((const bf16*)bp.out + row * D);
-  const bf16x8* g = (const bf16x8*)((const bf16*)bp.dout + row * D);
+  constexpr int L = D / 8;  // lanes per row (16 or 8), a power of two within a wave
+  const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t rows = (int64_t)p.B * p.S_q * p.Hq;
+  const int64_t row = u / L;  // (b * S_q + i) * Hq + h
   float acc = 0.f;
+  if (row < rows) {
+    const bf16x8 a = *((const bf16x8*)bp.out + u), b8 = *((const bf16x8*)bp.dout + u);
 #pragma unroll
-  for (int c = 0; c < D / 8; ++c) {
-    const bf16x8 a = o[c], b = g[c];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc = __builtin_fmaf((float)a[e], (float)b[e], acc);
+    for (int e = 0; e < 8; ++e) acc = __builtin_fmaf((float)a[e], (float)b8[e], acc);
   }
-  const int h = (int)(row % p.Hq);
-  const int64_t bi = row / p.Hq;
-  const int i = (int)(bi % p.S_q);
-  const int b = (int)(bi / p.S_q);
-  bp.dsum[((int64_t)b * p.Hq + h) * p.S_q + i] = acc;
+#pragma unroll
+  for (int m = L / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
+  if (row < rows && (u % L) == 0) {
+    const int h = (int)(row % p.Hq);
+    const int64_t bi = row / p.Hq;
+    const int i = (int)(bi % p.S_q);
+    const int b = (int)(bi / p.S_q);
+    bp.dsum[((int64_t)b * p.Hq + h) * p.S_q + i] = acc;
+  }
 }
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -409,7 +414,7 @@ static hipError_t launch_bwd_t(const AttnParams& p, const BwdParams& bp, hipStre
   const int64_t rows = (int64_t)p.B * p.S_q * p.Hq;
   const int64_t kvn = (int64_t)p.B * p.G * p.S_k * D;
   timer_start(tm, kKernBwd, s);
-  hipLaunchKernelGGL((bwd_dsum_kernel<D>), dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, s, p, bp);
+  hipLaunchKernelGGL((bwd_dsum_kernel<D>), dim3((unsigned)((rows * (D / 8) + 255) / 256)), dim3(256), 0, s, p, bp);
   // blocks no query selected get zero gradients
   hipLaunchKernelGGL(bwd_zero_kernel, dim3((unsigned)((kvn + 255) / 256)), dim3(256), 0, s, bp.dk, kvn);
   hipLaunchKernelGGL(bwd_zero_kernel, dim3((unsigned)((kvn + 255) / 256)), dim3(256), 0, s, bp.dv, kvn);
