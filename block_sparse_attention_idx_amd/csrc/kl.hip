@@ -14,14 +14,16 @@
 // pass, so every selected block contributes additive terms: its sum of
 // pbar (log pbar - s), plus the max and the exp-sum of its index scores.
 //
-// Work items and token lists are those of the main branch (the same gather).
-// Per item the block's K and index keys are staged in LDS, and passes of 4
-// waves x 32 (token, head) rows recompute S^T = K Q^T and the index scores
-// S_idx^T = K_idx Q_idx^T (each row with its token's index query) on 32x32
-// MFMA tiles.  The r heads of a token sit in r adjacent lanes; their
-// probabilities are summed by a butterfly that leaves lane hh of the group
-// owning 64 / r of its half's keys, so each logarithm is taken once per key,
-// not once per head.
+// Work items and token lists are those of the main branch's gather (items of
+// kKlTokensPerItem tokens).  Per item the block's K and index keys are staged
+// in LDS; the index scores S_idx^T = K_idx Q_idx^T of all the item's tokens are
+// formed first, 32 tokens per MFMA tile (the r heads of a token share its index
+// query, so they are computed once per token), and kept in LDS in place of the
+// index keys.  Passes of 4 waves x 32 (token, head) rows then recompute
+// S^T = K Q^T on 32x32 MFMA tiles.  The r heads of a token sit in r adjacent
+// lanes; their probabilities are summed by a butterfly that leaves lane hh of
+// the group owning 64 / r of its half's keys, so each logarithm is taken once
+// per key, not once per head, and each lane reads just those keys' index scores.
 #include <type_traits>
 
 #include "common.h"
@@ -54,10 +56,9 @@ __device__ __forceinline__ float partner(float x) {
 }
 
 // Butterfly over the R lanes of a token (steps O = R/2, R/4, ..., 1): at each
-// step a lane keeps the upper or lower half of its N values by bit O of hh.
-// sum() adds the partner's copy of the kept half, pick() only selects.
-// Afterwards each lane holds 64 / R of the slots in x[0, 64 / R), every slot
-// held by one lane of the token, and pick() leaves the same slots as sum().
+// step a lane keeps the upper or lower half of its N values by bit O of hh and
+// adds the partner's copy of that half.  Afterwards lane hh holds the sums of
+// slots hh * (64 / R) + k in x[k], k < 64 / R.
 template <int O, int N>
 struct Butterfly {
   __device__ static __forceinline__ void sum(f32x64& x, int hh) {
@@ -70,21 +71,11 @@ struct Butterfly {
     }
     Butterfly<O / 2, N / 2>::sum(x, hh);
   }
-  __device__ static __forceinline__ void pick(f32x64& x, int hh) {
-    const bool up = (hh & O) != 0;
-#pragma unroll
-    for (int k = 0; k < N / 2; ++k) {
-      const float lo = x[k], hi = x[k + N / 2];
-      x[k] = up ? hi : lo;
-    }
-    Butterfly<O / 2, N / 2>::pick(x, hh);
-  }
 };
 
 template <int N>
 struct Butterfly<0, N> {
   __device__ static __forceinline__ void sum(f32x64&, int) {}
-  __device__ static __forceinline__ void pick(f32x64&, int) {}
 };
 
 // Reductions over all lanes of one token: its R lanes (steps 1, 2, 4, ...: each
@@ -112,9 +103,18 @@ __global__ __launch_bounds__(256, 2) void kl_teacher_kernel(AttnParams p, KlPara
   constexpr int TPW = 32 / R, TPP = 4 * TPW;
   constexpr int NV = 64;      // score registers per lane: 4 key tiles x 16
   constexpr int NK = NV / R;  // keys a lane owns after the head butterfly
+  // index scores of the item's tokens, fp32 [token][h][register slot]: the C
+  // layout of the 32x32 tiles (lane = token, slot kt * 16 + j = key
+  // kt * 32 + c_row(j, h)); the token pitch is 4 floats past 128, so the 32
+  // tokens a store instruction writes fall in distinct banks
+  constexpr int LDSC = 2 * NV + 4;
+  static_assert(kKlTokensPerItem <= 64, "two 32-token index tiles per item");
+  constexpr int KI_BYTES = kBlock * LDI * (int)sizeof(T), SC_BYTES = kKlTokensPerItem * LDSC * 4;
   __shared__ __align__(16) T Ks[kBlock * LDK];
-  __shared__ __align__(16) T KIs[kBlock * LDI];
+  __shared__ __align__(16) char kis_raw[KI_BYTES > SC_BYTES ? KI_BYTES : SC_BYTES];  // index keys, then scores
   __shared__ int32_t ent_s[kBlock];  // the item's token entries ((row << 6) | slot)
+  T* KIs = (T*)kis_raw;
+  float* sc = (float*)kis_raw;
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int h = lane >> 5, l32 = lane & 31;
@@ -194,24 +194,60 @@ __global__ __launch_bounds__(256, 2) void kl_teacher_kernel(AttnParams p, KlPara
     }
     __syncthreads();
 
+    // index scores of the item's tokens: wave w forms key tiles 2 (w / 2) and
+    // 2 (w / 2) + 1 of token tile w % 2 (tokens past the list use the first
+    // entry's row and are never read)
+    {
+      const int tt = wave & 1;
+      const bool active = tt * 32 < ntok;  // uniform
+      f32x16 siacc[2];
+      siacc[0] = f32x16{};
+      siacc[1] = f32x16{};
+      if (active) {
+        const int32_t e0 = ent_s[min(tt * 32 + l32, ntok - 1)];
+        const T* qirow = (const T*)kp.q_idx + (((int64_t)b * p.S_q + (e0 >> 6)) * p.G + g) * DI;
+        frag qif[NKI];
+#pragma unroll
+        for (int ks = 0; ks < NKI; ++ks) qif[ks] = *(const frag*)(qirow + ks * KSTEP + h * KPL);
+#pragma unroll
+        for (int ks = 0; ks < NKI; ++ks)
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const int kt = 2 * (wave >> 1) + u;
+            const frag a = *(const frag*)&KIs[(kt * 32 + l32) * LDI + ks * KSTEP + h * KPL];
+            siacc[u] = M::mma(a, qif[ks], siacc[u]);
+          }
+      }
+      __syncthreads();  // every wave is done with the index keys
+      if (active) {
+        float* dst = sc + (tt * 32 + l32) * LDSC + h * NV;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int kt = 2 * (wave >> 1) + u;
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4)
+            *(f32x4*)(dst + kt * 16 + q4 * 4) =
+                f32x4{siacc[u][q4 * 4], siacc[u][q4 * 4 + 1], siacc[u][q4 * 4 + 2], siacc[u][q4 * 4 + 3]};
+        }
+      }
+      __syncthreads();
+    }
+
     const int64_t key0 = (int64_t)c * kBlock;
     const int head = g * R + hh;
     // A wave's rows of pass ps: the token entry (from LDS), its Q row, index
     // query row and main lse; loaded one pass ahead of their use.  Rows past
     // the token list read token 0's (valid) rows and are never stored.
-    auto load_rows = [&](int ps, frag (&qf)[NKS], frag (&qif)[NKI], float& lse2, int32_t& entry) {
+    auto load_rows = [&](int ps, frag (&qf)[NKS], float& lse2, int32_t& entry) {
       const int tslot = ps * TPP + wave * TPW + l32 / R;
       entry = tslot < ntok ? ent_s[tslot] : -1;
       const int i = entry >= 0 ? entry >> 6 : 0;
       const T* qrow = (const T*)p.q + (((int64_t)b * p.S_q + i) * p.Hq + head) * D;
-      const T* qirow = (const T*)kp.q_idx + (((int64_t)b * p.S_q + i) * p.G + g) * DI;
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) qf[ks] = *(const frag*)(qrow + ks * KSTEP + h * KPL);
-#pragma unroll
-      for (int ks = 0; ks < NKI; ++ks) qif[ks] = *(const frag*)(qirow + ks * KSTEP + h * KPL);
       lse2 = kp.lse[((int64_t)b * p.Hq + head) * p.S_q + i] * kLog2e;
     };
-    auto pass = [&](const frag (&qf)[NKS], const frag (&qif)[NKI], float lse2, int32_t entry) {
+    auto pass = [&](int ps, const frag (&qf)[NKS], float lse2, int32_t entry) {
       const int i = entry >= 0 ? entry >> 6 : 0, slot = entry & 63;
       const int64_t rel = qo + i - key0;  // query position relative to the block
       const bool rv = entry >= 0 && rel >= 0;
@@ -238,26 +274,15 @@ __global__ __launch_bounds__(256, 2) void kl_teacher_kernel(AttnParams p, KlPara
       }
       Butterfly<R / 2, NV>::sum(pv, hh);  // pv[0, NK): sums over the token's heads
 
-      // student: the token's index scores times index_scale
-      f32x64 sv;
+      // student: this lane's slots of the token's index scores times index_scale
+      float sv[NK];
       {
-        f32x16 siacc[4];
+        const int tslot = min(ps * TPP + wave * TPW + l32 / R, ntok - 1);
+        const float* src = sc + tslot * LDSC + h * NV + hh * NK;
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt) siacc[kt] = f32x16{};
-#pragma unroll
-        for (int ks = 0; ks < NKI; ++ks)
-#pragma unroll
-          for (int kt = 0; kt < 4; ++kt) {
-            const frag a = *(const frag*)&KIs[(kt * 32 + l32) * LDI + ks * KSTEP + h * KPL];
-            siacc[kt] = M::mma(a, qif[ks], siacc[kt]);
-          }
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-          for (int j = 0; j < 16; ++j) sv[kt * 16 + j] = siacc[kt][j] * kp.index_scale;
+        for (int k = 0; k < NK; ++k) sv[k] = src[k] * kp.index_scale;
       }
-      Butterfly<R / 2, NV>::pick(sv, hh);
-      // Lane hh now holds register slots hh * NK + k (slot s: key tile s / 16,
+      // Lane hh holds register slots hh * NK + k (slot s: key tile s / 16,
       // register s % 16).  The heads of a token share its visibility limit, so
       // the causal mask of a local block applies here, after the head sums.
       if (masked) {
@@ -298,18 +323,18 @@ __global__ __launch_bounds__(256, 2) void kl_teacher_kernel(AttnParams p, KlPara
 
     const int npass = wave * TPW < ntok ? (ntok - wave * TPW + TPP - 1) / TPP : 0;
     if (npass > 0) {
-      frag qfA[NKS], qiA[NKI], qfB[NKS], qiB[NKI];
+      frag qfA[NKS], qfB[NKS];
       float lseA, lseB;
       int32_t entA, entB;
-      load_rows(0, qfA, qiA, lseA, entA);
+      load_rows(0, qfA, lseA, entA);
       for (int ps = 0; ps < npass; ps += 2) {
-        load_rows(ps + 1, qfB, qiB, lseB, entB);
+        load_rows(ps + 1, qfB, lseB, entB);
         __builtin_amdgcn_sched_barrier(0);
-        pass(qfA, qiA, lseA, entA);
+        pass(ps, qfA, lseA, entA);
         if (ps + 1 < npass) {
-          load_rows(ps + 2, qfA, qiA, lseA, entA);
+          load_rows(ps + 2, qfA, lseA, entA);
           __builtin_amdgcn_sched_barrier(0);
-          pass(qfB, qiB, lseB, entB);
+          pass(ps + 1, qfB, lseB, entB);
         }
       }
     }

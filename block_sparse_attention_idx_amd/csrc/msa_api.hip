@@ -238,7 +238,8 @@ struct AttnPlan {
   size_t bytes;
 };
 
-AttnPlan plan_attn(const msa_shape* s, const msa_kv_cache* cache) {
+// tpi: query tokens per work item of the gather
+AttnPlan plan_attn(const msa_shape* s, const msa_kv_cache* cache, int tpi = kTokensPerItem) {
   AttnPlan ap{};
   msa::AttnParams& p = ap.p;
   p.cm = cache_map(cache);
@@ -253,7 +254,7 @@ AttnPlan plan_attn(const msa_shape* s, const msa_kv_cache* cache) {
   p.q_offset = s->q_offset;
   p.nb = (int)ceil_div(s->kv_len, msa::kBlock);
   p.nbuckets = p.B * p.G * p.nb;
-  p.tpi = kTokensPerItem;
+  p.tpi = tpi;
   const int64_t Lmax = s->q_len > 0 ? max_pos(s, cache) / msa::kBlock : 0;
   // queries per (b, g, block) on average; below 2 the gather buys nothing
   const double per_bucket = (double)s->q_len * std::min<int64_t>(s->topk, Lmax + 1) / (double)(Lmax + 1);
@@ -403,7 +404,8 @@ size_t msa_workspace_size_kvcache(const msa_shape* s, const msa_kv_cache* cache,
   if (op >= MSA_OP_INDEX_SELECT && op <= MSA_OP_SPARSE_ATTN_BWD && check_shape(s, op) == MSA_OK &&
       check_cache(s, cache) == MSA_OK && s->q_len > 0) {
     if (op == MSA_OP_INDEX_SELECT) r = plan_index(s, cache).bytes;
-    else if (op == MSA_OP_SPARSE_ATTN || op == MSA_OP_KL_TEACHER) r = plan_attn(s, cache).bytes;
+    else if (op == MSA_OP_SPARSE_ATTN) r = plan_attn(s, cache).bytes;
+    else if (op == MSA_OP_KL_TEACHER) r = plan_attn(s, cache, msa::kKlTokensPerItem).bytes;
     else if (op == MSA_OP_SPARSE_ATTN_BWD) {
       size_t od = 0;
       r = cache ? 0 : plan_bwd(s, &od).bytes;
@@ -505,7 +507,7 @@ msa_status msa_kl_teacher_fwd_kvcache(const msa_shape* s, const msa_kv_cache* ca
     return fail(MSA_ERR_INVALID, "q, k, q_idx, k_idx, sel, lse and kl must be non-NULL");
   if (!std::isfinite(index_scale)) return fail(MSA_ERR_INVALID, "index_scale must be finite");
   if (s->q_len == 0) return MSA_OK;
-  AttnPlan ap = plan_attn(s, cache);
+  AttnPlan ap = plan_attn(s, cache, msa::kKlTokensPerItem);
   if ((st = check_ws(ws, ws_bytes, ap.bytes)) != MSA_OK) return st;
   bind_attn(ap, (char*)ws);
   ap.p.q = q;

@@ -199,7 +199,8 @@ def test_kl_teacher_checks():
     assert "index_scale" in L.msa_last_error().decode()
     assert L.msa_kl_teacher_fwd(*args()) == -3  # valid: only the workspace is missing
     need = msa.workspace_size(sh, msa.OP_KL_TEACHER)
-    assert need == msa.workspace_size(sh, msa.OP_SPARSE_ATTN) > 0
+    # the main branch's gather and partial regions, cut into smaller work items
+    assert need >= msa.workspace_size(sh, msa.OP_SPARSE_ATTN) > 0
     assert msa.lib().msa_set_kernel_timer(9, None, None) == 0 and msa.lib().msa_set_kernel_timer(10, None, None) == -1
 
 
