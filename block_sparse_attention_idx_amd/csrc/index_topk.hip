@@ -378,13 +378,28 @@ __global__ __launch_bounds__(256, 2) void index_topk_small_kernel(IndexParams p)
   // two k-steps of e4m3 keys
   typedef typename std::conditional<kNative, frag, i32x4>::type kraw;
   static_assert(kNative || (sizeof(S) == 1 && KPL == 8 && NKS % 2 == 0), "e4m3 keys come as 16-byte runs");
-  constexpr int NKR = kNative ? NKS : NKS / 2;  // loads per lane per tile
-  // element offset of k-step ks, lane half h (16 elements per 16 bytes of e4m3)
+  constexpr int NKR = kNative ? NKS : NKS / 2;  // 16-byte loads per lane per tile
+  // A 32-key tile (32 rows of RB bytes, contiguous in memory) is read with
+  // linear non-temporal 16-byte loads (lane L, load u: byte 1024 u + 16 L), put
+  // in the wave's LDS tile and read back in the MFMA layout: lane l takes
+  // 16-byte chunk 2 u + h of row l % 32 (k-step u of native keys; k-steps 2u,
+  // 2u + 1 of e4m3 keys, whose dims the query fragments take in the same order).
+  // Chunk c of row r sits at chunk c ^ sw(r), which puts the 16 rows of a read
+  // and the 16 chunks of a write in distinct LDS banks.
+  constexpr int RB = DI * (int)sizeof(S);  // bytes per key row
+  constexpr int CPR = RB / 16;             // 16-byte chunks per row
+  static_assert(NKR * 1024 == 32 * RB, "a tile is NKR loads of 1 KiB per wave");
+  constexpr int SWS = CPR == 16 ? 0 : CPR == 8 ? 1 : CPR == 4 ? 2 : 3;
+  auto sw = [](int r) { return (r >> SWS) & (CPR - 1); };
+  // element offset of k-step ks, lane half h in the query row (16 elements per 16 bytes of e4m3)
   auto koff = [](int ks, int hh) { return kNative ? ks * KSTEP + hh * KPL : (ks / 2) * 32 + hh * 16 + (ks % 2) * 8; };
   constexpr int NL = 8;  // lists per row: 4 waves x 2 lane halves
-  static_assert(NL * CAP * 32 * 8 <= 65536, "list merge fits the static LDS");
-  __shared__ float xs[NL * CAP * 32];
-  __shared__ int xi[NL * CAP * 32];
+  constexpr int MERGE_BYTES = NL * CAP * 32 * 8, TILE_BYTES = 4 * 32 * RB;
+  static_assert(MERGE_BYTES <= 65536, "list merge fits the static LDS");
+  // the waves' key tiles during the block loop, the list merge afterwards
+  __shared__ __align__(16) char lds_raw[MERGE_BYTES > TILE_BYTES ? MERGE_BYTES : TILE_BYTES];
+  float* xs = (float*)lds_raw;
+  int* xi = (int*)(lds_raw + NL * CAP * 32 * 4);
 
   int b, split;  // one row tile per sequence: the tile is the sequence
   if (!unit_of(p, blockIdx.x, false, b, split)) return;
@@ -431,15 +446,30 @@ __global__ __launch_bounds__(256, 2) void index_topk_small_kernel(IndexParams p)
   };
   // tile tl of the wave; tl past the end re-reads the last one (just read, so from
   // L2); an unmapped page is read from the pool start and scored -inf
-  auto load_tile = [&](kraw (&a)[NKR], int tl) {
+  auto load_tile = [&](i32x4 (&a)[NKR], int tl) {
     const int tc = min(tl, ntl - 1);
     const int64_t o = blk_off(tc / 4);
-    const S* src = kpool + (o < 0 ? 0 : o) + ((tc % 4) * 32 + l32) * DI;
+    const char* src = (const char*)(kpool + (o < 0 ? 0 : o) + (tc % 4) * 32 * DI) + lane * 16;
 #pragma unroll
-    for (int u = 0; u < NKR; ++u) a[u] = *(const kraw*)(src + koff(kNative ? u : 2 * u, h));
+    for (int u = 0; u < NKR; ++u) a[u] = __builtin_nontemporal_load((const i32x4*)(src + u * 1024));
   };
+  char* wtile = lds_raw + wave * 32 * RB;
   // this lane's max over its 16 keys of the tile
-  auto tile_max = [&](const kraw (&a)[NKR]) {
+  auto tile_max = [&](const i32x4 (&ld)[NKR]) {
+#pragma unroll
+    for (int u = 0; u < NKR; ++u) {  // linear chunk 64 u + lane: row (64 u + lane) / CPR
+      const int r = (64 * u + lane) / CPR, c = (64 * u + lane) % CPR;
+      *(i32x4*)(wtile + (r * CPR + (c ^ sw(r))) * 16) = ld[u];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    kraw a[NKR];
+#pragma unroll
+    for (int u = 0; u < NKR; ++u) a[u] = *(const kraw*)(wtile + (l32 * CPR + ((2 * u + h) ^ sw(l32))) * 16);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     f32x16 acc = f32x16{};
 #pragma unroll
     for (int u = 0; u < NKR; ++u) {
@@ -459,7 +489,7 @@ __global__ __launch_bounds__(256, 2) void index_topk_small_kernel(IndexParams p)
   };
 
   float pm = kNegInf, pmA = kNegInf;
-  auto process = [&](const kraw (&a)[NKR], int tl) {
+  auto process = [&](const i32x4 (&a)[NKR], int tl) {
     pm = fmaxf(pm, tile_max(a));
     if (tl % 4 != 3) return;  // the block continues in the next tile
     const int j = tl / 4;
@@ -478,7 +508,7 @@ __global__ __launch_bounds__(256, 2) void index_topk_small_kernel(IndexParams p)
     }
   };
   if (nbw > 0) {
-    kraw ta[NKR], tb[NKR];
+    i32x4 ta[NKR], tb[NKR];
     load_tile(ta, 0);
     for (int tl = 0; tl < ntl; tl += 2) {  // ntl is a multiple of 4
       load_tile(tb, tl + 1);
@@ -491,6 +521,7 @@ __global__ __launch_bounds__(256, 2) void index_topk_small_kernel(IndexParams p)
   }
 
   // merge the 8 lists of each row through LDS: [list][CAP][32 rows]
+  __syncthreads();  // every wave is done with its key tile (the same LDS)
 #pragma unroll
   for (int j = 0; j < CAP; ++j) {
     const int o = ((wave * 2 + h) * CAP + j) * 32 + l32;
