@@ -97,6 +97,8 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_kernel(AttnParams p, BwdParam
   __shared__ __align__(16) T Or[2][32 * D];
   __shared__ __align__(16) float Ps[4 * 4 * 64 * 4];  // P handed from S waves to dS waves
   __shared__ __align__(16) T dSt[kBlock * LDST];  // dS^T [key][row]
+  constexpr int LDQS = D + 8;                      // dQ tile pitch: [row][d]
+  __shared__ __align__(16) T dQs[32 * LDQS];       // a pass's dQ in bf16, stored to the partials in full rows
   __shared__ float lse_s[2][32], dsum_s[2][32];
   __shared__ int lim_s[2][32];
   __shared__ int32_t ent_s[2][32];
@@ -232,11 +234,12 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_kernel(AttnParams p, BwdParam
     // dQ^T = K^T dS^T of the previous pass in 16 x 16 x 32 tiles, issued between
     // the next pass's S / dP products and its barrier (dS^T is rewritten only
     // after that barrier): wave w takes d rows 16 (w % (D / 16)) and row tiles
-    // (w + 8 u) / (D / 16); lane = row 16 rt + gl, registers = d 4 grp + j
-    int32_t q_ent[NQT];
-    int q_lim[NQT];
-#pragma unroll
-    for (int u = 0; u < NQT; ++u) q_ent[u] = -1;
+    // (w + 8 u) / (D / 16); lane = row 16 rt + gl, registers = d 4 grp + j.  The
+    // tile goes to LDS; after the barrier every thread stores 16 bytes of it.
+    constexpr int QCH = D / 8;  // 16-byte chunks per dQ row
+    const int srow = (int)threadIdx.x / QCH, schunk = (int)threadIdx.x % QCH;  // this thread's chunk to store
+    int32_t st_ent = -1;  // the stored pass's entry and visibility of row srow
+    int st_lim = -1;
     auto dq_pass = [&]() {
       f32x4 dq[NQT];
 #pragma unroll
@@ -252,17 +255,19 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_kernel(AttnParams p, BwdParam
           dq[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bb, dq[u], 0, 0, 0);
         }
       }
-      // partial per (token, slot): [head][d] bf16, 4 consecutive d per lane
 #pragma unroll
       for (int u = 0; u < NQT; ++u) {
-        if (q_ent[u] >= 0 && q_lim[u] >= 0) {
-          const int rt = (wave + 8 * u) / (D / 16);
-          const int row = 16 * rt + gl;
-          const int i = q_ent[u] >> 6, slot = q_ent[u] & 63;
-          const int64_t ptok = (((int64_t)b * p.S_q + i) * p.G + g) * p.topk + slot;
-          T* po = (T*)p.part_o + (ptok * R + row % R) * D + 16 * d16 + 4 * grp;
-          *(bf16x4*)po = bf16x4{(bf16)dq[u][0], (bf16)dq[u][1], (bf16)dq[u][2], (bf16)dq[u][3]};
-        }
+        const int rt = (wave + 8 * u) / (D / 16);
+        *(bf16x4*)&dQs[(16 * rt + gl) * LDQS + 16 * d16 + 4 * grp] =
+            bf16x4{(bf16)dq[u][0], (bf16)dq[u][1], (bf16)dq[u][2], (bf16)dq[u][3]};
+      }
+    };
+    // partial per (token, slot): [head][d] bf16; thread srow, schunk writes 16 bytes
+    auto dq_store = [&]() {
+      if (srow < 32 && st_ent >= 0 && st_lim >= 0) {
+        const int i = st_ent >> 6, slot = st_ent & 63;
+        const int64_t ptok = (((int64_t)b * p.S_q + i) * p.G + g) * p.topk + slot;
+        *(i32x4*)((T*)p.part_o + (ptok * R + srow % R) * D + schunk * 8) = *(const i32x4*)&dQs[srow * LDQS + schunk * 8];
       }
     };
 
@@ -314,7 +319,8 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_kernel(AttnParams p, BwdParam
 #pragma unroll
           for (int e = 0; e < 8; ++e) pa[ks2][e] = (bf16)pj[ks2 * 8 + e];
       }
-      __syncthreads();  // P is in LDS
+      __syncthreads();  // P is in LDS (and the previous pass's dQ tile)
+      if (p0 > 0) dq_store();
       if (!sw_wave) {
         float dsj[16];
 #pragma unroll
@@ -350,16 +356,16 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_kernel(AttnParams p, BwdParam
             acc[t] = M::mma(pa[ks2], bb, acc[t]);
           }
       }
-      // this pass's dQ rows, read before the metadata buffer turns over
-#pragma unroll
-      for (int u = 0; u < NQT; ++u) {
-        const int rt = (wave + 8 * u) / (D / 16);
-        q_ent[u] = ent_s[buf][16 * rt + gl];
-        q_lim[u] = lim_s[buf][16 * rt + gl];
+      // this pass's dQ row for the store, read before the metadata buffer turns over
+      if (srow < 32) {
+        st_ent = ent_s[buf][srow];
+        st_lim = lim_s[buf][srow];
       }
       __syncthreads();  // dS^T is in LDS; the pass's row buffers are free
     }
     dq_pass();  // the item's last pass
+    __syncthreads();
+    dq_store();
 
     // the block's dV (S waves) or dK times the scale (dS waves): lane = d, register j = key c_row(j, h)
     // (key kgrp * 32 + 4 h + c_row(j, 0), d 32 t + l32): one base per lane plus constants
