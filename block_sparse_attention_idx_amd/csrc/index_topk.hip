@@ -588,9 +588,24 @@ __global__ __launch_bounds__(256) void topk_merge_kernel(IndexParams p) {
   const int32_t* gi = p.part_i + row * p.nsplit * CAP;
   float* ss = (float*)msmem + wave * per_wave;
   int* si = (int*)msmem + 4 * per_wave + wave * per_wave;
-  for (int e = lane; e < nl * CAP; e += 64) {
-    ss[e] = gs[e];
-    si[e] = gi[e];
+  // the lists in batches of 8 loads per lane, all in flight before any is stored
+  for (int e0 = 0; e0 < nl * CAP; e0 += 64 * 8) {
+    float vs[8];
+    int vi[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int e = min(e0 + u * 64 + lane, nl * CAP - 1);
+      vs[u] = gs[e];
+      vi[u] = gi[e];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int e = e0 + u * 64 + lane;
+      if (e < nl * CAP) {
+        ss[e] = vs[u];
+        si[e] = vi[u];
+      }
+    }
   }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
