@@ -11,21 +11,23 @@
 // queries that selected it (the buckets of early blocks, visible to most
 // queries, are many times the mean); the block's dK and dV accumulate over the
 // item's queries in registers and are added to the (zeroed) outputs with fp32
-// atomics, so their summation order between items is not fixed.  Wave w owns the
-// block's keys [32w, 32w + 32) and keeps their K and V rows in registers as
-// MFMA B operands (8 waves: waves w and w + 4 own the same keys and split d
-// between their dK / dV accumulators, so two waves fit on each SIMD).  Passes of 32 rows ((token, head) pairs; the r heads of a
-// token adjacent) are shared by the 4 waves; a pass's Q and dO rows are
-// fetched one pass ahead (the bucket's token entries sit in LDS) and written to
-// LDS both row-major and transposed:
-//   S = Q K_w^T and dP = dO V_w^T put the wave's key in the lane and the rows in
-//   the registers -- directly the A operand of dV_w += P^T dO and
-//   dK_w += dS^T Q, whose B operands (dO, Q with rows as the reduction index)
-//   come from transposed tiles in LDS;
-//   dS goes to LDS ([row][key]) and wave w forms the d-slice [32w, 32w + 32) of
-//   dQ^T = K^T dS^T over all 128 keys (K^T staged once per item), stored as a
-//   bf16 partial per (token, slot) in the forward's lane-native layout and
-//   summed over the slots by bwd_dq_combine_kernel.
+// atomics, so their summation order between items is not fixed.
+//
+// Eight waves.  Waves 0-3 ("S waves") own the block's keys [32w, 32w + 32),
+// keep their K rows in registers as MFMA B operands and form S = Q K_w^T, P and
+// dV_w += P^T dO; waves 4-7 ("dS waves") own the same keys, keep their V rows
+// and form dP = dO V_w^T, dS = P o (dP - Dsum) (P handed over in fp32 through
+// LDS) and dK_w += dS^T Q.  S and dP put the key in the lane and the rows in the
+// registers, which is directly the A operand of the dV / dK products; their B
+// operands (dO and Q with the rows as the reduction index) come from the
+// row-major Q and dO tiles through gfx950's transposing LDS read.  A pass holds
+// 32 rows ((token, head) pairs, the r heads of a token adjacent); its Q and dO
+// rows are fetched three passes ahead into two register sets and written to a
+// double-buffered LDS tile one pass ahead.  dS^T goes to LDS and all 8 waves
+// form 16 x 16 tiles of dQ^T = K^T dS^T for the previous pass between the next
+// pass's products and its barrier; the tile is staged in LDS and stored as a
+// bf16 partial [head][d] per (token, slot), summed over the slots by
+// bwd_dq_combine_kernel.
 #include "common.h"
 #include "kernels.h"
 
