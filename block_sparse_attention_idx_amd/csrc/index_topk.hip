@@ -360,14 +360,15 @@ __global__ __launch_bounds__(256, 2) void index_topk_kernel(IndexParams p) {
 // Few rows per sequence (S_q * G <= 32, e.g. decode).  One 32-row tile holds
 // all of a sequence's (row, group) pairs, so rather than four waves sharing a
 // staged block, each wave takes whole blocks of the unit's key range (wave w:
-// blocks c_begin + w, c_begin + w + 4, ...).  K fragments are read straight from
-// global memory as the MFMA A operand, one 32-key tile ahead of their use, with
-// no LDS staging and no barrier in the block loop.  Every lane reads 16 bytes
-// per load: for e4m3 keys that is two k-steps, so the reduction dimension is
-// taken in the order d = 32 p + 16 h + 8 (ks % 2) + e (p = ks / 2) for both
-// operands; any order common to K and Q gives the same dot products.  As in the kernel above the
-// two lane halves of a wave rank alternate blocks of its sequence; the 4 x 2
-// lists of a row are merged through LDS at the end.
+// blocks c_begin + w, c_begin + w + 4, ...), with no barrier in the block loop.
+// A 32-key tile is read with linear non-temporal 16-byte loads one tile ahead of
+// its use (the pattern that streams fastest from HBM) and rearranged into the
+// MFMA A-operand layout through the wave's own LDS tile.  A lane's operand is 16
+// bytes of one key row: for e4m3 keys that is two k-steps, so the reduction
+// dimension is taken in the order d = 32 p + 16 h + 8 (ks % 2) + e (p = ks / 2)
+// for both operands; any order common to K and Q gives the same dot products.
+// As in the kernel above the two lane halves of a wave rank alternate blocks of
+// its sequence; the 4 x 2 lists of a row are merged through LDS at the end.
 template <typename T, typename S, int DI, int CAP>
 __global__ __launch_bounds__(256, 2) void index_topk_small_kernel(IndexParams p) {
   using M = Mma<T>;
