@@ -156,21 +156,32 @@ __global__ __launch_bounds__(256, 2) void index_topk_kernel(IndexParams p) {
   using M = Mma<T>;
   using frag = typename M::frag;
   constexpr int KPL = M::KPL, KSTEP = M::KSTEP, NKS = DI / KSTEP;
-  constexpr int PAD = 16 / (int)sizeof(T);
-  constexpr int LDW = DI + PAD;  // LDS pitch (elements): rows 16 B apart in bank space
+  // LDS tile of a block: 128 rows of DI elements of T, unpadded; 16-byte chunk c
+  // of row r sits at chunk c ^ sw(r), so the 16 rows an A-operand read touches
+  // at one column fall in distinct banks
+  constexpr int RB = DI * (int)sizeof(T);  // bytes per LDS row
+  constexpr int CPR = RB / 16;             // 16-byte chunks per LDS row
+  constexpr int EPC = 16 / (int)sizeof(T);  // elements per chunk
+  constexpr int SWS = CPR >= 16 ? 0 : CPR == 8 ? 1 : CPR == 4 ? 2 : 3;
+  constexpr int TILE_BYTES = kBlock * RB;
+  auto sw = [](int r) { return (r >> SWS) & (CPR - 1); };
+  auto at = [&](int r, int col) { return r * DI + (((col / EPC) ^ sw(r)) * EPC) + col % EPC; };
+  // native bf16 keys go straight from HBM into the tile (no registers); e4m3
+  // and fp32 keys are staged through registers
+  constexpr bool kDma = std::is_same<S, T>::value && sizeof(T) == 2 && TILE_BYTES % 4096 == 0;
   constexpr int ROWS_WAVE = 32 * RT;
   constexpr int ROWS_WG = 4 * ROWS_WAVE;
   // staging: 16-byte chunks of k_idx in its storage type S; a chunk holds SE
   // keys' elements and widens to SE / (16 / sizeof(T)) chunks of T in LDS
   constexpr int SE = 16 / (int)sizeof(S);
   constexpr int CH_PER_ROW = DI / SE;
-  constexpr int CH_PER_THREAD = kBlock * CH_PER_ROW / 256;
-  static_assert(CH_PER_THREAD >= 1 && (kBlock * CH_PER_ROW) % 256 == 0, "staging split");
-  constexpr int KS_BYTES = 2 * kBlock * LDW * (int)sizeof(T);
+  constexpr int CH_PER_THREAD = kDma ? 1 : kBlock * CH_PER_ROW / 256;
+  static_assert(kDma || (CH_PER_THREAD >= 1 && (kBlock * CH_PER_ROW) % 256 == 0), "staging split");
+  constexpr int KS_BYTES = 2 * TILE_BYTES;
   constexpr int LIST_BYTES = 4 * 2 * CAP * 32 * 8;  // one row tile of lists, all waves
   constexpr int SMEM = KS_BYTES > LIST_BYTES ? KS_BYTES : LIST_BYTES;
   __shared__ __align__(16) char smem[SMEM];
-  T* Ks = (T*)smem;  // [2][kBlock * LDW]
+  T* Ks = (T*)smem;  // [2][kBlock * DI]
 
   int tg, split;
   if (!unit_of(p, blockIdx.x, true, tg, split)) return;
@@ -222,20 +233,38 @@ __global__ __launch_bounds__(256, 2) void index_topk_kernel(IndexParams p) {
     const int64_t o = block_offset(p.cm, p.S_k, 1, DI, b, 0, c);
     return (const i32x4*)(kpool + (o < 0 ? 0 : o));
   };
-  // one staged chunk into the LDS tile: row-major, SE elements from column col
+  // one staged chunk into the LDS tile: SE elements from column col of a row
   auto stage = [&](T* tile, int ch, i32x4 x) {
-    const int row = ch / CH_PER_ROW, col = ch - row * CH_PER_ROW;
-    T* dst = &tile[row * LDW + col * SE];
+    const int row = ch / CH_PER_ROW, col = (ch - row * CH_PER_ROW) * SE;
     if constexpr (std::is_same<S, T>::value) {
-      *(i32x4*)dst = x;
-    } else {
+      *(i32x4*)&tile[at(row, col)] = x;
+    } else {  // 16 e4m3 keys widen to two chunks of bf16
       const uint2 a = e4m3x4_to_bf16((uint32_t)x[0]), b2 = e4m3x4_to_bf16((uint32_t)x[1]);
       const uint2 c2 = e4m3x4_to_bf16((uint32_t)x[2]), d2 = e4m3x4_to_bf16((uint32_t)x[3]);
-      *(i32x4*)dst = i32x4{(int)a.x, (int)a.y, (int)b2.x, (int)b2.y};
-      *(i32x4*)(dst + 8) = i32x4{(int)c2.x, (int)c2.y, (int)d2.x, (int)d2.y};
+      *(i32x4*)&tile[at(row, col)] = i32x4{(int)a.x, (int)a.y, (int)b2.x, (int)b2.y};
+      *(i32x4*)&tile[at(row, col + 8)] = i32x4{(int)c2.x, (int)c2.y, (int)d2.x, (int)d2.y};
     }
   };
-  if (has_blocks) {
+  // native keys: block c straight into tile bi.  Wave w fills 1 KiB pieces
+  // (w * NU + u) of the tile; the hardware puts lane L's 16 bytes at byte 16 L
+  // of a piece, so lane L reads the chunk the swizzle assigns to that slot.
+  constexpr int NU = TILE_BYTES / 4096;
+  auto dma_block = [&](int c, int bi) {
+    const char* src = (const char*)kblock(c);
+    char* tile = smem + bi * TILE_BYTES;
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const int piece = (wave * NU + u) * 1024;
+      const int kb = piece + lane * 16;
+      const int r = kb / RB, pc = (kb % RB) / 16;
+      __builtin_amdgcn_global_load_lds((const void*)(src + r * RB + (pc ^ sw(r)) * 16),
+                                       (__attribute__((address_space(3))) void*)(tile + piece), 16, 0, 0);
+    }
+  };
+  if (kDma) {
+    if (has_blocks) dma_block(c_begin, 0);
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's pieces are in LDS
+  } else if (has_blocks) {
     const i32x4* src = kblock(c_begin);
 #pragma unroll
     for (int u = 0; u < CH_PER_THREAD; ++u) pre[u] = src[threadIdx.x + u * 256];
@@ -255,7 +284,10 @@ __global__ __launch_bounds__(256, 2) void index_topk_kernel(IndexParams p) {
   int buf = 0;
   for (int c = c_begin; c < c_end; ++c) {
     const bool has_next = c + 1 < c_end;
-    if (c + 2 < c_end) {
+    if (kDma) {
+      // block c + 1 into the other tile (its last readers, block c - 1, passed the barrier)
+      if (has_next) dma_block(c + 1, buf ^ 1);
+    } else if (c + 2 < c_end) {
       const i32x4* src = kblock(c + 2);
 #pragma unroll
       for (int u = 0; u < CH_PER_THREAD; ++u) pre2[u] = src[threadIdx.x + u * 256];
@@ -266,18 +298,21 @@ __global__ __launch_bounds__(256, 2) void index_topk_kernel(IndexParams p) {
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) pm[rt] = kNegInf;
     if (wave_active) {
-      const T* kt_base = Ks + buf * (kBlock * LDW);
+      const T* kt_base = Ks + buf * (kBlock * DI);
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
         f32x16 acc[RT];
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) acc[rt] = f32x16{};
+        // the tile's A operands all in flight before the first product
+        frag a[NKS];
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-          const frag a = *(const frag*)&kt_base[(kt * 32 + l32) * LDW + ks * KSTEP + h * KPL];
+        for (int ks = 0; ks < NKS; ++ks) a[ks] = *(const frag*)&kt_base[at(kt * 32 + l32, ks * KSTEP + h * KPL)];
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int rt = 0; rt < RT; ++rt) acc[rt] = M::mma(a, qf[rt][ks], acc[rt]);
-        }
+        for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt) acc[rt] = M::mma(a[ks], qf[rt][ks], acc[rt]);
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
@@ -288,9 +323,11 @@ __global__ __launch_bounds__(256, 2) void index_topk_kernel(IndexParams p) {
         for (int rt = 0; rt < RT; ++rt) pm[rt] = kNegInf;
       }
     }
-    if (has_next) {
+    if (kDma) {
+      __builtin_amdgcn_s_waitcnt(0);  // this wave's pieces of block c + 1 are in LDS
+    } else if (has_next) {
 #pragma unroll
-      for (int u = 0; u < CH_PER_THREAD; ++u) stage(Ks + (buf ^ 1) * (kBlock * LDW), threadIdx.x + u * 256, pre[u]);
+      for (int u = 0; u < CH_PER_THREAD; ++u) stage(Ks + (buf ^ 1) * (kBlock * DI), threadIdx.x + u * 256, pre[u]);
 #pragma unroll
       for (int u = 0; u < CH_PER_THREAD; ++u) pre[u] = pre2[u];
     }
