@@ -367,7 +367,8 @@ def cpu_baseline(s: synth.Shape, x, out_gpu, sel_gpu, budget_s: float):
             max_err = max(max_err, float(np.abs(out_np[b, i] - o[b, i]).max()))
         rows_done += rows
     info = threadpoolctl.threadpool_info()
-    threads = max([d.get("num_threads", 1) for d in info if d.get("user_api") == "blas"] or [1])
+    blas = [d for d in info if d.get("user_api") == "blas"]
+    threads = max([d.get("num_threads", 1) for d in blas] or [1])
     return {
         "value": sum(flop_per_row) / elapsed / 1e12,
         "unit": "TFLOP/s",
@@ -376,8 +377,41 @@ def cpu_baseline(s: synth.Shape, x, out_gpu, sel_gpu, budget_s: float):
         "sample": f"{len(rows_done)} random query rows (all {s.groups} groups, both branches) of "
                   f"the {synth.WORKLOAD_NAMES.get(3)} workload, {elapsed:.1f} s of fp64 numpy",
         "host_cpus": os.cpu_count(),
+        "host": host_info(),
+        "blas": [{k: d.get(k) for k in ("internal_api", "version", "num_threads")} for d in blas],
         "gpu_rows_match": {"selection_equal": sel_ok, "max_abs_err": max_err},
     }
+
+
+def work_rates(flop_main, flop_index, step_tflops, kern):
+    """Each timed part's TFLOP/s and its fraction of the bf16 MFMA peak: the
+    index kernel (msa_index_select's work), the main branch alone (what
+    msa_sparse_attn_fwd runs: gather + attention + combine) and the whole step."""
+    out = {"flop_main": flop_main, "flop_index": flop_index,
+           "step_frac_of_mfma_peak": round(step_tflops / PEAK_BF16_TFLOPS, 4)}
+    if kern:
+        idx = flop_index / (kern["index_score"] * 1e-3) / 1e12
+        sa = flop_main / (sum(kern.get(k, 0.0) for k in ("gather", "attention", "combine")) * 1e-3) / 1e12
+        out.update({"index_tflops": round(idx, 2), "index_frac_of_mfma_peak": round(idx / PEAK_BF16_TFLOPS, 4),
+                    "sparse_attn_tflops": round(sa, 2),
+                    "sparse_attn_frac_of_mfma_peak": round(sa / PEAK_BF16_TFLOPS, 4)})
+    else:
+        out.update({"index_tflops": None, "sparse_attn_tflops": None})
+    return out
+
+
+def host_info():
+    """CPU model and memory of the machine the oracle ran on."""
+    model, mem_gb = None, None
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), None)
+        with open("/proc/meminfo") as f:
+            kb = next((int(ln.split()[1]) for ln in f if ln.startswith("MemTotal")), None)
+        mem_gb = round(kb / 2 ** 20, 1) if kb else None
+    except OSError:
+        pass
+    return {"cpu_model": model, "mem_gib": mem_gb}
 
 
 def main():
@@ -448,12 +482,7 @@ def main():
                      "traffic": recorded_traffic("attn_kvouter_prefill_32k_b2_hbm.md", "attn.hip")
                      if wid == 3 else None,
                      "traffic_unit": "bytes", "flop_per_launch": flop_main, "avg_launch_ms": round(attn_avg, 4)},
-        "work": {"flop_main": flop_main, "flop_index": flop_index,
-                 "index_tflops": round(flop_index / (kern["index_score"] * 1e-3) / 1e12, 2) if kern else None,
-                 # the main branch alone (what msa_sparse_attn_fwd runs): gather + attention + combine
-                 "sparse_attn_tflops": round(flop_main / (sum(kern.get(k, 0.0) for k in ("gather", "attention",
-                                                                                            "combine")) * 1e-3) / 1e12, 2)
-                 if kern else None},
+        "work": work_rates(flop_main, flop_index, value, kern),
         "kernels_ms": {k: round(v, 4) for k, v in kern.items()},
     }
     print(f"[bench] {ms:.3f} ms/step, attention {attn_avg:.3f} ms", file=sys.stderr, flush=True)
