@@ -419,7 +419,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--decode-steps", type=int, default=50)
+    ap.add_argument("--decode-steps", type=int, default=100)
     ap.add_argument("--workload", type=int, default=3)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the KL teacher, the backward and the 8K and 1M-context prefill workloads")
