@@ -13,10 +13,12 @@ events recorded around that kernel on the stream it runs on.  The decode
 workload (64 sequences x 128K cache) is reported beside it in GB/s of
 algorithmic HBM bytes, with bf16 caches (``decode``), with FP8 E4M3 caches
 (``decode_fp8``) and over 64 caches of unequal length (4K-128K tokens) in a
-shuffled page pool (``decode_paged``).  ``cpu_baseline`` times the fp64 CPU oracle on a bounded
-sample of query rows of the same workload.
+shuffled page pool (``decode_paged``).  ``kl_teacher`` and ``backward`` time the KL-alignment
+teacher forward and the main branch's backward on the prefill workload, and ``extra`` the 8K and
+1M-context prefill workloads (all skipped with --no-extra).  ``cpu_baseline`` times the fp64 CPU
+oracle on a bounded sample of query rows of the same workload.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--decode-steps 50]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--decode-steps 100]
 """
 from __future__ import annotations
 
