@@ -194,6 +194,35 @@ class Runner:
                 ev.destroy(b)
         return total / steps, per_kernel
 
+    def graph_time(self, steps, warmup=3):
+        """ms per step when one msa_fwd call is captured in a HIP graph (on a
+        stream of its own, default priority) and the graph is replayed."""
+        gs = torch.cuda.Stream()
+        args = list(self.args)
+        args[-1] = ctypes.c_void_p(gs.cuda_stream)
+        fn = self.L.msa_fwd_kvcache
+        gs.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(gs):
+            for _ in range(warmup):
+                if fn(*args) != 0:
+                    raise RuntimeError(self.L.msa_last_error().decode())
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=gs):
+            if fn(*args) != 0:
+                raise RuntimeError(self.L.msa_last_error().decode())
+        torch.cuda.synchronize()
+        for _ in range(warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(steps):
+            g.replay()
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / steps
+
     def kl_teacher(self, steps=10, warmup=2):
         """Time msa_kl_teacher_fwd on this workload's selection and lse: (ms per call,
         per-kernel ms).  One forward with lse first provides them."""
@@ -330,6 +359,10 @@ def decode_leg(msa, wid: int, args):
     }
     if paged:
         res["cache_tokens"] = {"total": kidx_tokens, "min": int(drun.lens.min()), "max": int(drun.lens.max())}
+    # the same call replayed from a HIP graph (launch gaps between its kernels removed)
+    gms = drun.graph_time(args.decode_steps, args.warmup)
+    res["graph"] = {"ms_per_step": round(gms, 4), "value": round(dec_bytes / (gms * 1e-3) / 1e9, 1),
+                    "frac_of_hbm_peak": round(dec_bytes / (gms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
     del drun
     torch.cuda.empty_cache()
     return res
