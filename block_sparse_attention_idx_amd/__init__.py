@@ -14,6 +14,11 @@ Functions (same names as the C entry points):
   lse fp32 [B, Hq, S_q])
 * ``fwd(q, k, v, q_idx, k_idx, topk, q_offset=0, scale=None, out_dtype=None,
   return_sel=False, return_lse=False, k_scale=None, v_scale=None)``
+* ``kl_teacher_fwd(q, k, q_idx, k_idx, sel, lse, q_offset=0, index_scale=1.0,
+  return_idx_lse=False)`` -> KL fp32 [B, G, S_q] of the index distribution
+  from the group-averaged main distribution (and the index log-sum-exp)
+* ``sparse_attn_bwd(q, k, v, sel, out, lse, dout, q_offset=0)`` -> (dq, dk, dv)
+  fp32, the main branch's gradients with the selection held constant (bf16)
 
 Layouts: q [B,S_q,Hq,d], k/v [B,Hkv,S_k,d], q_idx [B,S_q,G,D_idx],
 k_idx [B,S_k,D_idx] with G = Hkv; all contiguous, on the GPU, fp32 or bf16.
