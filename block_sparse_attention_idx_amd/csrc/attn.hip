@@ -567,14 +567,16 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnParams p) {
 // clamped address, so all of a thread's loads are in flight together; unused
 // slots are removed by selects.  When a workgroup covers whole (token, group)
 // rows, the result goes through LDS so the output is written in full lines.
+constexpr int kCombineThreads = 512;  // two (token, group) rows per workgroup at r = 16, d = 128: half the launches
+
 template <typename T, typename TO, int D, int R, int KMAX>
-__global__ __launch_bounds__(256) void combine_kernel(AttnParams p) {
+__global__ __launch_bounds__(kCombineThreads) void combine_kernel(AttnParams p) {
   constexpr int E = 16 / (int)sizeof(T);
   constexpr int NCHT = D * R / E;  // chunks per (token, slot) partial
-  constexpr bool STAGED = NCHT <= 256 && 256 % NCHT == 0;
-  constexpr int RPW = STAGED ? 256 / NCHT : 1;  // (token, group) rows per workgroup
+  constexpr bool STAGED = NCHT <= kCombineThreads && kCombineThreads % NCHT == 0;
+  constexpr int RPW = STAGED ? kCombineThreads / NCHT : 1;  // (token, group) rows per workgroup
   __shared__ __align__(16) TO ostage[STAGED ? RPW * R * D : 1];
-  const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t u = (int64_t)blockIdx.x * kCombineThreads + threadIdx.x;
   const int64_t rows_total = (int64_t)p.B * p.S_q * p.G;
   const int64_t total = rows_total * NCHT;
   const bool live = u < total;
@@ -599,7 +601,7 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnParams p) {
     __shared__ int sel_s[RPW][KMAX];
     __shared__ float lse_s[RPW][KMAX][R];
     const int64_t row0 = (int64_t)blockIdx.x * RPW;
-    for (int e = threadIdx.x; e < RPW * KMAX; e += 256) {
+    for (int e = threadIdx.x; e < RPW * KMAX; e += kCombineThreads) {
       const int lr = e / KMAX, s2 = e - lr * KMAX;
       const int64_t rg = min(row0 + lr, rows_total - 1);
       const int64_t rbi = rg / p.G;
@@ -613,7 +615,7 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnParams p) {
       }
       sel_s[lr][s2] = c;
     }
-    for (int e = threadIdx.x; e < RPW * KMAX * R; e += 256) {
+    for (int e = threadIdx.x; e < RPW * KMAX * R; e += kCombineThreads) {
       const int lr = e / (KMAX * R), rem = e - lr * (KMAX * R);
       const int s2 = rem / R, hd = rem - s2 * R;
       const int64_t rg = min(row0 + lr, rows_total - 1);
@@ -682,8 +684,8 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnParams p) {
     const Chunk16* src = (const Chunk16*)ostage;
     Chunk16* dst = (Chunk16*)((TO*)p.out + row0 * R * D);
 #pragma unroll
-    for (int k = 0; k < (CHUNKS + 255) / 256; ++k) {
-      const int c = (int)threadIdx.x + k * 256;
+    for (int k = 0; k < (CHUNKS + kCombineThreads - 1) / kCombineThreads; ++k) {
+      const int c = (int)threadIdx.x + k * kCombineThreads;
       if (c < live_chunks) dst[c] = src[c];
     }
   } else if (live) {
@@ -733,13 +735,13 @@ static hipError_t launch_attn_t(const AttnParams& p, hipStream_t s, const Kernel
   timer_start(tm, kKernCombine, s);
   constexpr int E = 16 / (int)sizeof(T);
   const int64_t units = (int64_t)p.B * p.S_q * p.G * (D * R / E);
-  const dim3 cgrid((unsigned)((units + 255) / 256));
+  const dim3 cgrid((unsigned)((units + kCombineThreads - 1) / kCombineThreads));
   if (p.topk <= 16) {
-    if (p.out_f32) hipLaunchKernelGGL((combine_kernel<T, float, D, R, 16>), cgrid, dim3(256), 0, s, p);
-    else hipLaunchKernelGGL((combine_kernel<T, T, D, R, 16>), cgrid, dim3(256), 0, s, p);
+    if (p.out_f32) hipLaunchKernelGGL((combine_kernel<T, float, D, R, 16>), cgrid, dim3(kCombineThreads), 0, s, p);
+    else hipLaunchKernelGGL((combine_kernel<T, T, D, R, 16>), cgrid, dim3(kCombineThreads), 0, s, p);
   } else {
-    if (p.out_f32) hipLaunchKernelGGL((combine_kernel<T, float, D, R, 32>), cgrid, dim3(256), 0, s, p);
-    else hipLaunchKernelGGL((combine_kernel<T, T, D, R, 32>), cgrid, dim3(256), 0, s, p);
+    if (p.out_f32) hipLaunchKernelGGL((combine_kernel<T, float, D, R, 32>), cgrid, dim3(kCombineThreads), 0, s, p);
+    else hipLaunchKernelGGL((combine_kernel<T, T, D, R, 32>), cgrid, dim3(kCombineThreads), 0, s, p);
   }
   timer_stop(tm, kKernCombine, s);
   return hipGetLastError();
