@@ -383,12 +383,14 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_kernel(AttnParams p, BwdParam
 }
 
 // dq[b, i, h, :] = scale * (sum over the row's visible selected blocks of the
-// partials [head][d]); a thread per 16-byte chunk.
-template <int D, int R>
-__global__ __launch_bounds__(256) void bwd_dq_combine_kernel(AttnParams p, BwdParams bp) {
+// partials [head][d]); a thread per 16-byte chunk.  The KMAX slots' chunks are
+// loaded from clamped addresses before any is used, and the slots that are not
+// visible selected blocks are dropped by selects.
+template <int D, int R, int KMAX>
+__global__ __launch_bounds__(512) void bwd_dq_combine_kernel(AttnParams p, BwdParams bp) {
   constexpr int E = 8;
   constexpr int CPR = D / E;  // chunks per head row
-  const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t u = (int64_t)blockIdx.x * 512 + threadIdx.x;
   if (u >= (int64_t)p.B * p.S_q * p.G * R * CPR) return;
   const int ch = (int)(u % CPR);
   const int64_t rest = u / CPR;
@@ -400,17 +402,25 @@ __global__ __launch_bounds__(256) void bwd_dq_combine_kernel(AttnParams p, BwdPa
   const int b = (int)(bi / p.S_q);
   const int64_t t = p.q_offset + i;
   const int32_t* srow = p.sel + (((int64_t)b * p.G + g) * p.S_q + i) * p.topk;
+  i32x4 x[KMAX];
+  int cs[KMAX];
+#pragma unroll
+  for (int s2 = 0; s2 < KMAX; ++s2) {
+    const int sc = min(s2, p.topk - 1);
+    cs[s2] = srow[sc];
+    x[s2] = __builtin_nontemporal_load(
+        (const i32x4*)((const bf16*)p.part_o + ((rowg * p.topk + sc) * R + hh) * D + ch * E));
+  }
   float acc[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) acc[e] = 0.f;
-  for (int s2 = 0; s2 < p.topk; ++s2) {
-    const int c = srow[s2];
-    if (c < 0 || c >= p.nb || (int64_t)c * kBlock > t) continue;
-    const bf16x8 x = __builtin_bit_cast(
-        bf16x8, __builtin_nontemporal_load(
-                    (const i32x4*)((const bf16*)p.part_o + ((rowg * p.topk + s2) * R + hh) * D + ch * E)));
 #pragma unroll
-    for (int e = 0; e < E; ++e) acc[e] += (float)x[e];
+  for (int s2 = 0; s2 < KMAX; ++s2) {
+    const int c = cs[s2];
+    const bool used = s2 < p.topk && c >= 0 && c < p.nb && (int64_t)c * kBlock <= t;
+    const bf16x8 xv = __builtin_bit_cast(bf16x8, x[s2]);
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] += used ? (float)xv[e] : 0.f;
   }
   f32x4* orow = (f32x4*)(bp.dq + (bi * p.Hq + g * R + hh) * D + ch * E);
   orow[0] = f32x4{acc[0], acc[1], acc[2], acc[3]} * bp.scale;
@@ -433,7 +443,9 @@ static hipError_t launch_bwd_t(const AttnParams& p, const BwdParams& bp, hipStre
   timer_stop(tm, kKernBwd, s);
   timer_start(tm, kKernBwdCombine, s);
   const int64_t units = (int64_t)p.B * p.S_q * p.G * (D * R / 8);
-  hipLaunchKernelGGL((bwd_dq_combine_kernel<D, R>), dim3((unsigned)((units + 255) / 256)), dim3(256), 0, s, p, bp);
+  const dim3 cgrid((unsigned)((units + 511) / 512));
+  if (p.topk <= 16) hipLaunchKernelGGL((bwd_dq_combine_kernel<D, R, 16>), cgrid, dim3(512), 0, s, p, bp);
+  else hipLaunchKernelGGL((bwd_dq_combine_kernel<D, R, 32>), cgrid, dim3(512), 0, s, p, bp);
   timer_stop(tm, kKernBwdCombine, s);
   return hipGetLastError();
 }
