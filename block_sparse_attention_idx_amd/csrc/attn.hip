@@ -592,8 +592,19 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(AttnParams p) 
   const int32_t* srow = p.sel + (((int64_t)b * p.G + g) * p.S_q + i) * p.topk;
   const int64_t pbase = rowg * p.topk;
 
+  // The slots' partial chunks are held in registers KC at a time: all of them
+  // for k <= 32, two rounds of 32 for larger k (the weights come first, from
+  // every slot's log-sum-exp).
+  constexpr int KC = KMAX < 32 ? KMAX : 32;
   float ls[KMAX];
-  i32x4 x[KMAX];
+  i32x4 x[KC];
+  auto load_chunks = [&](int s0) {
+#pragma unroll
+    for (int s2 = 0; s2 < KC; ++s2) {
+      const int sc = min(s0 + s2, p.topk - 1);
+      x[s2] = __builtin_nontemporal_load((const i32x4*)((const T*)p.part_o + (pbase + sc) * (R * D) + ch * E));
+    }
+  };
   float mx = kNegInf;
   if constexpr (STAGED) {
     // A workgroup's rows share their selection rows and log-sum-exps: load those
@@ -623,11 +634,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(AttnParams p) 
     }
     __syncthreads();
     const int lr = (int)(threadIdx.x / NCHT);
-#pragma unroll
-    for (int s2 = 0; s2 < KMAX; ++s2) {
-      const int sc = min(s2, p.topk - 1);
-      x[s2] = __builtin_nontemporal_load((const i32x4*)((const T*)p.part_o + (pbase + sc) * (R * D) + ch * E));
-    }
+    load_chunks(0);
 #pragma unroll
     for (int s2 = 0; s2 < KMAX; ++s2) {
       ls[s2] = sel_s[lr][s2] >= 0 ? lse_s[lr][s2][hh] : kNegInf;
@@ -640,8 +647,8 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(AttnParams p) 
       const int sc = min(s2, p.topk - 1);
       cs[s2] = srow[sc];
       ls[s2] = p.part_lse[(pbase + sc) * R + hh];
-      x[s2] = __builtin_nontemporal_load((const i32x4*)((const T*)p.part_o + (pbase + sc) * (R * D) + ch * E));
     }
+    load_chunks(0);
 #pragma unroll
     for (int s2 = 0; s2 < KMAX; ++s2) {
       const int c = cs[s2];
@@ -655,13 +662,18 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(AttnParams p) 
 #pragma unroll
   for (int e = 0; e < E; ++e) acc[e] = 0.f;
 #pragma unroll
-  for (int s = 0; s < KMAX; ++s) {
-    const bool used = ls[s] != kNegInf;
-    const float w = used ? exp2f(ls[s] - mx) : 0.f;
-    W += w;
-    const typename Vec16<T>::type xv = __builtin_bit_cast(typename Vec16<T>::type, x[s]);
+  for (int s0 = 0; s0 < KMAX; s0 += KC) {
+    if (s0 > 0) load_chunks(s0);
 #pragma unroll
-    for (int e = 0; e < E; ++e) acc[e] += used ? w * to_f32(xv[e]) : 0.f;
+    for (int s2 = 0; s2 < KC; ++s2) {
+      const int s = s0 + s2;
+      const bool used = ls[s] != kNegInf;
+      const float w = used ? exp2f(ls[s] - mx) : 0.f;
+      W += w;
+      const typename Vec16<T>::type xv = __builtin_bit_cast(typename Vec16<T>::type, x[s2]);
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[e] += used ? w * to_f32(xv[e]) : 0.f;
+    }
   }
   // the value cache's dequantisation scale (1 if none); a row that sees no key
   // (it precedes its cache) gets zeros and lse = -inf
@@ -739,9 +751,12 @@ static hipError_t launch_attn_t(const AttnParams& p, hipStream_t s, const Kernel
   if (p.topk <= 16) {
     if (p.out_f32) hipLaunchKernelGGL((combine_kernel<T, float, D, R, 16>), cgrid, dim3(kCombineThreads), 0, s, p);
     else hipLaunchKernelGGL((combine_kernel<T, T, D, R, 16>), cgrid, dim3(kCombineThreads), 0, s, p);
-  } else {
+  } else if (p.topk <= 32) {
     if (p.out_f32) hipLaunchKernelGGL((combine_kernel<T, float, D, R, 32>), cgrid, dim3(kCombineThreads), 0, s, p);
     else hipLaunchKernelGGL((combine_kernel<T, T, D, R, 32>), cgrid, dim3(kCombineThreads), 0, s, p);
+  } else {
+    if (p.out_f32) hipLaunchKernelGGL((combine_kernel<T, float, D, R, 64>), cgrid, dim3(kCombineThreads), 0, s, p);
+    else hipLaunchKernelGGL((combine_kernel<T, T, D, R, 64>), cgrid, dim3(kCombineThreads), 0, s, p);
   }
   timer_stop(tm, kKernCombine, s);
   return hipGetLastError();

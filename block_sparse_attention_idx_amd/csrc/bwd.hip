@@ -383,9 +383,10 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_kernel(AttnParams p, BwdParam
 }
 
 // dq[b, i, h, :] = scale * (sum over the row's visible selected blocks of the
-// partials [head][d]); a thread per 16-byte chunk.  The KMAX slots' chunks are
-// loaded from clamped addresses before any is used, and the slots that are not
-// visible selected blocks are dropped by selects.
+// partials [head][d]); a thread per 16-byte chunk.  The slots' chunks are
+// loaded from clamped addresses, up to 32 of them before any is used, and the
+// slots that are not visible selected blocks are dropped by selects; the sum
+// runs in slot order.
 template <int D, int R, int KMAX>
 __global__ __launch_bounds__(512) void bwd_dq_combine_kernel(AttnParams p, BwdParams bp) {
   constexpr int E = 8;
@@ -402,25 +403,29 @@ __global__ __launch_bounds__(512) void bwd_dq_combine_kernel(AttnParams p, BwdPa
   const int b = (int)(bi / p.S_q);
   const int64_t t = p.q_offset + i;
   const int32_t* srow = p.sel + (((int64_t)b * p.G + g) * p.S_q + i) * p.topk;
-  i32x4 x[KMAX];
-  int cs[KMAX];
-#pragma unroll
-  for (int s2 = 0; s2 < KMAX; ++s2) {
-    const int sc = min(s2, p.topk - 1);
-    cs[s2] = srow[sc];
-    x[s2] = __builtin_nontemporal_load(
-        (const i32x4*)((const bf16*)p.part_o + ((rowg * p.topk + sc) * R + hh) * D + ch * E));
-  }
+  constexpr int KC = KMAX < 32 ? KMAX : 32;  // slots held in registers at once
   float acc[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) acc[e] = 0.f;
 #pragma unroll
-  for (int s2 = 0; s2 < KMAX; ++s2) {
-    const int c = cs[s2];
-    const bool used = s2 < p.topk && c >= 0 && c < p.nb && (int64_t)c * kBlock <= t;
-    const bf16x8 xv = __builtin_bit_cast(bf16x8, x[s2]);
+  for (int s0 = 0; s0 < KMAX; s0 += KC) {
+    i32x4 x[KC];
+    int cs[KC];
 #pragma unroll
-    for (int e = 0; e < E; ++e) acc[e] += used ? (float)xv[e] : 0.f;
+    for (int s2 = 0; s2 < KC; ++s2) {
+      const int sc = min(s0 + s2, p.topk - 1);
+      cs[s2] = srow[sc];
+      x[s2] = __builtin_nontemporal_load(
+          (const i32x4*)((const bf16*)p.part_o + ((rowg * p.topk + sc) * R + hh) * D + ch * E));
+    }
+#pragma unroll
+    for (int s2 = 0; s2 < KC; ++s2) {
+      const int c = cs[s2];
+      const bool used = s0 + s2 < p.topk && c >= 0 && c < p.nb && (int64_t)c * kBlock <= t;
+      const bf16x8 xv = __builtin_bit_cast(bf16x8, x[s2]);
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[e] += used ? (float)xv[e] : 0.f;
+    }
   }
   f32x4* orow = (f32x4*)(bp.dq + (bi * p.Hq + g * R + hh) * D + ch * E);
   orow[0] = f32x4{acc[0], acc[1], acc[2], acc[3]} * bp.scale;
@@ -445,7 +450,8 @@ static hipError_t launch_bwd_t(const AttnParams& p, const BwdParams& bp, hipStre
   const int64_t units = (int64_t)p.B * p.S_q * p.G * (D * R / 8);
   const dim3 cgrid((unsigned)((units + 511) / 512));
   if (p.topk <= 16) hipLaunchKernelGGL((bwd_dq_combine_kernel<D, R, 16>), cgrid, dim3(512), 0, s, p, bp);
-  else hipLaunchKernelGGL((bwd_dq_combine_kernel<D, R, 32>), cgrid, dim3(512), 0, s, p, bp);
+  else if (p.topk <= 32) hipLaunchKernelGGL((bwd_dq_combine_kernel<D, R, 32>), cgrid, dim3(512), 0, s, p, bp);
+  else hipLaunchKernelGGL((bwd_dq_combine_kernel<D, R, 64>), cgrid, dim3(512), 0, s, p, bp);
   timer_stop(tm, kKernBwdCombine, s);
   return hipGetLastError();
 }

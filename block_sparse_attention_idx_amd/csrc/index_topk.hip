@@ -95,6 +95,20 @@ __device__ __forceinline__ void emit_row(const IndexParams& p, int b, int n, int
   for (int j = take + 1; j < p.topk; ++j) out[j] = -1;
 }
 
+// The wide form (lists of 63): a lane half's own list for row rowg, written as
+// partial list `list` of the row for topk_merge_kernel.
+template <int CAP>
+__device__ __forceinline__ void emit_half_list(const IndexParams& p, int64_t rowg, int list, const float (&ls)[CAP],
+                                               const int (&li)[CAP]) {
+  float* ds = p.part_s + (rowg * p.nsplit * p.lps + list) * CAP;
+  int32_t* di = p.part_i + (rowg * p.nsplit * p.lps + list) * CAP;
+#pragma unroll
+  for (int j = 0; j < CAP; ++j) {
+    ds[j] = ls[j];
+    di[j] = li[j];
+  }
+}
+
 // The unit (row tile tg = b * ntile + tile, key split) of workgroup lin, or
 // false when it has none.  With a unit list (sequences of their own lengths)
 // the units holding work come first.  Otherwise, with key splits, hardware
@@ -152,7 +166,7 @@ __global__ __launch_bounds__(1024) void index_units_kernel(IndexParams p) {
 }
 
 template <typename T, typename S, int DI, int CAP, int RT>
-__global__ __launch_bounds__(256, 2) void index_topk_kernel(IndexParams p) {
+__global__ __launch_bounds__(256, CAP == kIndexWideCap ? 1 : 2) void index_topk_kernel(IndexParams p) {
   using M = Mma<T>;
   using frag = typename M::frag;
   constexpr int KPL = M::KPL, KSTEP = M::KSTEP, NKS = DI / KSTEP;
@@ -178,7 +192,8 @@ __global__ __launch_bounds__(256, 2) void index_topk_kernel(IndexParams p) {
   constexpr int CH_PER_THREAD = kDma ? 1 : kBlock * CH_PER_ROW / 256;
   static_assert(kDma || (CH_PER_THREAD >= 1 && (kBlock * CH_PER_ROW) % 256 == 0), "staging split");
   constexpr int KS_BYTES = 2 * TILE_BYTES;
-  constexpr int LIST_BYTES = 4 * 2 * CAP * 32 * 8;  // one row tile of lists, all waves
+  constexpr bool kWide = CAP == kIndexWideCap;      // lane halves write their own lists
+  constexpr int LIST_BYTES = kWide ? 0 : 4 * 2 * CAP * 32 * 8;  // one row tile of lists, all waves
   constexpr int SMEM = KS_BYTES > LIST_BYTES ? KS_BYTES : LIST_BYTES;
   __shared__ __align__(16) char smem[SMEM];
   T* Ks = (T*)smem;  // [2][kBlock * DI]
@@ -355,6 +370,14 @@ __global__ __launch_bounds__(256, 2) void index_topk_kernel(IndexParams p) {
     }
   }
 
+  if constexpr (kWide) {  // list split * 2 + h of each row
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const int n = n_first + wave * ROWS_WAVE + rt * 32 + l32;
+      if (rvalid[rt]) emit_half_list<CAP>(p, (int64_t)b * p.rows_per_b + n, split * 2 + h, ls[rt], li[rt]);
+    }
+    return;
+  }
   // Merge the two half lists of each row through LDS (the K tiles are free
   // now), then write one list per (row, split).
   float* xs = (float*)smem;                       // [4 waves][2 halves][CAP][32 rows]
@@ -389,7 +412,7 @@ __global__ __launch_bounds__(256, 2) void index_topk_kernel(IndexParams p) {
         ia += take_a ? 1 : 0;
         ib += take_a ? 0 : 1;
       }
-      emit_row<CAP>(p, b, n, split, rowL[rt], ms, mi);
+      if constexpr (!kWide) emit_row<CAP>(p, b, n, split, rowL[rt], ms, mi);
     }
   }
 }
@@ -407,7 +430,7 @@ __global__ __launch_bounds__(256, 2) void index_topk_kernel(IndexParams p) {
 // As in the kernel above the two lane halves of a wave rank alternate blocks of
 // its sequence; the 4 x 2 lists of a row are merged through LDS at the end.
 template <typename T, typename S, int DI, int CAP>
-__global__ __launch_bounds__(256, 2) void index_topk_small_kernel(IndexParams p) {
+__global__ __launch_bounds__(256, CAP == kIndexWideCap ? 1 : 2) void index_topk_small_kernel(IndexParams p) {
   using M = Mma<T>;
   using frag = typename M::frag;
   constexpr int KPL = M::KPL, KSTEP = M::KSTEP, NKS = DI / KSTEP;
@@ -432,7 +455,8 @@ __global__ __launch_bounds__(256, 2) void index_topk_small_kernel(IndexParams p)
   // element offset of k-step ks, lane half h in the query row (16 elements per 16 bytes of e4m3)
   auto koff = [](int ks, int hh) { return kNative ? ks * KSTEP + hh * KPL : (ks / 2) * 32 + hh * 16 + (ks % 2) * 8; };
   constexpr int NL = 8;  // lists per row: 4 waves x 2 lane halves
-  constexpr int MERGE_BYTES = NL * CAP * 32 * 8, TILE_BYTES = 4 * 32 * RB;
+  constexpr bool kWide = CAP == kIndexWideCap;  // the 8 lists go to topk_merge_kernel unmerged
+  constexpr int MERGE_BYTES = kWide ? 0 : NL * CAP * 32 * 8, TILE_BYTES = 4 * 32 * RB;
   static_assert(MERGE_BYTES <= 65536, "list merge fits the static LDS");
   // the waves' key tiles during the block loop, the list merge afterwards
   __shared__ __align__(16) char lds_raw[MERGE_BYTES > TILE_BYTES ? MERGE_BYTES : TILE_BYTES];
@@ -558,6 +582,10 @@ __global__ __launch_bounds__(256, 2) void index_topk_small_kernel(IndexParams p)
     }
   }
 
+  if constexpr (kWide) {  // list split * 8 + wave * 2 + h of the row
+    if (rvalid) emit_half_list<CAP>(p, (int64_t)b * p.rows_per_b + l32, split * NL + wave * 2 + h, ls, li);
+    return;
+  }
   // merge the 8 lists of each row through LDS: [list][CAP][32 rows]
   __syncthreads();  // every wave is done with its key tile (the same LDS)
 #pragma unroll
@@ -594,21 +622,22 @@ __global__ __launch_bounds__(256, 2) void index_topk_small_kernel(IndexParams p)
 #pragma unroll
       for (int w = 0; w < NL; ++w) pos[w] += (w == bw) ? 1 : 0;
     }
-    emit_row<CAP>(p, b, l32, split, rowL, ms, mi);
+    if constexpr (!kWide) emit_row<CAP>(p, b, l32, split, rowL, ms, mi);
   }
 }
 
-// One wave per (b, i, g) row: the row's lists (one per key split, sorted by
-// score desc then block asc) are loaded into LDS, then k-1 rounds of a
-// wave-wide argmax over the list heads pick the Top-(k-1); the local block is
-// added, ids are sorted ascending and padded with -1.
-template <int CAP>
-__global__ __launch_bounds__(256) void topk_merge_kernel(IndexParams p) {
-  // dynamic LDS: [4 waves][nsplit * CAP] scores, then the same for block ids
+// One wave per (b, i, g) row: the row's lists (lps per key split, each sorted
+// by score desc then block asc; at most kMergeMaxLists) are loaded into LDS,
+// then k-1 rounds of a wave-wide argmax over the list heads pick the
+// Top-(k-1); the local block is added, ids are sorted ascending and padded
+// with -1.  WPB waves (rows) per workgroup.
+template <int CAP, int WPB>
+__global__ __launch_bounds__(64 * WPB) void topk_merge_kernel(IndexParams p) {
+  // dynamic LDS: [WPB waves][nsplit * lps * CAP] scores, then the same for block ids
   extern __shared__ __align__(16) char msmem[];
-  const int per_wave = p.nsplit * CAP;
+  const int per_wave = p.nsplit * p.lps * CAP;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t row = (int64_t)blockIdx.x * 4 + wave;
+  const int64_t row = (int64_t)blockIdx.x * WPB + wave;
   if (row >= (int64_t)p.B * p.rows_per_b) return;
   const int b = (int)(row / p.rows_per_b);
   const int n = (int)(row - (int64_t)b * p.rows_per_b);
@@ -619,13 +648,13 @@ __global__ __launch_bounds__(256) void topk_merge_kernel(IndexParams p) {
     if (lane < p.topk) out[lane] = -1;
     return;
   }
-  const int nl = L > 0 ? (L + p.chunk - 1) / p.chunk : 0;
+  const int nl = L > 0 ? (L + p.chunk - 1) / p.chunk * p.lps : 0;  // lists of the splits before L
   const int take = min(p.topk - 1, L);
 
-  const float* gs = p.part_s + row * p.nsplit * CAP;
-  const int32_t* gi = p.part_i + row * p.nsplit * CAP;
+  const float* gs = p.part_s + row * per_wave;
+  const int32_t* gi = p.part_i + row * per_wave;
   float* ss = (float*)msmem + wave * per_wave;
-  int* si = (int*)msmem + 4 * per_wave + wave * per_wave;
+  int* si = (int*)msmem + WPB * per_wave + wave * per_wave;
   // the lists in batches of 8 loads per lane, all in flight before any is stored
   for (int e0 = 0; e0 < nl * CAP; e0 += 64 * 8) {
     float vs[8];
@@ -698,6 +727,7 @@ static hipError_t launch_index_t(const IndexParams& p, hipStream_t s, const Kern
   if (p.units) hipLaunchKernelGGL(index_units_kernel, dim3(1), dim3(1024), 0, s, p);
   constexpr int RT = CAP <= 15 ? 2 : 1;
   static_assert(4 * 32 * RT == index_rows_per_wg(CAP + 1), "host and kernel agree on the row tile");
+  static_assert(index_cap(CAP + 1) == CAP, "host and kernel agree on the list length");
   bool small_done = false;
   if constexpr (sizeof(T) == 2) {  // the few-row form is built for bf16 queries
     if (p.small) {
@@ -710,11 +740,13 @@ static hipError_t launch_index_t(const IndexParams& p, hipStream_t s, const Kern
   timer_stop(tm, kKernIndexScore, s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (p.nsplit == 1) return hipGetLastError();  // the index kernel wrote the selection
+  if (p.nsplit == 1 && CAP != kIndexWideCap) return hipGetLastError();  // the index kernel wrote the selection
   const int64_t rows = (int64_t)p.B * p.rows_per_b;
   timer_start(tm, kKernTopkMerge, s);
-  const size_t lds = (size_t)8 * p.nsplit * CAP * 4;
-  hipLaunchKernelGGL((topk_merge_kernel<CAP>), dim3((unsigned)((rows + 3) / 4)), dim3(256), lds, s, p);
+  constexpr int WPB = merge_rows_per_wg(CAP);  // the host keeps nsplit * lps <= merge_max_lists(CAP)
+  const size_t lds = (size_t)2 * WPB * p.nsplit * p.lps * CAP * 4;
+  hipLaunchKernelGGL((topk_merge_kernel<CAP, WPB>), dim3((unsigned)((rows + WPB - 1) / WPB)), dim3(64 * WPB), lds, s,
+                     p);
   timer_stop(tm, kKernTopkMerge, s);
   return hipGetLastError();
 }
@@ -722,7 +754,8 @@ static hipError_t launch_index_t(const IndexParams& p, hipStream_t s, const Kern
 template <typename T, typename S, int DI>
 static hipError_t launch_index_d(const IndexParams& p, hipStream_t s, const KernelTimer* tm) {
   if (p.topk <= 16) return launch_index_t<T, S, DI, 15>(p, s, tm);
-  return launch_index_t<T, S, DI, 31>(p, s, tm);
+  if (p.topk <= 32) return launch_index_t<T, S, DI, 31>(p, s, tm);
+  return launch_index_t<T, S, DI, kIndexWideCap>(p, s, tm);
 }
 
 template <typename T, typename S>

@@ -72,7 +72,7 @@ __device__ __forceinline__ bool block_mapped(const CacheMap& m, int b, int c) {
 struct IndexParams {
   const void* q_idx;   // [B, S_q, G, D]
   const void* k_idx;   // [B, S_k, D]
-  float* part_s;       // [B*S_q*G, nsplit, CAP] partial top-list scores
+  float* part_s;       // [B*S_q*G, nsplit * lps, CAP] partial top-list scores
   int32_t* part_i;     // same shape: block ids (-1 = empty)
   int32_t* sel;        // [B, G, S_q, topk]
   CacheMap cm;
@@ -82,6 +82,7 @@ struct IndexParams {
   int ntile;           // row tiles per sequence
   int ntile_total;     // B * ntile
   int nsplit, chunk;   // key-block splits and blocks per split
+  int lps;             // partial lists per (row, split): 1, or 2 / 8 in the wide form (one per lane half)
   int nunits;          // ntile_total * nsplit
   int grid_per_xcd;    // ceil(nunits / 8)
   int small;           // 1: bf16 queries and rows_per_b <= kIndexSmallRows, one unit per (sequence, split)
@@ -96,8 +97,24 @@ struct IndexParams {
 // few-row form (each wave ranks whole blocks on its own).
 constexpr int kIndexSmallRows = 32;
 
+// Top lists hold up to k - 1 entries: 15 (k <= 16), 31 (k <= 32) or 63
+// (k <= 64).  Lists of 63 (the wide form) are not merged inside the index
+// kernels: every lane half writes its own list (2 per split in the prefill form,
+// 8 in the few-row form) and topk_merge_kernel merges them, at most
+// kMergeMaxLists per row.
+constexpr int kIndexWideCap = 63;
+constexpr int kMergeMaxLists = 128;
+constexpr int index_cap(int topk) { return topk <= 16 ? 15 : topk <= 32 ? 31 : kIndexWideCap; }
+// Rows per topk_merge_kernel workgroup, and the most lists per row whose
+// scores and ids fit 64 KiB of LDS for all of them.
+constexpr int merge_rows_per_wg(int cap) { return cap == kIndexWideCap ? 1 : 4; }
+constexpr int merge_max_lists(int cap) {
+  return 65536 / (2 * merge_rows_per_wg(cap) * cap * 4) < kMergeMaxLists ? 65536 / (2 * merge_rows_per_wg(cap) * cap * 4)
+                                                                           : kMergeMaxLists;
+}
+
 // Index rows per workgroup: 4 waves x 32 rows x RT row tiles, RT = 2 for lists
-// of up to 15 entries (k <= 16), 1 for the longer lists of k <= 32.
+// of up to 15 entries (k <= 16), 1 for the longer lists.
 constexpr int index_row_tiles(int topk) { return topk <= 16 ? 2 : 1; }
 constexpr int index_rows_per_wg(int topk) { return 4 * 32 * index_row_tiles(topk); }
 

@@ -82,7 +82,7 @@ msa_status check_shape(const msa_shape* s, int op) {
     return fail(MSA_ERR_UNSUPPORTED, "block_size %d: only 128 is built", s->block_size);
   if (fp8_cache(s) && s->dtype != MSA_BF16)
     return fail(MSA_ERR_UNSUPPORTED, "FP8 caches are built for bf16 queries only");
-  if (s->topk > 32) return fail(MSA_ERR_UNSUPPORTED, "topk %d: at most 32 is built", s->topk);
+  if (s->topk > 64) return fail(MSA_ERR_UNSUPPORTED, "topk %d: at most 64 is built", s->topk);
   if (s->q_len >= (1 << 25)) return fail(MSA_ERR_UNSUPPORTED, "q_len must be < 2^25");
   if ((int64_t)s->batch * s->num_kv_heads * ceil_div(s->kv_len, msa::kBlock) >= (1LL << 31))
     return fail(MSA_ERR_UNSUPPORTED, "batch * kv heads * blocks exceeds 2^31");
@@ -183,26 +183,29 @@ IndexPlan plan_index(const msa_shape* s, const msa_kv_cache* cache) {
   // Enough row tiles to fill the GPU: one unit per tile, no merge.  Otherwise
   // split the key blocks so that about kIndexTargetUnits units exist (at least
   // 16 blocks per unit, 8 in the few-row form where 4 waves share a unit's
-  // blocks, and at most 128 splits for the merge).
+  // blocks, and no more lists per row than the merge takes).
   // With per-sequence lengths the work per sequence is unknown here: a fixed,
   // small chunk keeps short caches from leaving most units idle, and a unit
   // list built on the device packs the units that hold work first.
+  ip.cap = msa::index_cap(s->topk);
+  const bool wide = ip.cap == msa::kIndexWideCap;  // every lane half's list goes to the merge
+  p.lps = wide ? (p.small ? 8 : 2) : 1;
+  const int64_t max_split = msa::merge_max_lists(ip.cap) / p.lps;
   int64_t chunk = std::max<int64_t>(1, Lmax), nsplit = 1;
   if (Lmax > 0 && p.ntile_total < kIndexMinTiles) {
     const int64_t min_chunk = p.small ? 8 : 16;
     const int64_t want = std::max<int64_t>(1, ceil_div(kIndexTargetUnits, std::max(1, p.ntile_total)));
     const bool varlen = cache && cache->seq_lens;
-    chunk = std::max<int64_t>({min_chunk, varlen ? kIndexVarlenChunk : ceil_div(Lmax, want), ceil_div(Lmax, 128)});
+    chunk = std::max<int64_t>({min_chunk, varlen ? kIndexVarlenChunk : ceil_div(Lmax, want), ceil_div(Lmax, max_split)});
     nsplit = ceil_div(Lmax, chunk);
   }
   p.chunk = (int)chunk;
   p.nsplit = (int)nsplit;
   p.nunits = p.ntile_total * p.nsplit;
   p.grid_per_xcd = (int)ceil_div(p.nunits, 8);
-  ip.cap = s->topk <= 16 ? 15 : 31;
-  const size_t entries = (size_t)p.B * p.rows_per_b * p.nsplit * ip.cap;
+  const size_t entries = (size_t)p.B * p.rows_per_b * p.nsplit * p.lps * ip.cap;
   size_t off = 0;
-  ip.lists = p.nsplit > 1;
+  ip.lists = p.nsplit > 1 || wide;
   if (ip.lists) {
     ip.off_s = off;
     off += align_up(entries * 4);

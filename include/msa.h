@@ -57,7 +57,7 @@
  * dequantisation scales).  Index keys are used as stored: a positive common
  * scale would not change any ranking, so none is taken.
  *
- * Supported on the GPU: block_size == 128; 1 <= topk <= 32; head_dim in
+ * Supported on the GPU: block_size == 128; 1 <= topk <= 64; head_dim in
  * {64, 128}; index_dim in {32, 64, 128}; r = Hq / Hkv in {1, 2, 4, 8, 16,
  * 32}; dtype MSA_F32 or MSA_BF16 (the same for q, k, v, q_idx, k_idx unless
  * the caches are FP8); out_dtype MSA_F32 or the input dtype.  Other values

@@ -68,7 +68,7 @@ def _fwd(sh, ws=None, ws_bytes=0, **ptrs):
     ("num_q_heads", 62, -1), ("num_kv_heads", 0, -1), ("topk", 0, -1), ("block_size", 0, -1),
     ("dtype", 7, -1), ("out_dtype", 9, -1), ("cache_format", 2, -1), ("cache_format", -1, -1), ("pad", 3, -1),
     ("head_dim", 0, -1),
-    ("block_size", 64, -2), ("topk", 33, -2), ("head_dim", 96, -2), ("index_dim", 48, -2),
+    ("block_size", 64, -2), ("topk", 65, -2), ("head_dim", 96, -2), ("index_dim", 48, -2),
     ("num_q_heads", 12, -2),
 ])
 def test_invalid_and_unsupported_shapes(field, value, status):

@@ -37,6 +37,7 @@ BWD_SHAPES = [
     (1, 400, 400, 0, 32, 1, 64, 32, 3),          # r = 32
     (2, 3, 2000, 1997, 64, 4, 128, 128, 16),     # few queries per block
     (1, 1000, 1000, 0, 64, 4, 128, 128, 16),     # the pages' shape, every block of every query
+    (1, 300, 9000, 8700, 16, 2, 128, 128, 64),   # k = 64: the dQ combine in two rounds of 32 slots
 ]
 
 

@@ -48,6 +48,7 @@ KL_SHAPES = [
     (1, 640, 640, 0, 32, 1, 64, 32, 32, "f32", "native", 1.0),          # r = 32, k = 32
     (2, 300, 900, 600, 8, 8, 64, 32, 4, "f32", "native", 0.5),          # r = 1
     (2, 400, 2400, 1700, 16, 4, 128, 128, 12, "bf16", "fp8", 1.0),      # FP8 caches
+    (1, 300, 9000, 8700, 16, 2, 128, 128, 64, "bf16", "native", 1.0),   # k = 64
 ]
 
 

@@ -52,6 +52,7 @@ DENSE_CASES = [
     ([1, 700, 2999, 3000, 1500], 1, 64, 4, 128, 128, 16, "native"),     # decode
     ([2, 130, 2048, 3000], 4, 32, 4, 128, 64, 8, "native"),             # speculative rows; one precedes its cache
     ([1, 700, 2999, 3000, 1500], 1, 64, 4, 128, 128, 32, "fp8"),
+    ([1, 9000, 12000, 8190], 1, 64, 4, 128, 128, 64, "native"),        # k = 64 (the wide top lists)
 ]
 
 
@@ -85,6 +86,8 @@ PAGED_CASES = [
     ([5000, 333, 4097], 1, 32, 4, 128, 128, 32, "native", 11),
     ([1000, 2600], 300, 32, 2, 128, 128, 8, "native", 5),    # a chunk of 300 rows: the gathered path
     ([2600, 1800, 700], 200, 16, 4, 128, 64, 12, "fp8", 2),
+    ([9000, 130, 12000], 1, 32, 4, 128, 128, 48, "fp8", 5),   # k = 48 over pages
+    ([9500, 6000], 160, 16, 2, 128, 128, 64, "native", 3),    # k = 64, a chunk of rows
 ]
 
 

@@ -58,6 +58,11 @@ SMALL_SHAPES = [
     (1, 640, 640, 0, 32, 1, 64, 32, 32, "f32"),        # k above the visible blocks
     (1, 700, 6000, 5300, 16, 2, 128, 128, 24, "bf16"), # k > 16: the longer top lists
     (2, 300, 9000, 8700, 32, 2, 128, 128, 32, "bf16"), # k = 32, several key splits
+    # k > 32: every lane half's top list of 63 goes to the merge kernel
+    (1, 500, 12000, 11500, 16, 2, 128, 128, 64, "bf16"),  # prefill form, six key splits
+    (2, 300, 9000, 8700, 16, 2, 64, 64, 48, "f32"),       # fp32 inputs, k = 48
+    (3, 1, 20000, 19999, 64, 4, 128, 128, 64, "bf16"),    # decode (few-row form), 16 key splits
+    (1, 900, 900, 0, 8, 2, 64, 32, 64, "bf16"),           # k above the visible blocks
 ]
 
 
@@ -170,6 +175,32 @@ def test_workload_8k_bf16():
 
 
 @gpu
+def test_workload_8k_k64_is_dense_causal():
+    # With k = 64 every row of the 8K workload (64 blocks) selects all of its
+    # visible blocks, so MSA is plain causal attention: the selection is known in
+    # closed form and the output must match the dense causal reference.
+    msa = _msa()
+    s = synth.WORKLOADS[2].replace(topk=64)
+    x, xh = _inputs(s, 2)
+    print("8K workload, k = 64", flush=True)
+    out, sel, lse = msa.fwd(x["q"], x["k"], x["v"], x["q_idx"], x["k_idx"], s.topk, return_sel=True,
+                            return_lse=True)
+    torch.cuda.synchronize()
+    L = np.arange(s.q_len) // 128
+    slot = np.arange(s.topk)
+    want = np.where(slot[None, :] <= L[:, None], slot[None, :], -1)
+    sg = sel.cpu().numpy()
+    assert (sg == want[None, None]).all()
+    f = {n: synth.as_f64(xh[n]) for n in ("q", "k", "v")}
+    rng = np.random.default_rng(4)
+    lg = lse.cpu().numpy()
+    for i in [int(v) for v in np.concatenate([rng.integers(0, s.q_len, 24), [0, 127, 128, 8191]])]:
+        ro, rl = orc.dense_causal_attention(f["q"][:, i:i + 1], f["k"], f["v"], q_offset=i)
+        assert float(np.abs(out[0, i].float().cpu().numpy() - ro[0, 0]).max()) <= TOL["bf16"], i
+        assert float(np.abs(lg[0, :, i] - rl[0, :, 0]).max()) <= 1e-3, i
+
+
+@gpu
 @pytest.mark.parametrize("seed", range(12))
 def test_random_shapes_match_oracle(seed):
     # seeded sweep over the supported shape space (several tiles, ragged tails)
@@ -224,3 +255,34 @@ def test_user_selection_with_invalid_ids_is_safe():
     torch.cuda.synchronize()
     ref, _ = orc.sparse_attention(f["q"], f["k"], f["v"], good, s.q_offset)
     assert _max_err(out, ref) <= TOL["bf16"]
+
+
+@gpu
+@pytest.mark.parametrize("seed", range(6))
+def test_random_shapes_wide_k(seed):
+    # seeded sweep over k = 33..64 with caches long enough that most rows rank
+    # more blocks than they keep (the wide top lists and the merge of up to 128)
+    msa = _msa()
+    rng = np.random.default_rng(3000 + seed)
+    dt = "f32" if seed % 3 == 0 else "bf16"
+    G = int(rng.choice([1, 2, 4]))
+    r = int(rng.choice([1, 2, 4, 8]))
+    d = int(rng.choice([64, 128]))
+    D = int(rng.choice([32, 64, 128]))
+    k = int(rng.integers(33, 65))
+    B = int(rng.integers(1, 3))
+    S_q = int(rng.choice([1, 3, int(rng.integers(1, 300))]))
+    q_offset = int(rng.integers(4000, 12000))
+    S_k = q_offset + S_q + int(rng.integers(0, 300))
+    lo, hi = (-8, 8) if dt == "f32" else (-4, 4)
+    s = synth.Shape(B, S_q, S_k, q_offset, G * r, G, d, D, k, dtype=dt, idx_lo=lo, idx_hi=hi)
+    print(f"case {s}", flush=True)
+    x, xh = _inputs(s, 4000 + seed)
+    out, sel, lse = msa.fwd(x["q"], x["k"], x["v"], x["q_idx"], x["k_idx"], k, q_offset=q_offset,
+                            return_sel=True, return_lse=True)
+    torch.cuda.synchronize()
+    f = {n: synth.as_f64(t) for n, t in xh.items()}
+    ref_out, ref_sel, ref_lse = orc.msa_forward(f["q"], f["k"], f["v"], f["q_idx"], f["k_idx"], k, q_offset)
+    _check_sel_rows(sel, ref_sel)
+    assert _max_err(out, ref_out) <= TOL[dt]
+    assert float(np.abs(lse.cpu().numpy() - ref_lse).max()) <= 1e-3
