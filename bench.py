@@ -494,6 +494,7 @@ def main():
     attn_avg = float(np.mean(attn_ms))
     value = (flop_main + flop_index) / (ms * 1e-3) / 1e12
     achieved = flop_main / (attn_avg * 1e-3) / 1e12
+    traffic = recorded_traffic("attn_kvouter_prefill_32k_b2_hbm.md", "attn.hip") if wid == 3 else None
     result = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -514,9 +515,11 @@ def main():
                    "block_size": s.block_size, "topk": s.topk},
         "roofline": {"bound": "mfma", "kernel": "attn_kvouter", "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": recorded_traffic("attn_kvouter_prefill_32k_b2_hbm.md", "attn.hip")
-                     if wid == 3 else None,
-                     "traffic_unit": "bytes", "flop_per_launch": flop_main, "avg_launch_ms": round(attn_avg, 4)},
+                     "traffic": traffic, "traffic_unit": "bytes",
+                     # the counted HBM bytes per launch over this run's launch time, against 8 TB/s
+                     "traffic_frac_of_hbm_peak": (round(traffic / (attn_avg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
+                                                  if traffic else None),
+                     "flop_per_launch": flop_main, "avg_launch_ms": round(attn_avg, 4)},
         "work": work_rates(flop_main, flop_index, value, kern),
         "kernels_ms": {k: round(v, 4) for k, v in kern.items()},
     }
