@@ -20,7 +20,8 @@
 // two are merged through LDS into one list per (row, key split).  The lists of
 // a row's splits are merged by topk_merge_kernel, which also adds the local
 // block, sorts ascending and pads with -1; with a single split the index kernel
-// does that itself.
+// does that itself.  For k > 32 (lists of 63) each lane half writes its own
+// list and topk_merge_kernel always merges them.
 //
 // Index keys stored as OCP FP8 E4M3 (S = e4m3) are widened exactly to bf16 as
 // they are staged, so the scores are the same as for the bf16 values they hold.
