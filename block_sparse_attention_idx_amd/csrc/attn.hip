@@ -560,6 +560,281 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnParams p) {
   }
 }
 
+// Decode rows form: one workgroup per (b, i, g) row runs the row's whole main
+// branch -- the merge of the index kernel's split lists when it left them,
+// attention over the selected blocks with a running softmax, and the row's
+// output and log-sum-exp -- so no partial state goes through HBM and no merge
+// or combine kernel runs.  8 waves in two teams of 4: team u takes the row's
+// visible selected blocks u, u + 2, ... (ascending ids).  Per block, each wave
+// of the team scores 32 of the block's keys (K read straight from HBM as the A
+// operand), the block's row maxima and sums meet in the team's LDS, P^T and V^T
+// go to the team's LDS, and wave w accumulates the d-slice [32w, 32w + 32) of
+// O^T, rescaled by 2^(m_old - m_new) when the running maximum grows.  The next
+// block's K and V are loaded while the current one is computed.  At the end the
+// two teams' (m, l, O) are merged and the row is written.
+template <typename S, int D, int R>
+__global__ __launch_bounds__(512) void attn_decode_rows_kernel(AttnParams p) {
+  using T = bf16;
+  using M = Mma<T>;
+  using IO = ChunkIO<T, S>;
+  constexpr bool kNative = std::is_same<S, T>::value;
+  typedef typename std::conditional<kNative, typename Mma<T>::frag, uint2>::type kraw;
+  using frag = typename M::frag;
+  constexpr int KPL = M::KPL, KSTEP = M::KSTEP, NKS = D / KSTEP;
+  constexpr int E = 8;             // bf16 per 16-byte chunk
+  constexpr int LDV = kBlock + E;  // V^T pitch (elements), 16-byte aligned rows
+  constexpr int LDP = kBlock + E;  // P^T pitch
+  constexpr int NDT = D / 32;      // waves of a team that own a d-slice of O^T
+  constexpr int NPV = kBlock / KSTEP;
+  constexpr int VT = (D / E) * (kBlock / E);  // 8x8 transpose tiles of a V block
+  constexpr int VU = (VT + 255) / 256;        // per thread of a team
+  static_assert(R <= 32, "one 32-row tile holds the token's heads");
+  constexpr int TEAM_BYTES = (D * LDV + 32 * LDP) * (int)sizeof(T);
+  constexpr int MERGE_BYTES = kMergeMaxLists * kIndexWideCap * 8;  // the largest list set of a row
+  constexpr int XBYTES = 4 * 16 * 64 * 4 + 64 * 4;                 // team 1's O^T, m and l at the end
+  constexpr int RAW = 2 * TEAM_BYTES > MERGE_BYTES ? 2 * TEAM_BYTES : MERGE_BYTES;
+  static_assert(RAW >= XBYTES, "the final exchange fits");
+  __shared__ __align__(16) char raw[RAW];
+  __shared__ float red_m[2][4][32];
+  __shared__ float red_l[2][4][32];
+  __shared__ int pos_s[64];  // the row's selection by position
+  __shared__ int blk_s[64];  // its visible blocks, ascending
+  __shared__ int nv_s;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int team = wave >> 2, wt = wave & 3, ttid = tid & 255;
+  const int h = lane >> 5, l32 = lane & 31;
+  const float sl2 = p.scale_log2;
+  const int64_t row = blockIdx.x;  // (b * S_q + i) * G + g
+  const int g = (int)(row % p.G);
+  const int64_t bi = row / p.G;  // b * S_q + i
+  const int i = (int)(bi % p.S_q);
+  const int b = (int)(bi / p.S_q);
+  const int64_t t = first_pos(p.cm, p.q_offset, p.S_q, p.S_k, b) + i;
+  const int L = local_block(t);
+  const int slen = cache_len(p.cm, p.S_k, b);
+
+  // the token's query rows (rows past r repeat head 0 and are never stored)
+  frag qb[NKS];
+  {
+    const int qh = l32 < R ? l32 : 0;
+    const T* qp = (const T*)p.q + (bi * p.Hq + g * R + qh) * D;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) qb[ks] = *(const frag*)(qp + ks * KSTEP + h * KPL);
+  }
+
+  // the row's selection (merged here from the split lists, or read) and its
+  // visible, mapped blocks in ascending order
+  if (wave == 0) {
+    const int64_t srow = (((int64_t)b * p.G + g) * p.S_q + i) * p.topk;
+    pos_s[lane] = -1;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (p.lists_s) {  // merge the split lists; the selection goes to sel_w
+      if (L >= 0) {
+        const int nl = L > 0 ? (L + p.list_chunk - 1) / p.list_chunk * p.list_lps : 0;
+        const int64_t base = row * p.list_stride * p.list_cap;
+        float* ss = (float*)raw;
+        int* si = (int*)(raw + MERGE_BYTES / 2);
+        const MergedSlot m =
+            merge_row_lists(p.lists_s + base, p.lists_i + base, nl, p.list_cap, min(p.topk - 1, L), L, ss, si, lane);
+        if (m.pos >= 0) {
+          p.sel_w[srow + m.pos] = m.id;
+          pos_s[m.pos] = m.id;
+        } else if (lane < p.topk) {
+          p.sel_w[srow + lane] = -1;
+        }
+      } else if (lane < p.topk) {
+        p.sel_w[srow + lane] = -1;  // a row before the start of its cache selects nothing
+      }
+    } else if (L >= 0 && lane < p.topk) {
+      pos_s[lane] = p.sel[srow + lane];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int c = lane < p.topk ? pos_s[lane] : -1;
+    const int64_t key0 = (int64_t)c * kBlock;
+    const bool ok = c >= 0 && c < p.nb && key0 <= t && key0 < slen && block_mapped(p.cm, b, c);
+    const uint64_t bal = __ballot(ok);
+    if (ok) blk_s[__popcll(bal & ((1ull << lane) - 1))] = c;
+    if (lane == 0) nv_s = __popcll(bal);
+  }
+  __syncthreads();
+  const int nv = nv_s;
+
+  // one block of the team: this wave's 32 K rows and this thread's share of V
+  struct Blk {
+    kraw ka[NKS];
+    typename IO::raw vin[VU][E];
+    int lim, rows_ok;
+    bool has;
+  };
+  auto load_blk = [&](int j, Blk& x) {
+    const int ci = 2 * j + team;
+    x.has = ci < nv;  // uniform across the team
+    if (!x.has) return;
+    const int c = blk_s[ci];
+    const int64_t key0 = (int64_t)c * kBlock;
+    const int64_t rel = t - key0;
+    x.lim = rel >= kBlock ? kBlock : (int)rel;
+    x.rows_ok = (int)min((int64_t)kBlock, (int64_t)slen - key0);
+    const int64_t kv0 = block_offset(p.cm, p.S_k, p.G, D, b, g, c);
+    const int krow = min(wt * 32 + l32, x.rows_ok - 1);
+    const S* kp = (const S*)p.k + kv0 + (int64_t)krow * D;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) x.ka[ks] = *(const kraw*)(kp + ks * KSTEP + h * KPL);
+    const S* vsrc = (const S*)p.v + kv0;
+#pragma unroll
+    for (int u = 0; u < VU; ++u) {
+      const int tl = min(ttid + u * 256, VT - 1);
+      const int dg = tl % (D / E), kg = tl / (D / E);
+#pragma unroll
+      for (int r = 0; r < E; ++r)
+        x.vin[u][r] = IO::load(vsrc + (int64_t)min(kg * E + r, x.rows_ok - 1) * D + dg * E);
+    }
+  };
+
+  T* Vt = (T*)(raw + team * TEAM_BYTES);
+  T* Ps = Vt + D * LDV;
+  float m_run = kNegInf, l_run = 0.f;  // of row l32, the same in every lane of the row
+  f32x16 oacc = f32x16{};
+  auto step = [&](const Blk& x) {
+    __syncthreads();  // the previous block's V^T and P^T reads are done (and the list merge)
+    f32x16 sacc = f32x16{};
+    if (x.has) {
+#pragma unroll
+      for (int u = 0; u < VU; ++u) {
+        const int tl = ttid + u * 256;
+        if (VT % 256 != 0 && tl >= VT) break;
+        const int dg = tl % (D / E), kg = tl / (D / E);
+        i32x4 vw[E];
+#pragma unroll
+        for (int r = 0; r < E; ++r) vw[r] = kg * E + r < x.rows_ok ? IO::widen(x.vin[u][r]) : i32x4{};
+        i32x4 outc[E];
+        transpose_tile<T, E>(vw, outc);
+#pragma unroll
+        for (int r = 0; r < E; ++r) *(i32x4*)&Vt[(dg * E + r) * LDV + kg * E] = outc[r];
+      }
+      // S^T for keys [32 wt, 32 wt + 32): lane (row l32, half h) holds keys 32 wt + c_row(j, h)
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        frag a;
+        if constexpr (kNative) a = x.ka[ks];
+        else a = __builtin_bit_cast(frag, IO::widen(x.ka[ks]));
+        sacc = M::mma(a, qb[ks], sacc);
+      }
+      if (x.lim < kBlock - 1) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          if (wt * 32 + c_row(j, h) > x.lim) sacc[j] = kNegInf;
+      }
+      float mw = kNegInf;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) mw = fmaxf(mw, sacc[j]);
+      mw = wave_max_xor32(mw);
+      if (h == 0) red_m[team][wt][l32] = mw;
+    }
+    __syncthreads();
+    float alpha = 1.f, m_new = m_run;
+    if (x.has) {
+      // key 0 of a visible block is visible, so the block maximum is finite
+      const float mb = fmaxf(fmaxf(red_m[team][0][l32], red_m[team][1][l32]),
+                             fmaxf(red_m[team][2][l32], red_m[team][3][l32]));
+      m_new = fmaxf(m_run, mb);
+      alpha = __builtin_amdgcn_exp2f((m_run - m_new) * sl2);  // 0 for the first block
+      const float moff = -m_new * sl2;
+      float lw = 0.f;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[j], sl2, moff));
+        sacc[j] = e;
+        lw += e;
+      }
+      lw += __shfl_xor(lw, 32);
+      if (h == 0) red_l[team][wt][l32] = lw;
+      // P^T row l32: keys 32 wt + c_row(j, h) come in runs of four
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        T* dst = &Ps[l32 * LDP + wt * 32 + q4 * 8 + h * 4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dst[e] = from_f32<T>(sacc[q4 * 4 + e]);
+      }
+    }
+    __syncthreads();
+    if (x.has) {
+      l_run = l_run * alpha + (red_l[team][0][l32] + red_l[team][1][l32] + red_l[team][2][l32] + red_l[team][3][l32]);
+      m_run = m_new;
+      if (wt < NDT) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) oacc[j] *= alpha;
+#pragma unroll
+        for (int ks2 = 0; ks2 < NPV; ++ks2) {
+          const frag va = *(const frag*)&Vt[(wt * 32 + l32) * LDV + ks2 * KSTEP + h * KPL];
+          const frag pb = *(const frag*)&Ps[l32 * LDP + ks2 * KSTEP + h * KPL];
+          oacc = M::mma(va, pb, oacc);
+        }
+      }
+    }
+  };
+
+  // rounds of two blocks (one per team), the next round's loads in flight
+  const int rounds = (nv + 1) / 2;
+  Blk xa, xb;
+  load_blk(0, xa);
+  for (int j = 0; j < rounds; j += 2) {
+    load_blk(j + 1, xb);
+    step(xa);
+    if (j + 1 >= rounds) break;
+    load_blk(j + 2, xa);
+    step(xb);
+  }
+
+  // merge the teams: team 1 hands (m, l, O^T slices) to team 0 through LDS
+  __syncthreads();
+  float* xo = (float*)raw;  // [4 waves][16][64 lanes]
+  float* xm = xo + 4 * 16 * 64;
+  if (team == 1) {
+    if (wt < NDT) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) xo[(wt * 16 + j) * 64 + lane] = oacc[j];
+    }
+    if (wt == 0 && h == 0) {
+      xm[l32] = m_run;
+      xm[32 + l32] = l_run;
+    }
+  }
+  __syncthreads();
+  if (team == 0 && wt < NDT && l32 < R) {
+    const float m1 = xm[l32], l1 = xm[32 + l32];
+    const float mt = fmaxf(m_run, m1);
+    const bool any = mt != kNegInf;  // false only for a row that sees no key
+    const float a0 = any ? __builtin_amdgcn_exp2f((m_run - mt) * sl2) : 0.f;
+    const float a1 = any ? __builtin_amdgcn_exp2f((m1 - mt) * sl2) : 0.f;
+    const float W = l_run * a0 + l1 * a1;
+    const float inv = any ? p.v_scale / W : 0.f;
+    const int64_t orow = (bi * p.Hq + g * R + l32) * D;
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int d0 = wt * 32 + q4 * 8 + h * 4;
+      float o4[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        o4[e] = (oacc[q4 * 4 + e] * a0 + xo[(wt * 16 + q4 * 4 + e) * 64 + lane] * a1) * inv;
+      if (p.out_f32) {
+        *(f32x4*)((float*)p.out + orow + d0) = f32x4{o4[0], o4[1], o4[2], o4[3]};
+      } else {
+        *(bf16x4*)((T*)p.out + orow + d0) =
+            bf16x4{from_f32<T>(o4[0]), from_f32<T>(o4[1]), from_f32<T>(o4[2]), from_f32<T>(o4[3])};
+      }
+    }
+    if (wt == 0 && h == 0 && p.lse)
+      p.lse[((int64_t)b * p.Hq + g * R + l32) * p.S_q + i] =
+          any ? (mt * sl2 + __builtin_amdgcn_logf(W)) * 0.69314718055994531f : kNegInf;
+  }
+}
+
 // Merge the partial states of one (token, group) over its selected slots:
 // out = sum_s 2^(lse_s - M) o_s / sum_s 2^(lse_s - M), M = max_s lse_s.
 // A thread owns one 16-byte chunk of the lane-native partial layout (E values
@@ -737,6 +1012,15 @@ void launch_gather(const AttnParams& p, hipStream_t s, const KernelTimer* tm) {
 
 template <typename T, typename S, int D, int R>
 static hipError_t launch_attn_t(const AttnParams& p, hipStream_t s, const KernelTimer* tm) {
+  if constexpr (std::is_same<T, bf16>::value) {
+    if (p.rows_mode) {  // the whole main branch in one launch, no combine
+      timer_start(tm, kKernAttention, s);
+      hipLaunchKernelGGL((attn_decode_rows_kernel<S, D, R>), dim3((unsigned)((int64_t)p.B * p.S_q * p.G)), dim3(512),
+                         0, s, p);
+      timer_stop(tm, kKernAttention, s);
+      return hipGetLastError();
+    }
+  }
   launch_gather(p, s, tm);
   timer_start(tm, kKernAttention, s);
   if (p.direct)

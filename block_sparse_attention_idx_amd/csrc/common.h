@@ -124,4 +124,99 @@ struct ChunkIO<bf16, e4m3> {
   }
 };
 
+// Top-k order: the higher block score first, on equal scores the lower block.
+__device__ __forceinline__ bool ranks_before(float s1, int i1, float s2, int i2) {
+  return s1 > s2 || (s1 == s2 && i1 < i2);
+}
+
+// This lane's entry of a merged selection row: position pos (ascending block
+// ids) holds block id; pos = -1 for lanes past the row's selected blocks.
+struct MergedSlot {
+  int pos, id;
+};
+
+// One wave merges the partial top lists of one (query row, group): nl lists of
+// cap entries at gs / gi (scores, block ids; each list ordered by ranks_before,
+// empty entries id -1 last; a block id appears in at most one list), staged
+// through the wave's LDS ss / si (nl * cap entries each; nl <= 128).  The
+// first `take` blocks by rank are kept (fewer when the lists hold fewer) and
+// the local block L is added.  Lane j < n returns the j-th pick's position
+// among the n picks in ascending id order, lane n returns L at position n, the
+// other lanes pos = -1.
+__device__ inline MergedSlot merge_row_lists(const float* gs, const int32_t* gi, int nl, int cap, int take, int L,
+                                             float* ss, int* si, int lane) {
+  // the lists in batches of 8 loads per lane, all in flight before any is stored
+  for (int e0 = 0; e0 < nl * cap; e0 += 64 * 8) {
+    float vs[8];
+    int vi[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int e = min(e0 + u * 64 + lane, nl * cap - 1);
+      vs[u] = gs[e];
+      vi[u] = gi[e];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int e = e0 + u * 64 + lane;
+      if (e < nl * cap) {
+        ss[e] = vs[u];
+        si[e] = vi[u];
+      }
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+  // take rounds of a wave-wide argmax over the list heads (lists lane and lane + 64)
+  int pos0 = 0, pos1 = 0;
+  int mywin = 0x7fffffff;
+  for (int it = 0; it < take; ++it) {
+    float bs = kNegInf;
+    int bi = 0x7fffffff, bl = -1;
+    if (lane < nl && pos0 < cap) {
+      const float s = ss[lane * cap + pos0];
+      const int id = si[lane * cap + pos0];
+      if (id >= 0) {
+        bs = s;
+        bi = id;
+        bl = 0;
+      }
+    }
+    if (lane + 64 < nl && pos1 < cap) {
+      const float s = ss[(lane + 64) * cap + pos1];
+      const int id = si[(lane + 64) * cap + pos1];
+      if (id >= 0 && ranks_before(s, id, bs, bi)) {
+        bs = s;
+        bi = id;
+        bl = 1;
+      }
+    }
+    float ws = bs;
+    int wi = bi;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float os = __shfl_xor(ws, off);
+      const int oi = __shfl_xor(wi, off);
+      if (ranks_before(os, oi, ws, wi)) {
+        ws = os;
+        wi = oi;
+      }
+    }
+    // block ids are unique across the lists, so exactly one lane owns the winner
+    if (bl >= 0 && bi == wi) {
+      if (bl == 0) ++pos0;
+      else ++pos1;
+    }
+    if (lane == it) mywin = wi;
+  }
+  // rounds that found no entry (lists shorter than take) leave the sentinel
+  const int n = __popcll(__ballot(lane < take && mywin != 0x7fffffff));
+  int rank = 0;
+  for (int m = 0; m < n; ++m) rank += (__shfl(mywin, m) < mywin) ? 1 : 0;
+  if (lane < n) return MergedSlot{rank, mywin};
+  if (lane == n) return MergedSlot{n, L};
+  return MergedSlot{-1, -1};
+}
+
 }  // namespace msa

@@ -54,10 +54,6 @@ __device__ __forceinline__ void list_insert(float (&s)[CAP], int (&id)[CAP], flo
   id[0] = gt[0] ? c : id[0];
 }
 
-__device__ __forceinline__ bool ranks_before(float s1, int i1, float s2, int i2) {
-  return s1 > s2 || (s1 == s2 && i1 < i2);
-}
-
 // One (row, key split) result: with several splits the merged list goes to
 // the partial lists for topk_merge_kernel; with one split the first min(k-1, L)
 // entries are the selection, and the local block and -1 padding are added
@@ -656,69 +652,8 @@ __global__ __launch_bounds__(64 * WPB) void topk_merge_kernel(IndexParams p) {
   const int32_t* gi = p.part_i + row * per_wave;
   float* ss = (float*)msmem + wave * per_wave;
   int* si = (int*)msmem + WPB * per_wave + wave * per_wave;
-  // the lists in batches of 8 loads per lane, all in flight before any is stored
-  for (int e0 = 0; e0 < nl * CAP; e0 += 64 * 8) {
-    float vs[8];
-    int vi[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int e = min(e0 + u * 64 + lane, nl * CAP - 1);
-      vs[u] = gs[e];
-      vi[u] = gi[e];
-    }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int e = e0 + u * 64 + lane;
-      if (e < nl * CAP) {
-        ss[e] = vs[u];
-        si[e] = vi[u];
-      }
-    }
-  }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
-  int pos0 = 0, pos1 = 0;  // heads of lists lane and lane + 64
-  int mywin = 0x7fffffff;
-  for (int it = 0; it < take; ++it) {
-    float bs = kNegInf;
-    int bi = 0x7fffffff, bl = -1;
-    if (lane < nl && pos0 < CAP) {
-      const float s = ss[lane * CAP + pos0];
-      const int id = si[lane * CAP + pos0];
-      if (id >= 0) { bs = s; bi = id; bl = 0; }
-    }
-    if (lane + 64 < nl && pos1 < CAP) {
-      const float s = ss[(lane + 64) * CAP + pos1];
-      const int id = si[(lane + 64) * CAP + pos1];
-      if (id >= 0 && ranks_before(s, id, bs, bi)) { bs = s; bi = id; bl = 1; }
-    }
-    float ws = bs;
-    int wi = bi;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float os = __shfl_xor(ws, off);
-      const int oi = __shfl_xor(wi, off);
-      if (ranks_before(os, oi, ws, wi)) {
-        ws = os;
-        wi = oi;
-      }
-    }
-    // block ids are unique across a row's lists, so exactly one lane owns the winner
-    if (bl >= 0 && bi == wi) {
-      if (bl == 0) ++pos0;
-      else ++pos1;
-    }
-    if (lane == it) mywin = wi;
-  }
-  int rank = 0;
-  for (int m = 0; m < take; ++m) {
-    const int w = __shfl(mywin, m);
-    rank += (w < mywin) ? 1 : 0;
-  }
-  if (lane < take) out[rank] = mywin;
-  else if (lane == take) out[take] = L;
+  const MergedSlot m = merge_row_lists(gs, gi, nl, CAP, take, L, ss, si, lane);
+  if (m.pos >= 0) out[m.pos] = m.id;
   else if (lane < p.topk) out[lane] = -1;
 }
 
@@ -742,6 +677,7 @@ static hipError_t launch_index_t(const IndexParams& p, hipStream_t s, const Kern
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (p.nsplit == 1 && CAP != kIndexWideCap) return hipGetLastError();  // the index kernel wrote the selection
+  if (p.merge_in_consumer) return hipGetLastError();  // the decode rows kernel merges the lists
   const int64_t rows = (int64_t)p.B * p.rows_per_b;
   timer_start(tm, kKernTopkMerge, s);
   constexpr int WPB = merge_rows_per_wg(CAP);  // the host keeps nsplit * lps <= merge_max_lists(CAP)

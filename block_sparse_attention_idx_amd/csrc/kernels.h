@@ -91,6 +91,7 @@ struct IndexParams {
   // (row tile << 7) | split by index_units_kernel, and their number.  Null otherwise.
   int32_t* units;
   int32_t* unit_count;
+  int merge_in_consumer;  // host only: the lists are merged by the decode rows kernel, not topk_merge_kernel
 };
 
 // At most this many (row, group) pairs per sequence: the index kernel's
@@ -154,7 +155,20 @@ struct AttnParams {
   float scale_log2;    // softmax scale * key scale * log2(e)
   float v_scale;       // dequantisation scale of the value cache (1 if none)
   int out_f32;         // output dtype: 1 fp32, 0 input dtype
+  // Decode rows form (direct, bf16 queries, enough rows): one workgroup per
+  // (b, i, g) row runs the whole main branch, no partial states or combine.
+  int rows_mode;
+  // with it, the index kernel's partial lists when it left them unmerged
+  // (lists_s null: sel holds the selection); the rows kernel then writes sel
+  const float* lists_s;    // [rows, list_stride, list_cap]
+  const int32_t* lists_i;
+  int list_cap, list_stride, list_chunk, list_lps;
+  int32_t* sel_w;          // the selection buffer the merged rows are written to
 };
+
+// Rows (B * S_q * G) from which decode uses the rows form: one workgroup per
+// row fills the 256 CUs.
+constexpr int kDecodeRowsMin = 256;
 
 // fp8_cache: k and v hold OCP FP8 E4M3 values (q and the partial states bf16).
 hipError_t launch_sparse_attention(const AttnParams& p, bool bf16_inputs, bool fp8_cache, hipStream_t s,

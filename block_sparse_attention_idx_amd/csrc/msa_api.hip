@@ -262,6 +262,10 @@ AttnPlan plan_attn(const msa_shape* s, const msa_kv_cache* cache, int tpi = kTok
   // queries per (b, g, block) on average; below 2 the gather buys nothing
   const double per_bucket = (double)s->q_len * std::min<int64_t>(s->topk, Lmax + 1) / (double)(Lmax + 1);
   p.direct = per_bucket < 2.0 ? 1 : 0;
+  // decode with enough (b, i, g) rows to give every CU one: a workgroup per row
+  // runs the whole main branch (bf16 queries; the fp32 form's LDS does not fit)
+  p.rows_mode = p.direct && s->dtype == MSA_BF16 &&
+                (int64_t)s->batch * s->q_len * s->num_kv_heads >= msa::kDecodeRowsMin ? 1 : 0;
   p.n_direct = (int64_t)p.B * p.G * p.S_q * p.topk;
   p.grid = kAttnGrid;
   // 6 workgroups per CU, twice what fits at once (44 KiB of LDS each): measured
@@ -484,6 +488,10 @@ msa_status msa_fwd_kvcache(const msa_shape* s, const msa_kv_cache* cache, const 
   int32_t* sel = sel_out ? sel_out : (int32_t*)w;
   char* scratch = w + sel_bytes(s);  // index lists and attention state reuse one region
   bind_index(ip, scratch, q_idx, k_idx, sel);
+  // the decode rows kernel merges the split lists itself (it writes no partial
+  // state, so the lists stay intact in the shared region)
+  const bool merge_in_rows = ap.p.rows_mode && ip.lists;
+  ip.p.merge_in_consumer = merge_in_rows ? 1 : 0;
   hipStream_t hs = (hipStream_t)stream;
   clear_stale_hip_error();
   st = hip_status(msa::launch_index_select(ip.p, s->dtype == MSA_BF16, fp8_cache(s), s->index_dim, hs, timer()),
@@ -496,6 +504,15 @@ msa_status msa_fwd_kvcache(const msa_shape* s, const msa_kv_cache* cache, const 
   ap.p.sel = sel;
   ap.p.out = out;
   ap.p.lse = lse;
+  if (merge_in_rows) {
+    ap.p.lists_s = ip.p.part_s;
+    ap.p.lists_i = ip.p.part_i;
+    ap.p.list_cap = ip.cap;
+    ap.p.list_stride = ip.p.nsplit * ip.p.lps;
+    ap.p.list_chunk = ip.p.chunk;
+    ap.p.list_lps = ip.p.lps;
+    ap.p.sel_w = sel;
+  }
   return hip_status(msa::launch_sparse_attention(ap.p, s->dtype == MSA_BF16, fp8_cache(s), hs, timer()),
                     "sparse attention launch");
 }
