@@ -25,7 +25,11 @@
 //      dtype plus the fp32 log2-sum-exp of the block's scaled scores.
 //   3. combine: per (token, head) the partial states of its slots are merged
 //      (weights 2^(lse_s - max)) into the output and the log-sum-exp.
-// With S_q small (decode) the gather is skipped: one item per selection entry.
+// With S_q small (decode) the gather is skipped: one item per selection entry,
+// or, with bf16 queries and enough (b, i, g) rows to give every CU one, the
+// rows form: one workgroup per row merges the index kernel's split lists,
+// attends over the row's blocks with a running softmax and writes the row, so
+// neither partial states nor the merge and combine launches are needed.
 //
 // K and V may be stored as OCP FP8 E4M3 (storage type S = e4m3, compute type
 // T = bf16): staging widens them exactly to bf16, the per-tensor key scale is
