@@ -603,6 +603,7 @@ __global__ __launch_bounds__(512) void attn_decode_rows_kernel(AttnParams p) {
   __shared__ float red_l[2][4][32];
   __shared__ int pos_s[64];  // the row's selection by position
   __shared__ int blk_s[64];  // its visible blocks, ascending
+  __shared__ int64_t off_s[64];  // and their element offsets in k and v (pages resolved here, once)
   __shared__ int nv_s;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -662,7 +663,11 @@ __global__ __launch_bounds__(512) void attn_decode_rows_kernel(AttnParams p) {
     const int64_t key0 = (int64_t)c * kBlock;
     const bool ok = c >= 0 && c < p.nb && key0 <= t && key0 < slen && block_mapped(p.cm, b, c);
     const uint64_t bal = __ballot(ok);
-    if (ok) blk_s[__popcll(bal & ((1ull << lane) - 1))] = c;
+    if (ok) {
+      const int ci = __popcll(bal & ((1ull << lane) - 1));
+      blk_s[ci] = c;
+      off_s[ci] = block_offset(p.cm, p.S_k, p.G, D, b, g, c);
+    }
     if (lane == 0) nv_s = __popcll(bal);
   }
   __syncthreads();
@@ -675,16 +680,23 @@ __global__ __launch_bounds__(512) void attn_decode_rows_kernel(AttnParams p) {
     int lim, rows_ok;
     bool has;
   };
+  // A team without a block still issues its loads (row 0 at the start of the
+  // pool, always valid memory; the values are not used), so that every path
+  // leaves the same loads in flight and no wait covers the next block's.
   auto load_blk = [&](int j, Blk& x) {
     const int ci = 2 * j + team;
     x.has = ci < nv;  // uniform across the team
-    if (!x.has) return;
-    const int c = blk_s[ci];
-    const int64_t key0 = (int64_t)c * kBlock;
-    const int64_t rel = t - key0;
-    x.lim = rel >= kBlock ? kBlock : (int)rel;
-    x.rows_ok = (int)min((int64_t)kBlock, (int64_t)slen - key0);
-    const int64_t kv0 = block_offset(p.cm, p.S_k, p.G, D, b, g, c);
+    int64_t kv0 = 0;
+    x.lim = 0;
+    x.rows_ok = 1;
+    if (x.has) {
+      const int c = blk_s[ci];
+      const int64_t key0 = (int64_t)c * kBlock;
+      const int64_t rel = t - key0;
+      x.lim = rel >= kBlock ? kBlock : (int)rel;
+      x.rows_ok = (int)min((int64_t)kBlock, (int64_t)slen - key0);
+      kv0 = off_s[ci];
+    }
     const int krow = min(wt * 32 + l32, x.rows_ok - 1);
     const S* kp = (const S*)p.k + kv0 + (int64_t)krow * D;
 #pragma unroll
@@ -706,7 +718,7 @@ __global__ __launch_bounds__(512) void attn_decode_rows_kernel(AttnParams p) {
   f32x16 oacc = f32x16{};
   auto step = [&](const Blk& x) {
     __syncthreads();  // the previous block's V^T and P^T reads are done (and the list merge)
-    f32x16 sacc = f32x16{};
+    f32x16 sacc;  // defined (and used) only when the team has a block
     if (x.has) {
 #pragma unroll
       for (int u = 0; u < VU; ++u) {
@@ -727,7 +739,7 @@ __global__ __launch_bounds__(512) void attn_decode_rows_kernel(AttnParams p) {
         frag a;
         if constexpr (kNative) a = x.ka[ks];
         else a = __builtin_bit_cast(frag, IO::widen(x.ka[ks]));
-        sacc = M::mma(a, qb[ks], sacc);
+        sacc = M::mma(a, qb[ks], ks == 0 ? f32x16{} : sacc);
       }
       if (x.lim < kBlock - 1) {
 #pragma unroll
