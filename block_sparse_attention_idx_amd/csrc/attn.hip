@@ -183,6 +183,7 @@ __global__ __launch_bounds__(256, 2) void attn_kvouter_kernel(AttnParams p) {
   constexpr int NPV = kBlock / KSTEP;     // PV instructions per d tile
   __shared__ __align__(16) T Ks[kBlock * LDK];
   __shared__ __align__(16) T Vt[D * LDV];
+  __shared__ int32_t tok_s[kMaxItemTokens];  // the item's (row << 6) | slot entries
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int h = lane >> 5, l32 = lane & 31;
@@ -235,6 +236,8 @@ __global__ __launch_bounds__(256, 2) void attn_kvouter_kernel(AttnParams p) {
       const S* vsrc = (const S*)p.v + kv0;
       typename IO::raw kx[KU];
       typename IO::raw vin[VU][E];
+      // the item's entries go to LDS with the staging, so no pass waits on a global read for its rows
+      const int32_t ent = toks ? toks[min((int)threadIdx.x, ntok - 1)] : direct_tok;
 #pragma unroll
       for (int u = 0; u < KU; ++u) {
         const int ch = threadIdx.x + u * 256;
@@ -250,6 +253,7 @@ __global__ __launch_bounds__(256, 2) void attn_kvouter_kernel(AttnParams p) {
           vin[u][r] = IO::load(vsrc + (int64_t)min(kg * E + r, rows_ok - 1) * D + dg * E);
       }
       __builtin_amdgcn_sched_barrier(0);  // keep every staging load ahead of the first use
+      if ((int)threadIdx.x < ntok) tok_s[threadIdx.x] = ent;
 #pragma unroll
       for (int u = 0; u < KU; ++u) {
         const int ch = threadIdx.x + u * 256;
@@ -283,7 +287,7 @@ __global__ __launch_bounds__(256, 2) void attn_kvouter_kernel(AttnParams p) {
       if (p0 + wave * TPW >= ntok) continue;  // this wave has no rows in this pass
       const int tslot = p0 + wave * TPW + l32 / R;
       const bool in_list = tslot < ntok;
-      const int32_t entry = in_list ? (toks ? toks[tslot] : direct_tok) : 0;
+      const int32_t entry = in_list ? tok_s[tslot] : 0;
       const int i = entry >> 6, slot = entry & 63;
       // keys of this block visible to the row: index within block <= lim
       const int64_t rel = qo + i - key0;  // query position relative to the block
@@ -1037,6 +1041,7 @@ static hipError_t launch_attn_t(const AttnParams& p, hipStream_t s, const Kernel
       return hipGetLastError();
     }
   }
+  if (!p.direct && p.tpi > kMaxItemTokens) return hipErrorInvalidValue;  // the item's entries must fit its LDS list
   launch_gather(p, s, tm);
   timer_start(tm, kKernAttention, s);
   if (p.direct)

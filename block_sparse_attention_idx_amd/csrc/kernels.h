@@ -11,6 +11,7 @@ namespace msa {
 constexpr int kBlock = 128;  // Bk: tokens per KV block, fixed on the GPU path
 constexpr int kBwdTokensPerItem = 512;  // query tokens per backward work item (dK, dV meet in fp32 atomics)
 constexpr int kKlTokensPerItem = 64;    // query tokens per KL-teacher work item (their index scores fit in LDS)
+constexpr int kMaxItemTokens = 256;     // most query tokens per KV-outer attention item (its LDS entry list)
 
 // Optional events recorded around one kernel (see msa_set_kernel_timer).
 struct KernelTimer {
