@@ -497,17 +497,25 @@ __global__ __launch_bounds__(256, CAP == kIndexWideCap ? 1 : 2) void index_topk_
   const bool paged = p.cm.pages != nullptr;
   const int pg_lane = paged && lane < nbw ? p.cm.pages[(int64_t)b * p.cm.max_pages + c_begin + wave + 4 * lane] : 0;
   // element offset of the wave's block j, or -1 when its page is unmapped
-  auto blk_off = [&](int j) -> int64_t {
+  // `far` (a compile-time flag): the wave has more than 64 blocks, and those past
+  // the 64th read the page table directly.  The block loop is built once with and
+  // once without that read: a load whose result the next tile's address needs
+  // makes the compiler wait for every load in flight, the prefetch included.
+  auto blk_off = [&](int j, auto far) -> int64_t {
     const int c = c_begin + wave + 4 * j;
     if (!paged) return ((int64_t)b * p.S_k + (int64_t)c * kBlock) * DI;
-    const int pg = j < 64 ? __builtin_amdgcn_readlane(pg_lane, j) : p.cm.pages[(int64_t)b * p.cm.max_pages + c];
+    int pg;
+    if constexpr (decltype(far)::value)
+      pg = j < 64 ? __builtin_amdgcn_readlane(pg_lane, j) : p.cm.pages[(int64_t)b * p.cm.max_pages + c];
+    else
+      pg = __builtin_amdgcn_readlane(pg_lane, j);  // j < nbw <= 64
     return pg >= 0 && pg < p.cm.num_pages ? (int64_t)pg * kBlock * DI : -1;
   };
   // tile tl of the wave; tl past the end re-reads the last one (just read, so from
   // L2); an unmapped page is read from the pool start and scored -inf
-  auto load_tile = [&](i32x4 (&a)[NKR], int tl) {
+  auto load_tile = [&](i32x4 (&a)[NKR], int tl, auto far) {
     const int tc = min(tl, ntl - 1);
-    const int64_t o = blk_off(tc / 4);
+    const int64_t o = blk_off(tc / 4, far);
     const char* src = (const char*)(kpool + (o < 0 ? 0 : o) + (tc % 4) * 32 * DI) + lane * 16;
 #pragma unroll
     for (int u = 0; u < NKR; ++u) a[u] = __builtin_nontemporal_load((const i32x4*)(src + u * 1024));
@@ -548,13 +556,13 @@ __global__ __launch_bounds__(256, CAP == kIndexWideCap ? 1 : 2) void index_topk_
   };
 
   float pm = kNegInf, pmA = kNegInf;
-  auto process = [&](const i32x4 (&a)[NKR], int tl) {
+  auto process = [&](const i32x4 (&a)[NKR], int tl, auto far) {
     pm = fmaxf(pm, tile_max(a));
     if (tl % 4 != 3) return;  // the block continues in the next tile
     const int j = tl / 4;
     float full = fmaxf(pm, __shfl_xor(pm, 32));
     pm = kNegInf;
-    if (blk_off(j) < 0) full = kNegInf;
+    if (blk_off(j, far) < 0) full = kNegInf;
     // blocks pair up: half 0 ranks the wave's even blocks, half 1 the odd ones
     const bool second = (j & 1) != 0;
     if (!second) pmA = full;
@@ -566,17 +574,21 @@ __global__ __launch_bounds__(256, CAP == kIndexWideCap ? 1 : 2) void index_topk_
       list_insert<CAP>(ls, li, x, cc);
     }
   };
-  if (nbw > 0) {
+  auto scan = [&](auto far) {
     i32x4 ta[NKR], tb[NKR];
-    load_tile(ta, 0);
+    load_tile(ta, 0, far);
     for (int tl = 0; tl < ntl; tl += 2) {  // ntl is a multiple of 4
-      load_tile(tb, tl + 1);
+      load_tile(tb, tl + 1, far);
       __builtin_amdgcn_sched_barrier(0);
-      process(ta, tl);
-      load_tile(ta, tl + 2);
+      process(ta, tl, far);
+      load_tile(ta, tl + 2, far);
       __builtin_amdgcn_sched_barrier(0);
-      process(tb, tl + 1);
+      process(tb, tl + 1, far);
     }
+  };
+  if (nbw > 0) {
+    if (paged && nbw > 64) scan(std::true_type{});
+    else scan(std::false_type{});
   }
 
   if constexpr (kWide) {  // list split * 8 + wave * 2 + h of the row
