@@ -260,7 +260,10 @@ typedef enum {
  * start_event (a hipEvent_t) on its stream right before launching `kernel` and
  * stop_event right after it, so hipEventElapsedTime gives that kernel's own
  * duration.  kernel = MSA_KERNEL_NONE (or NULL events) turns the hook off.
- * The events stay owned by the caller. */
+ * The events stay owned by the caller.  A kernel a call does not launch
+ * records nothing: decode calls with bf16 queries and at least 256
+ * (batch, query row, group) rows run the merge of the split lists, the
+ * attention and the combine as one kernel, timed as MSA_KERNEL_ATTENTION. */
 msa_status msa_set_kernel_timer(int kernel, void* start_event, void* stop_event);
 
 /* Static string naming a status code. */
