@@ -146,3 +146,43 @@ def test_rows_form_in_a_graph():
         torch.cuda.synchronize()
         for a, b in zip(got, ref):
             assert torch.equal(a, b), f"replay {rep}"
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_rows_form_random_shapes(seed):
+    # seeded sweep over shapes that take the rows form (>= 256 rows, few queries
+    # per (b, g, block)): head layout, dims, k up to 64, FP8 caches, unequal lengths
+    msa = _msa()
+    rng = np.random.default_rng(5000 + seed)
+    G = int(rng.choice([2, 4]))
+    r = int(rng.choice([1, 2, 4, 8, 16, 32]))
+    d = int(rng.choice([64, 128]))
+    D = int(rng.choice([32, 64, 128]))
+    k = int(rng.integers(1, 65))
+    S_q = int(rng.choice([1, 1, 2]))
+    B = 256 // (G * S_q) + int(rng.integers(0, 16))
+    cache = "fp8" if seed % 4 == 3 else "native"
+    S_k = int(rng.integers(600, 6000)) + 128 * k  # most rows rank more blocks than they keep
+    varlen = seed % 3 == 1
+    s = synth.Shape(B, S_q, S_k, 0 if varlen else S_k - S_q, G * r, G, d, D, k, cache=cache,
+                    k_scale=0.03 if cache == "fp8" else 1.0, v_scale=0.02 if cache == "fp8" else 1.0)
+    print(f"rows sweep {s} varlen={varlen}", flush=True)
+    xh = synth.host_inputs(s, 6000 + seed)
+    x = {n: t.cuda() for n, t in xh.items()}
+    f = {n: _f64(s, n, t) for n, t in xh.items()}
+    if varlen:
+        lens = [int(v) for v in rng.integers(1, S_k + 1, B)]
+        sl = torch.tensor(lens, dtype=torch.int32, device="cuda")
+        out, sel, lse = msa.fwd_kvcache(x["q"], x["k"], x["v"], x["q_idx"], x["k_idx"], k, seq_lens=sl,
+                                        return_sel=True, return_lse=True, **_scales(s))
+        ks = [f["k"][b, :, :n] for b, n in enumerate(lens)]
+        vs = [f["v"][b, :, :n] for b, n in enumerate(lens)]
+        kis = [f["k_idx"][b, :n] for b, n in enumerate(lens)]
+        torch.cuda.synchronize()
+        ref = orc.msa_forward_varlen(f["q"], ks, vs, f["q_idx"], kis, k)
+    else:
+        out, sel, lse = msa.fwd(x["q"], x["k"], x["v"], x["q_idx"], x["k_idx"], k, q_offset=s.q_offset,
+                                return_sel=True, return_lse=True, **_scales(s))
+        torch.cuda.synchronize()
+        ref = orc.msa_forward(f["q"], f["k"], f["v"], f["q_idx"], f["k_idx"], k, s.q_offset)
+    _check(out, sel, lse, *ref)
