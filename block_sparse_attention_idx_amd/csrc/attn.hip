@@ -855,6 +855,270 @@ __global__ __launch_bounds__(512) void attn_decode_rows_kernel(AttnParams p) {
   }
 }
 
+// s_waitcnt immediate that waits until at most vm vector-memory operations
+// are outstanding (expcnt and lgkmcnt left at their maxima).
+constexpr int vmcnt_imm(int vm) { return (vm & 0xF) | ((vm >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+
+// Transposing LDS read of four bf16 (gfx950): in each 16-lane group, lane i
+// gets column c0 + i of rows r0 .. r0 + 3 when lane s points at row r0 + s / 4,
+// column c0 + 4 (s % 4).
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ bf16x4 lds_read_tr(const bf16* ptr) {
+  return __builtin_bit_cast(bf16x4,
+                            __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)(ptr)));
+}
+
+// Workgroup barrier for LDS data: this wave's LDS writes complete, then the
+// barrier; the memory clobber keeps the compiler from moving memory accesses
+// across it.  A fence (as in __syncthreads) would, in a kernel that moves
+// data into LDS by DMA, make every barrier wait for all vector-memory
+// operations in flight; the block loop below waits for exactly the DMA it
+// needs before its first barrier.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Decode rows form for native bf16 caches and r <= 16: one workgroup per
+// (b, i, g) row, as attn_decode_rows_kernel, but all 8 waves work on one block
+// at a time so that a row keeps NBUF blocks in flight.  Each wave scores 16 of
+// the block's keys with 16x16x32 MFMA tiles (K read straight from HBM as the
+// A operand, 16 VGPRs per block), V goes from HBM into a ring of NBUF LDS
+// tiles by DMA (no registers), and wave w accumulates the d-slice
+// [16w, 16w + 16) of O^T, its V^T operand read from the row-major V tile with
+// transposing LDS reads.  Row maxima and sums meet in LDS; O^T is rescaled by
+// 2^(m_old - m_new) as the running maximum grows.
+template <int D, int R>
+__global__ __launch_bounds__(512) void attn_decode_rows16_kernel(AttnParams p) {
+  using T = bf16;
+  typedef bf16x8 frag;
+  constexpr int NW = 8;                   // waves
+  constexpr int KPW = kBlock / NW;        // keys per wave (16)
+  constexpr int NKS = D / 32;             // k-steps of S^T = K Q^T
+  constexpr int CPR = D / 8;              // 16-byte chunks per K / V row
+  constexpr int RPP = 1024 / (2 * D);     // rows per 1 KiB DMA piece
+  constexpr int PPW = kBlock / RPP / NW;  // DMA pieces per wave per block
+  constexpr int VMB = NKS + PPW;          // vector-memory instructions per lane per block
+  constexpr int NBUF = 4;                 // blocks in flight
+  constexpr int VBYTES = kBlock * D * 2;
+  constexpr int LDP = kBlock + 8;         // P^T pitch [row][key]
+  constexpr int NDW = D / 16;             // waves that own a d-slice of O^T
+  constexpr int MERGE_BYTES = kMergeMaxLists * kIndexWideCap * 8;  // the largest list set of a row
+  static_assert(R <= 16, "16 rows per tile");
+  static_assert(PPW * RPP * NW == kBlock && CPR * RPP == 64, "the DMA pieces cover a block");
+  // the V ring: one array per slot, so that reading one slot is visibly
+  // independent of the DMA into the others; the list merge uses slots 0 and 1
+  // (scores, block ids) before the ring starts
+  constexpr int SLOT = VBYTES > MERGE_BYTES / 2 ? VBYTES : MERGE_BYTES / 2;
+  __shared__ __align__(16) char vr0[SLOT];
+  __shared__ __align__(16) char vr1[SLOT];
+  __shared__ __align__(16) char vr2[SLOT];
+  __shared__ __align__(16) char vr3[SLOT];
+  __shared__ __align__(16) T Ps[16 * LDP];
+  __shared__ float red_m[NW][16];
+  __shared__ float red_l[NW][16];
+  __shared__ int pos_s[64];
+  __shared__ int blk_s[64];
+  __shared__ int64_t off_s[64];
+  __shared__ int nv_s;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g4 = lane >> 4, l16 = lane & 15;
+  const float sl2 = p.scale_log2;
+  const int64_t row = blockIdx.x;  // (b * S_q + i) * G + g
+  const int g = (int)(row % p.G);
+  const int64_t bi = row / p.G;  // b * S_q + i
+  const int i = (int)(bi % p.S_q);
+  const int b = (int)(bi / p.S_q);
+  const int64_t t = first_pos(p.cm, p.q_offset, p.S_q, p.S_k, b) + i;
+  const int L = local_block(t);
+  const int slen = cache_len(p.cm, p.S_k, b);
+
+  // Q^T operand: Q[row l16][d 32 ks + 8 g4 ..] (rows past r repeat head 0, never stored)
+  frag qb[NKS];
+  {
+    const int qh = l16 < R ? l16 : 0;
+    const T* qp = (const T*)p.q + (bi * p.Hq + g * R + qh) * D;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) qb[ks] = *(const frag*)(qp + ks * 32 + g4 * 8);
+  }
+
+  // the row's selection (merged here from the split lists, or read) and its
+  // visible, mapped blocks in ascending order with their offsets
+  if (wave == 0) {
+    const int64_t srow = (((int64_t)b * p.G + g) * p.S_q + i) * p.topk;
+    pos_s[lane] = -1;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (p.lists_s) {
+      if (L >= 0) {
+        const int nl = L > 0 ? (L + p.list_chunk - 1) / p.list_chunk * p.list_lps : 0;
+        const int64_t base = row * p.list_stride * p.list_cap;
+        float* ss = (float*)vr0;
+        int* si = (int*)vr1;
+        const MergedSlot m =
+            merge_row_lists(p.lists_s + base, p.lists_i + base, nl, p.list_cap, min(p.topk - 1, L), L, ss, si, lane);
+        if (m.pos >= 0) {
+          p.sel_w[srow + m.pos] = m.id;
+          pos_s[m.pos] = m.id;
+        } else if (lane < p.topk) {
+          p.sel_w[srow + lane] = -1;
+        }
+      } else if (lane < p.topk) {
+        p.sel_w[srow + lane] = -1;
+      }
+    } else if (L >= 0 && lane < p.topk) {
+      pos_s[lane] = p.sel[srow + lane];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int c = lane < p.topk ? pos_s[lane] : -1;
+    const int64_t key0 = (int64_t)c * kBlock;
+    const bool ok = c >= 0 && c < p.nb && key0 <= t && key0 < slen && block_mapped(p.cm, b, c);
+    const uint64_t bal = __ballot(ok);
+    if (ok) {
+      const int ci = __popcll(bal & ((1ull << lane) - 1));
+      blk_s[ci] = c;
+      off_s[ci] = block_offset(p.cm, p.S_k, p.G, D, b, g, c);
+    }
+    if (lane == 0) nv_s = __popcll(bal);
+  }
+  __syncthreads();  // the selection is in LDS and the merge is done with the ring
+  const int nv = nv_s;
+
+  // 16-byte chunk c of row r of a V tile sits at chunk c ^ sw(r) (the swizzle of
+  // the backward's [row][d] tiles: the rows of one transposing read fall in
+  // distinct banks)
+  auto sw = [](int r) { return CPR == 16 ? (((r & 3) << 2) | ((r >> 2) & 3)) : (((r & 3) << 1) | ((r >> 2) & 1)); };
+  auto vat = [&](int r, int col) { return r * D + ((((col >> 3) ^ sw(r))) << 3) + (col & 7); };
+
+  // Issue block n: this wave's 16 K rows into kf and its PPW pieces of V into
+  // ring slot n % NBUF.  Past the row's blocks the loads read row 0 of the pool
+  // (valid memory, never used), so every block issues the same VMB
+  // instructions and the explicit waits below count them exactly.
+  auto issue = [&](int n, frag (&kf)[NKS], char* slot) {
+    const bool has = n < nv;
+    const int nc = min(n, 63);
+    const int64_t o = off_s[nc];  // read on every path (unused past the row's blocks)
+    const int c = blk_s[nc];
+    const int64_t kv0 = has ? o : 0;
+    const int rows_ok = has ? (int)min((int64_t)kBlock, (int64_t)slen - (int64_t)c * kBlock) : 1;
+    const int krow = min(wave * KPW + l16, rows_ok - 1);
+    const T* kp = (const T*)p.k + kv0 + (int64_t)krow * D;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) kf[ks] = *(const frag*)(kp + ks * 32 + g4 * 8);
+    const T* vb = (const T*)p.v + kv0;
+#pragma unroll
+    for (int u = 0; u < PPW; ++u) {
+      const int piece = wave * PPW + u;
+      const int r = piece * RPP + lane / CPR;
+      const int cq = (lane % CPR) ^ sw(r);
+      const int rs = min(r, rows_ok - 1);  // rows past the cache end re-read its last row (masked)
+      __builtin_amdgcn_global_load_lds((const void*)(vb + (int64_t)rs * D + cq * 8),
+                                       (__attribute__((address_space(3))) void*)(slot + piece * 1024), 16, 0, 0);
+    }
+  };
+
+  float m_run = kNegInf, l_run = 0.f;  // of row l16, the same in every lane of the row
+  f32x4 oacc = f32x4{};
+  auto step = [&](int n, const frag (&kf)[NKS], frag (&knext)[NKS], const char* cur, char* nxt) {
+    // block n's own loads are done (the two after it may still be in flight) ...
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm((NBUF - 2) * VMB));
+    // ... and every wave's: block n's V tile is in LDS, block n - 1 is done with its slot
+    lds_barrier();
+    issue(n + NBUF - 1, knext, nxt);  // into the slot and registers block n - 1 used
+    __builtin_amdgcn_sched_barrier(0);
+    const T* V = (const T*)cur;
+    const int64_t rel = t - (int64_t)blk_s[n] * kBlock;
+    const int lim = rel >= kBlock ? kBlock : (int)rel;
+    // S^T for keys [16 wave, 16 wave + 16): lane (row l16, group g4) holds keys 16 wave + 4 g4 + j
+    f32x4 sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[0], qb[0], f32x4{}, 0, 0, 0);
+#pragma unroll
+    for (int ks = 1; ks < NKS; ++ks) sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks], qb[ks], sacc, 0, 0, 0);
+    if (lim < kBlock - 1) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (wave * KPW + g4 * 4 + j > lim) sacc[j] = kNegInf;
+    }
+    float mw = fmaxf(fmaxf(sacc[0], sacc[1]), fmaxf(sacc[2], sacc[3]));
+    mw = fmaxf(mw, __shfl_xor(mw, 16));
+    mw = fmaxf(mw, __shfl_xor(mw, 32));
+    if (g4 == 0) red_m[wave][l16] = mw;
+    lds_barrier();
+    // key 0 of a visible block is visible, so the block maximum is finite
+    float mb = red_m[0][l16];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) mb = fmaxf(mb, red_m[w][l16]);
+    const float m_new = fmaxf(m_run, mb);
+    const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * sl2);  // 0 for the first block
+    const float moff = -m_new * sl2;
+    float lw = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[j], sl2, moff));
+      sacc[j] = e;
+      lw += e;
+    }
+    lw += __shfl_xor(lw, 16);
+    lw += __shfl_xor(lw, 32);
+    if (g4 == 0) red_l[wave][l16] = lw;
+    *(bf16x4*)&Ps[l16 * LDP + wave * KPW + g4 * 4] =
+        bf16x4{from_f32<T>(sacc[0]), from_f32<T>(sacc[1]), from_f32<T>(sacc[2]), from_f32<T>(sacc[3])};
+    lds_barrier();
+    float lb = red_l[0][l16];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) lb += red_l[w][l16];
+    l_run = l_run * alpha + lb;
+    m_run = m_new;
+    if (wave < NDW) {
+      oacc *= alpha;
+      // O^T slice d in [16 wave, 16 wave + 16): V^T rows read transposed from the
+      // row-major tile (keys 32 kk + 8 g4 + (0..7) at d 16 wave + l16), P^T rows
+      // straight from Ps
+#pragma unroll
+      for (int kk = 0; kk < kBlock / 32; ++kk) {
+        const int r0 = kk * 32 + g4 * 8 + (l16 >> 2), c0 = wave * 16 + 4 * (l16 & 3);
+        const frag va = __builtin_shufflevector(lds_read_tr(V + vat(r0, c0)), lds_read_tr(V + vat(r0 + 4, c0)), 0, 1,
+                                                2, 3, 4, 5, 6, 7);
+        const frag pb = *(const frag*)&Ps[l16 * LDP + kk * 32 + g4 * 8];
+        oacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, oacc, 0, 0, 0);
+      }
+    }
+  };
+
+  frag k0[NKS], k1[NKS], k2[NKS], k3[NKS];
+  static_assert(NBUF == 4, "four slots below");
+  issue(0, k0, vr0);
+  issue(1, k1, vr1);
+  issue(2, k2, vr2);
+  for (int n = 0; n < nv; n += 4) {
+    step(n, k0, k3, vr0, vr3);
+    if (n + 1 >= nv) break;
+    step(n + 1, k1, k0, vr1, vr0);
+    if (n + 2 >= nv) break;
+    step(n + 2, k2, k1, vr2, vr1);
+    if (n + 3 >= nv) break;
+    step(n + 3, k3, k2, vr3, vr2);
+  }
+  // no DMA may still be writing this workgroup's LDS when it ends
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+
+  if (wave < NDW && l16 < R) {
+    const bool any = m_run != kNegInf;  // false only for a row that sees no key
+    const float inv = any ? p.v_scale / l_run : 0.f;
+    const int64_t o = (bi * p.Hq + g * R + l16) * D + wave * 16 + g4 * 4;
+    if (p.out_f32) {
+      *(f32x4*)((float*)p.out + o) = f32x4{oacc[0] * inv, oacc[1] * inv, oacc[2] * inv, oacc[3] * inv};
+    } else {
+      *(bf16x4*)((T*)p.out + o) = bf16x4{from_f32<T>(oacc[0] * inv), from_f32<T>(oacc[1] * inv),
+                                         from_f32<T>(oacc[2] * inv), from_f32<T>(oacc[3] * inv)};
+    }
+    if (wave == 0 && g4 == 0 && p.lse)
+      p.lse[((int64_t)b * p.Hq + g * R + l16) * p.S_q + i] =
+          any ? (m_run * sl2 + __builtin_amdgcn_logf(l_run)) * 0.69314718055994531f : kNegInf;
+  }
+}
+
 // Merge the partial states of one (token, group) over its selected slots:
 // out = sum_s 2^(lse_s - M) o_s / sum_s 2^(lse_s - M), M = max_s lse_s.
 // A thread owns one 16-byte chunk of the lane-native partial layout (E values
@@ -1035,8 +1299,11 @@ static hipError_t launch_attn_t(const AttnParams& p, hipStream_t s, const Kernel
   if constexpr (std::is_same<T, bf16>::value) {
     if (p.rows_mode) {  // the whole main branch in one launch, no combine
       timer_start(tm, kKernAttention, s);
-      hipLaunchKernelGGL((attn_decode_rows_kernel<S, D, R>), dim3((unsigned)((int64_t)p.B * p.S_q * p.G)), dim3(512),
-                         0, s, p);
+      const dim3 rgrid((unsigned)((int64_t)p.B * p.S_q * p.G));
+      if constexpr (std::is_same<S, T>::value && R <= 16)
+        hipLaunchKernelGGL((attn_decode_rows16_kernel<D, R>), rgrid, dim3(512), 0, s, p);
+      else
+        hipLaunchKernelGGL((attn_decode_rows_kernel<S, D, R>), rgrid, dim3(512), 0, s, p);
       timer_stop(tm, kKernAttention, s);
       return hipGetLastError();
     }
