@@ -995,13 +995,18 @@ __global__ __launch_bounds__(512) void attn_decode_rows16_kernel(AttnParams p) {
   // ring slot n % NBUF.  Past the row's blocks the loads read row 0 of the pool
   // (valid memory, never used), so every block issues the same VMB
   // instructions and the explicit waits below count them exactly.
+  // lane j holds block j's element offset and rows (past the row's blocks:
+  // offset 0 and one row), read by block index with readlane, so issuing a
+  // block needs no LDS read
+  const int64_t lane_off = lane < nv ? off_s[lane] : 0;
+  const int lane_rows = lane < nv ? (int)min((int64_t)kBlock, (int64_t)slen - (int64_t)blk_s[lane] * kBlock) : 1;
   auto issue = [&](int n, frag (&kf)[NKS], char* slot) {
-    const bool has = n < nv;
-    const int nc = min(n, 63);
-    const int64_t o = off_s[nc];  // read on every path (unused past the row's blocks)
-    const int c = blk_s[nc];
-    const int64_t kv0 = has ? o : 0;
-    const int rows_ok = has ? (int)min((int64_t)kBlock, (int64_t)slen - (int64_t)c * kBlock) : 1;
+    // n >= nv reads lane 63: offset 0 and one row, or with 64 blocks the last
+    // block (valid memory either way; the slot is never read)
+    const int nl = n < nv ? n : 63;
+    const int64_t kv0 = ((int64_t)__builtin_amdgcn_readlane((int)(lane_off >> 32), nl) << 32) |
+                        (uint32_t)__builtin_amdgcn_readlane((int)lane_off, nl);
+    const int rows_ok = __builtin_amdgcn_readlane(lane_rows, nl);
     const int krow = min(wave * KPW + l16, rows_ok - 1);
     const T* kp = (const T*)p.k + kv0 + (int64_t)krow * D;
 #pragma unroll
