@@ -876,41 +876,52 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const bf16* ptr) {
 // needs before its first barrier.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// Decode rows form for native bf16 caches and r <= 16: one workgroup per
-// (b, i, g) row, as attn_decode_rows_kernel, but all 8 waves work on one block
-// at a time so that a row keeps NBUF blocks in flight.  Each wave scores 16 of
-// the block's keys with 16x16x32 MFMA tiles (K read straight from HBM as the
-// A operand, 16 VGPRs per block), V goes from HBM into a ring of NBUF LDS
-// tiles by DMA (no registers), and wave w accumulates the d-slice
-// [16w, 16w + 16) of O^T, its V^T operand read from the row-major V tile with
-// transposing LDS reads.  Row maxima and sums meet in LDS; O^T is rescaled by
+// Decode rows form for r <= 16: one workgroup per (b, i, g) row, as
+// attn_decode_rows_kernel, but all 8 waves work on one block at a time so that
+// a row keeps NBUF blocks in flight.  Each wave scores 16 of the block's keys
+// with 16x16x32 MFMA tiles (K read straight from HBM as the A operand: 16
+// VGPRs per block, 8 for e4m3), V goes from HBM into a ring of NBUF LDS tiles
+// by DMA (no registers), and wave w accumulates the d-slice [16w, 16w + 16) of
+// O^T, its V^T operand read from a row-major bf16 V tile with transposing LDS
+// reads (native keys: the ring slot itself; e4m3: a tile the block's bytes are
+// widened into first).  Row maxima and sums meet in LDS; O^T is rescaled by
 // 2^(m_old - m_new) as the running maximum grows.
-template <int D, int R>
+template <typename S, int D, int R>
 __global__ __launch_bounds__(512) void attn_decode_rows16_kernel(AttnParams p) {
   using T = bf16;
   typedef bf16x8 frag;
+  constexpr bool kNative = std::is_same<S, T>::value;
+  typedef typename std::conditional<kNative, frag, uint2>::type kraw;  // 8 elements of S
+  constexpr int SB = (int)sizeof(S);
   constexpr int NW = 8;                   // waves
   constexpr int KPW = kBlock / NW;        // keys per wave (16)
   constexpr int NKS = D / 32;             // k-steps of S^T = K Q^T
-  constexpr int CPR = D / 8;              // 16-byte chunks per K / V row
-  constexpr int RPP = 1024 / (2 * D);     // rows per 1 KiB DMA piece
+  constexpr int CPR = D / 8;              // 16-byte chunks per row of the bf16 V tile
+  constexpr int SCPR = D * SB / 16;       // 16-byte chunks per row of a stored V block
+  constexpr int RPP = 1024 / (D * SB);    // stored rows per 1 KiB DMA piece
   constexpr int PPW = kBlock / RPP / NW;  // DMA pieces per wave per block
   constexpr int VMB = NKS + PPW;          // vector-memory instructions per lane per block
   constexpr int NBUF = 4;                 // blocks in flight
-  constexpr int VBYTES = kBlock * D * 2;
+  constexpr int VBYTES = kBlock * D * SB; // one stored V block
+  constexpr int TBYTES = kBlock * D * 2;  // the bf16 V tile
   constexpr int LDP = kBlock + 8;         // P^T pitch [row][key]
   constexpr int NDW = D / 16;             // waves that own a d-slice of O^T
   constexpr int MERGE_BYTES = kMergeMaxLists * kIndexWideCap * 8;  // the largest list set of a row
+  constexpr int HALF = MERGE_BYTES / 2;
   static_assert(R <= 16, "16 rows per tile");
-  static_assert(PPW * RPP * NW == kBlock && CPR * RPP == 64, "the DMA pieces cover a block");
+  static_assert(PPW * RPP * NW == kBlock && SCPR * RPP == 64, "the DMA pieces cover a block");
   // the V ring: one array per slot, so that reading one slot is visibly
-  // independent of the DMA into the others; the list merge uses slots 0 and 1
-  // (scores, block ids) before the ring starts
-  constexpr int SLOT = VBYTES > MERGE_BYTES / 2 ? VBYTES : MERGE_BYTES / 2;
-  __shared__ __align__(16) char vr0[SLOT];
-  __shared__ __align__(16) char vr1[SLOT];
-  __shared__ __align__(16) char vr2[SLOT];
-  __shared__ __align__(16) char vr3[SLOT];
+  // independent of the DMA into the others.  The list merge (scores, block
+  // ids) runs before the ring starts, in slot 0 and slot 1 (native) or the
+  // bf16 tile (e4m3).
+  constexpr int S0 = VBYTES > HALF ? VBYTES : HALF;
+  constexpr int S1 = kNative ? S0 : VBYTES;
+  constexpr int STB = kNative ? 16 : (TBYTES > HALF ? TBYTES : HALF);
+  __shared__ __align__(16) char vr0[S0];
+  __shared__ __align__(16) char vr1[S1];
+  __shared__ __align__(16) char vr2[VBYTES];
+  __shared__ __align__(16) char vr3[VBYTES];
+  __shared__ __align__(16) char vtb[STB];
   __shared__ __align__(16) T Ps[16 * LDP];
   __shared__ float red_m[NW][16];
   __shared__ float red_l[NW][16];
@@ -953,7 +964,7 @@ __global__ __launch_bounds__(512) void attn_decode_rows16_kernel(AttnParams p) {
         const int nl = L > 0 ? (L + p.list_chunk - 1) / p.list_chunk * p.list_lps : 0;
         const int64_t base = row * p.list_stride * p.list_cap;
         float* ss = (float*)vr0;
-        int* si = (int*)vr1;
+        int* si = (int*)(kNative ? vr1 : vtb);
         const MergedSlot m =
             merge_row_lists(p.lists_s + base, p.lists_i + base, nl, p.list_cap, min(p.topk - 1, L), L, ss, si, lane);
         if (m.pos >= 0) {
@@ -992,15 +1003,16 @@ __global__ __launch_bounds__(512) void attn_decode_rows16_kernel(AttnParams p) {
   auto vat = [&](int r, int col) { return r * D + ((((col >> 3) ^ sw(r))) << 3) + (col & 7); };
 
   // Issue block n: this wave's 16 K rows into kf and its PPW pieces of V into
-  // ring slot n % NBUF.  Past the row's blocks the loads read row 0 of the pool
-  // (valid memory, never used), so every block issues the same VMB
-  // instructions and the explicit waits below count them exactly.
+  // ring slot n % NBUF (native keys in the bf16 tile's swizzled layout, e4m3
+  // as stored).  Past the row's blocks the loads read row 0 of the pool (valid
+  // memory, never used), so every block issues the same VMB instructions and
+  // the explicit waits below count them exactly.
   // lane j holds block j's element offset and rows (past the row's blocks:
   // offset 0 and one row), read by block index with readlane, so issuing a
   // block needs no LDS read
   const int64_t lane_off = lane < nv ? off_s[lane] : 0;
   const int lane_rows = lane < nv ? (int)min((int64_t)kBlock, (int64_t)slen - (int64_t)blk_s[lane] * kBlock) : 1;
-  auto issue = [&](int n, frag (&kf)[NKS], char* slot) {
+  auto issue = [&](int n, kraw (&kf)[NKS], char* slot) {
     // n >= nv reads lane 63: offset 0 and one row, or with 64 blocks the last
     // block (valid memory either way; the slot is never read)
     const int nl = n < nv ? n : 63;
@@ -1008,24 +1020,24 @@ __global__ __launch_bounds__(512) void attn_decode_rows16_kernel(AttnParams p) {
                         (uint32_t)__builtin_amdgcn_readlane((int)lane_off, nl);
     const int rows_ok = __builtin_amdgcn_readlane(lane_rows, nl);
     const int krow = min(wave * KPW + l16, rows_ok - 1);
-    const T* kp = (const T*)p.k + kv0 + (int64_t)krow * D;
+    const S* kp = (const S*)p.k + kv0 + (int64_t)krow * D;
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) kf[ks] = *(const frag*)(kp + ks * 32 + g4 * 8);
-    const T* vb = (const T*)p.v + kv0;
+    for (int ks = 0; ks < NKS; ++ks) kf[ks] = *(const kraw*)(kp + ks * 32 + g4 * 8);
+    const char* vb = (const char*)((const S*)p.v + kv0);
 #pragma unroll
     for (int u = 0; u < PPW; ++u) {
       const int piece = wave * PPW + u;
-      const int r = piece * RPP + lane / CPR;
-      const int cq = (lane % CPR) ^ sw(r);
+      const int r = piece * RPP + lane / SCPR;
+      const int cq = kNative ? (lane % SCPR) ^ sw(r) : lane % SCPR;
       const int rs = min(r, rows_ok - 1);  // rows past the cache end re-read its last row (masked)
-      __builtin_amdgcn_global_load_lds((const void*)(vb + (int64_t)rs * D + cq * 8),
+      __builtin_amdgcn_global_load_lds((const void*)(vb + ((int64_t)rs * D * SB + cq * 16)),
                                        (__attribute__((address_space(3))) void*)(slot + piece * 1024), 16, 0, 0);
     }
   };
 
   float m_run = kNegInf, l_run = 0.f;  // of row l16, the same in every lane of the row
   f32x4 oacc = f32x4{};
-  auto step = [&](int n, const frag (&kf)[NKS], frag (&knext)[NKS], const char* cur, char* nxt) {
+  auto step = [&](int n, const kraw (&kf)[NKS], kraw (&knext)[NKS], const char* cur, char* nxt) {
     // block n's own loads are done (the two after it may still be in flight) ...
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(vmcnt_imm((NBUF - 2) * VMB));
@@ -1033,13 +1045,32 @@ __global__ __launch_bounds__(512) void attn_decode_rows16_kernel(AttnParams p) {
     lds_barrier();
     issue(n + NBUF - 1, knext, nxt);  // into the slot and registers block n - 1 used
     __builtin_amdgcn_sched_barrier(0);
-    const T* V = (const T*)cur;
+    const T* V = (const T*)(kNative ? cur : vtb);
+    if constexpr (!kNative) {
+      // widen the block's e4m3 values (exact) into the bf16 tile; its readers
+      // come after the next barrier, its previous readers were before the last
+      constexpr int NCV = kBlock * SCPR / 512;
+#pragma unroll
+      for (int u = 0; u < NCV; ++u) {
+        const int q = tid + u * 512;
+        const int r = q / SCPR, c = q % SCPR;
+        const i32x4 x = *(const i32x4*)(cur + r * (D * SB) + c * 16);
+        const uint2 w0 = e4m3x4_to_bf16((uint32_t)x[0]), w1 = e4m3x4_to_bf16((uint32_t)x[1]);
+        const uint2 w2 = e4m3x4_to_bf16((uint32_t)x[2]), w3 = e4m3x4_to_bf16((uint32_t)x[3]);
+        *(i32x4*)((T*)vtb + vat(r, c * 16)) = i32x4{(int)w0.x, (int)w0.y, (int)w1.x, (int)w1.y};
+        *(i32x4*)((T*)vtb + vat(r, c * 16 + 8)) = i32x4{(int)w2.x, (int)w2.y, (int)w3.x, (int)w3.y};
+      }
+    }
     const int64_t rel = t - (int64_t)blk_s[n] * kBlock;
     const int lim = rel >= kBlock ? kBlock : (int)rel;
     // S^T for keys [16 wave, 16 wave + 16): lane (row l16, group g4) holds keys 16 wave + 4 g4 + j
-    f32x4 sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[0], qb[0], f32x4{}, 0, 0, 0);
+    auto kfrag = [&](int ks) -> frag {
+      if constexpr (kNative) return kf[ks];
+      else return __builtin_bit_cast(frag, ChunkIO<T, S>::widen(kf[ks]));
+    };
+    f32x4 sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kfrag(0), qb[0], f32x4{}, 0, 0, 0);
 #pragma unroll
-    for (int ks = 1; ks < NKS; ++ks) sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks], qb[ks], sacc, 0, 0, 0);
+    for (int ks = 1; ks < NKS; ++ks) sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kfrag(ks), qb[ks], sacc, 0, 0, 0);
     if (lim < kBlock - 1) {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
@@ -1091,7 +1122,7 @@ __global__ __launch_bounds__(512) void attn_decode_rows16_kernel(AttnParams p) {
     }
   };
 
-  frag k0[NKS], k1[NKS], k2[NKS], k3[NKS];
+  kraw k0[NKS], k1[NKS], k2[NKS], k3[NKS];
   static_assert(NBUF == 4, "four slots below");
   issue(0, k0, vr0);
   issue(1, k1, vr1);
@@ -1305,8 +1336,8 @@ static hipError_t launch_attn_t(const AttnParams& p, hipStream_t s, const Kernel
     if (p.rows_mode) {  // the whole main branch in one launch, no combine
       timer_start(tm, kKernAttention, s);
       const dim3 rgrid((unsigned)((int64_t)p.B * p.S_q * p.G));
-      if constexpr (std::is_same<S, T>::value && R <= 16)
-        hipLaunchKernelGGL((attn_decode_rows16_kernel<D, R>), rgrid, dim3(512), 0, s, p);
+      if constexpr (R <= 16)
+        hipLaunchKernelGGL((attn_decode_rows16_kernel<S, D, R>), rgrid, dim3(512), 0, s, p);
       else
         hipLaunchKernelGGL((attn_decode_rows_kernel<S, D, R>), rgrid, dim3(512), 0, s, p);
       timer_stop(tm, kKernAttention, s);
