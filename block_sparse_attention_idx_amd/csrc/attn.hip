@@ -167,7 +167,8 @@ __global__ __launch_bounds__(1024) void gather_scan_kernel(AttnParams p) {
 }
 
 template <typename T, typename S, int D, int R>
-__global__ __launch_bounds__(256, 2) void attn_kvouter_kernel(AttnParams p) {
+// two workgroups per CU for bf16; the fp32 form (correctness path) takes the registers of one
+__global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void attn_kvouter_kernel(AttnParams p) {
   using M = Mma<T>;
   using IO = ChunkIO<T, S>;
   using frag = typename M::frag;

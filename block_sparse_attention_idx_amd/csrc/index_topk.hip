@@ -163,7 +163,7 @@ __global__ __launch_bounds__(1024) void index_units_kernel(IndexParams p) {
 }
 
 template <typename T, typename S, int DI, int CAP, int RT>
-__global__ __launch_bounds__(256, CAP == kIndexWideCap ? 1 : 2) void index_topk_kernel(IndexParams p) {
+__global__ __launch_bounds__(256, CAP == kIndexWideCap || sizeof(T) != 2 ? 1 : 2) void index_topk_kernel(IndexParams p) {
   using M = Mma<T>;
   using frag = typename M::frag;
   constexpr int KPL = M::KPL, KSTEP = M::KSTEP, NKS = DI / KSTEP;

@@ -93,7 +93,8 @@ __device__ __forceinline__ float token_max(float x) {
 }
 
 template <typename T, typename S, int D, int R, int DI>
-__global__ __launch_bounds__(256, 2) void kl_teacher_kernel(AttnParams p, KlParams kp) {
+// two workgroups per CU for bf16; the fp32 form (correctness path) takes the registers of one
+__global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void kl_teacher_kernel(AttnParams p, KlParams kp) {
   using M = Mma<T>;
   using IO = ChunkIO<T, S>;
   using frag = typename M::frag;
