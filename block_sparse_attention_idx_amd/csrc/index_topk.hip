@@ -113,7 +113,59 @@ __device__ __forceinline__ void emit_half_list(const IndexParams& p, int64_t row
 // each XCD a contiguous run of units (one key range, many row tiles) whose
 // k_idx range stays in its L2; without splits, heavy_first puts the tiles with
 // the most causal blocks first.
+// Unit lin of the packed unit list, derived by the calling wave from the
+// sequence lengths (the few-row form, one row tile per sequence): lane j counts
+// the busy splits of sequences PER j .. PER j + PER - 1, loaded together; a
+// wave-wide inclusive scan orders the counts by sequence, a ballot finds the
+// lane whose range holds lin, and that lane walks its own sequences.  The same
+// units in the same order as index_units_kernel writes, without its launch and
+// the two dependent loads of its list.
+__device__ __forceinline__ bool inline_unit(const IndexParams& p, int lin, int& b, int& split) {
+  constexpr int PER = kInlineUnitsPerLane;
+  const int lane = threadIdx.x & 63;
+  int cnt[PER];
+  int sum = 0;
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int bb = lane * PER + u;
+    int c = 0;
+    if (bb < p.B) {
+      if (p.nsplit == 1) {
+        c = 1;
+      } else {
+        const int L = local_block(first_pos(p.cm, p.q_offset, p.S_q, p.S_k, bb) + (p.rows_per_b - 1) / p.G);
+        c = L > 0 ? (L + p.chunk - 1) / p.chunk : 0;
+      }
+    }
+    cnt[u] = c;
+    sum += c;
+  }
+  int incl = sum;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(incl, off);
+    if (lane >= off) incl += o;
+  }
+  if (lin >= __shfl(incl, 63)) return false;
+  const int owner = __popcll(__ballot(incl <= lin));  // lanes whose units all precede lin
+  int r = lin - (incl - sum), sb = 0, ss = 0;
+  bool found = false;
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    if (!found && r < cnt[u]) {
+      found = true;
+      sb = lane * PER + u;
+      ss = r;
+    }
+    r -= cnt[u];
+  }
+  b = __shfl(sb, owner);
+  split = __shfl(ss, owner);
+  return true;
+}
+
 __device__ __forceinline__ bool unit_of(const IndexParams& p, int lin, bool heavy_first, int& tg, int& split) {
+  if (p.units_inline) return inline_unit(p, lin, tg, split);  // one row tile per sequence: tg = b
   if (p.units) {
     if (lin >= *p.unit_count) return false;
     const int u = p.units[lin];

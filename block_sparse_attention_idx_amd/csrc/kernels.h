@@ -92,12 +92,17 @@ struct IndexParams {
   // (row tile << 7) | split by index_units_kernel, and their number.  Null otherwise.
   int32_t* units;
   int32_t* unit_count;
+  // With per-sequence lengths in the few-row form and B <= 64 * kInlineUnitsPerLane:
+  // each wave finds its unit from the lengths itself (units and unit_count null).
+  int units_inline;
   int merge_in_consumer;  // host only: the lists are merged by the decode rows kernel, not topk_merge_kernel
 };
 
 // At most this many (row, group) pairs per sequence: the index kernel's
 // few-row form (each wave ranks whole blocks on its own).
 constexpr int kIndexSmallRows = 32;
+// Sequences per lane when a wave derives its unit from the lengths (B <= 256).
+constexpr int kInlineUnitsPerLane = 4;
 
 // Top lists hold up to k - 1 entries: 15 (k <= 16), 31 (k <= 32) or 63
 // (k <= 64).  Lists of 63 (the wide form) are not merged inside the index

@@ -213,6 +213,9 @@ IndexPlan plan_index(const msa_shape* s, const msa_kv_cache* cache) {
     off += align_up(entries * 4);
   }
   ip.unit_list = cache && cache->seq_lens;  // work per sequence known only on the device
+  // the few-row form (one row tile per sequence) derives its units in the kernel
+  p.units_inline = ip.unit_list && p.small && p.ntile == 1 && p.B <= 64 * msa::kInlineUnitsPerLane ? 1 : 0;
+  if (p.units_inline) ip.unit_list = false;
   if (ip.unit_list) {
     ip.off_units = off;
     off += align_up((size_t)p.nunits * 4);
