@@ -197,3 +197,36 @@ def test_paged_decode_workload_sampled():
     err = float(np.abs(out[picks].float().cpu().numpy() - ref_out).max())
     print(f"  max abs err {err:.3e}", flush=True)
     assert err <= TOL
+
+
+@pytest.mark.parametrize("B,paged", [(256, True), (300, True), (256, False), (300, False)])
+def test_decode_batch_around_the_in_kernel_unit_limit(B, paged):
+    # few-row index form with per-sequence lengths: up to 256 sequences each wave
+    # derives its key-split unit from the lengths; beyond that a unit list is built
+    msa = _msa()
+    rng = np.random.default_rng(B + 7 * paged)
+    lens = [int(v) for v in rng.integers(1, 2500, B)]
+    lens[:4] = [1, 128, 129, 2499]
+    print(f"decode batch B={B} paged={paged}", flush=True)
+    if paged:
+        case = (lens, 1, 4, 2, 64, 32, 8, "native", 5)
+        s, table, P, xh = _paged(case, 900 + B)
+        pt = torch.from_numpy(table).cuda()
+    else:
+        s = synth.Shape(B, 1, max(lens) + 3, 0, 4, 2, 64, 32, 8)
+        xh = synth.host_inputs(s, 900 + B)
+        pt = None
+    x = {n: t.cuda() for n, t in xh.items()}
+    sl = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    out, sel, lse = msa.fwd_kvcache(x["q"], x["k"], x["v"], x["q_idx"], x["k_idx"], s.topk, seq_lens=sl,
+                                    page_table=pt, return_sel=True, return_lse=True)
+    torch.cuda.synchronize()
+    if paged:
+        ref = _paged_oracle(s, lens, table, xh)
+    else:
+        f = {n: synth.as_f64(t) for n, t in xh.items()}
+        ks = [f["k"][b, :, :n] for b, n in enumerate(lens)]
+        vs = [f["v"][b, :, :n] for b, n in enumerate(lens)]
+        kis = [f["k_idx"][b, :n] for b, n in enumerate(lens)]
+        ref = orc.msa_forward_varlen(f["q"], ks, vs, f["q_idx"], kis, s.topk)
+    _compare(out, sel, lse, *ref)
