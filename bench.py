@@ -328,16 +328,21 @@ def step_stats(step_ms):
     return {"ms_p50": round(float(np.median(step_ms)), 4), "ms_p99": round(float(np.percentile(step_ms, 99)), 4)}
 
 
-def decode_leg(msa, wid: int, args):
+DECODE_WORKLOADS = (4, 6, 7)
+
+
+def decode_leg(msa, wid: int, args, steps=None, graph=True):
     """One decode workload: GB/s of algorithmic bytes, and the k_idx scan kernel
-    (the index kernel) against the HBM roofline."""
+    (the index kernel) against the HBM roofline.  steps defaults to --decode-steps;
+    graph=False skips the HIP-graph replays."""
+    steps = args.decode_steps if steps is None else steps
     sd = synth.WORKLOADS[wid]
     name = synth.WORKLOAD_NAMES[wid]
     print(f"[bench] {name}: generating inputs", file=sys.stderr, flush=True)
     drun = Runner(msa, sd, wid)
     paged = drun.cache is not None
     dec_bytes = paged_decode_bytes(sd, drun.lens) if paged else algorithmic_work(sd)[2]
-    dms, idx_ms = drun.time_steps(args.decode_steps, args.warmup, "index_score")
+    dms, idx_ms = drun.time_steps(steps, args.warmup, "index_score")
     stats = step_stats(drun.step_ms)
     dk = {} if args.no_breakdown else drun.kernel_breakdown()
     gbs = dec_bytes / (dms * 1e-3) / 1e9
@@ -348,7 +353,7 @@ def decode_leg(msa, wid: int, args):
                7: "index_topk_decode_paged_varlen_b64_hbm.md"}[wid]
     res = {
         "workload": name, "value": round(gbs, 1), "unit": "GB/s",
-        "ms_per_step": round(dms, 4), **stats, "steps": args.decode_steps, "bytes_per_step": dec_bytes,
+        "ms_per_step": round(dms, 4), **stats, "steps": steps, "bytes_per_step": dec_bytes,
         "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
         "roofline": {"bound": "hbm", "kernel": "index_topk", "achieved": round(kidx_bytes / (idx_avg * 1e-3) / 1e9, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -359,10 +364,11 @@ def decode_leg(msa, wid: int, args):
     }
     if paged:
         res["cache_tokens"] = {"total": kidx_tokens, "min": int(drun.lens.min()), "max": int(drun.lens.max())}
-    # the same call replayed from a HIP graph (launch gaps between its kernels removed)
-    gms = drun.graph_time(args.decode_steps, args.warmup)
-    res["graph"] = {"ms_per_step": round(gms, 4), "value": round(dec_bytes / (gms * 1e-3) / 1e9, 1),
-                    "frac_of_hbm_peak": round(dec_bytes / (gms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    if graph:
+        # the same call replayed from a HIP graph (launch gaps between its kernels removed)
+        gms = drun.graph_time(steps, args.warmup)
+        res["graph"] = {"ms_per_step": round(gms, 4), "value": round(dec_bytes / (gms * 1e-3) / 1e9, 1),
+                        "frac_of_hbm_peak": round(dec_bytes / (gms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
     del drun
     torch.cuda.empty_cache()
     return res
@@ -484,6 +490,25 @@ def main():
         print("[bench] copy calibration: 4 copies of 1073741824 bytes", file=sys.stderr, flush=True)
     wid = args.workload
     s = synth.WORKLOADS[wid]
+    if wid in DECODE_WORKLOADS:
+        # a decode workload on its own: its GB/s line (the k_idx scan's HBM roofline)
+        leg = decode_leg(msa, wid, args, steps=args.steps, graph=not args.no_breakdown)
+        result = {"metric": METRIC, "value": leg["value"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+                  "warmup": args.warmup, "ms_per_step": leg["ms_per_step"],
+                  **{k: leg[k] for k in ("ms_p50", "ms_p99") if k in leg},
+                  "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+                  "data": "synthetic",
+                  "config": {"workload": leg["workload"], "batch": s.batch, "q_len": s.q_len, "kv_len": s.kv_len,
+                             "num_q_heads": s.num_q_heads, "num_kv_heads": s.num_kv_heads, "head_dim": s.head_dim,
+                             "index_dim": s.index_dim, "block_size": s.block_size, "topk": s.topk,
+                             "cache": "e4m3" if s.fp8 else "bf16"},
+                  "roofline": leg["roofline"], "frac_of_hbm_peak": leg["frac_of_hbm_peak"],
+                  "kernels_ms": leg["kernels_ms"], "cpu_baseline": None}
+        for k in ("cache_tokens", "graph"):
+            if k in leg:
+                result[k] = leg[k]
+        print(json.dumps(result))
+        return
     flop_main, flop_index, _ = algorithmic_work(s)
     print(f"[bench] {synth.WORKLOAD_NAMES[wid]}: generating inputs", file=sys.stderr, flush=True)
     run = Runner(msa, s, wid)
