@@ -166,6 +166,22 @@ class Runner:
         if st != 0:
             raise RuntimeError(self.L.msa_last_error().decode())
 
+    def clean_time(self, steps, warmup):
+        """ms per step over exactly `steps` calls with nothing recorded between them:
+        one event pair around the whole timed region, synchronised on both sides.
+        (An event recorded between steps or around a kernel adds a few microseconds
+        of its own, which would be charged to short decode steps.)"""
+        for _ in range(warmup):
+            self.step()
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record(self.stream)
+        for _ in range(steps):
+            self.step()
+        t1.record(self.stream)
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / steps
+
     def time_steps(self, steps, warmup, timed_kernel=None):
         """Returns (ms per step, list of per-step ms of timed_kernel or None).  The
         per-step times of the last call are kept in self.step_ms."""
@@ -342,7 +358,8 @@ def decode_leg(msa, wid: int, args, steps=None, graph=True):
     drun = Runner(msa, sd, wid)
     paged = drun.cache is not None
     dec_bytes = paged_decode_bytes(sd, drun.lens) if paged else algorithmic_work(sd)[2]
-    dms, idx_ms = drun.time_steps(steps, args.warmup, "index_score")
+    dms = drun.clean_time(steps, args.warmup)
+    _, idx_ms = drun.time_steps(steps, 0, "index_score")  # per-step and per-kernel events
     stats = step_stats(drun.step_ms)
     dk = {} if args.no_breakdown else drun.kernel_breakdown()
     gbs = dec_bytes / (dms * 1e-3) / 1e9
@@ -513,7 +530,8 @@ def main():
     print(f"[bench] {synth.WORKLOAD_NAMES[wid]}: generating inputs", file=sys.stderr, flush=True)
     run = Runner(msa, s, wid)
     print("[bench] timing msa_fwd", file=sys.stderr, flush=True)
-    ms, attn_ms = run.time_steps(args.steps, args.warmup, "attention")
+    ms = run.clean_time(args.steps, args.warmup)
+    _, attn_ms = run.time_steps(args.steps, 0, "attention")  # per-step and per-kernel events
     stats = step_stats(run.step_ms)
     kern = {} if args.no_breakdown else run.kernel_breakdown()
     attn_avg = float(np.mean(attn_ms))
@@ -580,7 +598,8 @@ def main():
             fm, fi, _ = algorithmic_work(se)
             print(f"[bench] {synth.WORKLOAD_NAMES[ew]}: generating inputs", file=sys.stderr, flush=True)
             er = Runner(msa, se, ew)
-            ems, eatt = er.time_steps(10, 2, "attention")
+            ems = er.clean_time(10, 2)
+            eatt = er.time_steps(10, 0, "attention")[1]
             eidx = er.time_steps(5, 0, "index_score")[1]
             eatt_ms, eidx_ms = float(np.mean(eatt)), float(np.median(eidx))
             result["extra"][synth.WORKLOAD_NAMES[ew]] = {
