@@ -166,18 +166,39 @@ class Runner:
         if st != 0:
             raise RuntimeError(self.L.msa_last_error().decode())
 
-    def clean_time(self, steps, warmup):
+    def layer_copies(self, n):
+        """Argument lists of n more calls over copies of this workload's inputs (the
+        same values in other buffers), as the same step of other layers would be."""
+        copies = []
+        for _ in range(n):
+            xc = {k: t.clone() for k, t in self.x.items()}
+            a = list(self.args)
+            for j, name in enumerate(("q", "k", "v", "q_idx", "k_idx")):
+                a[2 + j] = ctypes.c_void_p(xc[name].data_ptr())
+            copies.append((xc, a))
+        return copies
+
+    def clean_time(self, steps, warmup, layers=()):
         """ms per step over exactly `steps` calls with nothing recorded between them:
         one event pair around the whole timed region, synchronised on both sides.
         (An event recorded between steps or around a kernel adds a few microseconds
-        of its own, which would be charged to short decode steps.)"""
-        for _ in range(warmup):
-            self.step()
+        of its own, which would be charged to short decode steps.)  With `layers`
+        (from layer_copies) consecutive calls take this workload's inputs and the
+        copies in turn, so no call finds the previous call's K/V in the caches."""
+        arglists = [self.args] + [a for _, a in layers]
+        fn = self.L.msa_fwd_kvcache
+
+        def call(n):
+            if fn(*arglists[n % len(arglists)]) != 0:
+                raise RuntimeError(self.L.msa_last_error().decode())
+
+        for n in range(warmup):
+            call(n)
         torch.cuda.synchronize()
         t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t0.record(self.stream)
-        for _ in range(steps):
-            self.step()
+        for n in range(steps):
+            call(n)
         t1.record(self.stream)
         torch.cuda.synchronize()
         return t0.elapsed_time(t1) / steps
@@ -345,6 +366,7 @@ def step_stats(step_ms):
 
 
 DECODE_WORKLOADS = (4, 6, 7)
+DECODE_LAYERS = 4  # input copies the decode step rotates through
 
 
 def decode_leg(msa, wid: int, args, steps=None, graph=True):
@@ -358,7 +380,11 @@ def decode_leg(msa, wid: int, args, steps=None, graph=True):
     drun = Runner(msa, sd, wid)
     paged = drun.cache is not None
     dec_bytes = paged_decode_bytes(sd, drun.lens) if paged else algorithmic_work(sd)[2]
-    dms = drun.clean_time(steps, args.warmup)
+    # decode steps of four layers in turn: a 128K x 64 step reads 0.3 GB of K/V that
+    # the 256 MB Infinity Cache could otherwise keep from one repeat of it to the next
+    layers = drun.layer_copies(DECODE_LAYERS - 1)
+    dms = drun.clean_time(steps, args.warmup, layers)
+    del layers
     _, idx_ms = drun.time_steps(steps, 0, "index_score")  # per-step and per-kernel events
     stats = step_stats(drun.step_ms)
     dk = {} if args.no_breakdown else drun.kernel_breakdown()
