@@ -514,7 +514,7 @@ def main():
                     help="first run 4 plain device copies of 1 GiB (known bytes, for scaling HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only: this MSA build has no multi-GPU path (asked for --gpus {args.gpus})",
+        print(f"bench.py runs on one GPU only: the MSA library has no multi-GPU path (asked for --gpus {args.gpus})",
               file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():

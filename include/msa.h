@@ -78,7 +78,7 @@ extern "C" {
 typedef enum {
   MSA_OK = 0,
   MSA_ERR_INVALID = -1,      /* a null pointer, a negative or inconsistent size */
-  MSA_ERR_UNSUPPORTED = -2,  /* a valid shape this build has no kernel for      */
+  MSA_ERR_UNSUPPORTED = -2,  /* a valid shape the library has no kernel for    */
   MSA_ERR_WORKSPACE = -3,    /* workspace missing, too small or misaligned      */
   MSA_ERR_HIP = -4           /* a HIP launch or runtime call failed             */
 } msa_status;
