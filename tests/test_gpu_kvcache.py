@@ -230,3 +230,35 @@ def test_decode_batch_around_the_in_kernel_unit_limit(B, paged):
         kis = [f["k_idx"][b, :n] for b, n in enumerate(lens)]
         ref = orc.msa_forward_varlen(f["q"], ks, vs, f["q_idx"], kis, s.topk)
     _compare(out, sel, lse, *ref)
+
+
+@pytest.mark.parametrize("paged", [True, False])
+def test_decode_batch_of_short_caches_one_split(paged):
+    # every cache under 15 blocks: with contiguous caches one key split per sequence,
+    # so every sequence is one unit, also those whose rows rank no block (the paged
+    # pool's table is two pages longer than the longest cache: two splits)
+    msa = _msa()
+    rng = np.random.default_rng(31 + paged)
+    lens = [int(v) for v in rng.integers(1, 1900, 64)]
+    lens[:3] = [1, 128, 1900]
+    print(f"short caches paged={paged}", flush=True)
+    if paged:
+        s, table, P, xh = _paged((lens, 1, 64, 4, 128, 128, 16, "native", 3), 950)
+        pt = torch.from_numpy(table).cuda()
+    else:
+        s = synth.Shape(64, 1, max(lens) + 5, 0, 64, 4, 128, 128, 16)
+        xh = synth.host_inputs(s, 950)
+        pt = None
+    x = {n: t.cuda() for n, t in xh.items()}
+    sl = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    out, sel, lse = msa.fwd_kvcache(x["q"], x["k"], x["v"], x["q_idx"], x["k_idx"], s.topk, seq_lens=sl,
+                                    page_table=pt, return_sel=True, return_lse=True)
+    torch.cuda.synchronize()
+    if paged:
+        ref = _paged_oracle(s, lens, table, xh)
+    else:
+        f = {n: synth.as_f64(t) for n, t in xh.items()}
+        ref = orc.msa_forward_varlen(f["q"], [f["k"][b, :, :n] for b, n in enumerate(lens)],
+                                     [f["v"][b, :, :n] for b, n in enumerate(lens)], f["q_idx"],
+                                     [f["k_idx"][b, :n] for b, n in enumerate(lens)], s.topk)
+    _compare(out, sel, lse, *ref)
