@@ -467,6 +467,24 @@ def cpu_baseline(s: synth.Shape, x, out_gpu, sel_gpu, budget_s: float):
     }
 
 
+def selection_check(s: synth.Shape, wid: int, x, sel_gpu) -> dict:
+    """Every selection row of the timed workload against the fp64 oracle's, reported
+    as the issue write-up's check after its fix reports it (section 验证方法):
+    diverging rows out of all (b, g, i) rows, and the mean overlap of each row's
+    blocks with the oracle's."""
+    from oracle import msa_oracle as orc
+    t0 = time.perf_counter()
+    ref = np.empty((s.batch, s.groups, s.q_len, s.topk), dtype=np.int32)
+    for b in range(s.batch):
+        qi = x["q_idx"][b:b + 1].float().numpy().astype(np.float64)  # exact upcasts of the stored values
+        ki = x["k_idx"][b:b + 1].float().numpy().astype(np.float64)
+        ref[b] = orc.index_select(qi, ki, s.topk, s.q_offset, s.block_size)[0]
+    rep = orc.selection_agreement(sel_gpu.numpy(), ref)
+    rep["workload"] = synth.WORKLOAD_NAMES[wid]
+    rep["oracle_s"] = round(time.perf_counter() - t0, 1)
+    return rep
+
+
 def work_rates(flop_main, flop_index, step_tflops, kern):
     """Each timed part's TFLOP/s and its fraction of the bf16 MFMA peak: the
     index kernel (msa_index_select's work), the main branch alone (what
@@ -608,11 +626,11 @@ def main():
                               "frac_of_mfma_peak": round(flop_bwd / (bms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                               "flop": flop_bwd, "kernels_ms": {k: round(v, 4) for k, v in bper.items() if v}}
 
+    # the CPU legs run after every GPU leg (so GPU-busy samples land on GPU work):
+    # keep host copies of this workload's inputs and results for them
+    host = None
     if not args.no_cpu:
-        print("[bench] cpu baseline (oracle on sampled rows)", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(s, run.x, run.out, run.sel, args.cpu_budget)
-    else:
-        result["cpu_baseline"] = None
+        host = ({n: t.cpu() for n, t in run.x.items()}, run.out.cpu(), run.sel.cpu())
     del run
     torch.cuda.empty_cache()
 
@@ -640,6 +658,15 @@ def main():
         result["decode"] = decode_leg(msa, 4, args)
         result["decode_fp8"] = decode_leg(msa, 6, args)
         result["decode_paged"] = decode_leg(msa, 7, args)
+
+    if host is not None:
+        hx, hout, hsel = host
+        print("[bench] selection check (oracle on every row)", file=sys.stderr, flush=True)
+        result["selection_check"] = selection_check(s, wid, hx, hsel)
+        print("[bench] cpu baseline (oracle on sampled rows)", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(s, hx, hout, hsel, args.cpu_budget)
+    else:
+        result["cpu_baseline"] = None
     print(json.dumps(result))
 
 

@@ -80,6 +80,7 @@ from typing import Iterable, Optional, Sequence, Tuple
 import numpy as np
 
 __all__ = [
+    "selection_agreement",
     "sparse_attention_bwd",
     "kl_teacher",
     "page_gather",
@@ -206,6 +207,37 @@ def index_select(q_idx, k_idx, topk: int, q_offset: int = 0, block_size: int = 1
                     M = block_maxima(q_idx[b, part, g, :], k_idx[b], L, block_size)
                     sel[b, g, part, :] = select_from_maxima(M, L, topk)
     return sel
+
+
+def selection_agreement(sel, ref) -> dict:
+    """How a selection compares with a reference one, in the terms of the check
+    the issue write-up runs after its fix (section 验证方法): the number of
+    (b, g, i) rows that differ, out of all rows, and the mean number of block ids
+    a row shares with its reference row (k of k when nothing diverges).
+
+    sel, ref: int arrays [..., k] of block ids, -1 padded.  A row diverges when
+    it is not identical to its reference row (ids, order and padding).  Returns
+    {"rows", "diverging", "mean_overlap", "mean_ref_blocks", "k"}.
+    """
+    a = np.asarray(sel)
+    b = np.asarray(ref)
+    if a.shape != b.shape:
+        raise ValueError(f"shapes differ: {a.shape} vs {b.shape}")
+    k = a.shape[-1]
+    a2 = a.reshape(-1, k).astype(np.int64)
+    b2 = b.reshape(-1, k).astype(np.int64)
+    rows = a2.shape[0]
+    diverging = int((a2 != b2).any(axis=1).sum())
+    # an id of a row counts once if it appears anywhere among the reference row's ids
+    shared = ((a2[:, :, None] == b2[:, None, :]) & (b2[:, None, :] >= 0)).any(axis=2) & (a2 >= 0)
+    overlap = shared.sum(axis=1)
+    return {
+        "rows": rows,
+        "diverging": diverging,
+        "mean_overlap": float(overlap.mean()) if rows else 0.0,
+        "mean_ref_blocks": float((b2 >= 0).sum(axis=1).mean()) if rows else 0.0,
+        "k": int(k),
+    }
 
 
 # ---------------------------------------------------------------------------

@@ -1,24 +1,12 @@
 import os
 import sys
 
-import pytest
-
-ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-if ROOT not in sys.path:
-    sys.path.insert(0, ROOT)
+ROOT = os.path.dirname(os.path.abspath(__file__))
+REPO = os.path.dirname(ROOT)
+for p in (REPO, ROOT):
+    if p not in sys.path:
+        sys.path.insert(0, p)
 
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
-    config.addinivalue_line("markers", "big: full-size workloads (minutes of oracle time); opt in with -m big")
-
-
-def pytest_collection_modifyitems(config, items):
-    # full-size parity jobs run only when asked for by name or marker
-    mexpr = config.getoption("-m") or ""
-    if "big" in mexpr:
-        return
-    skip = pytest.mark.skip(reason="full-size workload: run with -m big")
-    for it in items:
-        if "big" in it.keywords:
-            it.add_marker(skip)

@@ -169,7 +169,11 @@ def test_unmapped_pages_are_skipped_safely():
         assert float(np.abs(og[b] - ref[0][b]).max()) <= TOL
 
 
-def test_paged_decode_workload_sampled():
+@pytest.mark.timeout(900)
+def test_paged_decode_workload_every_sequence():
+    # every sequence: its selection against the oracle's (ranked over its own cache,
+    # read out of the page pool) and its output against the oracle's main branch
+    from fullsize import check_selection, sparse_kv
     msa = _msa()
     wid = 7
     s = synth.WORKLOADS[wid]
@@ -180,23 +184,30 @@ def test_paged_decode_workload_sampled():
     out, sel = msa.fwd_kvcache(x["q"], x["k"], x["v"], x["q_idx"], x["k_idx"], s.topk, seq_lens=sl, page_table=pt,
                                kv_len=s.kv_len, return_sel=True)
     torch.cuda.synchronize()
-    print("  forward done", flush=True)
-    picks = [int(np.argmin(lens)), int(np.argmax(lens)), 17]
-    pools = {n: x[n] for n in ("k", "v", "k_idx")}
-    f = {}
-    for n in ("k", "v", "k_idx"):  # only the picked sequences' pages come back to the host
-        f[n] = []
-        for b in picks:
-            nb = -(-int(lens[b]) // 128)
-            pg = torch.from_numpy(table[b, :nb].astype(np.int64)).cuda()
-            f[n].append(orc.page_gather(_f64(s, n, pools[n].index_select(0, pg).cpu()), np.arange(nb), int(lens[b])))
-    q = _f64(s, "q", x["q"][picks].cpu())
-    qi = _f64(s, "q_idx", x["q_idx"][picks].cpu())
-    ref_out, ref_sel, _ = orc.msa_forward_varlen(q, f["k"], f["v"], qi, f["k_idx"], s.topk)
-    assert np.array_equal(sel[picks].cpu().numpy(), ref_sel)
-    err = float(np.abs(out[picks].float().cpu().numpy() - ref_out).max())
-    print(f"  max abs err {err:.3e}", flush=True)
-    assert err <= TOL
+    print("  forward done; oracle on every sequence", flush=True)
+    sg = sel.cpu().numpy()
+    og = out.float().cpu().numpy()
+    ref_sel = np.empty_like(sg)
+    worst = 0.0
+    for b in range(s.batch):
+        n = int(lens[b])
+        nb = -(-n // 128)
+        pg = torch.from_numpy(table[b, :nb].astype(np.int64)).cuda()
+        kib = orc.page_gather(_f64(s, "k_idx", x["k_idx"].index_select(0, pg).cpu()), np.arange(nb), n)
+        qi = _f64(s, "q_idx", x["q_idx"][b:b + 1].cpu())
+        # query row i of a cache of n tokens sits at n - S_q + i
+        ref_sel[b] = orc.index_select(qi, kib[None], s.topk, n - s.q_len, 128)[0]
+        # the cache as the oracle reads it: the sequence's pages in logical order, only the selected ones filled
+        kseq = x["k"].index_select(0, pg).permute(1, 0, 2, 3).reshape(s.num_kv_heads, nb * 128, s.head_dim)
+        vseq = x["v"].index_select(0, pg).permute(1, 0, 2, 3).reshape(s.num_kv_heads, nb * 128, s.head_dim)
+        blocks = [ref_sel[b, g].reshape(-1) for g in range(s.groups)]
+        kb = sparse_kv(s, "k", kseq, blocks, n)
+        vb = sparse_kv(s, "v", vseq, blocks, n)
+        ro, _ = orc.sparse_attention(_f64(s, "q", x["q"][b:b + 1].cpu()), kb, vb, ref_sel[b:b + 1], n - s.q_len, 128)
+        worst = max(worst, float(np.abs(og[b:b + 1] - ro).max()))
+    check_selection(synth.WORKLOAD_NAMES[wid], sg, ref_sel)
+    print(f"  outputs of all {s.batch} sequences: max abs err {worst:.3e}", flush=True)
+    assert worst <= TOL
 
 
 @pytest.mark.parametrize("B,paged", [(256, True), (300, True), (256, False), (300, False)])

@@ -273,7 +273,38 @@ def test_pooled_variant_diverges_like_the_issue_reports():
     rows = [(g, i) for g in range(G) for i in range(S) if i // Bk >= k]  # rows with a real choice
     div = sum(not np.array_equal(a[0, g, i], b[0, g, i]) for g, i in rows)
     assert div / len(rows) > 0.5
-    assert sum(not np.array_equal(a[0, g, i], a[0, g, i]) for g, i in rows) == 0
+    # after the fix (one selection per index head), 0 of N rows diverge from a
+    # per-group recomputation in pure Python and every row shares all k blocks
+    def py_select(M, L):  # Python's own sort on (score desc, id asc), no numpy
+        take = sorted(range(L), key=lambda c: (-M[c], c))[:min(k - 1, L)]
+        chosen = sorted(take + [L])
+        return chosen + [-1] * (k - len(chosen))
+
+    brute = np.array([py_select(_brute_maxima(q_idx[0, i, g], k_idx[0], i // Bk, Bk), i // Bk) for g, i in rows],
+                     dtype=np.int32)
+    mine = np.array([a[0, g, i] for g, i in rows])
+    pooled = np.array([b[0, g, i] for g, i in rows])
+    rep = orc.selection_agreement(mine, brute)
+    assert rep["rows"] == len(rows) and rep["diverging"] == 0 and rep["mean_overlap"] == k
+    rep_pooled = orc.selection_agreement(pooled, brute)
+    assert rep_pooled["diverging"] == div and rep_pooled["mean_overlap"] < k
+
+
+def test_selection_agreement_counts_by_hand():
+    ref = np.array([[0, 3, 5, -1], [1, 2, 4, 7], [0, 1, -1, -1]], dtype=np.int32)
+    same = orc.selection_agreement(ref, ref)
+    assert same == {"rows": 3, "diverging": 0, "mean_overlap": 3.0, "mean_ref_blocks": 3.0, "k": 4}
+    sel = np.array([[0, 3, 5, -1],     # identical
+                    [1, 2, 6, 7],      # one block swapped: 3 shared
+                    [0, 1, 2, -1]],    # an extra block: 2 shared, diverges
+                   dtype=np.int32)
+    rep = orc.selection_agreement(sel, ref)
+    assert rep["diverging"] == 2
+    assert rep["mean_overlap"] == pytest.approx((3 + 3 + 2) / 3)
+    # padding never counts as a shared block, and shapes must agree
+    assert orc.selection_agreement(np.full((1, 4), -1), np.full((1, 4), -1))["mean_overlap"] == 0.0
+    with pytest.raises(ValueError):
+        orc.selection_agreement(sel[:2], ref)
 
 
 # ---------------------------------------------------------------------------
