@@ -19,6 +19,8 @@ Functions (same names as the C entry points):
   from the group-averaged main distribution (and the index log-sum-exp)
 * ``sparse_attn_bwd(q, k, v, sel, out, lse, dout, q_offset=0)`` -> (dq, dk, dv)
   fp32, the main branch's gradients with the selection held constant (bf16)
+* ``fwd_noalloc(q, k, v, q_idx, k_idx, topk, ..., out=None, sel=None, lse=None)``
+  -> (out, sel, lse): ``fwd`` in the library's fixed scratch, no workspace
 
 Layouts: q [B,S_q,Hq,d], k/v [B,Hkv,S_k,d], q_idx [B,S_q,G,D_idx],
 k_idx [B,S_k,D_idx] with G = Hkv; all contiguous, on the GPU, fp32 or bf16.
@@ -43,7 +45,7 @@ import torch
 __all__ = ["index_select", "sparse_attn_fwd", "fwd", "index_select_kvcache", "sparse_attn_fwd_kvcache",
            "fwd_kvcache", "kl_teacher_fwd", "kl_teacher_fwd_kvcache", "workspace_size", "MsaShape", "MsaKvCache",
            "lib", "LIB_PATH", "MsaError", "OP_INDEX_SELECT", "OP_SPARSE_ATTN", "OP_FWD", "OP_KL_TEACHER",
-           "sparse_attn_bwd", "OP_SPARSE_ATTN_BWD"]
+           "sparse_attn_bwd", "OP_SPARSE_ATTN_BWD", "fwd_noalloc", "noalloc_scratch_bytes"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmsa.so")
 
@@ -111,6 +113,10 @@ def lib() -> ctypes.CDLL:
         L.msa_sparse_attn_fwd.restype = ctypes.c_int
         L.msa_fwd.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.msa_fwd.restype = ctypes.c_int
+        L.msa_fwd_noalloc.argtypes = [shp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.msa_fwd_noalloc.restype = ctypes.c_int
+        L.msa_noalloc_scratch_bytes.argtypes = []
+        L.msa_noalloc_scratch_bytes.restype = sz
         L.msa_status_string.argtypes = [ctypes.c_int]
         L.msa_status_string.restype = ctypes.c_char_p
         L.msa_last_error.argtypes = []
@@ -309,6 +315,49 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_idx: torch.Tensor, 
     if return_lse:
         res.append(lse)
     return res[0] if len(res) == 1 else tuple(res)
+
+
+def fwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_idx: torch.Tensor, k_idx: torch.Tensor,
+                topk: int, q_offset: int = 0, scale: Optional[float] = None, out_dtype: Optional[torch.dtype] = None,
+                out: Optional[torch.Tensor] = None, sel: Optional[torch.Tensor] = None,
+                lse: Optional[torch.Tensor] = None, k_scale: Optional[float] = None, v_scale: Optional[float] = None):
+    """msa_fwd_noalloc: fwd without a workspace (the library's fixed scratch).  The
+    outputs may be passed in (then nothing at all is allocated); returns (out, sel, lse)."""
+    _need(q, "q", 4)
+    dev = q.device
+    _need(q_idx, "q_idx", 4, dev, q.dtype)
+    for name, t, nd in (("k", k, 4), ("v", v, 4), ("k_idx", k_idx, 3)):
+        _need(t, name, nd, dev)
+    cf = _cache_format(q.dtype, [("k", k), ("v", v), ("k_idx", k_idx)])
+    B, S_q, Hq, d = q.shape
+    Hkv, S_k = k.shape[1], k.shape[2]
+    D = q_idx.shape[3]
+    if tuple(k.shape) != (B, Hkv, S_k, d) or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("k and v must be [B, Hkv, S_k, d] matching q")
+    if tuple(q_idx.shape) != (B, S_q, Hkv, D) or tuple(k_idx.shape) != (B, S_k, D):
+        raise ValueError("q_idx must be [B, S_q, Hkv, D_idx] and k_idx [B, S_k, D_idx]")
+    shape = make_shape(B, S_q, S_k, q_offset, Hq, Hkv, d, D, topk, q.dtype, out_dtype, scale,
+                       cache_format=cf, k_scale=k_scale, v_scale=v_scale)
+    if out is None:
+        out = torch.empty((B, S_q, Hq, d), dtype=out_dtype or q.dtype, device=dev)
+    _need(out, "out", 4, dev)
+    if tuple(out.shape) != (B, S_q, Hq, d):
+        raise ValueError("out must be [B, S_q, Hq, d]")
+    for name, t, shp, dt in (("sel", sel, (B, Hkv, S_q, topk), torch.int32), ("lse", lse, (B, Hq, S_q), torch.float32)):
+        if t is not None:
+            _need(t, name, len(shp), dev, dt)
+            if tuple(t.shape) != shp:
+                raise ValueError(f"{name} must be {list(shp)}")
+    L = lib()
+    st = L.msa_fwd_noalloc(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(q_idx), _ptr(k_idx), _ptr(out),
+                           _ptr(sel), _ptr(lse), _stream(dev))
+    _check(st)
+    return out, sel, lse
+
+
+def noalloc_scratch_bytes() -> int:
+    """Bytes of the scratch msa_fwd_noalloc works in."""
+    return int(lib().msa_noalloc_scratch_bytes())
 
 
 # ---- caches of unequal length, optionally paged ----------------------------

@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "../../include/msa.h"
@@ -378,6 +379,36 @@ msa_status hip_status(hipError_t e, const char* what) {
   return fail(MSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// ---- the allocation-free entry point's scratch ---------------------------
+//
+// msa_fwd_noalloc takes its workspace from this array (each GPU the library runs
+// on holds its own copy until the process ends).  In host code the name is only
+// a stand-in: kernels get the device address hipGetSymbolAddress returns for the
+// current device, looked up once per device and kept below.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+msa_status scratch_for_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MSA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(MSA_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(MSA_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MSA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -577,6 +608,26 @@ msa_status msa_fwd(const msa_shape* s, const void* q, const void* k, const void*
                    const void* k_idx, void* out, int32_t* sel_out, float* lse, void* ws, size_t ws_bytes,
                    void* stream) {
   return msa_fwd_kvcache(s, nullptr, q, k, v, q_idx, k_idx, out, sel_out, lse, ws, ws_bytes, stream);
+}
+
+size_t msa_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+msa_status msa_fwd_noalloc(const msa_shape* s, const void* q, const void* k, const void* v, const void* q_idx,
+                           const void* k_idx, void* out, int32_t* sel_out, float* lse, void* stream) {
+  // the checks msa_fwd runs, first, so that errors name the arguments, not the scratch
+  msa_status st = check_shape(s, MSA_OP_FWD);
+  if (st != MSA_OK) return st;
+  if (!q || !k || !v || !q_idx || !k_idx || !out)
+    return fail(MSA_ERR_INVALID, "q, k, v, q_idx, k_idx and out must be non-NULL");
+  if (s->q_len == 0) return MSA_OK;
+  const size_t need =
+      sel_bytes(s) + std::max(plan_index(s, nullptr).bytes, plan_attn(s, nullptr).bytes);
+  if (need > kScratchBytes)
+    return fail(MSA_ERR_WORKSPACE, "this shape needs %zu bytes of scratch; msa_fwd_noalloc holds %zu (use msa_fwd)",
+                need, kScratchBytes);
+  void* ws = nullptr;
+  if ((st = scratch_for_current_device(&ws)) != MSA_OK) return st;
+  return msa_fwd_kvcache(s, nullptr, q, k, v, q_idx, k_idx, out, sel_out, lse, ws, kScratchBytes, stream);
 }
 
 }  // extern "C"

@@ -34,12 +34,15 @@
  *                                    scores over the attended tokens
  *
  * Ownership and threading.  Every data pointer is a device pointer owned by
- * the caller.  The library allocates no device memory and keeps no state
- * between calls; scratch memory is the caller's workspace (256-byte aligned,
- * at least msa_workspace_size() bytes).  Work is enqueued on the given HIP
- * stream (hipStream_t passed as void*, NULL = the null stream) and the calls
- * return without synchronising.  Different threads may call concurrently on
- * different streams with different workspaces.
+ * the caller.  The library allocates no device memory; scratch memory is the
+ * caller's workspace (256-byte aligned, at least msa_workspace_size() bytes),
+ * except for msa_fwd_noalloc, which works in a fixed scratch array of the
+ * library's own (see there).  Work is enqueued on the given HIP stream
+ * (hipStream_t passed as void*, NULL = the null stream) and the calls return
+ * without synchronising.  Different threads may call concurrently on
+ * different streams with different workspaces.  Two things persist between
+ * calls: the profiling hook of msa_set_kernel_timer (thread-local, off unless
+ * set) and msa_fwd_noalloc's scratch with its per-device address.
  *
  * Errors.  Arguments are checked on the host before anything is enqueued; on
  * an error nothing is launched and outputs are untouched.  A failed launch
@@ -143,6 +146,27 @@ msa_status msa_sparse_attn_fwd(const msa_shape* shape, const void* q, const void
 msa_status msa_fwd(const msa_shape* shape, const void* q, const void* k, const void* v,
                    const void* q_idx, const void* k_idx, void* out, int32_t* sel_out,
                    float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---- Without a workspace --------------------------------------------------
+ *
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): msa_fwd with
+ * the library's own scratch instead of a caller workspace.  Arguments, results
+ * and errors are those of msa_fwd.  The scratch is a static device array of
+ * msa_noalloc_scratch_bytes() bytes (64 MiB) that each GPU the library runs on
+ * holds until the process ends; its device address is looked up on the first
+ * call on each device (with that device current).  Shapes whose workspace
+ * (msa_workspace_size(shape, MSA_OP_FWD)) exceeds it are refused with
+ * MSA_ERR_WORKSPACE before anything is enqueued.  Every call on one GPU uses
+ * the same array: calls that overlap on one GPU (different streams, or other
+ * threads) race and give undefined results; calls ordered on one stream are
+ * fine.  Nothing is allocated or freed by the call. */
+msa_status msa_fwd_noalloc(const msa_shape* shape, const void* q, const void* k, const void* v,
+                           const void* q_idx, const void* k_idx, void* out, int32_t* sel_out, float* lse,
+                           void* stream);
+
+/* Bytes of the scratch msa_fwd_noalloc works in. */
+size_t msa_noalloc_scratch_bytes(void);
 
 /* ---- Caches of unequal length, optionally paged -------------------------
  *
@@ -256,11 +280,15 @@ typedef enum {
   MSA_KERNEL_BWD_COMBINE = 9  /* backward: dQ partials summed                        */
 } msa_kernel;
 
-/* Profiling hook.  For the calling thread, every later msa_* call records
- * start_event (a hipEvent_t) on its stream right before launching `kernel` and
- * stop_event right after it, so hipEventElapsedTime gives that kernel's own
- * duration.  kernel = MSA_KERNEL_NONE (or NULL events) turns the hook off.
- * The events stay owned by the caller.  A kernel a call does not launch
+/* Profiling hook (thread-local state: the one exception to calls being
+ * independent of each other).  For the calling thread, every later msa_* call
+ * records start_event (a hipEvent_t) on its stream right before launching
+ * `kernel` and stop_event right after it, so hipEventElapsedTime gives that
+ * kernel's own duration.  kernel = MSA_KERNEL_NONE (or NULL events) turns the
+ * hook off; it is off until set.  The events stay owned by the caller.  A call
+ * captured into a HIP graph while the hook is set records the two event nodes
+ * into the graph, and every replay records them again: turn the hook off
+ * before capturing.  A kernel a call does not launch
  * records nothing: decode calls with bf16 queries and at least 256
  * (batch, query row, group) rows run the merge of the split lists, the
  * attention and the combine as one kernel, timed as MSA_KERNEL_ATTENTION. */

@@ -216,3 +216,19 @@ def test_backward_checks():
     for field, value in (("dtype", 0), ("out_dtype", 0), ("cache_format", 1), ("k_scale", 0.5)):
         bad = _shape(2, **{field: value})
         assert L.msa_sparse_attn_bwd(ctypes.byref(bad), *args()[1:]) == -2, field
+
+
+def test_noalloc_validates_before_touching_a_device():
+    L = msa.lib()
+    sh = _shape(2)
+    # a NULL input: refused by the argument checks msa_fwd runs
+    st = L.msa_fwd_noalloc(ctypes.byref(sh), None, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None)
+    assert st == -1 and b"non-NULL" in L.msa_last_error()
+    # the 8K prefill needs ~2 GiB of workspace: more than the fixed scratch holds
+    assert msa.workspace_size(sh, msa.OP_FWD) > msa.noalloc_scratch_bytes()
+    st = L.msa_fwd_noalloc(ctypes.byref(sh), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None)
+    assert st == -3 and b"msa_fwd_noalloc holds" in L.msa_last_error()
+    # a bad shape is reported as such
+    bad = _shape(2, topk=0)
+    assert L.msa_fwd_noalloc(ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None) == -1
+    assert msa.noalloc_scratch_bytes() == 64 << 20
