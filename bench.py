@@ -467,6 +467,42 @@ def cpu_baseline(s: synth.Shape, x, out_gpu, sel_gpu, budget_s: float):
     }
 
 
+WORKSPACE_CAP_MIB = 3500  # keeps the 32K x 2 workspace under 4 GB
+
+
+def bounded_leg(msa, run, s: synth.Shape, args) -> dict:
+    """ms per msa_fwd step of this workload with workspace_cap_mib = WORKSPACE_CAP_MIB,
+    next to the uncapped workspace; outputs must equal the uncapped call's."""
+    sh = msa.make_shape(s.batch, s.q_len, s.kv_len, s.q_offset, s.num_q_heads, s.num_kv_heads, s.head_dim,
+                        s.index_dim, s.topk, s.torch_dtype, workspace_cap_mib=WORKSPACE_CAP_MIB)
+    n = msa.workspace_size(sh, msa.OP_FWD)
+    dev = run.x["q"].device
+    wsr = torch.empty(n + 256, dtype=torch.uint8, device=dev)
+    ws = wsr[(-wsr.data_ptr()) % 256:][:n]
+    out = torch.empty_like(run.out)
+    a = list(run.args)
+    a[0] = ctypes.byref(sh)
+    a[7] = ctypes.c_void_p(out.data_ptr())
+    a[-3], a[-2] = ctypes.c_void_p(ws.data_ptr()), ctypes.c_size_t(n)
+    fn = run.L.msa_fwd_kvcache
+    for _ in range(args.warmup):
+        if fn(*a) != 0:
+            raise RuntimeError(run.L.msa_last_error().decode())
+    run.step()
+    torch.cuda.synchronize()
+    same = bool(torch.equal(out, run.out))
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(run.stream)
+    for _ in range(args.steps):
+        fn(*a)
+    t1.record(run.stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    del ws, wsr, out
+    return {"workspace_cap_mib": WORKSPACE_CAP_MIB, "workspace_bytes": n, "uncapped_workspace_bytes": run.ws.numel(),
+            "ms_per_step": round(ms, 4), "equal_to_uncapped": same}
+
+
 def selection_check(s: synth.Shape, wid: int, x, sel_gpu) -> dict:
     """Every selection row of the timed workload against the fp64 oracle's, reported
     as the issue write-up's check after its fix reports it (section 验证方法):
@@ -626,6 +662,10 @@ def main():
                               "frac_of_mfma_peak": round(flop_bwd / (bms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                               "flop": flop_bwd, "kernels_ms": {k: round(v, 4) for k, v in bper.items() if v}}
 
+    if not args.no_extra and wid == 3:
+        # the same step with the workspace capped (msa_shape.workspace_cap_mib): the main
+        # branch runs over query-row chunks whose partial states fit the cap
+        result["bounded_workspace"] = bounded_leg(msa, run, s, args)
     # the CPU legs run after every GPU leg (so GPU-busy samples land on GPU work):
     # keep host copies of this workload's inputs and results for them
     host = None

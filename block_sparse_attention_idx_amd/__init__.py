@@ -73,7 +73,7 @@ class MsaShape(ctypes.Structure):
         ("out_dtype", ctypes.c_int32),
         ("k_scale", ctypes.c_float),
         ("v_scale", ctypes.c_float),
-        ("pad", ctypes.c_int32),
+        ("workspace_cap_mib", ctypes.c_int32),
     ]
 
 
@@ -154,7 +154,8 @@ def _dtype_code(dt: torch.dtype) -> int:
 
 
 def make_shape(B, S_q, S_k, q_offset, Hq, Hkv, d, D_idx, topk, dtype, out_dtype=None, scale=None,
-               block_size=BLOCK_SIZE, cache_format=CACHE_NATIVE, k_scale=None, v_scale=None) -> MsaShape:
+               block_size=BLOCK_SIZE, cache_format=CACHE_NATIVE, k_scale=None, v_scale=None,
+               workspace_cap_mib=0) -> MsaShape:
     s = MsaShape()
     s.batch, s.q_len, s.kv_len, s.cache_format = B, S_q, S_k, cache_format
     s.q_offset = q_offset
@@ -166,7 +167,7 @@ def make_shape(B, S_q, S_k, q_offset, Hq, Hkv, d, D_idx, topk, dtype, out_dtype=
     s.out_dtype = _dtype_code(out_dtype if out_dtype is not None else dtype)
     s.k_scale = 0.0 if k_scale is None else float(k_scale)
     s.v_scale = 0.0 if v_scale is None else float(v_scale)
-    s.pad = 0
+    s.workspace_cap_mib = int(workspace_cap_mib)
     return s
 
 

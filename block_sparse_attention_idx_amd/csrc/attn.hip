@@ -59,8 +59,8 @@ template <bool SCATTER>
 __global__ __launch_bounds__(256) void gather_hist_kernel(AttnParams p) {
   extern __shared__ int32_t hist[];
   const int bg = blockIdx.y;
-  const int i0 = blockIdx.x * kGatherRows;
-  const int rows = min(kGatherRows, p.S_q - i0);
+  const int i0 = p.row0 + blockIdx.x * kGatherRows;
+  const int rows = min(kGatherRows, p.row0 + p.nrows - i0);
   for (int c = threadIdx.x; c < p.nb; c += 256) hist[c] = 0;
   __syncthreads();
   const int32_t* sbase = p.sel + ((int64_t)bg * p.S_q + i0) * p.topk;
@@ -92,12 +92,13 @@ __global__ __launch_bounds__(256) void gather_hist_kernel(AttnParams p) {
 
 // Same result for caches too long for an LDS histogram: one global atomic per entry.
 __global__ __launch_bounds__(256) void gather_count_kernel(AttnParams p) {
-  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t total = (int64_t)p.B * p.G * p.S_q * p.topk;
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;  // over the pass's rows
+  const int64_t total = (int64_t)p.B * p.G * p.nrows * p.topk;
   if (e >= total) return;
-  const int c = p.sel[e];
+  const int64_t per_bg = (int64_t)p.nrows * p.topk;
+  const int64_t bg = e / per_bg;  // b * G + g
+  const int c = p.sel[(bg * p.S_q + p.row0) * p.topk + (e - bg * per_bg)];
   if (c < 0 || c >= p.nb) return;
-  const int64_t bg = e / ((int64_t)p.S_q * p.topk);  // b * G + g
   atomicAdd(&p.counts[bg * p.nb + c], 1);
 }
 
@@ -110,15 +111,15 @@ __global__ __launch_bounds__(256) void item_table_kernel(AttnParams p) {
 }
 
 __global__ __launch_bounds__(256) void gather_scatter_kernel(AttnParams p) {
-  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t total = (int64_t)p.B * p.G * p.S_q * p.topk;
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;  // over the pass's rows
+  const int64_t total = (int64_t)p.B * p.G * p.nrows * p.topk;
   if (e >= total) return;
-  const int c = p.sel[e];
-  if (c < 0 || c >= p.nb) return;
   const int slot = (int)(e % p.topk);
   const int64_t rest = e / p.topk;
-  const int i = (int)(rest % p.S_q);
-  const int64_t bg = rest / p.S_q;
+  const int i = p.row0 + (int)(rest % p.nrows);
+  const int64_t bg = rest / p.nrows;
+  const int c = p.sel[(bg * p.S_q + i) * p.topk + slot];
+  if (c < 0 || c >= p.nb) return;
   const int pos = atomicAdd(&p.cursor[bg * p.nb + c], 1);
   p.entries[pos] = (i << 6) | slot;
 }
@@ -380,7 +381,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void attn_kvouter_kern
       // so one store instruction writes 2 * R * 16 contiguous bytes per token.
       if (rv) {
         const float inv = 1.0f / lsum;
-        const int64_t ptok = (((int64_t)b * p.S_q + i) * p.G + g) * p.topk + slot;
+        const int64_t ptok = (((int64_t)b * p.nrows + i - p.row0) * p.G + g) * p.topk + slot;
         T* po = (T*)p.part_o + ptok * (R * D);
         constexpr int NQ = NDT * 16 / E;
 #pragma unroll
@@ -550,7 +551,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnParams p) {
       const float lsum = red_l[0][l32] + red_l[1][l32] + red_l[2][l32] + red_l[3][l32];
       if (l32 < R) {
         const float inv = 1.0f / lsum;
-        const int64_t ptok = (((int64_t)b * p.S_q + i) * p.G + g) * p.topk + slot;
+        const int64_t ptok = (((int64_t)b * p.nrows + i - p.row0) * p.G + g) * p.topk + slot;
         T* po = (T*)p.part_o + ptok * (R * D);
         // lane-native chunks q = (wave * 16 + j) / E of this lane's registers
 #pragma unroll
@@ -1173,16 +1174,17 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(AttnParams p) 
   constexpr int RPW = STAGED ? kCombineThreads / NCHT : 1;  // (token, group) rows per workgroup
   __shared__ __align__(16) TO ostage[STAGED ? RPW * R * D : 1];
   const int64_t u = (int64_t)blockIdx.x * kCombineThreads + threadIdx.x;
-  const int64_t rows_total = (int64_t)p.B * p.S_q * p.G;
+  const int64_t rows_total = (int64_t)p.B * p.nrows * p.G;  // the pass's (b, i, g) rows
   const int64_t total = rows_total * NCHT;
   const bool live = u < total;
   const int64_t uc = live ? u : total - 1;
   const int ch = (int)(uc % NCHT);
-  const int64_t rowg = uc / NCHT;  // (b * S_q + i) * G + g
+  const int64_t rowg = uc / NCHT;  // (b * nrows + i - row0) * G + g: its partial states
   const int g = (int)(rowg % p.G);
-  const int64_t bi = rowg / p.G;
-  const int i = (int)(bi % p.S_q);
-  const int b = (int)(bi / p.S_q);
+  const int64_t bic = rowg / p.G;
+  const int i = p.row0 + (int)(bic % p.nrows);
+  const int b = (int)(bic / p.nrows);
+  const int64_t bi = (int64_t)b * p.S_q + i;
   const int hh = ch % R, h = (ch / R) & 1, q = ch / (2 * R);
   const int64_t t = first_pos(p.cm, p.q_offset, p.S_q, p.S_k, b) + i;
   const int32_t* srow = p.sel + (((int64_t)b * p.G + g) * p.S_q + i) * p.topk;
@@ -1213,7 +1215,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(AttnParams p) 
       const int64_t rg = min(row0 + lr, rows_total - 1);
       const int64_t rbi = rg / p.G;
       const int rgg = (int)(rg - rbi * p.G);
-      const int ri = (int)(rbi % p.S_q), rb = (int)(rbi / p.S_q);
+      const int ri = p.row0 + (int)(rbi % p.nrows), rb = (int)(rbi / p.nrows);
       int c = -1;
       if (s2 < p.topk) {
         c = p.sel[(((int64_t)rb * p.G + rgg) * p.S_q + ri) * p.topk + s2];
@@ -1284,17 +1286,23 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(AttnParams p) 
       for (int e = 0; e < 4; ++e) srow_o[d0 + e] = from_f32<TO>(acc[4 * m + e] * inv);
     }
     __syncthreads();
-    // the workgroup's rows are consecutive (b, i, g) rows: one contiguous output range
-    const int64_t row0 = (int64_t)blockIdx.x * RPW;
-    const int64_t nrows = rows_total - row0 < RPW ? rows_total - row0 : RPW;
-    constexpr int CHUNKS = RPW * R * D * (int)sizeof(TO) / 16;
-    const int live_chunks = (int)(nrows * R * D * (int64_t)sizeof(TO) / 16);
+    // each staged (b, i, g) row is one contiguous R * D run of out, written in full lines
+    const int64_t wrow0 = (int64_t)blockIdx.x * RPW;
+    const int64_t wrows = rows_total - wrow0 < RPW ? rows_total - wrow0 : RPW;
+    constexpr int ROW_CHUNKS = R * D * (int)sizeof(TO) / 16;
+    constexpr int CHUNKS = RPW * ROW_CHUNKS;
     const Chunk16* src = (const Chunk16*)ostage;
-    Chunk16* dst = (Chunk16*)((TO*)p.out + row0 * R * D);
 #pragma unroll
     for (int k = 0; k < (CHUNKS + kCombineThreads - 1) / kCombineThreads; ++k) {
       const int c = (int)threadIdx.x + k * kCombineThreads;
-      if (c < live_chunks) dst[c] = src[c];
+      const int lr = c / ROW_CHUNKS;
+      if (lr < wrows) {
+        const int64_t rg = wrow0 + lr;
+        const int64_t rbi = rg / p.G;
+        const int rgg = (int)(rg - rbi * p.G);
+        const int64_t orow = ((rbi / p.nrows) * p.S_q + p.row0 + rbi % p.nrows) * p.G + rgg;
+        ((Chunk16*)((TO*)p.out + orow * R * D))[c - lr * ROW_CHUNKS] = src[c];
+      }
     }
   } else if (live) {
     TO* orow = (TO*)p.out + (bi * p.Hq + g * R + hh) * D;
@@ -1310,13 +1318,13 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(AttnParams p) 
 }
 
 void launch_gather(const AttnParams& p, hipStream_t s, const KernelTimer* tm) {
-  const int64_t entries = (int64_t)p.B * p.G * p.S_q * p.topk;
+  const int64_t entries = (int64_t)p.B * p.G * p.nrows * p.topk;  // this pass's rows
   if (!p.direct) {
     timer_start(tm, kKernGather, s);
     hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)((p.nbuckets + 255) / 256)), dim3(256), 0, s,
                        p.counts, (int64_t)p.nbuckets);
     const bool lds_hist = p.nb <= kMaxHistBins;
-    const dim3 hgrid((unsigned)((p.S_q + kGatherRows - 1) / kGatherRows), (unsigned)(p.B * p.G));
+    const dim3 hgrid((unsigned)((p.nrows + kGatherRows - 1) / kGatherRows), (unsigned)(p.B * p.G));
     if (lds_hist)
       hipLaunchKernelGGL(gather_hist_kernel<false>, hgrid, dim3(256), p.nb * 4, s, p);
     else
@@ -1346,29 +1354,39 @@ static hipError_t launch_attn_t(const AttnParams& p, hipStream_t s, const Kernel
     }
   }
   if (!p.direct && p.tpi > kMaxItemTokens) return hipErrorInvalidValue;  // the item's entries must fit its LDS list
-  launch_gather(p, s, tm);
-  timer_start(tm, kKernAttention, s);
-  if (p.direct)
-    hipLaunchKernelGGL((attn_decode_kernel<T, S, D, R>), dim3(p.grid_decode), dim3(256), 0, s, p);
-  else
-    hipLaunchKernelGGL((attn_kvouter_kernel<T, S, D, R>), dim3(p.grid), dim3(256), 0, s, p);
-  timer_stop(tm, kKernAttention, s);
-  timer_start(tm, kKernCombine, s);
-  constexpr int E = 16 / (int)sizeof(T);
-  const int64_t units = (int64_t)p.B * p.S_q * p.G * (D * R / E);
-  const dim3 cgrid((unsigned)((units + kCombineThreads - 1) / kCombineThreads));
-  if (p.topk <= 16) {
-    if (p.out_f32) hipLaunchKernelGGL((combine_kernel<T, float, D, R, 16>), cgrid, dim3(kCombineThreads), 0, s, p);
-    else hipLaunchKernelGGL((combine_kernel<T, T, D, R, 16>), cgrid, dim3(kCombineThreads), 0, s, p);
-  } else if (p.topk <= 32) {
-    if (p.out_f32) hipLaunchKernelGGL((combine_kernel<T, float, D, R, 32>), cgrid, dim3(kCombineThreads), 0, s, p);
-    else hipLaunchKernelGGL((combine_kernel<T, T, D, R, 32>), cgrid, dim3(kCombineThreads), 0, s, p);
-  } else {
-    if (p.out_f32) hipLaunchKernelGGL((combine_kernel<T, float, D, R, 64>), cgrid, dim3(kCombineThreads), 0, s, p);
-    else hipLaunchKernelGGL((combine_kernel<T, T, D, R, 64>), cgrid, dim3(kCombineThreads), 0, s, p);
+  // One pass over all query rows, or (workspace capped) passes over chunks of
+  // chunk_rows rows that share the gather buckets and the partial-state region.
+  const int step = p.direct || p.chunk_rows <= 0 ? p.S_q : p.chunk_rows;
+  for (int r0 = 0; r0 < p.S_q; r0 += step) {
+    AttnParams pc = p;
+    pc.row0 = r0;
+    pc.nrows = min(step, p.S_q - r0);
+    launch_gather(pc, s, tm);
+    timer_start(tm, kKernAttention, s);
+    if (pc.direct)
+      hipLaunchKernelGGL((attn_decode_kernel<T, S, D, R>), dim3(pc.grid_decode), dim3(256), 0, s, pc);
+    else
+      hipLaunchKernelGGL((attn_kvouter_kernel<T, S, D, R>), dim3(pc.grid), dim3(256), 0, s, pc);
+    timer_stop(tm, kKernAttention, s);
+    timer_start(tm, kKernCombine, s);
+    constexpr int E = 16 / (int)sizeof(T);
+    const int64_t units = (int64_t)pc.B * pc.nrows * pc.G * (D * R / E);
+    const dim3 cgrid((unsigned)((units + kCombineThreads - 1) / kCombineThreads));
+    if (pc.topk <= 16) {
+      if (pc.out_f32) hipLaunchKernelGGL((combine_kernel<T, float, D, R, 16>), cgrid, dim3(kCombineThreads), 0, s, pc);
+      else hipLaunchKernelGGL((combine_kernel<T, T, D, R, 16>), cgrid, dim3(kCombineThreads), 0, s, pc);
+    } else if (pc.topk <= 32) {
+      if (pc.out_f32) hipLaunchKernelGGL((combine_kernel<T, float, D, R, 32>), cgrid, dim3(kCombineThreads), 0, s, pc);
+      else hipLaunchKernelGGL((combine_kernel<T, T, D, R, 32>), cgrid, dim3(kCombineThreads), 0, s, pc);
+    } else {
+      if (pc.out_f32) hipLaunchKernelGGL((combine_kernel<T, float, D, R, 64>), cgrid, dim3(kCombineThreads), 0, s, pc);
+      else hipLaunchKernelGGL((combine_kernel<T, T, D, R, 64>), cgrid, dim3(kCombineThreads), 0, s, pc);
+    }
+    timer_stop(tm, kKernCombine, s);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
-  timer_stop(tm, kKernCombine, s);
-  return hipGetLastError();
+  return hipSuccess;
 }
 
 template <typename T, typename S, int D>

@@ -151,6 +151,11 @@ struct AttnParams {
   float* part_lse;     // log2 of sum_j 2^(s'_j), s' = scale * log2(e) * q.k
   int64_t q_offset;
   int B, S_q, S_k, Hq, G, r, d, topk;
+  // Query rows [row0, row0 + nrows) of every sequence are gathered, attended and
+  // combined by one pass; the partial states hold those rows only, indexed
+  // ((b * nrows + i - row0) * G + g) * topk + slot.  One pass covers all rows
+  // unless the caller capped the workspace (chunk_rows < S_q).
+  int row0, nrows, chunk_rows;
   int nb;              // key blocks per sequence, ceil(S_k / 128)
   int nbuckets;        // B * G * nb
   int tpi;             // query tokens per work item

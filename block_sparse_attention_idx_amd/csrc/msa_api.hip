@@ -53,7 +53,7 @@ bool scale_ok(float x) { return std::isfinite(x) && x >= 0.0f; }
 msa_status check_shape(const msa_shape* s, int op) {
   if (!s) return fail(MSA_ERR_INVALID, "shape is NULL");
   static_assert(sizeof(msa_shape) == 72, "msa_shape layout");
-  if (s->pad != 0) return fail(MSA_ERR_INVALID, "msa_shape padding field must be 0");
+  if (s->workspace_cap_mib < 0) return fail(MSA_ERR_INVALID, "workspace_cap_mib must be >= 0");
   if (s->cache_format != MSA_CACHE_NATIVE && s->cache_format != MSA_CACHE_FP8_E4M3)
     return fail(MSA_ERR_INVALID, "unknown cache_format %d", s->cache_format);
   if (s->batch < 1) return fail(MSA_ERR_INVALID, "batch must be >= 1 (got %d)", s->batch);
@@ -245,8 +245,10 @@ struct AttnPlan {
   size_t bytes;
 };
 
-// tpi: query tokens per work item of the gather
-AttnPlan plan_attn(const msa_shape* s, const msa_kv_cache* cache, int tpi = kTokensPerItem) {
+// tpi: query tokens per work item of the gather; fwd_main: the forward's main
+// branch (msa_sparse_attn_fwd, msa_fwd), whose partial states the shape's
+// workspace_cap_mib may bound
+AttnPlan plan_attn(const msa_shape* s, const msa_kv_cache* cache, int tpi = kTokensPerItem, bool fwd_main = false) {
   AttnPlan ap{};
   msa::AttnParams& p = ap.p;
   p.cm = cache_map(cache);
@@ -281,8 +283,19 @@ AttnPlan plan_attn(const msa_shape* s, const msa_kv_cache* cache, int tpi = kTok
   p.v_scale = s->v_scale != 0.0f ? s->v_scale : 1.0f;
   p.out_f32 = s->out_dtype == MSA_F32 ? 1 : 0;
 
+  p.row0 = 0;
+  p.nrows = p.chunk_rows = p.S_q;
+  if (fwd_main && !p.direct && s->workspace_cap_mib > 0) {
+    // rows per chunk: the partial states (and gather entries) of that many rows of
+    // every sequence fit the cap; full gather tiles when the cap allows them
+    const size_t per_row = (size_t)p.B * p.G * p.topk * ((size_t)p.r * (p.d * elem_bytes(s->dtype) + 4) + 4);
+    const size_t cap = (size_t)s->workspace_cap_mib << 20;
+    int64_t rows = std::max<int64_t>(1, (int64_t)(cap / per_row));
+    if (rows >= 256) rows = rows / 256 * 256;
+    p.chunk_rows = (int)std::min<int64_t>(rows, p.S_q);
+  }
   const size_t nbk = (size_t)p.nbuckets + 1;
-  const size_t entries = (size_t)p.B * p.G * p.S_q * p.topk;
+  const size_t entries = (size_t)p.B * p.G * p.chunk_rows * p.topk;  // the partial states one pass holds
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t o = off;
@@ -445,13 +458,13 @@ size_t msa_workspace_size_kvcache(const msa_shape* s, const msa_kv_cache* cache,
   if (op >= MSA_OP_INDEX_SELECT && op <= MSA_OP_SPARSE_ATTN_BWD && check_shape(s, op) == MSA_OK &&
       check_cache(s, cache) == MSA_OK && s->q_len > 0) {
     if (op == MSA_OP_INDEX_SELECT) r = plan_index(s, cache).bytes;
-    else if (op == MSA_OP_SPARSE_ATTN) r = plan_attn(s, cache).bytes;
+    else if (op == MSA_OP_SPARSE_ATTN) r = plan_attn(s, cache, kTokensPerItem, true).bytes;
     else if (op == MSA_OP_KL_TEACHER) r = plan_attn(s, cache, msa::kKlTokensPerItem).bytes;
     else if (op == MSA_OP_SPARSE_ATTN_BWD) {
       size_t od = 0;
       r = cache ? 0 : plan_bwd(s, &od).bytes;
     }
-    else r = sel_bytes(s) + std::max(plan_index(s, cache).bytes, plan_attn(s, cache).bytes);
+    else r = sel_bytes(s) + std::max(plan_index(s, cache).bytes, plan_attn(s, cache, kTokensPerItem, true).bytes);
   }
   g_last_error = saved;
   return r;
@@ -486,7 +499,7 @@ msa_status msa_sparse_attn_fwd_kvcache(const msa_shape* s, const msa_kv_cache* c
   if (st != MSA_OK || (st = check_cache(s, cache)) != MSA_OK) return st;
   if (!q || !k || !v || !sel || !out) return fail(MSA_ERR_INVALID, "q, k, v, sel and out must be non-NULL");
   if (s->q_len == 0) return MSA_OK;
-  AttnPlan ap = plan_attn(s, cache);
+  AttnPlan ap = plan_attn(s, cache, kTokensPerItem, true);
   if ((st = check_ws(ws, ws_bytes, ap.bytes)) != MSA_OK) return st;
   bind_attn(ap, (char*)ws);
   ap.p.q = q;
@@ -515,7 +528,7 @@ msa_status msa_fwd_kvcache(const msa_shape* s, const msa_kv_cache* cache, const 
     return fail(MSA_ERR_INVALID, "q, k, v, q_idx, k_idx and out must be non-NULL");
   if (s->q_len == 0) return MSA_OK;
   IndexPlan ip = plan_index(s, cache);
-  AttnPlan ap = plan_attn(s, cache);
+  AttnPlan ap = plan_attn(s, cache, kTokensPerItem, true);
   const size_t need = sel_bytes(s) + std::max(ip.bytes, ap.bytes);
   if ((st = check_ws(ws, ws_bytes, need)) != MSA_OK) return st;
   char* w = (char*)ws;
@@ -621,7 +634,7 @@ msa_status msa_fwd_noalloc(const msa_shape* s, const void* q, const void* k, con
     return fail(MSA_ERR_INVALID, "q, k, v, q_idx, k_idx and out must be non-NULL");
   if (s->q_len == 0) return MSA_OK;
   const size_t need =
-      sel_bytes(s) + std::max(plan_index(s, nullptr).bytes, plan_attn(s, nullptr).bytes);
+      sel_bytes(s) + std::max(plan_index(s, nullptr).bytes, plan_attn(s, nullptr, kTokensPerItem, true).bytes);
   if (need > kScratchBytes)
     return fail(MSA_ERR_WORKSPACE, "this shape needs %zu bytes of scratch; msa_fwd_noalloc holds %zu (use msa_fwd)",
                 need, kScratchBytes);

@@ -111,8 +111,17 @@ typedef struct {
   int32_t out_dtype;    /* msa_dtype of out                                     */
   float k_scale;        /* keys attended to are k_scale * k; 0 means 1          */
   float v_scale;        /* values attended to are v_scale * v; 0 means 1        */
-  int32_t pad;          /* must be 0                                            */
+  int32_t workspace_cap_mib; /* 0, or a bound on the main branch's partial states */
 } msa_shape;            /* 72 bytes                                             */
+
+/* workspace_cap_mib.  The KV-outer main branch keeps one partial softmax state
+ * per selection entry (about r * d * e bytes per (query row, group, slot); 16 GiB
+ * for B = 2, S_q = 32768, Hq = 64, d = 128, k = 16 in bf16).  With a cap > 0, a
+ * call that gathers queries (prefill; decode-sized calls never do) processes the
+ * query rows in chunks of as many rows of every sequence as keep the partial
+ * states within that many MiB (at least one row per chunk), reusing one region;
+ * msa_workspace_size reports the smaller workspace that results.  The results do
+ * not depend on the cap.  Negative values are invalid. */
 
 enum { MSA_OP_INDEX_SELECT = 0, MSA_OP_SPARSE_ATTN = 1, MSA_OP_FWD = 2, MSA_OP_KL_TEACHER = 3,
        MSA_OP_SPARSE_ATTN_BWD = 4 };

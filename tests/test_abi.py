@@ -40,7 +40,7 @@ def test_struct_layout_matches_header():
     assert msa.MsaShape.softmax_scale.offset == 48
     assert msa.MsaShape.k_scale.offset == 60
     assert msa.MsaShape.v_scale.offset == 64
-    assert msa.MsaShape.pad.offset == 68
+    assert msa.MsaShape.workspace_cap_mib.offset == 68
     text = open(HEADER).read()
     assert "MSA_CACHE_NATIVE = 0" in text and "MSA_CACHE_FP8_E4M3 = 1" in text
 
@@ -66,7 +66,7 @@ def _fwd(sh, ws=None, ws_bytes=0, **ptrs):
 @pytest.mark.parametrize("field,value,status", [
     ("batch", 0, -1), ("q_len", -1, -1), ("kv_len", 0, -1), ("q_offset", -5, -1), ("kv_len", 100, -1),
     ("num_q_heads", 62, -1), ("num_kv_heads", 0, -1), ("topk", 0, -1), ("block_size", 0, -1),
-    ("dtype", 7, -1), ("out_dtype", 9, -1), ("cache_format", 2, -1), ("cache_format", -1, -1), ("pad", 3, -1),
+    ("dtype", 7, -1), ("out_dtype", 9, -1), ("cache_format", 2, -1), ("cache_format", -1, -1), ("workspace_cap_mib", -3, -1),
     ("head_dim", 0, -1),
     ("block_size", 64, -2), ("topk", 65, -2), ("head_dim", 96, -2), ("index_dim", 48, -2),
     ("num_q_heads", 12, -2),

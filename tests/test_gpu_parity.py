@@ -286,3 +286,72 @@ def test_random_shapes_wide_k(seed):
     _check_sel_rows(sel, ref_sel)
     assert _max_err(out, ref_out) <= TOL[dt]
     assert float(np.abs(lse.cpu().numpy() - ref_lse).max()) <= 1e-3
+
+
+@gpu
+@pytest.mark.parametrize("out_f32", [False, True])
+def test_given_selection_with_invalid_ids_r16_d128(out_f32):
+    # The prefill shape of the workloads (16 query heads per group, d = 128, bf16)
+    # with a caller's selection holding ids past the cache, after the row's own
+    # block and -1 padding in any position: those are ignored, the rest is exact
+    # attention; fp32 or bf16 output, lse
+    msa = _msa()
+    s = synth.Shape(2, 333, 1400, 900, 32, 2, 128, 64, 7, dtype="bf16")
+    x, xh = _inputs(s, 12)
+    f = {n: synth.as_f64(t) for n, t in xh.items()}
+    good = orc.index_select(f["q_idx"], f["k_idx"], s.topk, s.q_offset)
+    bad = good.copy()
+    nb = (s.kv_len + 127) // 128
+    rng = np.random.default_rng(5)
+    for b in range(s.batch):
+        for g in range(s.groups):
+            for i in range(s.q_len):
+                row = [c for c in good[b, g, i] if c >= 0]
+                L = (s.q_offset + i) // 128
+                extra = [nb + 3, 10 ** 6, L + 1] if L + 1 < nb else [nb + 3, 10 ** 6]
+                row = row + extra[: s.topk - len(row)]
+                rng.shuffle(row)
+                bad[b, g, i, :len(row)] = row
+                bad[b, g, i, len(row):] = -1
+    out, lse = msa.sparse_attn_fwd(x["q"], x["k"], x["v"], torch.from_numpy(bad).cuda(), q_offset=s.q_offset,
+                                   out_dtype=torch.float32 if out_f32 else None, return_lse=True)
+    torch.cuda.synchronize()
+    ref, ref_lse = orc.sparse_attention(f["q"], f["k"], f["v"], good, s.q_offset)
+    assert _max_err(out, ref) <= TOL["bf16"]
+    assert float(np.abs(lse.cpu().numpy() - ref_lse).max()) <= 1e-3
+
+
+@gpu
+@pytest.mark.parametrize("case", ["large_logits", "all_scores_very_negative"])
+def test_extreme_logit_ranges(case):
+    # Scaled scores of several hundred, and rows whose every score is far below
+    # zero (exp of the raw scores would overflow or underflow in fp32): the block
+    # maxima subtracted inside the kernels keep both exact against the oracle.
+    msa = _msa()
+    s = synth.Shape(1, 200, 700, 500, 16, 1, 128, 32, 4, dtype="bf16")
+    x, xh = _inputs(s, 13)
+    q = xh["q"].float()
+    k = xh["k"].float()
+    if case == "large_logits":
+        q = q * 40.0                     # scaled scores of a few hundred (exponents far above 64)
+    else:
+        k[:] = k[:, :, :1, :]            # every key the same vector k0 ...
+        q[:] = -12.0 * k[:, :, :1, :].squeeze(1).unsqueeze(1).expand_as(q)  # ... and q = -12 k0: all scores << 0
+    qb, kb = q.to(torch.bfloat16), k.to(torch.bfloat16)
+    f = {n: synth.as_f64(t) for n, t in xh.items()}
+    f["q"], f["k"] = synth.as_f64(qb), synth.as_f64(kb)
+    sel = orc.index_select(f["q_idx"], f["k_idx"], s.topk, s.q_offset)
+    out, lse = msa.sparse_attn_fwd(qb.cuda(), kb.cuda(), x["v"], torch.from_numpy(sel).cuda(), q_offset=s.q_offset,
+                                   return_lse=True)
+    torch.cuda.synchronize()
+    ref, ref_lse = orc.sparse_attention(f["q"], f["k"], f["v"], sel, s.q_offset)
+    o = out.float().cpu().numpy().astype(np.float64)
+    assert np.isfinite(o).all()
+    # Such peaked rows put the whole weight on one or two keys, so an output can be
+    # a single value of v (|v| up to ~4.5 here) where one bf16 half-ulp is 2^-9 |v|.
+    # The partial state and the output are both rounded to bf16: two half-ulps on
+    # top of the bar that holds for the workloads' rows (whose outputs are averages).
+    bound = TOL["bf16"] + 2.0 * 2.0 ** -9 * np.abs(ref)
+    assert bool((np.abs(o - ref) <= bound).all()), float(np.abs(o - ref).max())
+    rel = np.abs(lse.cpu().numpy() - ref_lse) / np.maximum(1.0, np.abs(ref_lse))
+    assert float(rel.max()) <= 1e-4
