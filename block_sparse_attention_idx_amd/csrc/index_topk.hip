@@ -41,17 +41,21 @@ namespace msa {
 template <int CAP>
 __device__ __forceinline__ void list_insert(float (&s)[CAP], int (&id)[CAP], float x, int c) {
   // s is sorted descending; every index already present is smaller than c, so
-  // an equal score keeps the earlier (lower-index) entry first.
-  bool gt[CAP];
-#pragma unroll
-  for (int j = 0; j < CAP; ++j) gt[j] = x > s[j];
+  // an equal score keeps the earlier (lower-index) entry first.  Slot j takes
+  // s[j - 1] when x > s[j - 1], x when s[j] < x <= s[j - 1], else keeps s[j]:
+  // the median of the three.  The ids follow through bit masks, which keeps
+  // the update free of branches.
+  unsigned m_hi = x > s[CAP - 1] ? ~0u : 0u;  // x > s[j], for the slot j being updated
 #pragma unroll
   for (int j = CAP - 1; j >= 1; --j) {
-    s[j] = gt[j - 1] ? s[j - 1] : (gt[j] ? x : s[j]);
-    id[j] = gt[j - 1] ? id[j - 1] : (gt[j] ? c : id[j]);
+    const unsigned m_lo = x > s[j - 1] ? ~0u : 0u;
+    s[j] = __builtin_amdgcn_fmed3f(s[j - 1], x, s[j]);
+    const unsigned t = (m_lo & (unsigned)id[j - 1]) | (~m_lo & (unsigned)c);
+    id[j] = (int)((m_hi & t) | (~m_hi & (unsigned)id[j]));
+    m_hi = m_lo;
   }
-  s[0] = gt[0] ? x : s[0];
-  id[0] = gt[0] ? c : id[0];
+  s[0] = m_hi ? x : s[0];
+  id[0] = m_hi ? c : id[0];
 }
 
 // One (row, key split) result: with several splits the merged list goes to
@@ -173,7 +177,16 @@ __device__ __forceinline__ bool unit_of(const IndexParams& p, int lin, bool heav
     tg = u >> 7;
     return true;
   }
-  const int logical = (p.nsplit > 1 || !heavy_first) ? (lin & 7) * p.grid_per_xcd + (lin >> 3) : p.nunits - 1 - lin;
+  if (p.nsplit == 1 && heavy_first) {
+    // heaviest row tiles first, the sequences interleaved: workgroup lin goes
+    // to XCD lin % 8, so each XCD gets the tiles of as few sequences as possible
+    // (one when B divides 8), whose k_idx blocks its running tiles share in L2
+    if (lin >= p.nunits) return false;
+    split = 0;
+    tg = (lin % p.B) * p.ntile + p.ntile - 1 - lin / p.B;
+    return true;
+  }
+  const int logical = (lin & 7) * p.grid_per_xcd + (lin >> 3);
   if (logical < 0 || logical >= p.nunits) return false;
   split = logical / p.ntile_total;
   tg = logical - split * p.ntile_total;
@@ -214,8 +227,26 @@ __global__ __launch_bounds__(1024) void index_units_kernel(IndexParams p) {
   if (threadIdx.x == 1023) *p.unit_count = s_cnt[1023];
 }
 
+// Issue order of one accumulator chain of index_topk_kernel: each of its N
+// products is followed by up to V VALU instructions and, when DS, one LDS read.
+template <int N, int V, bool DS>
+__device__ __forceinline__ void chain_schedule() {
+  if constexpr (N > 0) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, V, 0);
+    if constexpr (DS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    chain_schedule<N - 1, V, DS>();
+  }
+}
+
+// Keeps the work producing x where it stands in program order: the empty asm
+// takes x in a VGPR and counts as a side effect, so the optimisers cannot sink
+// that work past the scheduling fences that follow.
+__device__ __forceinline__ void pin(float& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void pin(int& x) { asm volatile("" : "+v"(x)); }
+
 template <typename T, typename S, int DI, int CAP, int RT>
-__global__ __launch_bounds__(256, CAP == kIndexWideCap || sizeof(T) != 2 ? 1 : 2) void index_topk_kernel(IndexParams p) {
+__global__ __launch_bounds__(64 * index_waves(CAP + 1, sizeof(T) == 2), 1) void index_topk_kernel(IndexParams p) {
   using M = Mma<T>;
   using frag = typename M::frag;
   constexpr int KPL = M::KPL, KSTEP = M::KSTEP, NKS = DI / KSTEP;
@@ -229,26 +260,35 @@ __global__ __launch_bounds__(256, CAP == kIndexWideCap || sizeof(T) != 2 ? 1 : 2
   constexpr int TILE_BYTES = kBlock * RB;
   auto sw = [](int r) { return (r >> SWS) & (CPR - 1); };
   auto at = [&](int r, int col) { return r * DI + (((col / EPC) ^ sw(r)) * EPC) + col % EPC; };
+  constexpr int kWaves = index_waves(CAP + 1, sizeof(T) == 2);
+  constexpr int NT = 64 * kWaves;
   // native bf16 keys go straight from HBM into the tile (no registers); e4m3
   // and fp32 keys are staged through registers
-  constexpr bool kDma = std::is_same<S, T>::value && sizeof(T) == 2 && TILE_BYTES % 4096 == 0;
+  constexpr bool kDma = std::is_same<S, T>::value && sizeof(T) == 2 && TILE_BYTES % (kWaves * 1024) == 0;
   constexpr int ROWS_WAVE = 32 * RT;
-  constexpr int ROWS_WG = 4 * ROWS_WAVE;
+  constexpr int ROWS_WG = kWaves * ROWS_WAVE;
   // staging: 16-byte chunks of k_idx in its storage type S; a chunk holds SE
   // keys' elements and widens to SE / (16 / sizeof(T)) chunks of T in LDS
   constexpr int SE = 16 / (int)sizeof(S);
   constexpr int CH_PER_ROW = DI / SE;
-  constexpr int CH_PER_THREAD = kDma ? 1 : kBlock * CH_PER_ROW / 256;
-  static_assert(kDma || (CH_PER_THREAD >= 1 && (kBlock * CH_PER_ROW) % 256 == 0), "staging split");
-  constexpr int KS_BYTES = 2 * TILE_BYTES;
+  constexpr int CH_TOTAL = kBlock * CH_PER_ROW;  // staged chunks per block: chunk threadIdx.x + u NT, u < CH_PER_THREAD
+  constexpr int CH_PER_THREAD = kDma ? 1 : (CH_TOTAL + NT - 1) / NT;
+  static_assert(kDma || CH_TOTAL % NT == 0 || CH_TOTAL < NT, "staging split");
+  // LDS tiles: a ring of NBUF with native keys (DMA runs NBUF - 1 blocks
+  // ahead; the workgroup has the CU's LDS to itself), two with staged keys
+  constexpr int NBUF = kDma ? 4 : 2;
+  constexpr int KS_BYTES = NBUF * TILE_BYTES;
   constexpr bool kWide = CAP == kIndexWideCap;      // lane halves write their own lists
-  constexpr int LIST_BYTES = kWide ? 0 : 4 * 2 * CAP * 32 * 8;  // one row tile of lists, all waves
+  constexpr int LIST_BYTES = kWide ? 0 : kWaves * 2 * CAP * 32 * 8;  // one row tile of lists, all waves
   constexpr int SMEM = KS_BYTES > LIST_BYTES ? KS_BYTES : LIST_BYTES;
+  static_assert(SMEM <= 160 * 1024, "LDS of one CU");
   __shared__ __align__(16) char smem[SMEM];
-  T* Ks = (T*)smem;  // [2][kBlock * DI]
+  T* Ks = (T*)smem;  // [NBUF][kBlock * DI]
 
   int tg, split;
   if (!unit_of(p, blockIdx.x, true, tg, split)) return;
+  tg = __builtin_amdgcn_readfirstlane(tg);  // uniform: block and page indices stay in scalar registers
+  split = __builtin_amdgcn_readfirstlane(split);
   const int b = tg / p.ntile;
   const int tile = tg - b * p.ntile;
   const int n_first = tile * ROWS_WG;
@@ -262,7 +302,6 @@ __global__ __launch_bounds__(256, CAP == kIndexWideCap || sizeof(T) != 2 ? 1 : 2
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int h = lane >> 5, l32 = lane & 31;
-  const bool wave_active = n_first + wave * ROWS_WAVE < p.rows_per_b;
 
   int rowL[RT];
   bool rvalid[RT];
@@ -289,13 +328,28 @@ __global__ __launch_bounds__(256, CAP == kIndexWideCap || sizeof(T) != 2 ? 1 : 2
     }
 
   const S* kpool = (const S*)p.k_idx;
-  // K tiles are prefetched two blocks ahead: `pre` holds block c + 1 (stored to
-  // LDS after block c is scored), `pre2` is in flight for block c + 2.  Native
-  // vector types keep both in registers.
+  // Keys arrive PD blocks ahead of the block being scored.  Native bf16 keys go
+  // by DMA into a ring of NBUF LDS tiles, PD = NBUF - 1 blocks ahead; staged
+  // keys are loaded two blocks ahead into registers (`pre` holds block c + 1,
+  // stored to the other tile after block c is scored, `pre2` is in flight for
+  // block c + 2).  Past the range's end the last block is fetched again into a
+  // tile nobody reads, so every block runs the same straight-line code.
+  constexpr int PD = kDma ? NBUF - 1 : 2;
   i32x4 pre[CH_PER_THREAD], pre2[CH_PER_THREAD];
-  auto kblock = [&](int c) {  // an unmapped page is read from the pool start and scored -inf
-    const int64_t o = block_offset(p.cm, p.S_k, 1, DI, b, 0, c);
-    return (const i32x4*)(kpool + (o < 0 ? 0 : o));
+  // Element offset of block c in the key pool and whether its page is mapped
+  // (an unmapped page is read from the pool start and scored -inf).  The page
+  // id is a scalar load (the constant address space), so it does not count
+  // against the vector loads in flight that the ring's waits count.
+  typedef const int32_t __attribute__((address_space(4))) cint32;
+  auto lookup = [&](int c, int64_t& off, bool& mapped) {
+    if (!p.cm.pages) {
+      mapped = true;
+      off = ((int64_t)b * p.S_k + (int64_t)c * kBlock) * DI;
+      return;
+    }
+    const int pg = ((cint32*)p.cm.pages)[(int64_t)b * p.cm.max_pages + c];
+    mapped = pg >= 0 && pg < p.cm.num_pages;
+    off = mapped ? (int64_t)pg * kBlock * DI : 0;
   };
   // one staged chunk into the LDS tile: SE elements from column col of a row
   auto stage = [&](T* tile, int ch, i32x4 x) {
@@ -309,114 +363,218 @@ __global__ __launch_bounds__(256, CAP == kIndexWideCap || sizeof(T) != 2 ? 1 : 2
       *(i32x4*)&tile[at(row, col + 8)] = i32x4{(int)c2.x, (int)c2.y, (int)d2.x, (int)d2.y};
     }
   };
-  // native keys: block c straight into tile bi.  Wave w fills 1 KiB pieces
+  auto load_staged = [&](i32x4(&dst)[CH_PER_THREAD], int64_t off) {
+    const i32x4* src = (const i32x4*)(kpool + off);
+#pragma unroll
+    for (int u = 0; u < CH_PER_THREAD; ++u)
+      if (threadIdx.x + u * NT < CH_TOTAL) dst[u] = src[threadIdx.x + u * NT];
+  };
+  auto stage_all = [&](T* tile, const i32x4(&src)[CH_PER_THREAD]) {
+#pragma unroll
+    for (int u = 0; u < CH_PER_THREAD; ++u)
+      if (threadIdx.x + u * NT < CH_TOTAL) stage(tile, threadIdx.x + u * NT, src[u]);
+  };
+  // native keys: a block straight into tile bi.  Wave w fills 1 KiB pieces
   // (w * NU + u) of the tile; the hardware puts lane L's 16 bytes at byte 16 L
   // of a piece, so lane L reads the chunk the swizzle assigns to that slot.
-  constexpr int NU = TILE_BYTES / 4096;
-  auto dma_block = [&](int c, int bi) {
-    const char* src = (const char*)kblock(c);
+  constexpr int NU = kDma ? TILE_BYTES / (kWaves * 1024) : 1;
+  uint32_t dma_src[NU];  // byte offset within the block of lane L's chunk of piece u
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    const int kb = (wave * NU + u) * 1024 + lane * 16;
+    const int r = kb / RB, pc = (kb % RB) / 16;
+    dma_src[u] = (uint32_t)(r * RB + (pc ^ sw(r)) * 16);
+  }
+  auto dma_block = [&](int64_t off, int bi) {
+    const char* src = (const char*)(kpool + off);
     char* tile = smem + bi * TILE_BYTES;
 #pragma unroll
-    for (int u = 0; u < NU; ++u) {
-      const int piece = (wave * NU + u) * 1024;
-      const int kb = piece + lane * 16;
-      const int r = kb / RB, pc = (kb % RB) / 16;
-      __builtin_amdgcn_global_load_lds((const void*)(src + r * RB + (pc ^ sw(r)) * 16),
-                                       (__attribute__((address_space(3))) void*)(tile + piece), 16, 0, 0);
-    }
+    for (int u = 0; u < NU; ++u)
+      __builtin_amdgcn_global_load_lds((const void*)(src + dma_src[u]),
+                                       (__attribute__((address_space(3))) void*)(tile + (wave * NU + u) * 1024), 16,
+                                       0, 0);
   };
-  if (kDma) {
-    if (has_blocks) dma_block(c_begin, 0);
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's pieces are in LDS
-  } else if (has_blocks) {
-    const i32x4* src = kblock(c_begin);
-#pragma unroll
-    for (int u = 0; u < CH_PER_THREAD; ++u) pre[u] = src[threadIdx.x + u * 256];
-    if (c_begin + 1 < c_end) {
-      const i32x4* src1 = kblock(c_begin + 1);
-#pragma unroll
-      for (int u = 0; u < CH_PER_THREAD; ++u) pre2[u] = src1[threadIdx.x + u * 256];
-    }
-#pragma unroll
-    for (int u = 0; u < CH_PER_THREAD; ++u) stage(Ks, threadIdx.x + u * 256, pre[u]);
-#pragma unroll
-    for (int u = 0; u < CH_PER_THREAD; ++u) pre[u] = pre2[u];
-  }
-  __syncthreads();
+  // Wait until at most n of this wave's vector loads are in flight (s_waitcnt
+  // vmcnt(n); the export and LDS counters are left alone).
+  auto wait_vm = [](auto n_tag) {
+    constexpr int n = decltype(n_tag)::value;
+    static_assert(n >= 0 && n < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+  };
+  using kRingWait = std::integral_constant<int, (PD - 1) * NU>;  // block c + 1 landed, c + 2 .. c + PD in flight
+  // Workgroup barrier of the block loop.  With DMA it leaves out the release
+  // fence of __syncthreads(), which would wait for every DMA in flight (they
+  // count as LDS writes), the ring's later blocks included: this wave's LDS
+  // accesses are complete (lgkmcnt 0), its pieces of the next block have landed
+  // (wait_vm before it), and the asm's memory clobber keeps the compiler from
+  // moving memory operations across it.
+  auto block_barrier = [] {
+    if constexpr (kDma) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else __syncthreads();
+  };
 
-  float pmA[RT], pmB[RT];
-  int buf = 0;
-  for (int c = c_begin; c < c_end; ++c) {
-    const bool has_next = c + 1 < c_end;
-    if (kDma) {
-      // block c + 1 into the other tile (its last readers, block c - 1, passed the barrier)
-      if (has_next) dma_block(c + 1, buf ^ 1);
-    } else if (c + 2 < c_end) {
-      const i32x4* src = kblock(c + 2);
+  // mq: bit j = block c + j is mapped, for the block c about to be scored;
+  // off_ahead: offset of block c + PD, whose keys that block's code loads
+  int mq = 0;
+  int64_t off_ahead = 0;
+  if (has_blocks) {
+    int64_t o;
+    bool m;
+    lookup(c_begin, o, m);
+    mq |= (int)m;
+    if constexpr (kDma) {
+      dma_block(o, 0);
 #pragma unroll
-      for (int u = 0; u < CH_PER_THREAD; ++u) pre2[u] = src[threadIdx.x + u * 256];
-    }
-    // block max of scores q_idx . k_idx over the block's 128 keys, one 32-key
-    // tile of accumulators at a time
-    float pm[RT];
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) pm[rt] = kNegInf;
-    if (wave_active) {
-      const T* kt_base = Ks + buf * (kBlock * DI);
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        f32x16 acc[RT];
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) acc[rt] = f32x16{};
-        // the tile's A operands all in flight before the first product
-        frag a[NKS];
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) a[ks] = *(const frag*)&kt_base[at(kt * 32 + l32, ks * KSTEP + h * KPL)];
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks)
-#pragma unroll
-          for (int rt = 0; rt < RT; ++rt) acc[rt] = M::mma(a[ks], qf[rt][ks], acc[rt]);
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-          for (int j = 0; j < 16; ++j) pm[rt] = fmaxf(pm[rt], acc[rt][j]);
+      for (int j = 1; j < PD; ++j) {
+        int64_t oj;
+        bool mj;
+        lookup(min(c_begin + j, c_end - 1), oj, mj);
+        dma_block(oj, j);
       }
-      if (!block_mapped(p.cm, b, c)) {
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) pm[rt] = kNegInf;
-      }
-    }
-    if (kDma) {
-      __builtin_amdgcn_s_waitcnt(0);  // this wave's pieces of block c + 1 are in LDS
-    } else if (has_next) {
-#pragma unroll
-      for (int u = 0; u < CH_PER_THREAD; ++u) stage(Ks + (buf ^ 1) * (kBlock * DI), threadIdx.x + u * 256, pre[u]);
+    } else {
+      load_staged(pre, o);
+      int64_t o1;
+      bool m1;
+      lookup(min(c_begin + 1, c_end - 1), o1, m1);
+      load_staged(pre2, o1);
+      stage_all(Ks, pre);
 #pragma unroll
       for (int u = 0; u < CH_PER_THREAD; ++u) pre[u] = pre2[u];
     }
-    __syncthreads();
-    buf ^= 1;
-    // blocks pair up: lanes of half 0 rank the even one, half 1 the odd one
-    const bool second = ((c - c_begin) & 1) != 0;
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      if (!second) pmA[rt] = pm[rt];
-      else pmB[rt] = pm[rt];
+    for (int j = 1; j <= PD; ++j) {
+      lookup(min(c_begin + j, c_end - 1), o, m);
+      mq |= (int)m << j;
+      off_ahead = o;
     }
-    if (second || c + 1 == c_end) {
-      const int c0 = second ? c - 1 : c;
+    if constexpr (kDma) wait_vm(kRingWait{});  // this wave's pieces of block c_begin are in LDS
+  }
+  block_barrier();
+
+  // Software pipeline of one wave.  A block is 4 key tiles x RT row tiles =
+  // 4 RT accumulator chains of NKS products; chain q accumulates into acc[q & 1].
+  // While chain q runs on the matrix core the lanes fold chain q - 1's finished
+  // tile into the running block max (and, in the first block of a pair, rank
+  // the previous pair), and after a key tile's last chain the next key tile's
+  // A operands are loaded into the registers that chain has finished with.
+  // (bf16 operands; fp32 ones have too few registers left for the overlap, so
+  // their chains are folded as they finish and operands load per key tile)
+  constexpr bool kPipe = sizeof(T) == 2;
+  float pm[RT], pmA[RT], pmB[RT];
+  f32x16 acc[2];
+  frag a[NKS];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) pm[rt] = pmA[rt] = pmB[rt] = kNegInf;
+  auto fold = [&](float& m, const f32x16& t) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) m = fmaxf(m, t[j]);
+  };
+  // Blocks pair up: lanes of half 0 insert the first block of a pair into their
+  // row's list, lanes of half 1 the second (one exchange of the half maxima).
+  auto rank_pair = [&](int rt, int c0) {
+    // lanes 0-31 get block c0's full max, lanes 32-63 block c0 + 1's
+    const auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(pmA[rt]), __float_as_uint(pmB[rt]), false, false);
+    const int cc = c0 + h;
+    const bool keep = rvalid[rt] & (cc < rowL[rt]);
+    const float full = keep ? fmaxf(__uint_as_float(x[0]), __uint_as_float(x[1])) : kNegInf;
+    list_insert<CAP>(ls[rt], li[rt], full, cc);
+  };
+  int buf = 0;  // the tile of the block being scored
+  auto score_block = [&](int c, auto first_of_pair) {
+    constexpr bool kFirst = decltype(first_of_pair)::value;
+    const T* tile = Ks + buf * (kBlock * DI);
+    const int ahead = buf + PD >= NBUF ? buf + PD - NBUF : buf + PD;  // the tile of block c + PD
+    if constexpr (kDma) dma_block(off_ahead, ahead);  // its last reader, block c - 1, passed the barrier
+    else load_staged(pre2, off_ahead);
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) a[ks] = *(const frag*)&tile[at(l32, ks * KSTEP + h * KPL)];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) pm[rt] = kNegInf;
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
-        const float b_val = second ? pmB[rt] : kNegInf;
-        const float mine = h ? b_val : pmA[rt];
-        const float send = h ? pmA[rt] : b_val;
-        float full = fmaxf(mine, __shfl_xor(send, 32));
-        const int cc = c0 + h;
-        if (!rvalid[rt] || cc >= rowL[rt]) full = kNegInf;
-        list_insert<CAP>(ls[rt], li[rt], full, cc);
+        // stage q: chain q's products; between them chain q - 1's fold, in the
+        // first block of a pair the previous pair's ranking (one row tile in
+        // each of stages 1 .. RT), and after a key tile's last row tile the
+        // next key tile's operands
+        const int q = kt * RT + rt;
+        if (!kPipe && rt == 0 && kt > 0) {
+#pragma unroll
+          for (int ks = 0; ks < NKS; ++ks) a[ks] = *(const frag*)&tile[at(kt * 32 + l32, ks * KSTEP + h * KPL)];
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        f32x16 t = M::mma(a[0], qf[rt][0], f32x16{});
+#pragma unroll
+        for (int ks = 1; ks < NKS; ++ks) t = M::mma(a[ks], qf[rt][ks], t);
+        const bool loads = kPipe && rt == RT - 1 && kt < 3;
+        if (loads) {
+#pragma unroll
+          for (int ks = 0; ks < NKS; ++ks)
+            a[ks] = *(const frag*)&tile[at((kt + 1) * 32 + l32, ks * KSTEP + h * KPL)];
+        }
+        if (!kPipe) {
+          fold(pm[rt], t);
+          pin(pm[rt]);
+        } else if (q > 0) {
+          fold(pm[(q - 1) % RT], acc[(q - 1) & 1]);
+          pin(pm[(q - 1) % RT]);
+        }
+        const bool ranks = kFirst && q >= 1 && q <= RT;
+        if (ranks) {
+          rank_pair(q - 1, c - 2);
+#pragma unroll
+          for (int j = 0; j < CAP; ++j) {
+            pin(ls[q - 1][j]);
+            pin(li[q - 1][j]);
+          }
+        }
+        if constexpr (kPipe) {
+          if (ranks && loads) chain_schedule<NKS, 12, true>();
+          else if (ranks) chain_schedule<NKS, 12, false>();
+          else if (loads) chain_schedule<NKS, 2, true>();
+          else chain_schedule<NKS, 2, false>();
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        acc[q & 1] = t;
       }
     }
+    if (kPipe) fold(pm[RT - 1], acc[1]);  // the last chain (4 RT is even)
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const float v = (mq & 1) ? pm[rt] : kNegInf;
+      if constexpr (kFirst) pmA[rt] = v;
+      else pmB[rt] = v;
+    }
+    if constexpr (!kDma) {  // block c + 1 into the other tile; block c + 2 moves up
+      stage_all(Ks + (buf ^ 1) * (kBlock * DI), pre);
+#pragma unroll
+      for (int u = 0; u < CH_PER_THREAD; ++u) pre[u] = pre2[u];
+    }
+    {  // the block the next one fetches (page lookups stay out of the code above)
+      bool m;
+      lookup(min(c + 1 + PD, c_end - 1), off_ahead, m);
+      mq = (mq | ((int)m << (PD + 1))) >> 1;
+    }
+    if constexpr (kDma) wait_vm(kRingWait{});  // this wave's pieces of block c + 1 are in LDS
+    block_barrier();
+    buf = buf + 1 == NBUF ? 0 : buf + 1;
+  };
+  for (int c = c_begin; c < c_end; c += 2) {
+    score_block(c, std::true_type{});
+    if (c + 1 < c_end) score_block(c + 1, std::false_type{});
+  }
+  // the ring's last fetches (blocks past the range, into tiles nobody reads)
+  // land before the tiles are reused below or the workgroup's LDS is released
+  if constexpr (kDma) wait_vm(std::integral_constant<int, 0>{});
+  if (has_blocks) {  // the last pair (a single block: the second is empty)
+    if ((c_end - c_begin) & 1) {
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) pmB[rt] = kNegInf;
+    }
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) rank_pair(rt, c_begin + ((c_end - c_begin - 1) & ~1));
   }
 
   if constexpr (kWide) {  // list split * 2 + h of each row
@@ -429,7 +587,7 @@ __global__ __launch_bounds__(256, CAP == kIndexWideCap || sizeof(T) != 2 ? 1 : 2
   }
   // Merge the two half lists of each row through LDS (the K tiles are free
   // now), then write one list per (row, split).
-  float* xs = (float*)smem;                       // [4 waves][2 halves][CAP][32 rows]
+  float* xs = (float*)smem;                       // [kWaves][2 halves][CAP][32 rows]
   int* xi = (int*)(smem + LIST_BYTES / 2);
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
@@ -725,8 +883,9 @@ template <typename T, typename S, int DI, int CAP>
 static hipError_t launch_index_t(const IndexParams& p, hipStream_t s, const KernelTimer* tm) {
   timer_start(tm, kKernIndexScore, s);
   if (p.units) hipLaunchKernelGGL(index_units_kernel, dim3(1), dim3(1024), 0, s, p);
-  constexpr int RT = CAP <= 15 ? 2 : 1;
-  static_assert(4 * 32 * RT == index_rows_per_wg(CAP + 1), "host and kernel agree on the row tile");
+  constexpr int RT = index_row_tiles(CAP + 1);
+  constexpr int NT = 64 * index_waves(CAP + 1, sizeof(T) == 2);
+  static_assert(NT / 2 * RT == index_rows_per_wg(CAP + 1, sizeof(T) == 2), "host and kernel agree on the row tile");
   static_assert(index_cap(CAP + 1) == CAP, "host and kernel agree on the list length");
   bool small_done = false;
   if constexpr (sizeof(T) == 2) {  // the few-row form is built for bf16 queries
@@ -736,7 +895,7 @@ static hipError_t launch_index_t(const IndexParams& p, hipStream_t s, const Kern
     }
   }
   if (!small_done)
-    hipLaunchKernelGGL((index_topk_kernel<T, S, DI, CAP, RT>), dim3(p.grid_per_xcd * 8), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((index_topk_kernel<T, S, DI, CAP, RT>), dim3(p.grid_per_xcd * 8), dim3(NT), 0, s, p);
   timer_stop(tm, kKernIndexScore, s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

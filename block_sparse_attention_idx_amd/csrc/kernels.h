@@ -120,10 +120,14 @@ constexpr int merge_max_lists(int cap) {
                                                                            : kMergeMaxLists;
 }
 
-// Index rows per workgroup: 4 waves x 32 rows x RT row tiles, RT = 2 for lists
-// of up to 15 entries (k <= 16), 1 for the longer lists.
+// Index rows per workgroup: waves x 32 rows x RT row tiles, RT = 2 for lists
+// of up to 15 entries (k <= 16), 1 for the longer lists.  bf16 queries with
+// lists of up to 31 entries run 8 waves (one workgroup per CU, two waves per
+// SIMD); fp32 queries and lists of 63 fill a SIMD's registers with one wave,
+// so they run 4.
 constexpr int index_row_tiles(int topk) { return topk <= 16 ? 2 : 1; }
-constexpr int index_rows_per_wg(int topk) { return 4 * 32 * index_row_tiles(topk); }
+constexpr int index_waves(int topk, bool bf16) { return bf16 && index_cap(topk) != kIndexWideCap ? 8 : 4; }
+constexpr int index_rows_per_wg(int topk, bool bf16) { return index_waves(topk, bf16) * 32 * index_row_tiles(topk); }
 
 // fp8_keys: k_idx holds OCP FP8 E4M3 values (q_idx bf16).
 hipError_t launch_index_select(const IndexParams& p, bool bf16_inputs, bool fp8_keys, int index_dim, hipStream_t s,

@@ -177,7 +177,7 @@ IndexPlan plan_index(const msa_shape* s, const msa_kv_cache* cache) {
   p.q_offset = s->q_offset;
   p.rows_per_b = s->q_len * s->num_kv_heads;
   p.small = p.rows_per_b <= msa::kIndexSmallRows && s->dtype == MSA_BF16 ? 1 : 0;
-  p.rows_wg = p.small ? p.rows_per_b : msa::index_rows_per_wg(s->topk);
+  p.rows_wg = p.small ? p.rows_per_b : msa::index_rows_per_wg(s->topk, s->dtype == MSA_BF16);
   p.ntile = (int)ceil_div(p.rows_per_b, p.rows_wg);
   p.ntile_total = p.B * p.ntile;
   const int64_t Lmax = s->q_len > 0 ? max_pos(s, cache) / msa::kBlock : 0;
