@@ -58,6 +58,35 @@ __device__ __forceinline__ void list_insert(float (&s)[CAP], int (&id)[CAP], flo
   id[0] = m_hi ? c : id[0];
 }
 
+// Slots HI down to LO of list_insert.  Called for descending ranges in turn
+// (CAP - 1 first), it finds the slots above HI already updated and those from
+// LO - 1 down still as they were, which is all a slot's update reads.
+template <int CAP, int HI, int LO>
+__device__ __forceinline__ void list_insert_range(float (&s)[CAP], int (&id)[CAP], float x, int c) {
+  unsigned m_hi = x > s[HI] ? ~0u : 0u;
+#pragma unroll
+  for (int j = HI; j >= (LO > 1 ? LO : 1); --j) {
+    const unsigned m_lo = x > s[j - 1] ? ~0u : 0u;
+    s[j] = __builtin_amdgcn_fmed3f(s[j - 1], x, s[j]);
+    const unsigned t = (m_lo & (unsigned)id[j - 1]) | (~m_lo & (unsigned)c);
+    id[j] = (int)((m_hi & t) | (~m_hi & (unsigned)id[j]));
+    m_hi = m_lo;
+  }
+  if constexpr (LO == 0) {
+    s[0] = m_hi ? x : s[0];
+    id[0] = m_hi ? c : id[0];
+  }
+}
+
+// f(std::integral_constant<int, I>) for I = B .. E - 1, in order.
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
 // One (row, key split) result: with several splits the merged list goes to
 // the partial lists for topk_merge_kernel; with one split the first min(k-1, L)
 // entries are the selection, and the local block and -1 padding are added
@@ -328,13 +357,14 @@ __global__ __launch_bounds__(64 * index_waves(CAP + 1, sizeof(T) == 2), 1) void 
     }
 
   const S* kpool = (const S*)p.k_idx;
-  // Keys arrive PD blocks ahead of the block being scored.  Native bf16 keys go
-  // by DMA into a ring of NBUF LDS tiles, PD = NBUF - 1 blocks ahead; staged
-  // keys are loaded two blocks ahead into registers (`pre` holds block c + 1,
-  // stored to the other tile after block c is scored, `pre2` is in flight for
-  // block c + 2).  Past the range's end the last block is fetched again into a
-  // tile nobody reads, so every block runs the same straight-line code.
-  constexpr int PD = kDma ? NBUF - 1 : 2;
+  // Keys arrive ahead of the blocks being scored.  Native bf16 keys go by DMA
+  // into a ring of four LDS tiles a pair of blocks at a time: while one pair is
+  // scored from two tiles the next lands in the other two, and the workgroup
+  // meets at a barrier once per pair.  Staged keys are loaded two blocks ahead
+  // into registers (`pre` holds block c + 1, stored to the other of two tiles
+  // after block c is scored, `pre2` is in flight for block c + 2).  Past the
+  // range's end the last block is fetched again and its scores are dropped, so
+  // every block runs the same straight-line code.
   i32x4 pre[CH_PER_THREAD], pre2[CH_PER_THREAD];
   // Element offset of block c in the key pool and whether its page is mapped
   // (an unmapped page is read from the pool start and scored -inf).  The page
@@ -401,180 +431,193 @@ __global__ __launch_bounds__(64 * index_waves(CAP + 1, sizeof(T) == 2), 1) void 
     static_assert(n >= 0 && n < 64, "vmcnt range");
     __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));
   };
-  using kRingWait = std::integral_constant<int, (PD - 1) * NU>;  // block c + 1 landed, c + 2 .. c + PD in flight
   // Workgroup barrier of the block loop.  With DMA it leaves out the release
-  // fence of __syncthreads(), which would wait for every DMA in flight (they
-  // count as LDS writes), the ring's later blocks included: this wave's LDS
-  // accesses are complete (lgkmcnt 0), its pieces of the next block have landed
-  // (wait_vm before it), and the asm's memory clobber keeps the compiler from
-  // moving memory operations across it.
+  // fence of __syncthreads(), which waits for every load in flight: this
+  // wave's LDS accesses are complete (lgkmcnt 0), its DMA of the next pair has
+  // landed (wait_vm before it), and the asm's memory clobber keeps the compiler
+  // from moving memory operations across it.
   auto block_barrier = [] {
     if constexpr (kDma) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     else __syncthreads();
   };
 
-  // mq: bit j = block c + j is mapped, for the block c about to be scored;
-  // off_ahead: offset of block c + PD, whose keys that block's code loads
+  // mq: bit j = block c + j is mapped, for the block (staged) or pair (DMA) c
+  // about to be scored; off_n: offsets of the blocks its code fetches (c + 2 and,
+  // with DMA, c + 3)
   int mq = 0;
-  int64_t off_ahead = 0;
+  int64_t off_n[2] = {0, 0};
   if (has_blocks) {
-    int64_t o;
-    bool m;
-    lookup(c_begin, o, m);
-    mq |= (int)m;
-    if constexpr (kDma) {
-      dma_block(o, 0);
+    int64_t o[4];
+    bool m[4];
 #pragma unroll
-      for (int j = 1; j < PD; ++j) {
-        int64_t oj;
-        bool mj;
-        lookup(min(c_begin + j, c_end - 1), oj, mj);
-        dma_block(oj, j);
-      }
+    for (int j = 0; j < 4; ++j) {
+      lookup(min(c_begin + j, c_end - 1), o[j], m[j]);
+      mq |= (int)m[j] << j;
+    }
+    off_n[0] = o[2];
+    off_n[1] = o[3];
+    if constexpr (kDma) {
+      dma_block(o[0], 0);
+      dma_block(o[1], 1);
+      wait_vm(std::integral_constant<int, 0>{});  // this wave's pieces of the first pair are in LDS
     } else {
-      load_staged(pre, o);
-      int64_t o1;
-      bool m1;
-      lookup(min(c_begin + 1, c_end - 1), o1, m1);
-      load_staged(pre2, o1);
+      load_staged(pre, o[0]);
+      load_staged(pre2, o[1]);
       stage_all(Ks, pre);
 #pragma unroll
       for (int u = 0; u < CH_PER_THREAD; ++u) pre[u] = pre2[u];
     }
-#pragma unroll
-    for (int j = 1; j <= PD; ++j) {
-      lookup(min(c_begin + j, c_end - 1), o, m);
-      mq |= (int)m << j;
-      off_ahead = o;
-    }
-    if constexpr (kDma) wait_vm(kRingWait{});  // this wave's pieces of block c_begin are in LDS
   }
   block_barrier();
 
   // Software pipeline of one wave.  A block is 4 key tiles x RT row tiles =
   // 4 RT accumulator chains of NKS products; chain q accumulates into acc[q & 1].
   // While chain q runs on the matrix core the lanes fold chain q - 1's finished
-  // tile into the running block max (and, in the first block of a pair, rank
-  // the previous pair), and after a key tile's last chain the next key tile's
-  // A operands are loaded into the registers that chain has finished with.
-  // (bf16 operands; fp32 ones have too few registers left for the overlap, so
-  // their chains are folded as they finish and operands load per key tile)
+  // tile into the running block max, and after a key tile's last chain the
+  // next key tile's A operands are loaded into the registers that chain has
+  // finished with.  Blocks pair up: lanes of half 0 rank the first block of a
+  // pair for their row, lanes of half 1 the second (one exchange of the half
+  // maxima); a pair's ranking is spread over the next pair's 8 RT chains, a
+  // quarter of one row tile's list after every other chain.  (bf16 operands;
+  // fp32 ones have too few registers left for the overlap, so their chains are
+  // folded as they finish and their operands load per key tile.)
   constexpr bool kPipe = sizeof(T) == 2;
-  float pm[RT], pmA[RT], pmB[RT];
+  float pm[RT], pmA[RT], pmB[RT], full[RT];
+  int fullc = 0;  // block of this lane half's entry in the pair being ranked
   f32x16 acc[2];
   frag a[NKS];
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) pm[rt] = pmA[rt] = pmB[rt] = kNegInf;
+  for (int rt = 0; rt < RT; ++rt) pm[rt] = pmA[rt] = pmB[rt] = full[rt] = kNegInf;
   auto fold = [&](float& m, const f32x16& t) {
 #pragma unroll
     for (int j = 0; j < 16; ++j) m = fmaxf(m, t[j]);
   };
-  // Blocks pair up: lanes of half 0 insert the first block of a pair into their
-  // row's list, lanes of half 1 the second (one exchange of the half maxima).
-  auto rank_pair = [&](int rt, int c0) {
-    // lanes 0-31 get block c0's full max, lanes 32-63 block c0 + 1's
-    const auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(pmA[rt]), __float_as_uint(pmB[rt]), false, false);
-    const int cc = c0 + h;
-    const bool keep = rvalid[rt] & (cc < rowL[rt]);
-    const float full = keep ? fmaxf(__uint_as_float(x[0]), __uint_as_float(x[1])) : kNegInf;
-    list_insert<CAP>(ls[rt], li[rt], full, cc);
+  // the full block maxima of the pair c0, c0 + 1 from pmA / pmB: lanes 0-31 get
+  // block c0's, lanes 32-63 block c0 + 1's
+  auto pair_full = [&](int c0) {
+    fullc = c0 + h;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(pmA[rt]), __float_as_uint(pmB[rt]), false,
+                                                      false);
+      const bool keep = rvalid[rt] & (fullc < rowL[rt]);
+      full[rt] = keep ? fmaxf(__uint_as_float(x[0]), __uint_as_float(x[1])) : kNegInf;
+    }
   };
-  int buf = 0;  // the tile of the block being scored
-  auto score_block = [&](int c, auto first_of_pair) {
-    constexpr bool kFirst = decltype(first_of_pair)::value;
-    const T* tile = Ks + buf * (kBlock * DI);
-    const int ahead = buf + PD >= NBUF ? buf + PD - NBUF : buf + PD;  // the tile of block c + PD
-    if constexpr (kDma) dma_block(off_ahead, ahead);  // its last reader, block c - 1, passed the barrier
-    else load_staged(pre2, off_ahead);
+  // chunk k (0 .. 4 RT - 1) of ranking a pair: row tile k / 4, the k % 4-th
+  // quarter of its list's slots from the bottom
+  auto rank_chunk = [&](auto k_tag) {
+    constexpr int k = decltype(k_tag)::value, rt = k / 4, W = (CAP + 3) / 4;
+    constexpr int HI = CAP - 1 - (k % 4) * W, LO = HI - W + 1 > 0 ? HI - W + 1 : 0;
+    if constexpr (HI >= 0) {
+      list_insert_range<CAP, HI, LO>(ls[rt], li[rt], full[rt], fullc);
+#pragma unroll
+      for (int j = LO; j <= HI; ++j) {
+        pin(ls[rt][j]);
+        pin(li[rt][j]);
+      }
+    }
+  };
+  // block c from `tile`, the blk-th (0, 1) of its pair; valid: its max counts
+  auto score_block = [&](int c, auto blk_tag, const T* tile, bool valid) {
+    constexpr int blk = decltype(blk_tag)::value;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) a[ks] = *(const frag*)&tile[at(l32, ks * KSTEP + h * KPL)];
+    if constexpr (blk == 0) pair_full(c - 2);
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) pm[rt] = kNegInf;
     __builtin_amdgcn_sched_barrier(0);
+    static_for<0, 4 * RT>([&](auto q_tag) {
+      // stage q: chain q's products; between them chain q - 1's fold, every
+      // other stage a chunk of the previous pair's ranking, and after a key
+      // tile's last row tile the next key tile's operands
+      constexpr int q = decltype(q_tag)::value, kt = q / RT, rt = q % RT;
+      constexpr int sp = blk * 4 * RT + q;  // stage within the pair
+      constexpr bool ranks = sp % 2 == 1;
+      constexpr bool loads = kPipe && rt == RT - 1 && kt < 3;
+      if constexpr (!kPipe && rt == 0 && kt > 0) {
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        // stage q: chain q's products; between them chain q - 1's fold, in the
-        // first block of a pair the previous pair's ranking (one row tile in
-        // each of stages 1 .. RT), and after a key tile's last row tile the
-        // next key tile's operands
-        const int q = kt * RT + rt;
-        if (!kPipe && rt == 0 && kt > 0) {
-#pragma unroll
-          for (int ks = 0; ks < NKS; ++ks) a[ks] = *(const frag*)&tile[at(kt * 32 + l32, ks * KSTEP + h * KPL)];
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        f32x16 t = M::mma(a[0], qf[rt][0], f32x16{});
-#pragma unroll
-        for (int ks = 1; ks < NKS; ++ks) t = M::mma(a[ks], qf[rt][ks], t);
-        const bool loads = kPipe && rt == RT - 1 && kt < 3;
-        if (loads) {
-#pragma unroll
-          for (int ks = 0; ks < NKS; ++ks)
-            a[ks] = *(const frag*)&tile[at((kt + 1) * 32 + l32, ks * KSTEP + h * KPL)];
-        }
-        if (!kPipe) {
-          fold(pm[rt], t);
-          pin(pm[rt]);
-        } else if (q > 0) {
-          fold(pm[(q - 1) % RT], acc[(q - 1) & 1]);
-          pin(pm[(q - 1) % RT]);
-        }
-        const bool ranks = kFirst && q >= 1 && q <= RT;
-        if (ranks) {
-          rank_pair(q - 1, c - 2);
-#pragma unroll
-          for (int j = 0; j < CAP; ++j) {
-            pin(ls[q - 1][j]);
-            pin(li[q - 1][j]);
-          }
-        }
-        if constexpr (kPipe) {
-          if (ranks && loads) chain_schedule<NKS, 12, true>();
-          else if (ranks) chain_schedule<NKS, 12, false>();
-          else if (loads) chain_schedule<NKS, 2, true>();
-          else chain_schedule<NKS, 2, false>();
-        }
+        for (int ks = 0; ks < NKS; ++ks) a[ks] = *(const frag*)&tile[at(kt * 32 + l32, ks * KSTEP + h * KPL)];
         __builtin_amdgcn_sched_barrier(0);
-        acc[q & 1] = t;
       }
-    }
-    if (kPipe) fold(pm[RT - 1], acc[1]);  // the last chain (4 RT is even)
+      f32x16 t = M::mma(a[0], qf[rt][0], f32x16{});
+#pragma unroll
+      for (int ks = 1; ks < NKS; ++ks) t = M::mma(a[ks], qf[rt][ks], t);
+      if constexpr (loads) {
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) a[ks] = *(const frag*)&tile[at((kt + 1) * 32 + l32, ks * KSTEP + h * KPL)];
+      }
+      if constexpr (!kPipe) {
+        fold(pm[rt], t);
+        pin(pm[rt]);
+      } else if constexpr (q > 0) {
+        fold(pm[(q - 1) % RT], acc[(q - 1) & 1]);
+        pin(pm[(q - 1) % RT]);
+      }
+      if constexpr (ranks) rank_chunk(std::integral_constant<int, (sp - 1) / 2>{});
+      if constexpr (kPipe) chain_schedule<NKS, ranks ? 4 : 2, loads>();
+      __builtin_amdgcn_sched_barrier(0);
+      acc[q & 1] = t;
+    });
+    if constexpr (kPipe) fold(pm[RT - 1], acc[1]);  // the last chain (4 RT is even)
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-      const float v = (mq & 1) ? pm[rt] : kNegInf;
-      if constexpr (kFirst) pmA[rt] = v;
+      const float v = valid ? pm[rt] : kNegInf;
+      if constexpr (blk == 0) pmA[rt] = v;
       else pmB[rt] = v;
     }
-    if constexpr (!kDma) {  // block c + 1 into the other tile; block c + 2 moves up
-      stage_all(Ks + (buf ^ 1) * (kBlock * DI), pre);
+  };
+  int buf = 0;  // the tile of block c (DMA: of the pair's first block)
+  if constexpr (kDma) {
+    for (int c = c_begin; c < c_end; c += 2) {
+      // the next pair into the other two tiles (their readers passed the barrier)
+      dma_block(off_n[0], buf ^ 2);
+      dma_block(off_n[1], (buf ^ 2) + 1);
+      score_block(c, std::integral_constant<int, 0>{}, Ks + buf * (kBlock * DI), (mq & 1) != 0);
+      score_block(c + 1, std::integral_constant<int, 1>{}, Ks + (buf + 1) * (kBlock * DI),
+                  (mq & 2) != 0 && c + 1 < c_end);
+      {  // the pair after next (page lookups stay out of the code above)
+        bool m0, m1;
+        lookup(min(c + 4, c_end - 1), off_n[0], m0);
+        lookup(min(c + 5, c_end - 1), off_n[1], m1);
+        mq = (mq | ((int)m0 << 4) | ((int)m1 << 5)) >> 2;
+      }
+      wait_vm(std::integral_constant<int, 0>{});  // this wave's pieces of the next pair are in LDS
+      block_barrier();
+      buf ^= 2;
+    }
+  } else {
+    auto staged_block = [&](int c, auto blk_tag) {
+      load_staged(pre2, off_n[0]);  // block c + 2
+      score_block(c, blk_tag, Ks + buf * (kBlock * DI), (mq & 1) != 0);
+      stage_all(Ks + (buf ^ 1) * (kBlock * DI), pre);  // block c + 1 into the other tile
 #pragma unroll
       for (int u = 0; u < CH_PER_THREAD; ++u) pre[u] = pre2[u];
+      {
+        bool m;
+        lookup(min(c + 3, c_end - 1), off_n[0], m);
+        mq = (mq | ((int)m << 3)) >> 1;
+      }
+      block_barrier();
+      buf ^= 1;
+    };
+    for (int c = c_begin; c < c_end; c += 2) {
+      staged_block(c, std::integral_constant<int, 0>{});
+      if (c + 1 < c_end) {
+        staged_block(c + 1, std::integral_constant<int, 1>{});
+      } else {  // no second block: its share of the previous pair's ranking, and an empty max
+        static_for<2 * RT, 4 * RT>([&](auto k_tag) { rank_chunk(k_tag); });
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) pmB[rt] = kNegInf;
+      }
     }
-    {  // the block the next one fetches (page lookups stay out of the code above)
-      bool m;
-      lookup(min(c + 1 + PD, c_end - 1), off_ahead, m);
-      mq = (mq | ((int)m << (PD + 1))) >> 1;
-    }
-    if constexpr (kDma) wait_vm(kRingWait{});  // this wave's pieces of block c + 1 are in LDS
-    block_barrier();
-    buf = buf + 1 == NBUF ? 0 : buf + 1;
-  };
-  for (int c = c_begin; c < c_end; c += 2) {
-    score_block(c, std::true_type{});
-    if (c + 1 < c_end) score_block(c + 1, std::false_type{});
   }
   // the ring's last fetches (blocks past the range, into tiles nobody reads)
   // land before the tiles are reused below or the workgroup's LDS is released
   if constexpr (kDma) wait_vm(std::integral_constant<int, 0>{});
-  if (has_blocks) {  // the last pair (a single block: the second is empty)
-    if ((c_end - c_begin) & 1) {
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) pmB[rt] = kNegInf;
-    }
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) rank_pair(rt, c_begin + ((c_end - c_begin - 1) & ~1));
+  if (has_blocks) {  // the last pair
+    pair_full(c_begin + ((c_end - c_begin - 1) & ~1));
+    static_for<0, 4 * RT>([&](auto k_tag) { rank_chunk(k_tag); });
   }
 
   if constexpr (kWide) {  // list split * 2 + h of each row
