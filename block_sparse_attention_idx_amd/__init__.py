@@ -47,7 +47,9 @@ __all__ = ["index_select", "sparse_attn_fwd", "fwd", "index_select_kvcache", "sp
            "lib", "LIB_PATH", "MsaError", "OP_INDEX_SELECT", "OP_SPARSE_ATTN", "OP_FWD", "OP_KL_TEACHER",
            "sparse_attn_bwd", "OP_SPARSE_ATTN_BWD", "fwd_noalloc", "noalloc_scratch_bytes"]
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmsa.so")
+# The in-tree build; MSA_LIBRARY may name another build of the same sources
+# (the host-sanitizer build the ABI tests run under, say).
+LIB_PATH = os.environ.get("MSA_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmsa.so")
 
 MSA_F32, MSA_BF16 = 0, 1
 CACHE_NATIVE, CACHE_FP8_E4M3 = 0, 1

@@ -61,3 +61,35 @@ def build(verbose: bool = False, extra_flags=None) -> str:
 if __name__ == "__main__":
     path = build(verbose="-v" in sys.argv)
     print(path)
+
+
+# Host code of msa_api.hip (argument checks, planning, the C ABI) with
+# AddressSanitizer and UBSan; device code and the other objects as built by
+# build().  For running the ABI tests without a GPU under the sanitizers: load
+# the result with MSA_LIBRARY and the ASan runtime (asan_runtime()) preloaded.
+SANITIZE_DIR = os.path.join(BUILD_DIR, "sanitize")
+SANITIZE_LIB = os.path.join(SANITIZE_DIR, "libmsa_sanitized.so")
+SANITIZE_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                  "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer",
+                  "-Xarch_host", "-g"]
+
+
+def asan_runtime() -> str:
+    """Path of the clang ASan runtime that the sanitized library links against."""
+    out = _run([HIPCC, "--print-file-name=libclang_rt.asan-x86_64.so"]).strip().splitlines()[-1]
+    if not os.path.isabs(out) or not os.path.exists(out):
+        raise RuntimeError("the clang ASan runtime was not found")
+    return out
+
+
+def build_sanitized() -> str:
+    objs = [os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o") for src in SOURCES if src != "msa_api.hip"]
+    if not all(os.path.exists(o) for o in objs):
+        build()
+    os.makedirs(SANITIZE_DIR, exist_ok=True)
+    obj = os.path.join(SANITIZE_DIR, "msa_api.o")
+    _run([HIPCC, *COMMON_FLAGS, *SANITIZE_FLAGS, "-c", os.path.join(CSRC, "msa_api.hip"), "-o", obj])
+    # the sanitizer hooks stay undefined in the library: the preloaded runtime provides them
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", obj, *objs, "-o", SANITIZE_LIB])
+    return SANITIZE_LIB
+
