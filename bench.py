@@ -46,6 +46,52 @@ KL_KERNELS = {"kl_teacher": 6, "kl_combine": 7}
 BWD_KERNELS = {"bwd": 8, "bwd_combine": 9}
 
 
+def main_branch_bytes(s: synth.Shape, sel: torch.Tensor) -> dict:
+    """HBM bytes of one msa_sparse_attn_fwd call in the KV-outer form (gather,
+    attention, combine), from the selection it runs on.  An edge is one
+    selection entry (b, g, i, slot) that names a block; per edge the attention
+    reads the query rows of the group (r*d*e) and writes a partial state
+    (r*(d*e + 4)), which the combine reads back; per used (b, g, block) bucket
+    the attention reads K and V once (2*Bk*d*c); the gather reads the selection
+    twice and writes and reads one 4-byte entry per edge; the combine writes the
+    output and the log-sum-exp."""
+    e = 2 if s.dtype == "bf16" else 4
+    c = 1 if s.fp8 else e
+    r = s.num_q_heads // s.num_kv_heads
+    valid = sel >= 0
+    edges = int(valid.sum().item())
+    nb = (s.kv_len + s.block_size - 1) // s.block_size
+    used = torch.zeros((s.batch * s.groups * nb,), dtype=torch.bool, device=sel.device)
+    bg = torch.arange(s.batch * s.groups, device=sel.device).view(s.batch, s.groups, 1, 1) * nb
+    used[(sel.long() + bg)[valid]] = True
+    buckets = int(used.sum().item())
+    sel_entries = s.batch * s.groups * s.q_len * s.topk
+    parts = {
+        "query_gather": edges * r * s.head_dim * e,
+        "partial_write": edges * r * (s.head_dim * e + 4),
+        "partial_read": edges * r * (s.head_dim * e + 4),
+        "kv_blocks": buckets * 2 * s.block_size * s.head_dim * c,
+        "gather": 2 * sel_entries * 4 + 2 * edges * 4,
+        "output": s.batch * s.q_len * s.num_q_heads * (s.head_dim * e + 4),
+    }
+    return {"edges": edges, "buckets": buckets, "bytes_per_edge": round(sum(parts.values()) / max(edges, 1), 1),
+            "total": float(sum(parts.values())), "parts": parts}
+
+
+def sparse_attn_leg(run, s: synth.Shape, flop_main: float, steps=10) -> dict:
+    """msa_sparse_attn_fwd (gather + attention + combine) on a workload's selection,
+    against the MFMA peak and against the HBM roofline of its modelled bytes."""
+    ms = run.sparse_attn(steps)
+    bm = main_branch_bytes(s, run.sel)
+    tfl = flop_main / (ms * 1e-3) / 1e12
+    gbs = bm["total"] / (ms * 1e-3) / 1e9
+    return {"ms": round(ms, 4), "tflops": round(tfl, 2), "frac_of_mfma_peak": round(tfl / PEAK_BF16_TFLOPS, 4),
+            "bytes": bm["total"], "gbs": round(gbs, 1), "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+            "hbm_floor_ms": round(bm["total"] / (PEAK_HBM_GBS * 1e9) * 1e3, 4),
+            "edges": bm["edges"], "buckets": bm["buckets"], "bytes_per_edge": bm["bytes_per_edge"],
+            "bytes_by_part": bm["parts"]}
+
+
 class HipEvents:
     """Raw hipEvent_t pairs (the library records them around one kernel)."""
 
@@ -351,6 +397,30 @@ class Runner:
         torch.cuda.synchronize()
         del ws, wsr, dq, dk, dv, dout
         return t0.elapsed_time(t1) / steps, per
+
+    def sparse_attn(self, steps=10, warmup=2):
+        """ms per msa_sparse_attn_fwd call (gather + attention + combine) on this
+        workload's selection, which one msa_fwd call first provides."""
+        self.step()
+        cref = ctypes.byref(self.cache) if self.cache is not None else None
+        sa = [ctypes.byref(self.shape), cref] + [ctypes.c_void_p(self.x[n].data_ptr()) for n in ("q", "k", "v")]
+        sa += [ctypes.c_void_p(self.sel.data_ptr()), ctypes.c_void_p(self.out.data_ptr()), None,
+               ctypes.c_void_p(self.ws.data_ptr()), ctypes.c_size_t(self.ws.numel()),
+               ctypes.c_void_p(self.stream.cuda_stream)]
+
+        def call():
+            if self.L.msa_sparse_attn_fwd_kvcache(*sa) != 0:
+                raise RuntimeError(self.L.msa_last_error().decode())
+        for _ in range(warmup):
+            call()
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record(self.stream)
+        for _ in range(steps):
+            call()
+        t1.record(self.stream)
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / steps
 
     def kernel_breakdown(self, steps=3):
         res = {}
@@ -662,6 +732,8 @@ def main():
                               "frac_of_mfma_peak": round(flop_bwd / (bms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                               "flop": flop_bwd, "kernels_ms": {k: round(v, 4) for k, v in bper.items() if v}}
 
+    if not args.no_extra:
+        result["sparse_attn"] = sparse_attn_leg(run, s, flop_main)
     if not args.no_extra and wid == 3:
         # the same step with the workspace capped (msa_shape.workspace_cap_mib): the main
         # branch runs over query-row chunks whose partial states fit the cap
@@ -690,7 +762,7 @@ def main():
                 "ms_per_step": round(ems, 4), "tflops": round((fm + fi) / (ems * 1e-3) / 1e12, 2),
                 "attention_ms": round(eatt_ms, 4), "attention_frac_of_mfma_peak": round(fm / (eatt_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                 "index_ms": round(eidx_ms, 4), "index_frac_of_mfma_peak": round(fi / (eidx_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-                "flop_main": fm, "flop_index": fi}
+                "flop_main": fm, "flop_index": fi, "sparse_attn": sparse_attn_leg(er, se, fm)}
             del er
             torch.cuda.empty_cache()
 

@@ -70,3 +70,23 @@ def test_more_than_one_gpu_is_refused():
     assert r.returncode != 0
     assert "one GPU" in (r.stdout + r.stderr)
     assert r.stdout.strip() == ""  # no JSON line
+
+
+def test_main_branch_bytes_by_hand():
+    # B=1, S_q=3, G=2, k=2, r=4, d=64, bf16; 128-token blocks over 300 keys (3 blocks)
+    s = synth.Shape(1, 3, 300, 297, 8, 2, 64, 32, 2, dtype="bf16")
+    import torch
+    sel = torch.tensor([[[[0, 2], [1, -1], [2, -1]],
+                         [[2, -1], [0, 1], [-1, -1]]]], dtype=torch.int32)
+    m = bench.main_branch_bytes(s, sel)
+    edges = 4 + 3                   # entries naming a block (group 0: 4, group 1: 3)
+    buckets = 3 + 3                 # group 0 uses blocks {0, 1, 2}, group 1 uses {0, 1, 2}
+    r, d = 4, 64
+    assert m["edges"] == edges and m["buckets"] == buckets
+    want = (edges * r * d * 2              # queries gathered
+            + 2 * edges * r * (d * 2 + 4)  # partial states written and read back
+            + buckets * 2 * 128 * d * 2    # K and V of every used block once
+            + 2 * (1 * 2 * 3 * 2) * 4 + 2 * edges * 4  # selection read twice, entries written and read
+            + 1 * 3 * 8 * (d * 2 + 4))     # output and lse
+    assert m["total"] == want
+    assert sum(m["parts"].values()) == want
