@@ -31,6 +31,9 @@
 // any order, and ties are broken by block index exactly as the definition says.
 // Only full blocks before the local block are ranked (block c < L ends at or
 // before t), so no causal mask is needed inside the ranked blocks.
+#include <atomic>
+#include <climits>
+#include <cstdint>
 #include <type_traits>
 
 #include "common.h"
@@ -87,6 +90,29 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
+constexpr int pow2_at_least(int n) { return n <= 1 ? 1 : 2 * pow2_at_least((n + 1) / 2); }
+
+// v in ascending order: Batcher's bitonic sorting network (NP a power of two),
+// min / max pairs with every index known at compile time.
+template <int NP>
+__device__ __forceinline__ void sort_ascending(int (&v)[NP]) {
+  static_assert((NP & (NP - 1)) == 0, "power of two");
+#pragma unroll
+  for (int lk = 1; (1 << lk) <= NP; ++lk)
+#pragma unroll
+    for (int lj = lk - 1; lj >= 0; --lj)
+#pragma unroll
+      for (int i = 0; i < NP; ++i) {
+        const int l = i ^ (1 << lj);
+        if (l > i) {
+          const int lo = min(v[i], v[l]), hi = max(v[i], v[l]);
+          const bool up = (i & (1 << lk)) == 0;  // direction of this bitonic run
+          v[i] = up ? lo : hi;
+          v[l] = up ? hi : lo;
+        }
+      }
+}
+
 // One (row, key split) result: with several splits the merged list goes to
 // the partial lists for topk_merge_kernel; with one split the first min(k-1, L)
 // entries are the selection, and the local block and -1 padding are added
@@ -112,17 +138,22 @@ __device__ __forceinline__ void emit_row(const IndexParams& p, int b, int n, int
     return;
   }
   const int take = min(p.topk - 1, L);
+  // the ids of the first `take` entries in ascending order; the other slots
+  // hold INT_MAX and sort last
+  constexpr int NP = pow2_at_least(CAP + 1);
+  int v[NP];
 #pragma unroll
-  for (int j = 0; j < CAP; ++j) {
-    if (j < take) {
-      int r = 0;
+  for (int j = 0; j < NP; ++j) v[j] = j < CAP && j < take ? mi[j] : INT_MAX;
+  sort_ascending(v);
+  auto val = [&](int j) { return j < take ? v[j] : j == take ? L : -1; };
+  if (p.topk == NP && (reinterpret_cast<uintptr_t>(p.sel) & 15) == 0) {  // whole 16-byte rows
 #pragma unroll
-      for (int m = 0; m < CAP; ++m) r += (m < take && mi[m] < mi[j]) ? 1 : 0;
-      out[r] = mi[j];
-    }
+    for (int j = 0; j < NP; j += 4) *(i32x4*)(out + j) = i32x4{val(j), val(j + 1), val(j + 2), val(j + 3)};
+  } else {
+#pragma unroll
+    for (int j = 0; j < NP; ++j)
+      if (j < p.topk) out[j] = val(j);
   }
-  out[take] = L;
-  for (int j = take + 1; j < p.topk; ++j) out[j] = -1;
 }
 
 // The wide form (lists of 63): a lane half's own list for row rowg, written as
@@ -274,8 +305,10 @@ __device__ __forceinline__ void chain_schedule() {
 __device__ __forceinline__ void pin(float& x) { asm volatile("" : "+v"(x)); }
 __device__ __forceinline__ void pin(int& x) { asm volatile("" : "+v"(x)); }
 
+// Row tile tg, key split `split` (both uniform over the workgroup); tid is
+// threadIdx.x.
 template <typename T, typename S, int DI, int CAP, int RT>
-__global__ __launch_bounds__(64 * index_waves(CAP + 1, sizeof(T) == 2), 1) void index_topk_kernel(IndexParams p) {
+__device__ __forceinline__ void index_topk_unit(const IndexParams& p, int tg, int split, int tid) {
   using M = Mma<T>;
   using frag = typename M::frag;
   constexpr int KPL = M::KPL, KSTEP = M::KSTEP, NKS = DI / KSTEP;
@@ -308,16 +341,12 @@ __global__ __launch_bounds__(64 * index_waves(CAP + 1, sizeof(T) == 2), 1) void 
   constexpr int NBUF = kDma ? 4 : 2;
   constexpr int KS_BYTES = NBUF * TILE_BYTES;
   constexpr bool kWide = CAP == kIndexWideCap;      // lane halves write their own lists
-  constexpr int LIST_BYTES = kWide ? 0 : kWaves * 2 * CAP * 32 * 8;  // one row tile of lists, all waves
+  constexpr int LIST_BYTES = kWide ? 0 : RT * kWaves * 2 * CAP * 32 * 8;  // every list of the workgroup
   constexpr int SMEM = KS_BYTES > LIST_BYTES ? KS_BYTES : LIST_BYTES;
   static_assert(SMEM <= 160 * 1024, "LDS of one CU");
   __shared__ __align__(16) char smem[SMEM];
   T* Ks = (T*)smem;  // [NBUF][kBlock * DI]
 
-  int tg, split;
-  if (!unit_of(p, blockIdx.x, true, tg, split)) return;
-  tg = __builtin_amdgcn_readfirstlane(tg);  // uniform: block and page indices stay in scalar registers
-  split = __builtin_amdgcn_readfirstlane(split);
   const int b = tg / p.ntile;
   const int tile = tg - b * p.ntile;
   const int n_first = tile * ROWS_WG;
@@ -329,7 +358,7 @@ __global__ __launch_bounds__(64 * index_waves(CAP + 1, sizeof(T) == 2), 1) void 
   const bool has_blocks = c_begin < c_end;
   if (!has_blocks && p.nsplit > 1) return;  // a single split still writes rows with L = 0
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, l32 = lane & 31;
 
   int rowL[RT];
@@ -397,12 +426,12 @@ __global__ __launch_bounds__(64 * index_waves(CAP + 1, sizeof(T) == 2), 1) void 
     const i32x4* src = (const i32x4*)(kpool + off);
 #pragma unroll
     for (int u = 0; u < CH_PER_THREAD; ++u)
-      if (threadIdx.x + u * NT < CH_TOTAL) dst[u] = src[threadIdx.x + u * NT];
+      if (tid + u * NT < CH_TOTAL) dst[u] = src[tid + u * NT];
   };
   auto stage_all = [&](T* tile, const i32x4(&src)[CH_PER_THREAD]) {
 #pragma unroll
     for (int u = 0; u < CH_PER_THREAD; ++u)
-      if (threadIdx.x + u * NT < CH_TOTAL) stage(tile, threadIdx.x + u * NT, src[u]);
+      if (tid + u * NT < CH_TOTAL) stage(tile, tid + u * NT, src[u]);
   };
   // native keys: a block straight into tile bi.  Wave w fills 1 KiB pieces
   // (w * NU + u) of the tile; the hardware puts lane L's 16 bytes at byte 16 L
@@ -629,41 +658,74 @@ __global__ __launch_bounds__(64 * index_waves(CAP + 1, sizeof(T) == 2), 1) void 
     return;
   }
   // Merge the two half lists of each row through LDS (the K tiles are free
-  // now), then write one list per (row, split).
-  float* xs = (float*)smem;                       // [kWaves][2 halves][CAP][32 rows]
+  // now), then write one list per (row, split).  Every list goes to LDS at
+  // once; with two row tiles the lanes of half h merge row tile h, with one
+  // the lanes of half 0.
+  float* xs = (float*)smem;  // [RT][kWaves][2 halves][CAP][32 rows]
   int* xi = (int*)(smem + LIST_BYTES / 2);
+  __syncthreads();
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    __syncthreads();
+  for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
     for (int j = 0; j < CAP; ++j) {
-      const int o = ((wave * 2 + h) * CAP + j) * 32 + l32;
+      const int o = (((rt * kWaves + wave) * 2 + h) * CAP + j) * 32 + l32;
       xs[o] = ls[rt][j];
       xi[o] = li[rt][j];
     }
-    __syncthreads();
-    if (h == 0 && rvalid[rt]) {
-      const int n = n_first + wave * ROWS_WAVE + rt * 32 + l32;
-      const int oa = ((wave * 2 + 0) * CAP) * 32 + l32;
-      const int ob = ((wave * 2 + 1) * CAP) * 32 + l32;
-      float ms[CAP];
-      int mi[CAP];
-      int ia = 0, ib = 0;
+  __syncthreads();
+  static_assert(RT == 1 || RT == 2, "one row tile per lane half");
+  const int mt = RT == 2 ? h : 0;  // the row tile this lane merges
+  const bool mvalid = (RT == 2 || h == 0) && (mt ? rvalid[RT - 1] : rvalid[0]);
+  if (mvalid) {
+    const int n = n_first + wave * ROWS_WAVE + mt * 32 + l32;
+    const int oa = (((mt * kWaves + wave) * 2 + 0) * CAP) * 32 + l32;
+    const int ob = oa + CAP * 32;
+    float ms[CAP];
+    int mi[CAP];
+    int ia = 0, ib = 0;
 #pragma unroll
-      for (int j = 0; j < CAP; ++j) {
-        const float sa = ia < CAP ? xs[oa + ia * 32] : kNegInf;
-        const int ida = ia < CAP ? xi[oa + ia * 32] : -1;
-        const float sb = ib < CAP ? xs[ob + ib * 32] : kNegInf;
-        const int idb = ib < CAP ? xi[ob + ib * 32] : -1;
-        // empty entries (id -1) rank last
-        const bool take_a = idb < 0 || (ida >= 0 && ranks_before(sa, ida, sb, idb));
-        ms[j] = take_a ? sa : sb;
-        mi[j] = take_a ? ida : idb;
-        ia += take_a ? 1 : 0;
-        ib += take_a ? 0 : 1;
-      }
-      if constexpr (!kWide) emit_row<CAP>(p, b, n, split, rowL[rt], ms, mi);
+    for (int j = 0; j < CAP; ++j) {
+      const float sa = ia < CAP ? xs[oa + ia * 32] : kNegInf;
+      const int ida = ia < CAP ? xi[oa + ia * 32] : -1;
+      const float sb = ib < CAP ? xs[ob + ib * 32] : kNegInf;
+      const int idb = ib < CAP ? xi[ob + ib * 32] : -1;
+      // empty entries (id -1) rank last
+      const bool take_a = idb < 0 || (ida >= 0 && ranks_before(sa, ida, sb, idb));
+      ms[j] = take_a ? sa : sb;
+      mi[j] = take_a ? ida : idb;
+      ia += take_a ? 1 : 0;
+      ib += take_a ? 0 : 1;
     }
+    if constexpr (!kWide) emit_row<CAP>(p, b, n, split, mt ? rowL[RT - 1] : rowL[0], ms, mi);
+  }
+}
+
+// The units of a launch: one per workgroup, or with p.persist a grid of at
+// most as many workgroups as the GPU holds at once, each taking one unit per
+// round q = 0, 1, ... in snake order (workgroup w: unit q G + w in even
+// rounds, q G + G - 1 - w in odd ones).  With the heaviest row tiles first the
+// rounds of every workgroup add up to about the same number of blocks, and a
+// CU goes on to its next unit without waiting for the dispatcher.
+// Each round reads the parameters and the thread id anew through an empty asm,
+// so what a unit derives from them is computed inside the round rather than
+// hoisted out of the loop and kept live across the block loop.
+template <typename T, typename S, int DI, int CAP, int RT>
+__global__ __launch_bounds__(64 * index_waves(CAP + 1, sizeof(T) == 2), 1) void index_topk_kernel(IndexParams p) {
+  typedef const IndexParams __attribute__((address_space(4))) kparams;
+  const int G = (int)gridDim.x, w = (int)blockIdx.x;
+  for (int q = 0;; ++q) {
+    kparams* kp = (kparams*)__builtin_amdgcn_kernarg_segment_ptr();  // p: the only argument
+    int tid = (int)threadIdx.x;
+    asm volatile("" : "+s"(kp), "+v"(tid));
+    const IndexParams pu = *(const IndexParams*)kp;  // loads of the constant address space
+    const int lin = (q & 1) ? (q + 1) * G - 1 - w : q * G + w;
+    int tg, split;
+    if (!unit_of(pu, lin, true, tg, split)) return;
+    // uniform: block and page indices stay in scalar registers
+    index_topk_unit<T, S, DI, CAP, RT>(pu, __builtin_amdgcn_readfirstlane(tg), __builtin_amdgcn_readfirstlane(split),
+                                       tid);
+    if (!pu.persist) return;
+    __syncthreads();  // the next unit's keys overwrite the LDS this one's lists used
   }
 }
 
@@ -922,6 +984,8 @@ __global__ __launch_bounds__(64 * WPB) void topk_merge_kernel(IndexParams p) {
   else if (lane < p.topk) out[lane] = -1;
 }
 
+constexpr int kMaxIndexDevices = 64;  // devices whose resident workgroup counts are kept
+
 template <typename T, typename S, int DI, int CAP>
 static hipError_t launch_index_t(const IndexParams& p, hipStream_t s, const KernelTimer* tm) {
   timer_start(tm, kKernIndexScore, s);
@@ -937,8 +1001,33 @@ static hipError_t launch_index_t(const IndexParams& p, hipStream_t s, const Kern
       small_done = true;
     }
   }
-  if (!small_done)
-    hipLaunchKernelGGL((index_topk_kernel<T, S, DI, CAP, RT>), dim3(p.grid_per_xcd * 8), dim3(NT), 0, s, p);
+  if (!small_done) {
+    // the persistent grid: the workgroups resident at once, counted once per device
+    static std::atomic<int> resident[kMaxIndexDevices];
+    IndexParams pl = p;
+    unsigned grid = (unsigned)p.grid_per_xcd * 8;
+    if (p.persist) {
+      int dev = -1;
+      pl.persist = 0;
+      if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < kMaxIndexDevices) {
+        int r = resident[dev].load(std::memory_order_relaxed);
+        if (r == 0) {
+          int cus = 0, per_cu = 0;
+          if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+              hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, index_topk_kernel<T, S, DI, CAP, RT>, NT, 0) ==
+                  hipSuccess)
+            r = cus * per_cu;
+          (void)hipGetLastError();  // a failed query leaves the one-unit grid and no error behind
+          if (r > 0) resident[dev].store(r, std::memory_order_relaxed);
+        }
+        if (r > 0 && r < p.nunits) {
+          pl.persist = 1;
+          grid = (unsigned)r;
+        }
+      }
+    }
+    hipLaunchKernelGGL((index_topk_kernel<T, S, DI, CAP, RT>), dim3(grid), dim3(NT), 0, s, pl);
+  }
   timer_stop(tm, kKernIndexScore, s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -96,6 +96,9 @@ struct IndexParams {
   // each wave finds its unit from the lengths itself (units and unit_count null).
   int units_inline;
   int merge_in_consumer;  // host only: the lists are merged by the decode rows kernel, not topk_merge_kernel
+  // One key split and one unit per row tile, heaviest first (no unit list):
+  // the launch may run the units on a persistent grid (index_topk_kernel).
+  int persist;
 };
 
 // At most this many (row, group) pairs per sequence: the index kernel's

@@ -223,6 +223,7 @@ IndexPlan plan_index(const msa_shape* s, const msa_kv_cache* cache) {
     ip.off_count = off;
     off += align_up(4);
   }
+  p.persist = p.nsplit == 1 && !p.small && !ip.unit_list && !p.units_inline ? 1 : 0;
   ip.bytes = off;
   return ip;
 }
