@@ -86,6 +86,22 @@ __device__ __forceinline__ float token_sum(float x) {
   else return x + __shfl_xor(x, 32);
 }
 
+// Sum / max over the 32 lanes of a lane half.
+__device__ __forceinline__ float half_sum(float x) {
+  x += partner<1>(x);
+  x += partner<2>(x);
+  x += partner<4>(x);
+  x += partner<8>(x);
+  return x + __shfl_xor(x, 16);
+}
+__device__ __forceinline__ float half_max(float x) {
+  x = fmaxf(x, partner<1>(x));
+  x = fmaxf(x, partner<2>(x));
+  x = fmaxf(x, partner<4>(x));
+  x = fmaxf(x, partner<8>(x));
+  return fmaxf(x, __shfl_xor(x, 16));
+}
+
 template <int R, int O = 1>
 __device__ __forceinline__ float token_max(float x) {
   if constexpr (O < R) return token_max<R, 2 * O>(fmaxf(x, partner<O>(x)));
@@ -114,6 +130,11 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void kl_teacher_kernel
   __shared__ __align__(16) T Ks[kBlock * LDK];
   __shared__ __align__(16) char kis_raw[KI_BYTES > SC_BYTES ? KI_BYTES : SC_BYTES];  // index keys, then scores
   __shared__ int32_t ent_s[kBlock];  // the item's token entries ((row << 6) | slot)
+  // r >= 8: the transposed pass (S = Q K^T, a lane holds one key per key tile
+  // and 16 rows); the log2-domain lse of each wave's 32 rows goes through LDS
+  // to the lanes whose registers hold those rows
+  constexpr bool kT = R >= 8;
+  __shared__ float lse_s[4][32];
   T* KIs = (T*)kis_raw;
   float* sc = (float*)kis_raw;
 
@@ -221,14 +242,17 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void kl_teacher_kernel
       }
       __syncthreads();  // every wave is done with the index keys
       if (active) {
-        float* dst = sc + (tt * 32 + l32) * LDSC + h * NV;
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
           const int kt = 2 * (wave >> 1) + u;
 #pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4)
-            *(f32x4*)(dst + kt * 16 + q4 * 4) =
-                f32x4{siacc[u][q4 * 4], siacc[u][q4 * 4 + 1], siacc[u][q4 * 4 + 2], siacc[u][q4 * 4 + 3]};
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const f32x4 v4 = f32x4{siacc[u][q4 * 4], siacc[u][q4 * 4 + 1], siacc[u][q4 * 4 + 2], siacc[u][q4 * 4 + 3]};
+            if constexpr (kT)  // [token][key]: registers 4 q4 .. 4 q4 + 3 are keys kt * 32 + c_row(4 q4, h) + 0 .. 3
+              *(f32x4*)(sc + (tt * 32 + l32) * LDSC + kt * 32 + c_row(q4 * 4, h)) = v4;
+            else
+              *(f32x4*)(sc + (tt * 32 + l32) * LDSC + h * NV + kt * 16 + q4 * 4) = v4;
+          }
         }
       }
       __syncthreads();
@@ -322,6 +346,128 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void kl_teacher_kernel
       }
     };
 
+    // The transposed pass (r >= 8): the Q rows are the A operand, so lane l
+    // holds key kt * 32 + l % 32 of each key tile and rows c_row(j, h) of the
+    // wave's 32 (token, head) rows in register j -- token j / JPT, the same in
+    // both lane halves.  A token's head sum is then JPT in-lane adds and one
+    // swap between the halves, after which half h carries tokens 2 u + h (one
+    // token per pass: both halves carry it and half 0 reports), and the key
+    // reductions run over the 32 lanes of a half.
+    constexpr int JPT = 16 / TPW;            // registers per token
+    constexpr int TPL = TPW >= 2 ? TPW / 2 : 1;  // tokens a lane carries after the swap
+    auto pass_t = [&](int ps, const frag (&qf)[NKS], float lse2, int32_t entry) {
+      // the per-row lse into the registers that hold the rows
+      if (h == 0) lse_s[wave][l32] = lse2;
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      float lr[16];
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const f32x4 v4 = *(const f32x4*)&lse_s[wave][a * 8 + h * 4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) lr[a * 4 + e] = v4[e];
+      }
+      (void)entry;
+      // the pass's tokens (uniform): entry, query index, visibility limit
+      int ti[TPW], tslot_c[TPW], tlim[TPW], tptok_slot[TPW];
+      bool trv[TPW];
+      bool masked = false;
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) {
+        const int tslot = ps * TPP + wave * TPW + t;
+        const int e = tslot < ntok ? ent_s[tslot] : -1;
+        ti[t] = e >= 0 ? e >> 6 : 0;
+        tptok_slot[t] = e & 63;
+        tslot_c[t] = min(tslot, ntok - 1);
+        const int64_t rel = qo + ti[t] - key0;
+        trv[t] = e >= 0 && rel >= 0;
+        tlim[t] = (!trv[t] || rel >= kBlock) ? kBlock - 1 : (int)rel;
+        masked |= tlim[t] < kBlock - 1;
+      }
+
+      f32x16 sacc[4];
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) sacc[kt] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+          const frag a = *(const frag*)&Ks[(kt * 32 + l32) * LDK + ks * KSTEP + h * KPL];
+          sacc[kt] = M::mma(qf[ks], a, sacc[kt]);
+        }
+      // this half's head sums of each token's probabilities, key kt * 32 + l32
+      float hs[TPW][4];
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+          float acc = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][t * JPT], sl2, -lr[t * JPT]));
+#pragma unroll
+          for (int j = t * JPT + 1; j < (t + 1) * JPT; ++j)
+            acc += __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][j], sl2, -lr[j]));
+          hs[t][kt] = acc;
+        }
+      // both halves' heads: token 2 u + h (u < TPL) in half h, or the one token in both
+      float pb[TPL][4], sv[TPL][4];
+#pragma unroll
+      for (int u = 0; u < TPL; ++u) {
+        const int t0 = TPW >= 2 ? 2 * u : 0, t1 = TPW >= 2 ? 2 * u + 1 : 0;
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+          const auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(hs[t0][kt]), __float_as_uint(hs[t1][kt]),
+                                                          false, false);
+          pb[u][kt] = (__uint_as_float(x[0]) + __uint_as_float(x[1])) * (1.0f / R);
+        }
+        const int tsl = h && TPW >= 2 ? tslot_c[t1] : tslot_c[t0];
+        const float* src = sc + tsl * LDSC + l32;
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) sv[u][kt] = src[kt * 32] * kp.index_scale;
+        if (masked) {  // the heads of a token share its limit: mask after the sums
+          const int lim = h && TPW >= 2 ? tlim[t1] : tlim[t0];
+#pragma unroll
+          for (int kt = 0; kt < 4; ++kt)
+            if (kt * 32 + l32 > lim) {
+              pb[u][kt] = 0.f;
+              sv[u][kt] = kNegInf;
+            }
+        }
+      }
+      // per token: the entropy terms and the index scores' max and exp-sum over its 128 keys
+#pragma unroll
+      for (int u = 0; u < TPL; ++u) {
+        float ent = 0.f, smax = kNegInf;
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+          const float q = pb[u][kt];
+          ent += q > 0.f ? q * (__builtin_amdgcn_logf(q) * kLn2 - sv[u][kt]) : 0.f;
+          smax = fmaxf(smax, sv[u][kt]);
+        }
+        ent = half_sum(ent);
+        smax = half_max(smax);
+        float sexp = 0.f;
+        if (smax != kNegInf) {
+#pragma unroll
+          for (int kt = 0; kt < 4; ++kt) sexp += __builtin_amdgcn_exp2f((sv[u][kt] - smax) * kLog2e);
+        }
+        sexp = half_sum(sexp);
+        const int t0 = TPW >= 2 ? 2 * u : 0, t1 = TPW >= 2 ? 2 * u + 1 : 0;
+        const bool rv = h && TPW >= 2 ? trv[t1] : trv[t0];
+        if (rv && l32 == 0 && (TPW >= 2 || h == 0)) {
+          const int i = h && TPW >= 2 ? ti[t1] : ti[t0];
+          const int slot = h && TPW >= 2 ? tptok_slot[t1] : tptok_slot[t0];
+          const int64_t ptok = (((int64_t)b * p.S_q + i) * p.G + g) * p.topk + slot;
+          kp.part[ptok * 3 + 0] = ent;
+          kp.part[ptok * 3 + 1] = smax;
+          kp.part[ptok * 3 + 2] = sexp;
+        }
+      }
+    };
+    auto run_pass = [&](int ps, const frag (&qf)[NKS], float lse2, int32_t entry) {
+      if constexpr (kT) pass_t(ps, qf, lse2, entry);
+      else pass(ps, qf, lse2, entry);
+    };
+
     const int npass = wave * TPW < ntok ? (ntok - wave * TPW + TPP - 1) / TPP : 0;
     if (npass > 0) {
       frag qfA[NKS], qfB[NKS];
@@ -331,11 +477,11 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void kl_teacher_kernel
       for (int ps = 0; ps < npass; ps += 2) {
         load_rows(ps + 1, qfB, lseB, entB);
         __builtin_amdgcn_sched_barrier(0);
-        pass(ps, qfA, lseA, entA);
+        run_pass(ps, qfA, lseA, entA);
         if (ps + 1 < npass) {
           load_rows(ps + 2, qfA, lseA, entA);
           __builtin_amdgcn_sched_barrier(0);
-          pass(ps + 1, qfB, lseB, entB);
+          run_pass(ps + 1, qfB, lseB, entB);
         }
       }
     }

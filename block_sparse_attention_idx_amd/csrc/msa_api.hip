@@ -33,7 +33,11 @@ msa_status fail(msa_status st, const char* fmt, ...) {
 constexpr size_t kAlign = 256;
 constexpr int kTokensPerItem = 128;
 constexpr int kAttnGrid = 512;      // persistent attention grid: 2 workgroups per CU
-constexpr int kIndexTargetUnits = 2048;
+// Units the key splits aim for: 4 per CU for the row-tile kernel (each unit
+// pays a fixed ~20 us for its queries, last ranking and list write), 8 per CU
+// for the few-row form, whose units stream keys from HBM.
+constexpr int kIndexTargetUnits = 1024;
+constexpr int kIndexTargetUnitsFewRows = 2048;
 constexpr int64_t kIndexVarlenChunk = 16;  // key blocks per unit when sequences have their own lengths
 constexpr int kIndexMinTiles = 512;  // row tiles that fill 256 CUs without key splits
 
@@ -195,7 +199,8 @@ IndexPlan plan_index(const msa_shape* s, const msa_kv_cache* cache) {
   int64_t chunk = std::max<int64_t>(1, Lmax), nsplit = 1;
   if (Lmax > 0 && p.ntile_total < kIndexMinTiles) {
     const int64_t min_chunk = p.small ? 8 : 16;
-    const int64_t want = std::max<int64_t>(1, ceil_div(kIndexTargetUnits, std::max(1, p.ntile_total)));
+    const int target = p.small ? kIndexTargetUnitsFewRows : kIndexTargetUnits;
+    const int64_t want = std::max<int64_t>(1, ceil_div(target, std::max(1, p.ntile_total)));
     const bool varlen = cache && cache->seq_lens;
     chunk = std::max<int64_t>({min_chunk, varlen ? kIndexVarlenChunk : ceil_div(Lmax, want), ceil_div(Lmax, max_split)});
     nsplit = ceil_div(Lmax, chunk);
