@@ -343,7 +343,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void attn_kvouter_kern
           sacc[kt][j] = e;
           lsum += e;
         }
-      lsum += __shfl_xor(lsum, 32);
+      lsum = xor_sum<32>(lsum);
 
       // O^T = V^T P^T.  Instruction ks2 consumes registers j0..j0+KPL-1 of key
       // tile kt; the A operand supplies V^T for exactly those keys.
@@ -528,7 +528,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnParams p) {
       sacc[j] = e;
       lw += e;
     }
-    lw += __shfl_xor(lw, 32);
+    lw = xor_sum<32>(lw);
     if (h == 0) red_l[wave][l32] = lw;
     // P^T row l32: keys 32w + c_row(j, h) come in runs of four
 #pragma unroll
@@ -774,7 +774,7 @@ __global__ __launch_bounds__(512) void attn_decode_rows_kernel(AttnParams p) {
         sacc[j] = e;
         lw += e;
       }
-      lw += __shfl_xor(lw, 32);
+      lw = xor_sum<32>(lw);
       if (h == 0) red_l[team][wt][l32] = lw;
       // P^T row l32: keys 32 wt + c_row(j, h) come in runs of four
 #pragma unroll
@@ -1079,8 +1079,8 @@ __global__ __launch_bounds__(512) void attn_decode_rows16_kernel(AttnParams p) {
         if (wave * KPW + g4 * 4 + j > lim) sacc[j] = kNegInf;
     }
     float mw = fmaxf(fmaxf(sacc[0], sacc[1]), fmaxf(sacc[2], sacc[3]));
-    mw = fmaxf(mw, __shfl_xor(mw, 16));
-    mw = fmaxf(mw, __shfl_xor(mw, 32));
+    mw = xor_max<16>(mw);
+    mw = xor_max<32>(mw);
     if (g4 == 0) red_m[wave][l16] = mw;
     lds_barrier();
     // key 0 of a visible block is visible, so the block maximum is finite
@@ -1097,8 +1097,8 @@ __global__ __launch_bounds__(512) void attn_decode_rows16_kernel(AttnParams p) {
       sacc[j] = e;
       lw += e;
     }
-    lw += __shfl_xor(lw, 16);
-    lw += __shfl_xor(lw, 32);
+    lw = xor_sum<16>(lw);
+    lw = xor_sum<32>(lw);
     if (g4 == 0) red_l[wave][l16] = lw;
     *(bf16x4*)&Ps[l16 * LDP + wave * KPW + g4 * 4] =
         bf16x4{from_f32<T>(sacc[0]), from_f32<T>(sacc[1]), from_f32<T>(sacc[2]), from_f32<T>(sacc[3])};

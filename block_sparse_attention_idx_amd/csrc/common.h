@@ -129,6 +129,54 @@ __device__ __forceinline__ bool ranks_before(float s1, int i1, float s2, int i2)
   return s1 > s2 || (s1 == s2 && i1 < i2);
 }
 
+// x combined with the value of the lane O = 16 or 32 away (lane index xor O)
+// by the lane-group swaps, without an LDS round trip: each lane receives its
+// own and its partner's value in some order, and sum and max do not care.
+template <int O>
+__device__ __forceinline__ float xor_sum(float x) {
+  static_assert(O == 16 || O == 32, "lane-group swaps");
+  const auto p = O == 16 ? __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false)
+                         : __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+template <int O>
+__device__ __forceinline__ float xor_max(float x) {
+  static_assert(O == 16 || O == 32, "lane-group swaps");
+  const auto p = O == 16 ? __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false)
+                         : __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+
+// One butterfly step of a wave-wide "best (score, block id)" reduction: the
+// better of this lane's pair and that of its partner, the lane whose index
+// differs in bit O and agrees above it.  O < 16 by DPP (quad permutes, then
+// the half-row and row mirrors, which pair lanes the same way), O = 16 and 32
+// by the lane-group swaps, which hand each lane its own and its partner's
+// value in some order -- enough for a symmetric choice.  No LDS round trip.
+template <int O>
+__device__ __forceinline__ void best_step(float& s, int& i) {
+  float os;
+  int oi;
+  if constexpr (O < 16) {
+    constexpr int ctrl = O == 1 ? 0xB1 : O == 2 ? 0x4E : O == 4 ? 0x141 : 0x140;
+    os = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s), ctrl, 0xF, 0xF, false));
+    oi = __builtin_amdgcn_update_dpp(0, i, ctrl, 0xF, 0xF, false);
+  } else {
+    const auto ps = O == 16 ? __builtin_amdgcn_permlane16_swap(__float_as_uint(s), __float_as_uint(s), false, false)
+                            : __builtin_amdgcn_permlane32_swap(__float_as_uint(s), __float_as_uint(s), false, false);
+    const auto pi = O == 16 ? __builtin_amdgcn_permlane16_swap((unsigned)i, (unsigned)i, false, false)
+                            : __builtin_amdgcn_permlane32_swap((unsigned)i, (unsigned)i, false, false);
+    s = __uint_as_float(ps[0]);
+    i = (int)pi[0];
+    os = __uint_as_float(ps[1]);
+    oi = (int)pi[1];
+  }
+  if (ranks_before(os, oi, s, i)) {
+    s = os;
+    i = oi;
+  }
+}
+
 // This lane's entry of a merged selection row: position pos (ascending block
 // ids) holds block id; pos = -1 for lanes past the row's selected blocks.
 struct MergedSlot {
@@ -194,15 +242,12 @@ __device__ inline MergedSlot merge_row_lists(const float* gs, const int32_t* gi,
     }
     float ws = bs;
     int wi = bi;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float os = __shfl_xor(ws, off);
-      const int oi = __shfl_xor(wi, off);
-      if (ranks_before(os, oi, ws, wi)) {
-        ws = os;
-        wi = oi;
-      }
-    }
+    best_step<1>(ws, wi);
+    best_step<2>(ws, wi);
+    best_step<4>(ws, wi);
+    best_step<8>(ws, wi);
+    best_step<16>(ws, wi);
+    best_step<32>(ws, wi);
     // block ids are unique across the lists, so exactly one lane owns the winner
     if (bl >= 0 && bi == wi) {
       if (bl == 0) ++pos0;
@@ -213,7 +258,7 @@ __device__ inline MergedSlot merge_row_lists(const float* gs, const int32_t* gi,
   // rounds that found no entry (lists shorter than take) leave the sentinel
   const int n = __popcll(__ballot(lane < take && mywin != 0x7fffffff));
   int rank = 0;
-  for (int m = 0; m < n; ++m) rank += (__shfl(mywin, m) < mywin) ? 1 : 0;
+  for (int m = 0; m < n; ++m) rank += (__builtin_amdgcn_readlane(mywin, m) < mywin) ? 1 : 0;
   if (lane < n) return MergedSlot{rank, mywin};
   if (lane == n) return MergedSlot{n, L};
   return MergedSlot{-1, -1};

@@ -875,7 +875,7 @@ __global__ __launch_bounds__(256, CAP == kIndexWideCap ? 1 : 2) void index_topk_
     pm = fmaxf(pm, tile_max(a));
     if (tl % 4 != 3) return;  // the block continues in the next tile
     const int j = tl / 4;
-    float full = fmaxf(pm, __shfl_xor(pm, 32));
+    float full = xor_max<32>(pm);
     pm = kNegInf;
     if (blk_off(j, far) < 0) full = kNegInf;
     // blocks pair up: half 0 ranks the wave's even blocks, half 1 the odd ones
@@ -889,16 +889,39 @@ __global__ __launch_bounds__(256, CAP == kIndexWideCap ? 1 : 2) void index_topk_
       list_insert<CAP>(ls, li, x, cc);
     }
   };
+  // ntl is a multiple of 4.  Native tiles: one in flight ahead of the one
+  // processed; e4m3 tiles, half the bytes, three (the same bytes in flight).
   auto scan = [&](auto far) {
-    i32x4 ta[NKR], tb[NKR];
-    load_tile(ta, 0, far);
-    for (int tl = 0; tl < ntl; tl += 2) {  // ntl is a multiple of 4
-      load_tile(tb, tl + 1, far);
-      __builtin_amdgcn_sched_barrier(0);
-      process(ta, tl, far);
-      load_tile(ta, tl + 2, far);
-      __builtin_amdgcn_sched_barrier(0);
-      process(tb, tl + 1, far);
+    if constexpr (kNative) {
+      i32x4 ta[NKR], tb[NKR];
+      load_tile(ta, 0, far);
+      for (int tl = 0; tl < ntl; tl += 2) {
+        load_tile(tb, tl + 1, far);
+        __builtin_amdgcn_sched_barrier(0);
+        process(ta, tl, far);
+        load_tile(ta, tl + 2, far);
+        __builtin_amdgcn_sched_barrier(0);
+        process(tb, tl + 1, far);
+      }
+    } else {
+      i32x4 ta[NKR], tb[NKR], tc[NKR], td[NKR];
+      load_tile(ta, 0, far);
+      load_tile(tb, 1, far);
+      load_tile(tc, 2, far);
+      for (int tl = 0; tl < ntl; tl += 4) {
+        load_tile(td, tl + 3, far);
+        __builtin_amdgcn_sched_barrier(0);
+        process(ta, tl, far);
+        load_tile(ta, tl + 4, far);
+        __builtin_amdgcn_sched_barrier(0);
+        process(tb, tl + 1, far);
+        load_tile(tb, tl + 5, far);
+        __builtin_amdgcn_sched_barrier(0);
+        process(tc, tl + 2, far);
+        load_tile(tc, tl + 6, far);
+        __builtin_amdgcn_sched_barrier(0);
+        process(td, tl + 3, far);
+      }
     }
   };
   if (nbw > 0) {
