@@ -92,6 +92,15 @@ def sparse_attn_leg(run, s: synth.Shape, flop_main: float, steps=10) -> dict:
             "bytes_by_part": bm["parts"]}
 
 
+def index_select_leg(run, flop_index: float, steps=20) -> dict:
+    """msa_index_select alone, called back to back (its inputs stay in the
+    Infinity Cache between calls), against the MFMA peak; beside the in-step
+    index kernel time, which follows the main branch's HBM-bound kernels."""
+    ms = run.index_select(steps)
+    tfl = flop_index / (ms * 1e-3) / 1e12
+    return {"ms": round(ms, 4), "tflops": round(tfl, 2), "frac_of_mfma_peak": round(tfl / PEAK_BF16_TFLOPS, 4)}
+
+
 class HipEvents:
     """Raw hipEvent_t pairs (the library records them around one kernel)."""
 
@@ -397,6 +406,27 @@ class Runner:
         torch.cuda.synchronize()
         del ws, wsr, dq, dk, dv, dout
         return t0.elapsed_time(t1) / steps, per
+
+    def index_select(self, steps=20, warmup=3):
+        """ms per msa_index_select call on this workload's index queries and keys."""
+        cref = ctypes.byref(self.cache) if self.cache is not None else None
+        ia = [ctypes.byref(self.shape), cref] + [ctypes.c_void_p(self.x[n].data_ptr()) for n in ("q_idx", "k_idx")]
+        ia += [ctypes.c_void_p(self.sel.data_ptr()), ctypes.c_void_p(self.ws.data_ptr()),
+               ctypes.c_size_t(self.ws.numel()), ctypes.c_void_p(self.stream.cuda_stream)]
+
+        def call():
+            if self.L.msa_index_select_kvcache(*ia) != 0:
+                raise RuntimeError(self.L.msa_last_error().decode())
+        for _ in range(warmup):
+            call()
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record(self.stream)
+        for _ in range(steps):
+            call()
+        t1.record(self.stream)
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / steps
 
     def sparse_attn(self, steps=10, warmup=2):
         """ms per msa_sparse_attn_fwd call (gather + attention + combine) on this
@@ -734,6 +764,7 @@ def main():
 
     if not args.no_extra:
         result["sparse_attn"] = sparse_attn_leg(run, s, flop_main)
+        result["index_select"] = index_select_leg(run, flop_index)
     if not args.no_extra and wid == 3:
         # the same step with the workspace capped (msa_shape.workspace_cap_mib): the main
         # branch runs over query-row chunks whose partial states fit the cap
@@ -762,7 +793,8 @@ def main():
                 "ms_per_step": round(ems, 4), "tflops": round((fm + fi) / (ems * 1e-3) / 1e12, 2),
                 "attention_ms": round(eatt_ms, 4), "attention_frac_of_mfma_peak": round(fm / (eatt_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                 "index_ms": round(eidx_ms, 4), "index_frac_of_mfma_peak": round(fi / (eidx_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-                "flop_main": fm, "flop_index": fi, "sparse_attn": sparse_attn_leg(er, se, fm)}
+                "flop_main": fm, "flop_index": fi, "sparse_attn": sparse_attn_leg(er, se, fm),
+                "index_select": index_select_leg(er, fi)}
             del er
             torch.cuda.empty_cache()
 
