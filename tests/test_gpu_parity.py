@@ -118,6 +118,24 @@ def test_index_select_only_matches_oracle():
 
 
 @gpu
+@pytest.mark.timeout(600)
+def test_index_persistent_grid_ragged_every_row():
+    # 8 groups x 32845 rows = 262760 (row, group) pairs: 514 tiles of 512, the last
+    # one holding 104 rows, so each tile is one unit with one key split and the
+    # index kernel runs its persistent grid (more tiles than resident workgroups,
+    # units handed out in snake order over several rounds); every row is checked
+    msa = _msa()
+    n = 32768 + 77
+    s = synth.Shape(1, n, n, 0, 32, 8, 64, 128, 16, dtype="bf16")
+    x, xh = _inputs(s, 11)
+    print(f"persistent-grid shape: {s.batch} x {n} rows, {s.groups} groups", flush=True)
+    sel = msa.index_select(x["q_idx"], x["k_idx"], s.topk, q_offset=0)
+    torch.cuda.synchronize()
+    ref = orc.index_select(synth.as_f64(xh["q_idx"]), synth.as_f64(xh["k_idx"]), s.topk, 0)
+    _check_sel_rows(sel, ref)
+
+
+@gpu
 def test_ties_resolve_to_lower_block():
     # all-zero index queries: every block ties, the lowest ids must win
     msa = _msa()
