@@ -119,19 +119,22 @@ def test_index_select_only_matches_oracle():
 
 @gpu
 @pytest.mark.timeout(600)
-def test_index_persistent_grid_ragged_every_row():
-    # 8 groups x 32845 rows = 262760 (row, group) pairs: 514 tiles of 512, the last
-    # one holding 104 rows, so each tile is one unit with one key split and the
-    # index kernel runs its persistent grid (more tiles than resident workgroups,
-    # units handed out in snake order over several rounds); every row is checked
+@pytest.mark.parametrize("topk,cache", [(16, "native"), (16, "fp8"), (32, "native")])
+def test_index_persistent_grid_ragged_every_row(topk, cache):
+    # 8 groups x 32845 rows = 262760 (row, group) pairs: 514 tiles of 512 (k <= 16)
+    # or 1027 of 256 (k = 32), the last one holding 104 rows, so each tile is one
+    # unit with one key split and the index kernel runs its persistent grid (more
+    # tiles than resident workgroups, units handed out in snake order over several
+    # rounds); e4m3 keys take the staged path.  Every row is checked.
     msa = _msa()
     n = 32768 + 77
-    s = synth.Shape(1, n, n, 0, 32, 8, 64, 128, 16, dtype="bf16")
+    s = synth.Shape(1, n, n, 0, 32, 8, 64, 128, topk, dtype="bf16", cache=cache)
     x, xh = _inputs(s, 11)
-    print(f"persistent-grid shape: {s.batch} x {n} rows, {s.groups} groups", flush=True)
+    print(f"persistent-grid shape: {s.batch} x {n} rows, {s.groups} groups, k = {topk}, {cache} keys", flush=True)
     sel = msa.index_select(x["q_idx"], x["k_idx"], s.topk, q_offset=0)
     torch.cuda.synchronize()
-    ref = orc.index_select(synth.as_f64(xh["q_idx"]), synth.as_f64(xh["k_idx"]), s.topk, 0)
+    k_idx = orc.dequantize_e4m3(synth.codes(xh["k_idx"]), 1.0) if cache == "fp8" else synth.as_f64(xh["k_idx"])
+    ref = orc.index_select(synth.as_f64(xh["q_idx"]), k_idx, s.topk, 0)
     _check_sel_rows(sel, ref)
 
 
