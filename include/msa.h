@@ -40,9 +40,12 @@
  * library's own (see there).  Work is enqueued on the given HIP stream
  * (hipStream_t passed as void*, NULL = the null stream) and the calls return
  * without synchronising.  Different threads may call concurrently on
- * different streams with different workspaces.  Two things persist between
+ * different streams with different workspaces.  Three things persist between
  * calls: the profiling hook of msa_set_kernel_timer (thread-local, off unless
- * set) and msa_fwd_noalloc's scratch with its per-device address.
+ * set), msa_fwd_noalloc's scratch with its per-device address, and, per
+ * device, the number of index-kernel workgroups the GPU holds at once (CU
+ * count x occupancy, queried once; it sizes the index kernel's persistent
+ * grid and changes no result).
  *
  * Errors.  Arguments are checked on the host before anything is enqueued; on
  * an error nothing is launched and outputs are untouched.  A failed launch
