@@ -8,12 +8,16 @@
 // keeps the Top-k blocks, always including the query's local block.  Softmax
 // preserves order, so raw scores are ranked (no exp).
 //
-// Design.  A workgroup owns 256 (query row, group) pairs of one sequence (the
+// Design.  A unit is a tile of (query row, group) pairs of one sequence (the
 // rows of q_idx [B,S_q,G,D] are contiguous per (i, g)) and a contiguous range of
-// key blocks.  Per block, the shared k_idx tile (128 keys x D) is staged in LDS
-// (double-buffered) and multiplied against the rows' index queries held in
-// registers: S^T = K_idx * Q_idx^T with 32x32 MFMA tiles, so each lane owns
-// one query row and 64 of the block's 128 keys (the other 64 sit in lane ^ 32).
+// key blocks; a workgroup of 8 waves (bf16 queries; 4 otherwise) takes 512
+// pairs (256 for k > 16), 64 per wave.  Per block, the shared k_idx tile (128
+// keys x D) reaches LDS -- by DMA into a ring of four tiles for native bf16
+// keys, through registers into two tiles otherwise -- and is multiplied
+// against the rows' index queries held in registers: S^T = K_idx * Q_idx^T with
+// 32x32 MFMA tiles, so each lane owns one query row and 64 of the block's 128
+// keys (the other 64 sit in lane ^ 32).  With one key split per tile the
+// units run on a persistent grid in snake order (index_topk_kernel).
 // The block max is a register reduction plus one cross-half exchange; it goes
 // straight into a running top list in registers and is never stored.  The two
 // lane halves take alternate blocks, so each keeps its own list; at the end the
