@@ -19,11 +19,15 @@
 // in LDS; the index scores S_idx^T = K_idx Q_idx^T of all the item's tokens are
 // formed first, 32 tokens per MFMA tile (the r heads of a token share its index
 // query, so they are computed once per token), and kept in LDS in place of the
-// index keys.  Passes of 4 waves x 32 (token, head) rows then recompute
-// S^T = K Q^T on 32x32 MFMA tiles.  The r heads of a token sit in r adjacent
-// lanes; their probabilities are summed by a butterfly that leaves lane hh of
-// the group owning 64 / r of its half's keys, so each logarithm is taken once
-// per key, not once per head, and each lane reads just those keys' index scores.
+// index keys.  Passes of 4 waves x 32 (token, head) rows then recompute the
+// main scores on 32x32 MFMA tiles.  For r >= 8 a pass forms S = Q K^T: a lane
+// holds one key of each key tile and 16 (token, head) rows in its registers,
+// so a token's head sum is in-lane adds plus one swap between the lane halves.
+// For r < 8 it forms S^T = K Q^T: the r heads of a token sit in r adjacent
+// lanes, and their probabilities are summed by a butterfly that leaves lane hh
+// of the group owning 64 / r of its half's keys.  Either way each logarithm is
+// taken once per key, not once per head, and each lane reads just its keys'
+// index scores.
 #include <type_traits>
 
 #include "common.h"
