@@ -119,20 +119,28 @@ def test_index_select_only_matches_oracle():
 
 @gpu
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("topk,cache", [(16, "native"), (16, "fp8"), (32, "native")])
-def test_index_persistent_grid_ragged_every_row(topk, cache):
+@pytest.mark.parametrize("topk,cache,offset", [(16, "native", 0), (16, "fp8", 0), (32, "native", 0),
+                                               (16, "native", 1)])
+def test_index_persistent_grid_ragged_every_row(topk, cache, offset):
     # 8 groups x 32845 rows = 262760 (row, group) pairs: 514 tiles of 512 (k <= 16)
     # or 1027 of 256 (k = 32), the last one holding 104 rows, so each tile is one
     # unit with one key split and the index kernel runs its persistent grid (more
     # tiles than resident workgroups, units handed out in snake order over several
-    # rounds); e4m3 keys take the staged path.  Every row is checked.
+    # rounds); e4m3 keys take the staged path; a selection buffer 4 bytes past a
+    # 16-byte boundary (offset 1) takes the per-entry stores instead of 16-byte
+    # rows.  Every row is checked.
     msa = _msa()
     n = 32768 + 77
     s = synth.Shape(1, n, n, 0, 32, 8, 64, 128, topk, dtype="bf16", cache=cache)
     x, xh = _inputs(s, 11)
     print(f"persistent-grid shape: {s.batch} x {n} rows, {s.groups} groups, k = {topk}, {cache} keys", flush=True)
-    sel = msa.index_select(x["q_idx"], x["k_idx"], s.topk, q_offset=0)
+    shape = (s.batch, s.groups, n, s.topk)
+    buf = torch.full((int(np.prod(shape)) + 4,), -7, dtype=torch.int32, device="cuda")
+    out = buf[offset:offset + int(np.prod(shape))].view(shape)
+    assert (out.data_ptr() % 16 == 0) == (offset == 0)
+    sel = msa.index_select(x["q_idx"], x["k_idx"], s.topk, q_offset=0, sel=out)
     torch.cuda.synchronize()
+    assert int(buf[:offset].ne(-7).sum()) == 0 and int(buf[offset + out.numel():].ne(-7).sum()) == 0
     k_idx = orc.dequantize_e4m3(synth.codes(xh["k_idx"]), 1.0) if cache == "fp8" else synth.as_f64(xh["k_idx"])
     ref = orc.index_select(synth.as_f64(xh["q_idx"]), k_idx, s.topk, 0)
     _check_sel_rows(sel, ref)
